@@ -1,0 +1,35 @@
+"""The oracle: a plain, slow CPU statement of what the AWQ hot path computes.
+
+TEST INFRASTRUCTURE ONLY.  Import it from tests, from the package's smoke check
+and from the bench's CPU-baseline leg; the product path never imports it.
+
+Parity status per function (what pins it is in the tests named here):
+  channel_mean_abs   pinned: exact sums vs math.fsum, constant columns, sign flips
+  scales_for_alpha   pinned: alpha = 0, a = 0, powers of two, monotonicity
+  quantize_groups    pinned: brute-force nearest code, error bound, hand-worked groups,
+                     power-of-two scale covariance, code ranges
+  dequantize / effective_weight / weight_error
+                     pinned: lossless on-grid construction, scaling invariance
+  output_mse / output_mse_gram
+                     pinned: Gram identity = direct form, brute-force loops, zero loss
+  search             pinned: alpha = 0 is round-to-nearest, L(alpha*) <= L(0),
+                     forced tie, known-answer construction
+  gemm               pinned: brute-force loops, one-hot inputs, codes = zeros
+"""
+from .awq_oracle import (  # noqa: F401
+    SCALE_FLOOR,
+    alpha_grid,
+    channel_mean_abs,
+    scales_for_alpha,
+    scale_weights,
+    quantize_groups,
+    dequantize,
+    effective_weight,
+    weight_error,
+    output_mse,
+    gram,
+    output_mse_gram,
+    quantize_at,
+    search,
+    gemm,
+)

@@ -1,0 +1,311 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test fixes one function by a closed form, a brute-force search over a tiny
+input, an invariant of the mathematics, or a group worked out by hand.  A
+plausible mistake in the oracle (a dropped term, a wrong sign or axis, /16
+instead of /15, floor instead of round-half-even, a transposed operand) fails
+at least one of them.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gen import activations_fp16, normal_fp16
+
+
+def F(x):
+    return Fraction(float(x))
+
+
+# ----------------------------------------------------------------- channel stats
+def test_mean_abs_equals_exact_sum_over_rows():
+    g = np.random.default_rng(1)
+    # fp16 values spanning subnormals to large magnitudes, both signs
+    mag = np.exp2(g.integers(-24, 15, size=(37, 16))).astype(np.float64)
+    X = (g.choice([-1.0, 1.0], size=mag.shape) * mag * g.uniform(1, 2, size=mag.shape)).astype(np.float16)
+    a = O.channel_mean_abs(X)
+    for k in range(X.shape[1]):
+        exact = math.fsum(abs(float(v)) for v in X[:, k])  # correctly rounded sum
+        assert a[k] == exact / X.shape[0]
+
+
+def test_mean_abs_constant_magnitude_and_signs():
+    M, K = 64, 8
+    g = np.random.default_rng(2)
+    c = np.array([0.0, 2.0 ** -24, 0.5, 1.0, 3.0, 4.0, 1000.0, 65504.0])
+    X = (g.choice([-1.0, 1.0], size=(M, K)) * c[None, :]).astype(np.float16)
+    assert np.array_equal(O.channel_mean_abs(X), c)
+
+
+# ----------------------------------------------------------------- s(alpha)
+def test_scales_closed_forms():
+    a = np.array([0.0, 1.0, 4.0, 16.0, 0.25, 2.0 ** 20, 3.0])
+    assert np.array_equal(O.scales_for_alpha(a, 0.0), np.ones(7, np.float32))
+    s = O.scales_for_alpha(a, 0.5)
+    assert s[0] == 1.0                      # a = 0 -> s = 1
+    assert list(s[1:6]) == [1.0, 2.0, 4.0, 0.5, 1024.0]
+    assert s[6] == np.float32(math.sqrt(3.0))
+    s25 = O.scales_for_alpha(np.array([16.0, 2.0 ** -8]), 0.25)
+    assert list(s25) == [2.0, 0.25]
+
+
+def test_scales_monotone_in_magnitude():
+    a = np.sort(np.random.default_rng(3).uniform(1e-3, 1e3, 500))
+    for al in (0.05, 0.5, 0.95):
+        s = O.scales_for_alpha(a, al)
+        assert np.all(np.diff(s) >= 0)
+        assert np.all(np.abs(s.astype(np.float64) - a ** np.float64(np.float32(al))) <= 2.0 ** -24 * s)
+
+
+def test_alpha_grid():
+    g = O.alpha_grid(20)
+    assert len(g) == 20 and g[0] == 0.0 and g[10] == 0.5 and g[19] < 1.0
+    assert np.all(np.diff(g) > 0)
+
+
+# ----------------------------------------------------------------- quantizer
+def _hand_group(values, fill):
+    v = np.full(128, fill, dtype=np.float32)
+    v[: len(values)] = np.array(values, dtype=np.float32)
+    return v[None, :]
+
+
+def test_quantizer_hand_worked_mixed_sign_group():
+    # lo = -1.5, hi = 6.0: step = 7.5 / 15 = 0.5 exactly, fp16 keeps it; z = rint(1.5 / 0.5) = 3.
+    # q = rint(2 v) + 3, with halves going to the even neighbour:
+    #  -1.5 -> -3 -> 0      6.0 -> 12 -> 15     0.25 -> 0.5 -> 0 -> 3    0.75 -> 1.5 -> 2 -> 5
+    #  1.25 -> 2.5 -> 2 -> 5   -0.25 -> -0.5 -> 0 -> 3   -0.75 -> -1.5 -> -2 -> 1
+    #  5.9 -> 11.8 -> 12 -> 15   0.0 -> 3   fill 1.0 -> 2 -> 5
+    V = _hand_group([-1.5, 6.0, 0.25, 0.75, 1.25, -0.25, -0.75, 5.9, 0.0], 1.0)
+    q, z, sc = O.quantize_groups(V)
+    assert sc[0, 0] == np.float16(0.5) and z[0, 0] == 3
+    assert list(q[0, :9]) == [0, 15, 3, 5, 5, 3, 1, 15, 3]
+    assert np.all(q[0, 9:] == 5)
+
+
+def test_quantizer_hand_worked_positive_group_fp16_step():
+    # lo = min(0, 1) = 0, hi = 3: step = fp32(0.2); the nearest fp16 is 1638 * 2**-13
+    # = 0.199951171875 (0.2 / 2**-13 = 1638.4).  z = 0.  q = rint(v / 0.19995...):
+    # 1 -> 5.0012 -> 5, 2 -> 10.0024 -> 10, 3 -> 15.0037 -> 15, 2.9 -> 14.5035 -> 15.
+    V = _hand_group([1.0, 2.0, 3.0, 2.9], 1.0)
+    q, z, sc = O.quantize_groups(V)
+    assert float(sc[0, 0]) == 1638 * 2.0 ** -13 and z[0, 0] == 0
+    assert list(q[0, :4]) == [5, 10, 15, 15]
+
+
+def test_quantizer_hand_worked_negative_and_zero_groups():
+    # all-negative: lo = -3, hi = 0, same step 0.19995...; z = rint(15.0037) = 15;
+    # -3 -> rint(-15.0037) + 15 = 0, -1.5 -> rint(-7.5018) + 15 = -8 + 15 = 7.
+    V = _hand_group([-3.0, -1.5], -3.0)
+    q, z, sc = O.quantize_groups(V)
+    assert z[0, 0] == 15 and list(q[0, :2]) == [0, 7]
+    # all-zero group: the step floors at 2**-14 (smallest normal fp16), z = 0, q = 0
+    q, z, sc = O.quantize_groups(np.zeros((1, 128), np.float32))
+    assert float(sc[0, 0]) == 2.0 ** -14 and z[0, 0] == 0 and np.all(q == 0)
+
+
+def _fp16_neighbours(x16):
+    up = np.nextafter(x16, np.float16(np.inf))
+    dn = np.nextafter(x16, np.float16(-np.inf))
+    return dn, up
+
+
+@pytest.mark.parametrize("group", [8, 16, 128])
+def test_quantizer_brute_force_nearest(group):
+    g = np.random.default_rng(10 + group)
+    N, K = 6, group * 3
+    V = (g.standard_normal((N, K)) * g.choice([0.01, 1.0, 50.0], size=(N, 1))).astype(np.float32)
+    V[0, :group] = np.abs(V[0, :group])            # a one-signed group
+    V[1, group:2 * group] = -np.abs(V[1, group:2 * group])
+    q, z, sc16 = O.quantize_groups(V, group)
+    for n in range(N):
+        for j in range(K // group):
+            vs = V[n, j * group:(j + 1) * group]
+            lo = min(0.0, float(vs.min()))
+            hi = max(0.0, float(vs.max()))
+            step = max(F(np.float32(np.float32(hi) - np.float32(lo))) / 15, F(2.0 ** -14))
+            sc = F(sc16[n, j])
+            # sc is the fp16 nearest to the float32 step (ties to even mantissa)
+            dn, up = _fp16_neighbours(sc16[n, j])
+            d0 = abs(sc - step)
+            assert d0 <= abs(F(dn) - step) and d0 <= abs(F(up) - step)
+            # z is the nearest integer in [0, 15] to -lo / sc (slack: one fp32 rounding)
+            t = F(-lo) / sc
+            dz = [abs(t - c) for c in range(16)]
+            assert dz[z[n, j]] <= min(dz) + Fraction(1, 2 ** 19)
+            # every code is a nearest grid point (q - z) * sc over q in [0, 15]
+            for i, v in enumerate(vs):
+                d = [abs(F(v) - (c - int(z[n, j])) * sc) for c in range(16)]
+                assert d[q[n, j * group + i]] <= min(d) + sc / 2 ** 19
+
+
+def test_quantizer_error_bound_and_ranges():
+    W = normal_fp16((64, 1024), 0.02, seed=11)
+    a = O.channel_mean_abs(activations_fp16(64, 1024, seed=12))
+    for al in (0.0, 0.35, 0.9):
+        q, z, sc16, s = O.quantize_at(W, a, al)
+        V = O.scale_weights(W, s).astype(np.float64)
+        assert q.max() <= 15 and z.max() <= 15
+        assert np.all(np.isfinite(sc16.astype(np.float32))) and np.all(sc16 > 0)
+        Wh = O.dequantize(q, z, sc16)
+        scf = np.repeat(sc16.astype(np.float64), 128, axis=1)
+        zz = np.repeat(z.astype(np.float64), 128, axis=1)
+        unclamped = (np.rint(V / scf) + zz >= 0) & (np.rint(V / scf) + zz <= 15)
+        err = np.abs(V - Wh)
+        assert np.all(err[unclamped] <= scf[unclamped] * (0.5 + 2.0 ** -20))
+        # clamped elements can only exist because fp16 rounding shrank the step
+        assert np.all(err <= scf * (0.5 + 16 * 2.0 ** -11))
+
+
+def test_quantizer_power_of_two_covariance():
+    V = (np.random.default_rng(13).standard_normal((8, 512)) * 0.3).astype(np.float32)
+    q0, z0, s0 = O.quantize_groups(V)
+    for e in (-3, 2, 5):
+        q1, z1, s1 = O.quantize_groups(V * np.float32(2.0 ** e))
+        assert np.array_equal(q0, q1) and np.array_equal(z0, z1)
+        assert np.array_equal(s1.astype(np.float64), s0.astype(np.float64) * 2.0 ** e)
+
+
+# ----------------------------------------------------------------- a lossless construction
+def _on_grid_layer(N=8, K=256, M=16, seed=20):
+    """W and X for which quantization at alpha = 0.5 is exact.
+
+    |X[:, k]| = 4**e_k (random signs) so a_k = 4**e_k and s_k(0.5) = 2**e_k exactly.
+    Per group the scaled weights V = (c - z0) * 2**-6 with codes c in [0, 15] that hit
+    both 0 and 15, and 0 <= z0 <= 15: the range is exactly 15 * 2**-6 and contains 0, so
+    the quantizer must return step 2**-6, zero z0 and codes c.  W = V / s is exact fp16.
+    """
+    g = np.random.default_rng(seed)
+    e = g.integers(-1, 2, size=K)
+    X = (g.choice([-1.0, 1.0], size=(M, K)) * (4.0 ** e)[None, :]).astype(np.float16)
+    c = g.integers(0, 16, size=(N, K))
+    c[:, 0::128] = 0
+    c[:, 1::128] = 15
+    z0 = g.integers(0, 16, size=(N, K // 128))
+    V = (c - np.repeat(z0, 128, axis=1)) * 2.0 ** -6
+    W = (V / 2.0 ** e[None, :]).astype(np.float16)
+    assert np.array_equal(W.astype(np.float64) * 2.0 ** e[None, :], V)
+    return W, X, c, z0
+
+
+def test_lossless_construction_dequantizes_exactly():
+    W, X, c, z0 = _on_grid_layer()
+    a = O.channel_mean_abs(X)
+    q, z, sc16, s = O.quantize_at(W, a, 0.5)
+    assert np.array_equal(q, c) and np.array_equal(z, z0) and np.all(sc16 == np.float16(2.0 ** -6))
+    assert np.array_equal(O.effective_weight(q, z, sc16, s), W.astype(np.float64))
+    assert O.output_mse(X, O.weight_error(W, q, z, sc16, s)) == 0.0
+
+
+def test_search_known_answer():
+    W, X, _, _ = _on_grid_layer()
+    r = O.search(W, X)
+    assert r["alpha_index"] == 10 and r["losses"][10] == 0.0
+    assert np.all(np.delete(r["losses"], 10) > 0)
+
+
+def test_scaling_invariance_fp64():
+    # (W diag(s)) (diag(1/s) x) = W x: the effective weight divides by s along the input axis.
+    g = np.random.default_rng(21)
+    W = normal_fp16((32, 512), 0.02, seed=22)
+    s = g.uniform(0.1, 30.0, 512).astype(np.float32)
+    q, z, sc16 = O.quantize_groups(O.scale_weights(W, s))
+    x = g.standard_normal((5, 512))
+    y1 = x @ O.effective_weight(q, z, sc16, s).T
+    y2 = (x / s.astype(np.float64)[None, :]) @ O.dequantize(q, z, sc16).T
+    assert np.max(np.abs(y1 - y2)) <= 1e-12 * np.max(np.abs(y1))
+    Wl, Xl, _, _ = _on_grid_layer()
+    ql, zl, scl, sl = O.quantize_at(Wl, O.channel_mean_abs(Xl), 0.5)
+    xl = g.standard_normal((3, Wl.shape[1]))
+    assert np.max(np.abs(xl @ O.effective_weight(ql, zl, scl, sl).T - xl @ Wl.astype(np.float64).T)) <= \
+        1e-12 * np.max(np.abs(xl @ Wl.astype(np.float64).T))
+
+
+# ----------------------------------------------------------------- loss
+def test_loss_brute_force_loops():
+    g = np.random.default_rng(30)
+    M, K, N = 3, 8, 2
+    X = g.standard_normal((M, K)).astype(np.float16)
+    E = g.standard_normal((N, K)) * 1e-3
+    ref = math.fsum(math.fsum(float(X[t, k]) * E[n, k] for k in range(K)) ** 2
+                    for t in range(M) for n in range(N)) / (M * N)
+    assert abs(O.output_mse(X, E) - ref) <= 1e-12 * ref
+
+
+def test_loss_gram_identity():
+    X = activations_fp16(300, 256, seed=31)
+    E = np.random.default_rng(32).standard_normal((40, 256)) * 1e-3
+    d = O.output_mse(X, E)
+    gm = O.output_mse_gram(O.gram(X), E, 300)
+    assert abs(d - gm) <= 1e-10 * d
+
+
+# ----------------------------------------------------------------- search
+def test_alpha_zero_is_round_to_nearest():
+    W = normal_fp16((64, 512), 0.02, seed=40)
+    X = activations_fp16(64, 512, seed=41)
+    q0, z0, sc0, s0 = O.quantize_at(W, O.channel_mean_abs(X), 0.0)
+    qr, zr, scr = O.quantize_groups(W.astype(np.float32))
+    assert np.all(s0 == 1.0)
+    assert np.array_equal(q0, qr) and np.array_equal(z0, zr) and np.array_equal(sc0, scr)
+    r = O.search(W, X)
+    assert r["losses"][0] == O.output_mse(X, O.weight_error(W, qr, zr, scr, s0))
+
+
+def test_search_never_worse_than_round_to_nearest():
+    W = normal_fp16((512, 512), 0.02, seed=1001)
+    X = activations_fp16(64, 512, seed=1002)
+    r = O.search(W, X)
+    assert r["losses"][r["alpha_index"]] <= r["losses"][0]
+    assert r["losses"][r["alpha_index"]] == r["losses"].min()
+    assert r["alpha_index"] == int(np.argmin(r["losses"]))
+
+
+def test_search_forced_tie_power_of_two():
+    # |x| = 4 everywhere -> a = 4, s(alpha_10 = 0.5) = 2: scaling by 2 is exact, so the codes
+    # and the loss at alpha_10 equal those at alpha_0 exactly.
+    g = np.random.default_rng(50)
+    X = (g.choice([-4.0, 4.0], size=(32, 256))).astype(np.float16)
+    W = normal_fp16((16, 256), 0.02, seed=51)
+    r = O.search(W, X)
+    assert r["losses"][10] == r["losses"][0]
+    a = O.channel_mean_abs(X)
+    qa, za, _, _ = O.quantize_at(W, a, 0.0)
+    qb, zb, _, _ = O.quantize_at(W, a, 0.5)
+    assert np.array_equal(qa, qb) and np.array_equal(za, zb)
+    assert r["alpha_index"] != 10  # the first of the tied pair wins, or a strictly better alpha
+
+
+# ----------------------------------------------------------------- product
+def test_gemm_brute_force_loops():
+    g = np.random.default_rng(60)
+    N, K, M = 3, 256, 2
+    q = g.integers(0, 16, size=(N, K)).astype(np.uint8)
+    z = g.integers(0, 16, size=(N, K // 128)).astype(np.uint8)
+    sc = g.uniform(1e-3, 1e-1, size=(N, K // 128)).astype(np.float16)
+    x = g.standard_normal((M, K)).astype(np.float16)
+    y = O.gemm(x, q, z, sc)
+    for m in range(M):
+        for n in range(N):
+            ref = math.fsum(float(x[m, k]) * (int(q[n, k]) - int(z[n, k // 128])) * float(sc[n, k // 128])
+                            for k in range(K))
+            assert abs(y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_gemm_one_hot_and_zero_codes():
+    g = np.random.default_rng(61)
+    N, K = 4, 384
+    q = g.integers(0, 16, size=(N, K)).astype(np.uint8)
+    z = g.integers(0, 16, size=(N, K // 128)).astype(np.uint8)
+    sc = g.uniform(1e-3, 1e-1, size=(N, K // 128)).astype(np.float16)
+    for k in (0, 1, 127, 128, 200, 383):
+        x = np.zeros((1, K), np.float16)
+        x[0, k] = 1.0
+        y = O.gemm(x, q, z, sc)[0]
+        for n in range(N):
+            assert y[n] == (int(q[n, k]) - int(z[n, k // 128])) * float(sc[n, k // 128])
+    qz = np.repeat(z, 128, axis=1)
+    assert np.all(O.gemm(g.standard_normal((2, K)).astype(np.float16), qz, z, sc) == 0.0)
