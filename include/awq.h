@@ -1,0 +1,194 @@
+/*
+ * libawq -- AWQ scale search, group-wise int4 weight quantizer and W4A16
+ * product, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed follows these pages (cited by title and paragraph/section):
+ *   [summary]  "AWQ: Activation-aware Weight Quantization for On-Device LLM
+ *              Compression and Acceleration", fdeinterviews.com/papers/awq,
+ *              paragraphs 1..10.
+ *   [abstract] OpenAlex record of the GetMobile article of that title, abstract.
+ *   [profile]  "AWQ: Activation-aware Weight Quantization for On-Device LLM
+ *              Compression", aiexpertsdirectory.org, "Execution Profile &
+ *              Computation Stack".
+ *
+ * Notation.  A linear layer maps an input row x[K] to y[N] = W x, with W an
+ * fp16 [N][K] row-major matrix (row n = output channel, like a torch Linear
+ * weight).  K is the input-channel (contraction) axis.  Calibration data X is
+ * fp16 [M][K] row-major.  Weights are quantized to 4-bit codes in groups of
+ * `group` consecutive input channels of one output row.
+ *
+ * Memory.  Every pointer argument documented "device" is device memory of the
+ * current HIP device; "host" pointers are ordinary host memory.  The caller
+ * owns all buffers; the library allocates nothing and keeps no pointer after a
+ * call returns.  Device pointers must be 16-byte aligned.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  All device work is enqueued on it in order and the calls return
+ * without waiting: outputs are valid once the stream has reached that point.
+ * No call synchronises the host with the device.
+ *
+ * Errors.  Every entry point returns an awq_status.  Argument checks happen
+ * before anything is enqueued: on any status other than AWQ_OK (and
+ * AWQ_ERROR_DEVICE) nothing was launched and no output was touched.
+ * awq_last_error() returns a thread-local message describing the last failure
+ * of the calling thread.  No call aborts or throws across this interface.
+ * Non-finite values in W, X or x are outside the contract: they do not crash
+ * the library, but the outputs are then unspecified.
+ *
+ * Thread safety.  Calls are reentrant; calls on different streams may overlap
+ * when they do not share output or workspace buffers.
+ */
+#ifndef AWQ_H_
+#define AWQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum awq_status {
+  AWQ_OK = 0,
+  AWQ_ERROR_INVALID_VALUE = 1,         /* null pointer, bad size, bad group, bad alpha */
+  AWQ_ERROR_MISALIGNED = 2,            /* a device pointer not 16-byte aligned */
+  AWQ_ERROR_WORKSPACE_TOO_SMALL = 3,   /* workspace_bytes below the size query */
+  AWQ_ERROR_DEVICE = 4,                /* a HIP call or kernel launch failed */
+  AWQ_ERROR_NOT_IMPLEMENTED = 5
+} awq_status;
+
+/* Supported quantization: 4-bit codes, group of 128 input channels. */
+#define AWQ_BITS 4
+#define AWQ_GROUP 128
+/* Most alpha values one search accepts. */
+#define AWQ_MAX_ALPHAS 64
+/* Most calibration rows: keeps every per-channel sum of |x| exact in 64 bits. */
+#define AWQ_MAX_CALIB_ROWS (1LL << 23)
+
+/* ------------------------------------------------------------------------
+ * Packed weight format (the "SIMD-aware weight packing" of [abstract],
+ * designed here for 64-wide gfx950 waves).  For an [N][K] layer, group g:
+ *
+ *   packed  uint32 [N][K/8]      word w of row n holds the codes of input
+ *                                channels 8w..8w+7.  Code of channel 8w+i sits
+ *                                in nibble p(i) = 4*(i%2) + i/2, i.e. bits
+ *                                4p..4p+3 hold, for p = 0..7, the codes of
+ *                                channels 8w+{0,2,4,6,1,3,5,7}.  Masking a word
+ *                                shifted right by 4j with 0x000F000F gives the
+ *                                codes of channels 8w+2j and 8w+2j+1 in the two
+ *                                16-bit halves.
+ *   scales  fp16   [N][K/g]      step of group j of row n.
+ *   zeros   uint8  [N][ceil(K/g/2)]  zero point of group j of row n in byte
+ *                                j/2, low nibble for even j, high nibble for
+ *                                odd j (unused high nibble = 0).
+ *
+ * Dequantized weight: w_hat[n][k] = (code[n][k] - zero[n][k/g]) * scale[n][k/g].
+ * At g = 128 this is 4 + 2.5*8/128 = 4.156 bits per weight.
+ * ------------------------------------------------------------------------ */
+size_t awq_packed_bytes(int64_t N, int64_t K);
+size_t awq_scales_bytes(int64_t N, int64_t K, int32_t group);
+size_t awq_zeros_bytes(int64_t N, int64_t K, int32_t group);
+
+/* Workspace bytes awq_quantize needs for these sizes (pure host function). */
+size_t awq_quantize_workspace_bytes(int64_t N, int64_t K, int64_t M, int32_t group, int32_t n_alpha);
+
+/*
+ * awq_channel_mean_abs -- activation statistics of the calibration set
+ * ([summary] paragraphs 3 and 7: the scale of a channel comes from its
+ * average activation magnitude; only activation statistics are collected).
+ *
+ *   X  device fp16 [M][K]   calibration rows
+ *   a  device fp64 [K]      out: a[k] = (1/M) * sum_t |X[t][k]|
+ *
+ * The sum is exact (every fp16 |x| is a multiple of 2^-24 and the sum is kept
+ * as a 64-bit count of 2^-24); only the final division rounds, so the result
+ * does not depend on the order of the rows.  a doubles as the accumulator.
+ * Requires 1 <= M <= AWQ_MAX_CALIB_ROWS, K >= 8, K % 8 == 0.
+ */
+int awq_channel_mean_abs(const void* X, int64_t M, int64_t K, double* a, void* stream);
+
+/*
+ * awq_pack -- quantize W * diag(s) group-wise to int4 and write the packed
+ * format above.  With s == NULL the weights are quantized unscaled (plain
+ * round-to-nearest, the baseline of [summary] paragraph 4).
+ *
+ *   W       device fp16 [N][K]
+ *   s       device fp32 [K] or NULL   per-input-channel factor
+ *   packed, scales, zeros   device outputs, sizes from the queries above
+ *
+ * Per group (float32 arithmetic, round-to-nearest-even everywhere):
+ *   v = w * s;  lo = min(0, min v);  hi = max(0, max v)
+ *   step = max((hi - lo) / 15, 2^-14);  scale = fp16(step)
+ *   zero = clamp(rint(-lo / scale), 0, 15);  code = clamp(rint(v / scale) + zero, 0, 15)
+ * Requires N >= 1, K % group == 0, group == AWQ_GROUP.
+ */
+int awq_pack(const void* W, const float* s, int64_t N, int64_t K, int32_t group,
+             void* packed, void* scales, void* zeros, void* stream);
+
+/*
+ * awq_quantize -- the activation-aware scale search of [summary] paragraph 3
+ * (also [abstract]) for one linear layer, then quantize-and-pack at the best
+ * alpha.
+ *
+ *   W          device fp16 [N][K]      layer weight
+ *   X          device fp16 [M][K]      calibration rows entering the layer
+ *   alphas     host fp32 [n_alpha]     grid, each finite and >= 0
+ *   packed, scales, zeros              device outputs (format above) at alpha*
+ *   s          device fp32 [K]         out: s at alpha*
+ *   best_alpha device int32 [1]        out: index of alpha* in `alphas`
+ *   loss       device fp64 [n_alpha] or NULL   out: L(alpha_i)
+ *   workspace  device, workspace_bytes >= awq_quantize_workspace_bytes(...)
+ *
+ * For each alpha_i: a = awq_channel_mean_abs(X); s_k = fp32(a_k ^ alpha_i)
+ * evaluated in fp64 (s_k = 1 where a_k = 0); quantize W diag(s) as awq_pack;
+ * E = w_hat / s - w in fp64; L_i = ||X E^T||_F^2 / (M N), the mean squared
+ * change of the layer's output on the calibration rows, evaluated as
+ * sum_n E_n G E_n^T / (M N) with G = X^T X.  alpha* is the first index with
+ * the smallest L.  The caller then feeds x / s (rounded to fp16) to awq_gemm.
+ * Requires 1 <= n_alpha <= AWQ_MAX_ALPHAS, 1 <= M <= AWQ_MAX_CALIB_ROWS,
+ * group == AWQ_GROUP, K % group == 0.
+ */
+int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, int32_t group,
+                 const float* alphas, int32_t n_alpha,
+                 void* packed, void* scales, void* zeros, float* s,
+                 int32_t* best_alpha, double* loss,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * awq_gemm -- the W4A16 product that 4-bit decoding runs on ([summary]
+ * paragraphs 1 and 6: decoding is memory-bound, 4-bit weights cut its
+ * traffic about 4x; [profile]: W4A16 GEMM kernels).  The int4 weights are
+ * dequantized on the fly in registers ([abstract]).
+ *
+ *   x       device fp16 [M][K]  activations (already divided by s)
+ *   packed, scales, zeros       device, format above
+ *   y       device fp16 [M][N]  out: y[m][n] = sum_k x[m][k] * w_hat[n][k]
+ *
+ * Accumulation is fp32; y is rounded to fp16 once.  M <= 8 runs the GEMV
+ * kernel ((code - zero) exact in fp16, scale applied per group in fp32);
+ * larger M runs the MFMA GEMM (w_hat rounded to fp16 before the matrix core).
+ * Requires M >= 1, N >= 1, K % group == 0, group == AWQ_GROUP.
+ */
+int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+             int64_t M, int64_t N, int64_t K, int32_t group, void* stream);
+
+/*
+ * awq_unpack -- logical view of the packed format, for checking it.
+ *   codes     device uint8 [N][K]     out: code of every weight
+ *   zeros_u8  device uint8 [N][K/g]   out: zero point of every group
+ */
+int awq_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, int32_t group,
+               uint8_t* codes, uint8_t* zeros_u8, void* stream);
+
+/* Message for a status code; message for the calling thread's last failure. */
+const char* awq_status_string(int status);
+const char* awq_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int awq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_H_ */

@@ -1,0 +1,158 @@
+"""The C ABI on the host: every declared symbol is exported, size queries match the
+documented format (and the pages' memory figures), and bad arguments are refused
+with the documented status before anything is launched (no GPU needed)."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import weight_only_quantization_gemm_amd as awq
+from weight_only_quantization_gemm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+OK, INVALID, MISALIGNED, WS_SMALL = 0, 1, 2, 3
+FAKE = 0x10000          # aligned, non-null; never dereferenced because validation fails first
+FAKE_MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("awq_quantize", "awq_gemm", "awq_pack", "awq_unpack", "awq_channel_mean_abs"):
+        assert n in names
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_version_and_status_strings():
+    assert awq.awq_version() >= 10000
+    assert awq.awq_status_string(0) == "AWQ_OK"
+    assert awq.awq_status_string(3) == "AWQ_ERROR_WORKSPACE_TOO_SMALL"
+    assert awq.awq_status_string(99) == "AWQ_UNKNOWN_STATUS"
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 384), (4096, 4096), (4096, 11008), (28672, 8192)])
+def test_size_queries(N, K):
+    G = K // 128
+    assert awq.awq_packed_bytes(N, K) == N * K // 2
+    assert awq.awq_scales_bytes(N, K) == 2 * N * G
+    assert awq.awq_zeros_bytes(N, K) == N * ((G + 1) // 2)
+    assert awq.awq_packed_bytes(N, K + 4) == 0  # K % 8 != 0
+    assert awq.awq_scales_bytes(N, K + 8) == 0  # K % group != 0
+
+
+def test_byte_accounting_matches_page_figures():
+    figs = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
+    N, K = 4096, 4096
+    fp16_bytes = 2 * N * K
+    codes = awq.awq_packed_bytes(N, K)
+    meta = awq.awq_scales_bytes(N, K) + awq.awq_zeros_bytes(N, K)
+    # the codes alone are exactly a quarter of fp16 weights; with group metadata
+    # 4.156 bits per weight, still "about a quarter" (within 5%)
+    assert codes / fp16_bytes == figs["weight_memory_fraction_4bit"]["value"]
+    assert abs((codes + meta) / fp16_bytes - 0.25) / 0.25 < 0.05
+    assert abs(8 * (codes + meta) / (N * K) - 4.15625) < 1e-12
+    assert abs(fp16_bytes / (codes + meta) - figs["decode_traffic_reduction"]["value"]) / 4.0 < 0.05
+
+
+def test_workspace_query():
+    assert awq.awq_quantize_workspace_bytes(512, 512, 64, 128, 20) > 0
+    assert awq.awq_quantize_workspace_bytes(512, 500, 64, 128, 20) == 0
+    assert awq.awq_quantize_workspace_bytes(512, 512, 64, 64, 20) == 0
+    assert awq.awq_quantize_workspace_bytes(512, 512, 64, 128, 65) == 0
+    big = awq.awq_quantize_workspace_bytes(4096, 11008, 65536, 128, 20)
+    assert big >= 8 * 11008 * 11008 + 2 * 11008 * 65536 + 8 * 4096 * 11008
+
+
+def _lib_():
+    return _lib.load()
+
+
+def test_gemm_argument_errors_before_launch():
+    lib = _lib_()
+    f = lib.awq_gemm
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, None) == INVALID
+    assert "NULL" in awq.awq_last_error()
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 128, None) == INVALID    # K % group
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 64, None) == INVALID     # group
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 128, 128, None) == INVALID    # M
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 128, 128, None) == INVALID     # N
+    assert f(FAKE_MISALIGNED, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, None) == MISALIGNED
+
+
+def test_pack_and_unpack_argument_errors_before_launch():
+    lib = _lib_()
+    assert lib.awq_pack(None, None, 4, 128, 128, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.awq_pack(FAKE, None, 4, 130, 128, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.awq_pack(FAKE, FAKE_MISALIGNED, 4, 128, 128, FAKE, FAKE, FAKE, None) == MISALIGNED
+    assert lib.awq_unpack(FAKE, FAKE, 4, 128, 32, FAKE, FAKE, None) == INVALID
+    assert lib.awq_channel_mean_abs(FAKE, 0, 128, FAKE, None) == INVALID
+    assert lib.awq_channel_mean_abs(FAKE, (1 << 23) + 1, 128, FAKE, None) == INVALID
+    assert lib.awq_channel_mean_abs(FAKE, 4, 12, FAKE, None) == INVALID
+    assert lib.awq_channel_mean_abs(FAKE_MISALIGNED, 4, 16, FAKE, None) == MISALIGNED
+
+
+def test_quantize_argument_errors_before_launch():
+    lib = _lib_()
+    q = lib.awq_quantize
+    al = np.arange(20, dtype=np.float32) / np.float32(20)
+    ws = awq.awq_quantize_workspace_bytes(64, 256, 32, 128, 20)
+    args = lambda **kw: dict(dict(W=FAKE, X=FAKE, N=64, K=256, M=32, g=128, al=al.ctypes.data, na=20,
+                                   packed=FAKE, scales=FAKE, zeros=FAKE, s=FAKE, best=FAKE, loss=None,
+                                   ws=FAKE, wsb=ws, st=None), **kw)
+    call = lambda d: q(*d.values())
+    assert call(args(wsb=ws - 1)) == WS_SMALL
+    assert "workspace" in awq.awq_last_error()
+    assert call(args(na=0)) == INVALID
+    assert call(args(na=65)) == INVALID
+    bad = al.copy()
+    bad[3] = np.nan
+    assert call(args(al=bad.ctypes.data)) == INVALID
+    bad[3] = -0.5
+    assert call(args(al=bad.ctypes.data)) == INVALID
+    assert call(args(M=0)) == INVALID
+    assert call(args(X=None)) == INVALID
+    assert call(args(ws=FAKE_MISALIGNED)) == MISALIGNED
+    assert call(args(K=200)) == INVALID
+
+
+def test_binding_refuses_cpu_tensors():
+    W = torch.zeros((8, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        awq.awq_pack(W)
+    with pytest.raises(ValueError, match="GPU"):
+        awq.awq_gemm(torch.zeros((1, 128), dtype=torch.float16), torch.zeros((8, 16), dtype=torch.int32),
+                     torch.zeros((8, 1), dtype=torch.float16), torch.zeros((8, 1), dtype=torch.uint8))
+
+
+def test_host_layout_codec_roundtrip():
+    from layout import decode_codes, decode_zeros, encode
+    g = np.random.default_rng(0)
+    for N, K in ((3, 128), (5, 384), (2, 1024)):
+        codes = g.integers(0, 16, size=(N, K)).astype(np.uint8)
+        zeros = g.integers(0, 16, size=(N, K // 128)).astype(np.uint8)
+        p, zb = encode(codes, zeros)
+        assert np.array_equal(decode_codes(p, K), codes)
+        assert np.array_equal(decode_zeros(zb, K // 128), zeros)
+    # word layout: channel 8w+1 lives in nibble 4, channel 8w+2 in nibble 1
+    c = np.zeros((1, 128), np.uint8)
+    c[0, 1] = 0xA
+    c[0, 2] = 0x5
+    p, _ = encode(c, np.zeros((1, 1), np.uint8))
+    assert int(p.view(np.uint32)[0, 0]) == (0xA << 16) | (0x5 << 4)

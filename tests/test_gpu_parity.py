@@ -1,0 +1,279 @@
+"""GPU parity: every libawq entry point against the CPU oracle on the same seeded inputs.
+
+Bars: codes, zero points, steps, s, channel statistics and the chosen alpha index
+bit-exact (the alpha index up to ties within 1e-6 relative loss); W4A16 outputs
+within relative Frobenius error 1e-3 and max |dy| <= 1e-2 max |y_ref|; search losses
+within 1e-5 relative of the oracle's (the device builds X^T X from fp32 partials of
+256 calibration rows, the oracle in fp64).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_quantization_gemm_amd as awq
+from gen import activations_fp16, normal_fp16, seed_for
+from layout import assert_y_close, decode_codes, decode_zeros, encode
+from test_oracle_pins import _on_grid_layer
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+ALPHAS = awq.default_alpha_grid(20)
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------------ statistics
+@pytest.mark.parametrize("M,K,seed,lognormal", [(64, 512, 1, False), (37, 384, 2, True), (1, 8, 3, False),
+                                                (1000, 4096, 4, True), (513, 11008, 5, True)])
+def test_channel_mean_abs_bit_exact(M, K, seed, lognormal):
+    note(f"channel_mean_abs M={M} K={K}")
+    X = activations_fp16(M, K, seed, lognormal=lognormal)
+    a = host(awq.awq_channel_mean_abs(dev(X)))
+    assert np.array_equal(a, oracle.channel_mean_abs(X))
+
+
+def test_channel_mean_abs_extreme_values():
+    note("channel_mean_abs extremes")
+    g = np.random.default_rng(7)
+    M, K = 700, 64  # spans three 256-row partial sums
+    X = (g.choice([-1.0, 1.0], size=(M, K)) * g.choice([65504.0, 2.0 ** -24, 6.1e-5, 1.0, 0.0], size=(M, K)))
+    X = X.astype(np.float16)
+    a = host(awq.awq_channel_mean_abs(dev(X)))
+    assert np.array_equal(a, oracle.channel_mean_abs(X))
+
+
+# ------------------------------------------------------------------ packer
+def _check_pack(W, s, packed, scales, zeros):
+    N, K = W.shape
+    q, z, sc = oracle.quantize_groups(oracle.scale_weights(W, np.ones(K, np.float32) if s is None else s))
+    assert np.array_equal(decode_codes(host(packed), K), q)
+    assert np.array_equal(decode_zeros(host(zeros), K // 128), z)
+    assert np.array_equal(host(scales).view(np.uint16), sc.view(np.uint16))
+    codes, zz = awq.awq_unpack(packed, zeros, K)
+    assert np.array_equal(host(codes), q) and np.array_equal(host(zz), z)
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 384), (100, 512), (7, 4096), (64, 11008)])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_pack_bit_exact(N, K, scaled):
+    note(f"pack N={N} K={K} scaled={scaled}")
+    W = normal_fp16((N, K), 0.02, seed=100 + N + K)
+    s = None
+    if scaled:
+        s = np.exp(np.random.default_rng(N * K).standard_normal(K) * 1.5).astype(np.float32)
+    packed, scales, zeros = awq.awq_pack(dev(W), None if s is None else dev(s))
+    _check_pack(W, s, packed, scales, zeros)
+
+
+def test_pack_degenerate_groups():
+    note("pack degenerate groups")
+    K = 512
+    W = normal_fp16((6, K), 0.02, seed=55)
+    W[0] = 0                        # all-zero groups: floor step 2^-14
+    W[1] = np.float16(0.125)        # constant positive
+    W[2] = np.float16(-3.0)         # constant negative
+    W[3, :128] = np.float16(60000)  # large magnitudes
+    W[3, 128:256] = np.float16(-60000)
+    W[4] = np.float16(6e-8)         # subnormal fp16 weights
+    packed, scales, zeros = awq.awq_pack(dev(W))
+    _check_pack(W, None, packed, scales, zeros)
+
+
+# ------------------------------------------------------------------ search
+def _check_search(W, X, r, ref, loss_rtol=1e-5):
+    best = int(host(r["best_alpha"])[0])
+    L = ref["losses"]
+    Lg = host(r["loss"])
+    assert L[best] <= (1 + 1e-6) * L.min(), f"alpha index {best} (L={L[best]}) vs oracle {ref['alpha_index']}"
+    nz = L > 0
+    assert np.all(np.abs(Lg[nz] - L[nz]) <= loss_rtol * L[nz]), np.max(np.abs(Lg[nz] - L[nz]) / L[nz])
+    assert np.all(Lg[~nz] == 0.0)
+    q, z, sc, s = oracle.quantize_at(W, ref["a"], ALPHAS[best])
+    s_gpu = host(r["s"])
+    assert np.array_equal(s_gpu, s), f"{np.sum(s_gpu != s)} of {s.size} s values differ"
+    _check_pack(W, s, r["packed"], r["scales"], r["zeros"])
+    return best
+
+
+def test_search_single_layer_512():
+    note("search single_layer_512")
+    W = normal_fp16((512, 512), 0.02, seed=seed_for(1, 1))
+    X = activations_fp16(64, 512, seed=seed_for(1, 2))
+    r = awq.awq_quantize(dev(W), dev(X), ALPHAS)
+    ref = oracle.search(W, X, alphas=ALPHAS)
+    _check_search(W, X, r, ref)
+
+
+@pytest.mark.parametrize("N,K,M,lognormal", [(100, 384, 50, False), (17, 128, 1, False), (96, 640, 300, True)])
+def test_search_ragged(N, K, M, lognormal):
+    note(f"search ragged N={N} K={K} M={M}")
+    W = normal_fp16((N, K), 0.02, seed=N + K)
+    X = activations_fp16(M, K, seed=M + 1, lognormal=lognormal)
+    r = awq.awq_quantize(dev(W), dev(X), ALPHAS)
+    _check_search(W, X, r, oracle.search(W, X, alphas=ALPHAS))
+
+
+def test_search_forced_tie():
+    note("search forced tie")
+    g = np.random.default_rng(50)
+    X = (g.choice([-4.0, 4.0], size=(32, 256))).astype(np.float16)
+    W = normal_fp16((16, 256), 0.02, seed=51)
+    r = awq.awq_quantize(dev(W), dev(X), ALPHAS)
+    ref = oracle.search(W, X, alphas=ALPHAS)
+    best = _check_search(W, X, r, ref)
+    Lg = host(r["loss"])
+    assert Lg[10] == Lg[0] and best != 10
+
+
+def test_search_known_answer():
+    note("search known answer")
+    W, X, c, z0 = _on_grid_layer()
+    r = awq.awq_quantize(dev(W), dev(X), ALPHAS)
+    assert int(host(r["best_alpha"])[0]) == 10
+    Lg = host(r["loss"])
+    assert Lg[10] == 0.0 and np.all(np.delete(Lg, 10) > 0)
+    codes, zz = awq.awq_unpack(r["packed"], r["zeros"], W.shape[1])
+    assert np.array_equal(host(codes), c) and np.array_equal(host(zz), z0)
+
+
+@pytest.mark.parametrize("N,K,M", [(512, 4096, 4096), (256, 11008, 2048)])
+def test_search_llama_shaped(N, K, M):
+    note(f"search llama-shaped N={N} K={K} M={M}")
+    W = normal_fp16((N, K), 0.02, seed=5000 + K)
+    X = activations_fp16(M, K, seed=5001 + K, lognormal=True)
+    r = awq.awq_quantize(dev(W), dev(X), ALPHAS)
+    ref = oracle.search(W, X, alphas=ALPHAS)
+    best = _check_search(W, X, r, ref)
+    note(f"  alpha*={ALPHAS[best]:.2f} L(alpha*)/L(0)={ref['losses'][best] / ref['losses'][0]:.4f}")
+
+
+def test_search_determinism():
+    note("search determinism")
+    W = normal_fp16((256, 512), 0.02, seed=77)
+    X = activations_fp16(300, 512, seed=78)
+    r1 = awq.awq_quantize(dev(W), dev(X), ALPHAS)
+    r2 = awq.awq_quantize(dev(W), dev(X), ALPHAS)
+    for k in ("packed", "scales", "zeros", "s", "best_alpha", "loss"):
+        assert np.array_equal(host(r1[k]).view(np.uint8), host(r2[k]).view(np.uint8)), k
+
+
+# ------------------------------------------------------------------ W4A16 product
+def _random_packed(N, K, seed, sigma=0.02):
+    g = np.random.default_rng(seed)
+    q = g.integers(0, 16, size=(N, K)).astype(np.uint8)
+    z = g.integers(0, 16, size=(N, K // 128)).astype(np.uint8)
+    sc = (np.abs(g.standard_normal((N, K // 128))) * sigma * 0.4 + 1e-4).astype(np.float16)
+    p, zb = encode(q, z)
+    return q, z, sc, dev(p), dev(sc), dev(zb)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 33, 64, 100, 256])
+def test_gemm_parity_ragged(M):
+    note(f"gemm M={M} N=300 K=1024")
+    N, K = 300, 1024
+    q, z, sc, p, scd, zd = _random_packed(N, K, seed=M)
+    x = activations_fp16(M, K, seed=900 + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    assert_y_close(y, oracle.gemm(x, q, z, sc), f"M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 8, 16])
+def test_gemm_one_hot_reproduces_dequantized_column(M):
+    note(f"gemm one-hot M={M}")
+    N, K = 80, 512
+    q, z, sc, p, scd, zd = _random_packed(N, K, seed=31 + M)
+    ks = [0, 1, 7, 8, 127, 128, 300, 511, 2, 129, 255, 256, 383, 384, 400, 510][:M]
+    x = np.zeros((M, K), np.float16)
+    for m, k in enumerate(ks):
+        x[m, k] = 1.0
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    for m, k in enumerate(ks):
+        col = (q[:, k].astype(np.float64) - z[:, k // 128]) * sc[:, k // 128].astype(np.float64)
+        assert np.array_equal(y[m], col.astype(np.float16)), (m, k)
+
+
+@pytest.mark.parametrize("M", [1, 8, 64])
+def test_gemm_codes_equal_zeros_gives_zero(M):
+    note(f"gemm zero codes M={M}")
+    N, K = 64, 256
+    g = np.random.default_rng(5)
+    z = g.integers(0, 16, size=(N, K // 128)).astype(np.uint8)
+    q = np.repeat(z, 128, axis=1)
+    sc = np.full((N, K // 128), 0.01, np.float16)
+    p, zb = encode(q, z)
+    y = host(awq.awq_gemm(dev(activations_fp16(M, K, seed=6)), dev(p), dev(sc), dev(zb)))
+    assert np.all(y == 0)
+
+
+def test_gemm_quantized_layer_end_to_end():
+    """x / s through the packed layer the search produced equals the oracle's product."""
+    note("gemm after search")
+    W = normal_fp16((512, 512), 0.02, seed=seed_for(1, 1))
+    X = activations_fp16(64, 512, seed=seed_for(1, 2))
+    r = awq.awq_quantize(dev(W), dev(X), ALPHAS)
+    best = int(host(r["best_alpha"])[0])
+    q, z, sc, s = oracle.quantize_at(W, oracle.channel_mean_abs(X), ALPHAS[best])
+    for M in (1, 4):
+        x = (activations_fp16(M, 512, seed=seed_for(1, 3 + M)).astype(np.float32) / s).astype(np.float16)
+        y = host(awq.awq_gemm(dev(x), r["packed"], r["scales"], r["zeros"]))
+        assert_y_close(y, oracle.gemm(x, q, z, sc), f"M={M}")
+
+
+_7B = [(4096, 4096), (4096, 11008), (11008, 4096)]
+_70B = [(8192, 10240), (8192, 8192), (8192, 28672), (28672, 8192)]
+
+
+@pytest.mark.parametrize("K,N", _7B)
+def test_gemv_llama2_7b_decode_full(K, N):
+    note(f"7B decode GEMV K={K} N={N}")
+    q, z, sc, p, scd, zd = _random_packed(N, K, seed=K + N)
+    x = activations_fp16(1, K, seed=K)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    assert_y_close(y, oracle.gemm(x, q, z, sc), f"K={K} N={N}")
+
+
+@pytest.mark.parametrize("K,N", _70B)
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_gemm_llama2_70b_sampled_rows(K, N, M):
+    note(f"70B K={K} N={N} M={M}")
+    g = np.random.default_rng(K * 3 + N)
+    q, z, sc, p, scd, zd = _random_packed(N, K, seed=K * 7 + N, sigma=0.015)
+    x = activations_fp16(M, K, seed=K + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    rows = np.sort(g.choice(N, size=384, replace=False))
+    assert_y_close(y[:, rows], oracle.gemm(x, q[rows], z[rows], sc[rows]), f"K={K} N={N} M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 64, 256, 1024])
+def test_batch_sweep_4096x11008(M):
+    note(f"batch sweep M={M}")
+    K, N = 4096, 11008
+    q, z, sc, p, scd, zd = _random_packed(N, K, seed=3)
+    x = activations_fp16(M, K, seed=3000 + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    assert_y_close(y, oracle.gemm(x, q, z, sc), f"M={M}")
+
+
+def test_gemm_determinism():
+    note("gemm determinism")
+    q, z, sc, p, scd, zd = _random_packed(1000, 2048, seed=8)
+    for M in (1, 8, 100):
+        x = dev(activations_fp16(M, 2048, seed=9))
+        a = host(awq.awq_gemm(x, p, scd, zd))
+        b = host(awq.awq_gemm(x, p, scd, zd))
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))

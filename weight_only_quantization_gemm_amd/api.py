@@ -1,0 +1,184 @@
+"""Torch-facing wrappers with the names of the C entry points.
+
+Each wrapper checks dtypes, devices and shapes, allocates outputs with torch on
+the input's device, and calls libawq on torch's current stream of that device.
+All arithmetic happens in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from ._lib import AwqError, check, load
+
+GROUP = 128
+MAX_ALPHAS = 64
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libawq has no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def default_alpha_grid(n: int = 20) -> np.ndarray:
+    """alpha_i = i / n for i = 0..n-1, in float32 (a grid over [0, 1))."""
+    return (np.arange(n, dtype=np.float32) / np.float32(n)).astype(np.float32)
+
+
+# ---------------------------------------------------------------- size queries
+def awq_packed_bytes(N: int, K: int) -> int:
+    return int(load().awq_packed_bytes(N, K))
+
+
+def awq_scales_bytes(N: int, K: int, group: int = GROUP) -> int:
+    return int(load().awq_scales_bytes(N, K, group))
+
+
+def awq_zeros_bytes(N: int, K: int, group: int = GROUP) -> int:
+    return int(load().awq_zeros_bytes(N, K, group))
+
+
+def awq_quantize_workspace_bytes(N: int, K: int, M: int, group: int = GROUP, n_alpha: int = 20) -> int:
+    return int(load().awq_quantize_workspace_bytes(N, K, M, group, n_alpha))
+
+
+def awq_status_string(status: int) -> str:
+    return load().awq_status_string(status).decode()
+
+
+def awq_last_error() -> str:
+    return load().awq_last_error().decode()
+
+
+def awq_version() -> int:
+    return int(load().awq_version())
+
+
+def empty_packed(N: int, K: int, device, group: int = GROUP):
+    """Output buffers of the packed format: packed int32 [N][K/8], scales fp16 [N][K/g],
+    zeros uint8 [N][ceil(K/g/2)]."""
+    G = K // group
+    packed = torch.empty((N, K // 8), dtype=torch.int32, device=device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=device)
+    zeros = torch.empty((N, (G + 1) // 2), dtype=torch.uint8, device=device)
+    return packed, scales, zeros
+
+
+# ---------------------------------------------------------------- entry points
+def awq_channel_mean_abs(X: torch.Tensor) -> torch.Tensor:
+    _need(X, "X", torch.float16, 2)
+    M, K = X.shape
+    a = torch.empty((K,), dtype=torch.float64, device=X.device)
+    with torch.cuda.device(X.device):
+        check(load().awq_channel_mean_abs(X.data_ptr(), M, K, a.data_ptr(), _stream(X.device)))
+    return a
+
+
+def awq_pack(W: torch.Tensor, s: Optional[torch.Tensor] = None, group: int = GROUP):
+    _need(W, "W", torch.float16, 2)
+    N, K = W.shape
+    if s is not None:
+        _need(s, "s", torch.float32, 1)
+        if s.shape[0] != K or s.device != W.device:
+            raise ValueError("s must be float32 [K] on W's device")
+    if K % group:
+        raise ValueError(f"K={K} is not a multiple of group {group}")
+    packed, scales, zeros = empty_packed(N, K, W.device, group)
+    with torch.cuda.device(W.device):
+        check(load().awq_pack(W.data_ptr(), _ptr(s), N, K, group, packed.data_ptr(), scales.data_ptr(),
+                              zeros.data_ptr(), _stream(W.device)))
+    return packed, scales, zeros
+
+
+def awq_quantize(W: torch.Tensor, X: torch.Tensor, alphas: Optional[Sequence[float]] = None,
+                 group: int = GROUP, workspace: Optional[torch.Tensor] = None) -> dict:
+    """AWQ scale search for one linear layer; returns packed, scales, zeros, s,
+    best_alpha (int32 [1] on device), loss (fp64 [n_alpha] on device)."""
+    _need(W, "W", torch.float16, 2)
+    _need(X, "X", torch.float16, 2)
+    N, K = W.shape
+    M = X.shape[0]
+    if X.shape[1] != K or X.device != W.device:
+        raise ValueError("X must be fp16 [M][K] on W's device")
+    if K % group:
+        raise ValueError(f"K={K} is not a multiple of group {group}")
+    al = np.ascontiguousarray(default_alpha_grid() if alphas is None else np.asarray(alphas, dtype=np.float32))
+    n_alpha = int(al.shape[0])
+    if not 1 <= n_alpha <= MAX_ALPHAS:
+        raise ValueError(f"need 1..{MAX_ALPHAS} alphas, got {n_alpha}")
+    lib = load()
+    ws_bytes = int(lib.awq_quantize_workspace_bytes(N, K, M, group, n_alpha))
+    if ws_bytes == 0:
+        raise ValueError("unsupported sizes for awq_quantize")
+    if workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
+    elif workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_cuda:
+        raise ValueError(f"workspace must be a GPU buffer of at least {ws_bytes} bytes")
+    packed, scales, zeros = empty_packed(N, K, W.device, group)
+    s = torch.empty((K,), dtype=torch.float32, device=W.device)
+    best = torch.empty((1,), dtype=torch.int32, device=W.device)
+    loss = torch.empty((n_alpha,), dtype=torch.float64, device=W.device)
+    with torch.cuda.device(W.device):
+        check(lib.awq_quantize(W.data_ptr(), X.data_ptr(), N, K, M, group, al.ctypes.data, n_alpha,
+                               packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), s.data_ptr(),
+                               best.data_ptr(), loss.data_ptr(), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(W.device)))
+    return dict(packed=packed, scales=scales, zeros=zeros, s=s, best_alpha=best, loss=loss, alphas=al)
+
+
+def awq_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+             out: Optional[torch.Tensor] = None, group: int = GROUP) -> torch.Tensor:
+    """y = x @ w_hat^T with fp32 accumulation; x fp16 [M][K] (already divided by s)."""
+    _need(x, "x", torch.float16, 2)
+    _need(packed, "packed", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    _need(zeros, "zeros", torch.uint8, 2)
+    M, K = x.shape
+    N = packed.shape[0]
+    G = K // group
+    if packed.shape[1] * 8 != K or tuple(scales.shape) != (N, G) or tuple(zeros.shape) != (N, (G + 1) // 2):
+        raise ValueError("packed/scales/zeros do not match x's K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be fp16 [M][N]")
+    with torch.cuda.device(x.device):
+        check(load().awq_gemm(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                              out.data_ptr(), M, N, K, group, _stream(x.device)))
+    return out
+
+
+def awq_unpack(packed: torch.Tensor, zeros: torch.Tensor, K: int, group: int = GROUP):
+    """Logical codes uint8 [N][K] and zero points uint8 [N][K/g] of a packed layer."""
+    _need(packed, "packed", torch.int32, 2)
+    _need(zeros, "zeros", torch.uint8, 2)
+    N = packed.shape[0]
+    codes = torch.empty((N, K), dtype=torch.uint8, device=packed.device)
+    z = torch.empty((N, K // group), dtype=torch.uint8, device=packed.device)
+    with torch.cuda.device(packed.device):
+        check(load().awq_unpack(packed.data_ptr(), zeros.data_ptr(), N, K, group, codes.data_ptr(),
+                                z.data_ptr(), _stream(packed.device)))
+    return codes, z
+
+
+__all__ = [n for n in dir() if n.startswith("awq_")] + ["AwqError", "default_alpha_grid", "empty_packed"]

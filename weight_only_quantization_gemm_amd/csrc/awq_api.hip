@@ -1,0 +1,232 @@
+// The extern "C" entry points of libawq declared in include/awq.h: argument
+// checks, workspace carving and kernel dispatch.  No entry point allocates
+// memory, synchronises the device or lets a C++ exception escape.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "awq.h"
+#include "awq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error = "no error";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  try {
+    g_last_error = buf;
+  } catch (...) {
+  }
+  return status;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return AWQ_OK;
+  return fail(AWQ_ERROR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define AWQ_REQUIRE(cond, status, ...) \
+  do {                                 \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define AWQ_GUARD_BEGIN try {
+#define AWQ_GUARD_END                                            \
+  }                                                              \
+  catch (...) {                                                  \
+    return fail(AWQ_ERROR_DEVICE, "unexpected C++ exception"); \
+  }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_layer(int64_t N, int64_t K, int32_t group) {
+  AWQ_REQUIRE(N >= 1 && K >= 1, AWQ_ERROR_INVALID_VALUE, "N and K must be >= 1 (got N=%lld K=%lld)", (long long)N,
+              (long long)K);
+  AWQ_REQUIRE(group == AWQ_GROUP, AWQ_ERROR_INVALID_VALUE, "group must be %d (got %d)", AWQ_GROUP, group);
+  AWQ_REQUIRE(K % group == 0, AWQ_ERROR_INVALID_VALUE, "K=%lld is not a multiple of group %d", (long long)K, group);
+  AWQ_REQUIRE(N <= (int64_t(1) << 31) && K <= (int64_t(1) << 20), AWQ_ERROR_INVALID_VALUE,
+              "N=%lld or K=%lld exceeds the supported range", (long long)N, (long long)K);
+  return AWQ_OK;
+}
+
+// Workspace of awq_quantize, carved in this order (each piece 256-byte aligned).
+struct QuantizeWorkspace {
+  size_t a, s_all, xt, g, e, partial, loss, total;
+  int64_t mp, partials;
+};
+
+QuantizeWorkspace quantize_workspace(int64_t N, int64_t K, int64_t M, int32_t n_alpha) {
+  QuantizeWorkspace w{};
+  w.mp = (M + 63) / 64 * 64;
+  w.partials = awq::loss_partial_count(N, K);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  w.a = take(sizeof(double) * (size_t)K);
+  w.s_all = take(sizeof(float) * (size_t)n_alpha * (size_t)K);
+  w.xt = take(2 * (size_t)K * (size_t)w.mp);
+  w.g = take(sizeof(double) * (size_t)K * (size_t)K);
+  w.e = take(sizeof(double) * (size_t)N * (size_t)K);
+  w.partial = take(sizeof(double) * (size_t)w.partials);
+  w.loss = take(sizeof(double) * (size_t)n_alpha);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int awq_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+const char* awq_status_string(int status) {
+  switch (status) {
+    case AWQ_OK: return "AWQ_OK";
+    case AWQ_ERROR_INVALID_VALUE: return "AWQ_ERROR_INVALID_VALUE";
+    case AWQ_ERROR_MISALIGNED: return "AWQ_ERROR_MISALIGNED";
+    case AWQ_ERROR_WORKSPACE_TOO_SMALL: return "AWQ_ERROR_WORKSPACE_TOO_SMALL";
+    case AWQ_ERROR_DEVICE: return "AWQ_ERROR_DEVICE";
+    case AWQ_ERROR_NOT_IMPLEMENTED: return "AWQ_ERROR_NOT_IMPLEMENTED";
+    default: return "AWQ_UNKNOWN_STATUS";
+  }
+}
+
+const char* awq_last_error(void) { return g_last_error.c_str(); }
+
+size_t awq_packed_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1 || K % 8 != 0) return 0;
+  return (size_t)N * (size_t)(K / 8) * 4;
+}
+
+size_t awq_scales_bytes(int64_t N, int64_t K, int32_t group) {
+  if (N < 1 || K < 1 || group < 1 || K % group != 0) return 0;
+  return (size_t)N * (size_t)(K / group) * 2;
+}
+
+size_t awq_zeros_bytes(int64_t N, int64_t K, int32_t group) {
+  if (N < 1 || K < 1 || group < 1 || K % group != 0) return 0;
+  return (size_t)N * (size_t)((K / group + 1) / 2);
+}
+
+size_t awq_quantize_workspace_bytes(int64_t N, int64_t K, int64_t M, int32_t group, int32_t n_alpha) {
+  if (N < 1 || K < 1 || M < 1 || group != AWQ_GROUP || K % group != 0 || n_alpha < 1 || n_alpha > AWQ_MAX_ALPHAS)
+    return 0;
+  return quantize_workspace(N, K, M, n_alpha).total;
+}
+
+int awq_channel_mean_abs(const void* X, int64_t M, int64_t K, double* a, void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(X && a, AWQ_ERROR_INVALID_VALUE, "X and a must not be NULL");
+  AWQ_REQUIRE(M >= 1 && M <= AWQ_MAX_CALIB_ROWS, AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^23]", (long long)M);
+  AWQ_REQUIRE(K >= 8 && K % 8 == 0 && K <= (int64_t(1) << 20), AWQ_ERROR_INVALID_VALUE,
+              "K=%lld must be a positive multiple of 8", (long long)K);
+  AWQ_REQUIRE(aligned16(X) && aligned16(a), AWQ_ERROR_MISALIGNED, "X and a must be 16-byte aligned");
+  return device_status(awq::launch_channel_mean_abs(X, M, K, a, as_stream(stream)), "awq_channel_mean_abs");
+  AWQ_GUARD_END
+}
+
+int awq_pack(const void* W, const float* s, int64_t N, int64_t K, int32_t group, void* packed, void* scales,
+             void* zeros, void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(W && packed && scales && zeros, AWQ_ERROR_INVALID_VALUE, "W, packed, scales, zeros must not be NULL");
+  int st = check_layer(N, K, group);
+  if (st != AWQ_OK) return st;
+  AWQ_REQUIRE(aligned16(W) && aligned16(packed) && (s == nullptr || aligned16(s)), AWQ_ERROR_MISALIGNED,
+              "W, s and packed must be 16-byte aligned");
+  return device_status(awq::launch_pack(W, s, N, K, packed, scales, zeros, as_stream(stream)), "awq_pack");
+  AWQ_GUARD_END
+}
+
+int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, int32_t group, const float* alphas,
+                 int32_t n_alpha, void* packed, void* scales, void* zeros, float* s, int32_t* best_alpha,
+                 double* loss, void* workspace, size_t workspace_bytes, void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(W && X && alphas && packed && scales && zeros && s && best_alpha && workspace, AWQ_ERROR_INVALID_VALUE,
+              "W, X, alphas, packed, scales, zeros, s, best_alpha and workspace must not be NULL");
+  int st = check_layer(N, K, group);
+  if (st != AWQ_OK) return st;
+  AWQ_REQUIRE(M >= 1 && M <= AWQ_MAX_CALIB_ROWS, AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^23]", (long long)M);
+  AWQ_REQUIRE(n_alpha >= 1 && n_alpha <= AWQ_MAX_ALPHAS, AWQ_ERROR_INVALID_VALUE, "n_alpha=%d outside [1, %d]",
+              n_alpha, AWQ_MAX_ALPHAS);
+  awq::AlphaGrid grid{};
+  for (int i = 0; i < n_alpha; ++i) {
+    AWQ_REQUIRE(std::isfinite(alphas[i]) && alphas[i] >= 0.0f, AWQ_ERROR_INVALID_VALUE,
+                "alphas[%d]=%g must be finite and >= 0", i, (double)alphas[i]);
+    grid.v[i] = alphas[i];
+  }
+  AWQ_REQUIRE(aligned16(W) && aligned16(X) && aligned16(packed) && aligned16(s) && aligned16(workspace) &&
+                  (loss == nullptr || aligned16(loss)),
+              AWQ_ERROR_MISALIGNED, "device pointers must be 16-byte aligned");
+  const QuantizeWorkspace w = quantize_workspace(N, K, M, n_alpha);
+  AWQ_REQUIRE(workspace_bytes >= w.total, AWQ_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu",
+              workspace_bytes, w.total);
+
+  char* base = static_cast<char*>(workspace);
+  double* a = reinterpret_cast<double*>(base + w.a);
+  float* s_all = reinterpret_cast<float*>(base + w.s_all);
+  void* xt = base + w.xt;
+  double* G = reinterpret_cast<double*>(base + w.g);
+  double* E = reinterpret_cast<double*>(base + w.e);
+  double* partial = reinterpret_cast<double*>(base + w.partial);
+  double* L = loss ? loss : reinterpret_cast<double*>(base + w.loss);
+  hipStream_t hs = as_stream(stream);
+
+  hipError_t e = awq::launch_channel_mean_abs(X, M, K, a, hs);
+  if (e == hipSuccess) e = awq::launch_scales(a, grid, n_alpha, K, s_all, hs);
+  if (e == hipSuccess) e = awq::launch_transpose(X, M, K, w.mp, xt, hs);
+  if (e == hipSuccess) e = awq::launch_gram(xt, w.mp, K, G, hs);
+  const double mn = (double)M * (double)N;
+  for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
+    e = awq::launch_quant_error(W, s_all + (size_t)i * (size_t)K, N, K, E, hs);
+    if (e == hipSuccess) e = awq::launch_loss_partials(E, G, N, K, partial, hs);
+    if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, L + i, hs);
+  }
+  if (e == hipSuccess) e = awq::launch_argmin(L, n_alpha, best_alpha, hs);
+  if (e == hipSuccess) e = awq::launch_select_scale(s_all, best_alpha, K, s, hs);
+  if (e == hipSuccess) e = awq::launch_pack(W, s, N, K, packed, scales, zeros, hs);
+  return device_status(e, "awq_quantize");
+  AWQ_GUARD_END
+}
+
+int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M, int64_t N,
+             int64_t K, int32_t group, void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(x && packed && scales && zeros && y, AWQ_ERROR_INVALID_VALUE,
+              "x, packed, scales, zeros and y must not be NULL");
+  int st = check_layer(N, K, group);
+  if (st != AWQ_OK) return st;
+  AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
+  AWQ_REQUIRE(aligned16(x) && aligned16(packed), AWQ_ERROR_MISALIGNED, "x and packed must be 16-byte aligned");
+  hipError_t e = (M <= 8) ? awq::launch_gemv(x, packed, scales, zeros, y, M, N, K, as_stream(stream))
+                          : awq::launch_gemm(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
+  return device_status(e, "awq_gemm");
+  AWQ_GUARD_END
+}
+
+int awq_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, int32_t group, uint8_t* codes,
+               uint8_t* zeros_u8, void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(packed && zeros && codes && zeros_u8, AWQ_ERROR_INVALID_VALUE, "pointers must not be NULL");
+  int st = check_layer(N, K, group);
+  if (st != AWQ_OK) return st;
+  AWQ_REQUIRE(aligned16(packed), AWQ_ERROR_MISALIGNED, "packed must be 16-byte aligned");
+  return device_status(awq::launch_unpack(packed, zeros, N, K, codes, zeros_u8, as_stream(stream)), "awq_unpack");
+  AWQ_GUARD_END
+}
+
+}  // extern "C"

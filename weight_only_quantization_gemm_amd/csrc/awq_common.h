@@ -1,0 +1,50 @@
+// Device-side helpers shared by the libawq kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;     // input channels per quantization group
+constexpr int kQmax = 15;       // largest 4-bit code
+
+// Nibble position of the code of channel 8w+i inside packed word w: channels
+// 8w+{0,2,4,6} sit in nibbles 0..3 and 8w+{1,3,5,7} in nibbles 4..7, so that
+// (word >> 4j) & 0x000F000F holds channels 8w+2j and 8w+2j+1 in its halves.
+__host__ __device__ constexpr int nibble_pos(int i) { return 4 * (i & 1) + (i >> 1); }
+
+__device__ inline uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ inline f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
+// The two codes of pair j of a packed word as fp16 (1024 + code): OR-ing a
+// 4-bit integer into the mantissa of fp16 1024.0 (0x6400) yields 1024 + code
+// exactly.
+__device__ inline f16x2 pair_biased(uint32_t word, int j) {
+  return as_f16x2(((word >> (4 * j)) & 0x000F000Fu) | 0x64006400u);
+}
+
+// fp16x2 (1024 + zero, 1024 + zero) for subtracting the zero point exactly.
+__device__ inline f16x2 zero_biased(uint32_t zero) {
+  return as_f16x2(0x64006400u | zero | (zero << 16));
+}
+
+__device__ inline uint32_t zero_of(const uint8_t* zeros_row, int g) {
+  return (zeros_row[g >> 1] >> (4 * (g & 1))) & 0xFu;
+}
+
+template <typename T>
+__device__ inline T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+}  // namespace awq

@@ -1,0 +1,206 @@
+// Per-channel scales s = a^alpha, the group-wise int4 quantizer, the fp64
+// weight error used by the search loss, and the packer.
+//
+// Method: a weight channel is multiplied by s and its input divided by s,
+// which leaves the layer's output unchanged in exact arithmetic while the
+// channel's rounding error shrinks relative to its size; s is the channel's
+// average activation magnitude raised to alpha ("AWQ: Activation-aware Weight
+// Quantization for On-Device LLM Compression and Acceleration",
+// fdeinterviews.com/papers/awq, paragraph 3).  The group quantizer (group 128,
+// min-max asymmetric, fp16 step, 4-bit zero point, round-half-even) is this
+// library's reading of the 4-bit weight-only format the pages name.
+//
+// Every float operation below is an IEEE fp32/fp64 operation rounded to
+// nearest-even (the file is built with -ffp-contract=off and correctly
+// rounded division), so codes, zero points and steps are reproducible
+// bit-for-bit by any implementation that performs the same operations.
+#include "awq_common.h"
+#include "awq_internal.h"
+
+namespace awq {
+
+__global__ void scales_kernel(const double* __restrict__ a, AlphaGrid al, int n_alpha, int64_t K,
+                              float* __restrict__ s_all) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int i = blockIdx.y;
+  if (k >= K || i >= n_alpha) return;
+  double ak = a[k];
+  float s = (ak == 0.0) ? 1.0f : (float)pow(ak, (double)al.v[i]);
+  s_all[(int64_t)i * K + k] = s;
+}
+
+hipError_t launch_scales(const double* a, const AlphaGrid& al, int n_alpha, int64_t K, float* s_all,
+                         hipStream_t st) {
+  dim3 grid((unsigned)((K + 255) / 256), (unsigned)n_alpha);
+  scales_kernel<<<grid, dim3(256), 0, st>>>(a, al, n_alpha, K, s_all);
+  return hipGetLastError();
+}
+
+// Quantizes the 8 consecutive weights one thread holds; the 16 threads of an
+// aligned 16-lane segment hold one 128-channel group and agree on its range.
+struct Quant8 {
+  float v[8];   // scaled weights
+  float q[8];   // codes
+  float z;      // zero point
+  float sc;     // fp16 step as float
+  f16 sc16;
+};
+
+__device__ inline void load_w8(const uint4* W, int64_t idx, float w[8]) {
+  uint4 raw = W[idx];
+  const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f16x2 h = as_f16x2(r[i]);
+    w[2 * i] = (float)h.x;
+    w[2 * i + 1] = (float)h.y;
+  }
+}
+
+__device__ inline void load_s8(const float* s, int64_t k0, float out[8]) {
+  if (s == nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = 1.0f;
+    return;
+  }
+  float4 a = *reinterpret_cast<const float4*>(s + k0);
+  float4 b = *reinterpret_cast<const float4*>(s + k0 + 4);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+__device__ inline void quantize8(const float w[8], const float s[8], Quant8& r) {
+  float mn = 0.0f, mx = 0.0f;  // the range always contains 0
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    r.v[i] = w[i] * s[i];
+    mn = fminf(mn, r.v[i]);
+    mx = fmaxf(mx, r.v[i]);
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+  }
+  float step = (mx - mn) / 15.0f;
+  step = fmaxf(step, 0x1p-14f);
+  r.sc16 = (f16)step;
+  r.sc = (float)r.sc16;
+  r.z = fminf(fmaxf(rintf(-mn / r.sc), 0.0f), 15.0f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.q[i] = fminf(fmaxf(rintf(r.v[i] / r.sc) + r.z, 0.0f), 15.0f);
+}
+
+// E[n][k] = (q - z) * sc / s - w in fp64, one thread per 8 channels.
+__global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
+                                                          int64_t N, int64_t K, double* __restrict__ E) {
+  const int64_t K8 = K / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // word index over N*K/8
+  // K8 is a multiple of 16, so a 16-lane segment never straddles rows; the
+  // grid covers whole segments, so every lane of a live segment is live.
+  if (idx >= N * K8) return;
+  const int64_t n = idx / K8, w = idx - n * K8;
+  float wf[8], sf[8];
+  load_w8(W, idx, wf);
+  load_s8(s, w * 8, sf);
+  Quant8 r;
+  quantize8(wf, sf, r);
+  double e[8];
+  const double scd = (double)r.sc;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = ((double)(r.q[i] - r.z) * scd) / (double)sf[i] - (double)wf[i];
+  double2* out = reinterpret_cast<double2*>(E + n * K + w * 8);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = make_double2(e[2 * i], e[2 * i + 1]);
+}
+
+hipError_t launch_quant_error(const void* W, const float* s, int64_t N, int64_t K, double* E, hipStream_t st) {
+  const int64_t words = N * (K / 8);
+  quant_error_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st>>>(
+      reinterpret_cast<const uint4*>(W), s, N, K, E);
+  return hipGetLastError();
+}
+
+// Packer: a 32-lane segment handles the group pair (2p, 2p+1) of one row so
+// that the two zero points of a zeros byte are known to one lane.
+__global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
+                                                   int64_t N, int64_t K, uint32_t* __restrict__ packed,
+                                                   f16* __restrict__ scales, uint8_t* __restrict__ zeros) {
+  const int64_t G = K / kGroup;
+  const int64_t P = (G + 1) / 2;  // group pairs per row == zeros bytes per row
+  const int64_t seg = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;
+  const int lane32 = threadIdx.x & 31;
+  if (seg >= N * P) return;  // whole 32-lane segments exit together
+  const int64_t n = seg / P, p = seg - n * P;
+  const int64_t g = 2 * p + (lane32 >> 4);
+  const bool live = g < G;
+  const int64_t w = g * 16 + (lane32 & 15);  // word within the row
+  float wf[8], sf[8];
+  if (live) {
+    load_w8(W, n * (K / 8) + w, wf);
+    load_s8(s, w * 8, sf);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { wf[i] = 0.0f; sf[i] = 1.0f; }
+  }
+  Quant8 r;
+  quantize8(wf, sf, r);  // a dead half-segment quantizes zeros and is discarded
+  uint32_t z_other = (uint32_t)__shfl_xor((int)r.z, 16, 32);
+  if (!live) return;
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) word |= ((uint32_t)r.q[i]) << (4 * nibble_pos(i));
+  packed[n * (K / 8) + w] = word;
+  if ((lane32 & 15) == 0) scales[n * G + g] = r.sc16;
+  if (lane32 == 0) {
+    uint32_t zlo = (uint32_t)r.z;
+    uint32_t zhi = (g + 1 < G) ? z_other : 0u;
+    zeros[n * P + p] = (uint8_t)(zlo | (zhi << 4));
+  }
+}
+
+hipError_t launch_pack(const void* W, const float* s, int64_t N, int64_t K, void* packed, void* scales,
+                       void* zeros, hipStream_t st) {
+  const int64_t G = K / kGroup, P = (G + 1) / 2;
+  const int64_t threads = N * P * 32;
+  pack_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st>>>(
+      reinterpret_cast<const uint4*>(W), s, N, K, reinterpret_cast<uint32_t*>(packed),
+      reinterpret_cast<f16*>(scales), reinterpret_cast<uint8_t*>(zeros));
+  return hipGetLastError();
+}
+
+__global__ void select_scale_kernel(const float* __restrict__ s_all, const int32_t* __restrict__ best, int64_t K,
+                                    float* __restrict__ s_out) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < K) s_out[k] = s_all[(int64_t)best[0] * K + k];
+}
+
+hipError_t launch_select_scale(const float* s_all, const int32_t* best, int64_t K, float* s_out, hipStream_t st) {
+  select_scale_kernel<<<dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st>>>(s_all, best, K, s_out);
+  return hipGetLastError();
+}
+
+__global__ void unpack_kernel(const uint32_t* __restrict__ packed, const uint8_t* __restrict__ zeros, int64_t N,
+                              int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ zeros_u8) {
+  const int64_t K8 = K / 8, G = K / kGroup, P = (G + 1) / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= N * K8) return;
+  const int64_t n = idx / K8, w = idx - n * K8;
+  const uint32_t word = packed[idx];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) codes[n * K + w * 8 + i] = (uint8_t)((word >> (4 * nibble_pos(i))) & 0xFu);
+  if ((w & 15) == 0) {
+    const int64_t g = w >> 4;
+    zeros_u8[n * G + g] = (uint8_t)((zeros[n * P + (g >> 1)] >> (4 * (g & 1))) & 0xFu);
+  }
+}
+
+hipError_t launch_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, uint8_t* codes,
+                         uint8_t* zeros_u8, hipStream_t st) {
+  const int64_t words = N * (K / 8);
+  unpack_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st>>>(
+      reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const uint8_t*>(zeros), N, K, codes, zeros_u8);
+  return hipGetLastError();
+}
+
+}  // namespace awq
