@@ -1,0 +1,354 @@
+"""Benchmark of the AWQ W4A16 hot path on one MI355X.
+
+Timed step: one decode pass (M = 1) through the 7 linear layers of a
+Llama-2-7B block -- (K, N) = (4096, 4096) x 4, (4096, 11008) x 2, (11008, 4096)
+-- with int4 group-128 weights, fp16 activations.  Each step is one replay of a
+HIP graph holding the 7 GEMV launches; successive steps rotate through copies of
+the weights totalling more than 1 GiB so that the 256 MB Infinity Cache cannot
+serve them.  `value` is algorithmic bytes moved per second (packed codes, fp16
+scales, 4-bit zeros, x and y).
+
+Also reported in the same JSON line:
+  roofline       the GEMV kernel's achieved algorithmic GB/s (per-launch HIP event
+                 timing of the same launches) against the 8 TB/s HBM peak, and the
+                 HBM traffic measured with rocprofv3 counters when a summary for the
+                 current kernel source exists under profiles/;
+  cpu_baseline   the CPU oracle's W4A16 product on the same layers, timed on the
+                 host cores (bounded sample);
+  legs           the M = 256 GEMM on the (4096, 11008) layer (TFLOP/s against the
+                 2.5 PFLOP/s dense fp16 peak), the batch sweep M = 1..1024 on that
+                 layer, and awq_quantize over the 7 layers of a 7B block with 65,536
+                 calibration rows (seconds per layer).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--no-search] [--no-sweep] [--profile-mode gemv|copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMV GB/s & % HBM peak (M=1); GEMM TFLOP/s (M=256); search s/layer"
+HBM_PEAK_GBS = 8000.0
+FP16_PEAK_TFLOPS = 2500.0
+LAYERS_7B = [("q_proj", 4096, 4096), ("k_proj", 4096, 4096), ("v_proj", 4096, 4096), ("o_proj", 4096, 4096),
+             ("gate_proj", 4096, 11008), ("up_proj", 4096, 11008), ("down_proj", 11008, 4096)]
+GEMV_SOURCES = ["weight_only_quantization_gemm_amd/csrc/gemv.hip", "weight_only_quantization_gemm_amd/csrc/awq_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_llama2_7b_decode_m1_counters.txt")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gemv_bytes(M: int, K: int, N: int) -> int:
+    G = K // 128
+    return N * K // 2 + 2 * N * G + N * ((G + 1) // 2) + 2 * M * K + 2 * M * N
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(per_launch_alg_bytes: float):
+    """HBM bytes per GEMV launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"^source_hash:\s*(\S+)", text, re.M)
+    m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not (m_hash and m_bytes) or m_hash.group(1) != source_hash(GEMV_SOURCES):
+        return None
+    return float(m_bytes.group(1))
+
+
+class Layer:
+    def __init__(self, name, K, N, torch, awq, copies, dev):
+        from gen import activations_fp16, normal_fp16
+        self.name, self.K, self.N = name, K, N
+        W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=2000 + K + N)).to(dev)
+        p, s, z = awq.awq_pack(W)  # plain round-to-nearest; values do not change the speed
+        del W
+        self.copies = [(p, s, z)] + [(p.clone(), s.clone(), z.clone()) for _ in range(copies - 1)]
+        self.x = torch.from_numpy(activations_fp16(1, K, seed=2100 + K)).to(dev)
+        self.y = torch.empty((1, N), dtype=torch.float16, device=dev)
+        self.bytes = gemv_bytes(1, K, N)
+
+
+def graph_of(torch, fn):
+    """Captures fn() (a sequence of libawq launches on the current stream) into a HIP graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(torch, graphs, steps, warmup):
+    """Mean ms per replay over `steps` replays (cycling through `graphs`), HIP events
+    on the replay stream bracketing the whole timed region."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def run_decode(args, torch, awq, dev):
+    step_bytes = sum(gemv_bytes(1, K, N) for _, K, N in LAYERS_7B)
+    copies = max(2, int(np.ceil((1 << 30) / step_bytes)) + 1)
+    layers = [Layer(n, K, N, torch, awq, copies, dev) for n, K, N in LAYERS_7B]
+    torch.cuda.synchronize()
+
+    def step(c):
+        for L in layers:
+            p, s, z = L.copies[c]
+            awq.awq_gemm(L.x, p, s, z, out=L.y)
+
+    # one graph per weight copy; a step replays one of them
+    graphs = [graph_of(torch, lambda c=c: step(c)) for c in range(copies)]
+    t0 = time.perf_counter()
+    ms_per_step = time_replays(torch, graphs, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+    launches = len(layers)
+    kern_ms = ms_per_step / launches  # the timed region holds nothing but these launches
+    bytes_per_launch = step_bytes / launches
+    achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
+    del graphs
+
+    # per layer: a graph of `copies` launches of that layer alone (each weight copy once)
+    detail = {}
+    for L in layers:
+        def one(L=L):
+            for c in range(copies):
+                p, s, z = L.copies[c]
+                awq.awq_gemm(L.x, p, s, z, out=L.y)
+        g = graph_of(torch, one)
+        ms = time_replays(torch, [g], max(5, args.steps // copies), 2) / copies
+        detail[L.name] = dict(K=L.K, N=L.N, bytes=L.bytes, us=round(ms * 1e3, 3),
+                              GBs=round(L.bytes / (ms * 1e-3) / 1e9, 1))
+        del g
+    return dict(step_bytes=step_bytes, copies=copies, ms_per_step=ms_per_step, wall_s=wall,
+                kern_ms=kern_ms, achieved=achieved, bytes_per_launch=bytes_per_launch, per_layer=detail,
+                layers=layers)
+
+
+def run_sweep(args, torch, awq, dev):
+    """awq_gemm on the (K=4096, N=11008) layer at M = 1..1024, rotating weight copies."""
+    from gen import activations_fp16, normal_fp16
+    K, N = 4096, 11008
+    W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=3001)).to(dev)
+    base = awq.awq_pack(W)
+    del W
+    copies = 48  # 48 x 23.4 MB > 1 GiB
+    packs = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
+    out = {}
+    for M in (1, 2, 4, 8, 16, 64, 256, 1024):
+        x = torch.from_numpy(activations_fp16(M, K, seed=3100 + M)).to(dev)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+        def run(x=x, y=y):
+            for c in range(copies):
+                awq.awq_gemm(x, *packs[c], out=y)
+        g = graph_of(torch, run)
+        ms = time_replays(torch, [g], max(3, args.steps // copies), 1) / copies
+        del g
+        us = ms * 1e3
+        nbytes = gemv_bytes(M, K, N)
+        flops = 2.0 * M * N * K
+        out[str(M)] = dict(us=round(us, 3), GBs=round(nbytes / us / 1e3, 1),
+                           hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                           TFLOPs=round(flops / us / 1e6, 2), mfma_frac=round(flops / us / 1e6 / FP16_PEAK_TFLOPS, 4),
+                           kernel="gemv_dot2" if M <= 2 else ("skinny_mfma" if M <= 16 else "mfma_gemm"))
+    return out
+
+
+def run_search(args, torch, awq, dev):
+    """awq_quantize on the 7 linears of a 7B block, 65,536 calibration rows per input."""
+    from gen import activations_fp16, normal_fp16, seed_for
+    from gen.workloads import layer_inputs_7b_block
+    M = 65536
+    inputs = {}
+    sizes = {"attn_in": 4096, "o_in": 4096, "mlp_in": 4096, "down_in": 11008}
+    for i, (name, K) in enumerate(sizes.items()):
+        inputs[name] = torch.from_numpy(activations_fp16(M, K, seed=seed_for(5, 10 + i), lognormal=True)).to(dev)
+    Ks = {n: (K, N) for n, K, N in LAYERS_7B}
+    res = {}
+    total_ms = 0.0
+    for li, (lname, src) in enumerate(layer_inputs_7b_block()):
+        K, N = Ks[lname]
+        W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=seed_for(5, 100 + li))).to(dev)
+        ws = torch.empty((awq.awq_quantize_workspace_bytes(N, K, M, 128, 20),), dtype=torch.uint8, device=dev)
+        awq.awq_quantize(W, inputs[src], None, workspace=ws)  # warm-up (first-touch of the workspace)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = awq.awq_quantize(W, inputs[src], None, workspace=ws)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        total_ms += ms
+        loss = r["loss"].cpu().numpy()
+        best = int(r["best_alpha"].item())
+        res[lname] = dict(K=K, N=N, ms=round(ms, 2), alpha_index=best, alpha=float(r["alphas"][best]),
+                          mse_ratio_vs_rtn=float(loss[best] / loss[0]))
+        del W, ws, r
+        torch.cuda.empty_cache()
+    return dict(layers=res, s_per_layer=round(total_ms / 7 / 1e3, 4), total_s=round(total_ms / 1e3, 3),
+                calib_rows=M, n_alpha=20)
+
+
+def run_cpu_baseline(layers_spec, budget_s: float):
+    """The oracle's fp64 W4A16 product over the 7 decode layers, on the host cores."""
+    import oracle
+    from gen import activations_fp16, normal_fp16
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    prepared = []
+    for name, K, N in layers_spec:
+        W = normal_fp16((N, K), 0.02, seed=2000 + K + N)
+        q, z, sc = oracle.quantize_groups(W.astype(np.float32))
+        x = activations_fp16(1, K, seed=2100 + K)
+        prepared.append((x, q, z, sc, gemv_bytes(1, K, N)))
+    nbytes = 0
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        for x, q, z, sc, b in prepared:
+            oracle.gemm(x, q, z, sc)
+            nbytes += b
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=round(nbytes / dt / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{steps} full decode steps (7 layers of the 7B block, M=1) through oracle.gemm "
+                       f"(fp64 dequantize + matmul), {dt:.1f} s")
+
+
+def profile_mode(args, torch, awq, dev):
+    """Short runs for rocprofv3 counter passes: the decode GEMVs, or a plain copy."""
+    if args.profile_mode == "copy":
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(profile_mode="copy", bytes_per_copy=n, launches=5)))
+        return
+    r = run_decode(args, torch, awq, dev)
+    print(json.dumps(dict(profile_mode="gemv", alg_bytes_per_launch=r["bytes_per_launch"], kern_ms=r["kern_ms"],
+                          per_layer=r["per_layer"])))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-search", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--profile-mode", choices=["gemv", "copy"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: the W4A16 kernels are measured on one MI355X; "
+              f"--gpus {args.gpus} is not supported (see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import weight_only_quantization_gemm_amd as awq
+
+    awq.load()  # fails loudly if libawq.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.profile_mode:
+        profile_mode(args, torch, awq, dev)
+        return
+
+    log("decode: building 7B-block layers and graphs")
+    dec = run_decode(args, torch, awq, dev)
+    value = dec["step_bytes"] / (dec["ms_per_step"] * 1e-3) / 1e9
+    log(f"decode: {dec['ms_per_step'] * 1e3:.2f} us/step, {value:.1f} GB/s; per launch {dec['kern_ms'] * 1e3:.2f} us")
+    dec.pop("layers")
+    torch.cuda.empty_cache()
+
+    legs = {}
+    if not args.no_sweep:
+        log("sweep: (4096, 11008) at M = 1..1024")
+        legs["batch_sweep_4096x11008"] = run_sweep(args, torch, awq, dev)
+        m256 = legs["batch_sweep_4096x11008"]["256"]
+        legs["gemm_m256_4096x11008"] = dict(TFLOPs=m256["TFLOPs"], mfma_frac=m256["mfma_frac"], us=m256["us"])
+        torch.cuda.empty_cache()
+    if not args.no_search:
+        log("search: awq_quantize over a 7B block, 65,536 calibration rows")
+        legs["search_llama2_7b_block"] = run_search(args, torch, awq, dev)
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on host cores")
+        cpu = run_cpu_baseline(LAYERS_7B, args.cpu_budget)
+
+    traffic = measured_traffic(dec["bytes_per_launch"])
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "llama2_7b_decode_m1", "M": 1, "weights": "int4 g128 (fp16 scales, 4-bit zeros)",
+                   "layers_KN": [[K, N] for _, K, N in LAYERS_7B], "bytes_per_step": dec["step_bytes"],
+                   "rotating_weight_copies": dec["copies"], "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic, 0),
+                     "kernel": "awq::gemv_kernel (M=1)", "avg_launch_us": round(dec["kern_ms"] * 1e3, 3),
+                     "alg_bytes_per_launch": round(dec["bytes_per_launch"], 1),
+                     "timing": "HIP events around the timed graph replays / launches in the region"},
+        "cpu_baseline": cpu,
+        "per_layer": dec["per_layer"],
+        "legs": legs,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -164,9 +164,11 @@ int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, 
  *   packed, scales, zeros       device, format above
  *   y       device fp16 [M][N]  out: y[m][n] = sum_k x[m][k] * w_hat[n][k]
  *
- * Accumulation is fp32; y is rounded to fp16 once.  M <= 8 runs the GEMV
- * kernel ((code - zero) exact in fp16, scale applied per group in fp32);
- * larger M runs the MFMA GEMM (w_hat rounded to fp16 before the matrix core).
+ * Accumulation is fp32; y is rounded to fp16 once.  M <= 16 runs the decode
+ * kernel: (code - zero) exact in fp16 on the matrix cores, fp32 sums per
+ * 128-channel group, scale applied per group in fp32.  Larger M runs the MFMA
+ * GEMM, which rounds w_hat = (code - zero) * scale to fp16 before the matrix
+ * core.
  * Requires M >= 1, N >= 1, K % group == 0, group == AWQ_GROUP.
  */
 int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y,

@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq.so")
 
-SOURCES = ["awq_api.hip", "stats.hip", "gram.hip", "quant.hip", "loss.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["awq_api.hip", "stats.hip", "gram.hip", "quant.hip", "loss.hip", "gemv.hip", "skinny.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -212,8 +212,8 @@ int awq_gemm(const void* x, const void* packed, const void* scales, const void* 
   if (st != AWQ_OK) return st;
   AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
   AWQ_REQUIRE(aligned16(x) && aligned16(packed), AWQ_ERROR_MISALIGNED, "x and packed must be 16-byte aligned");
-  hipError_t e = (M <= 8) ? awq::launch_gemv(x, packed, scales, zeros, y, M, N, K, as_stream(stream))
-                          : awq::launch_gemm(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
+  hipError_t e = (M <= 16) ? awq::launch_gemv(x, packed, scales, zeros, y, M, N, K, as_stream(stream))
+                           : awq::launch_gemm(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
   return device_status(e, "awq_gemm");
   AWQ_GUARD_END
 }

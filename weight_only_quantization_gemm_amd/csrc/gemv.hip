@@ -1,4 +1,5 @@
-// W4A16 GEMV for M <= 8 activation rows: y[m][n] = sum_k x[m][k] * w_hat[n][k].
+// W4A16 GEMV on the vector ALUs for M <= 2 activation rows (decode):
+// y[m][n] = sum_k x[m][k] * w_hat[n][k].
 //
 // Decoding reads every weight once per token and does little arithmetic with
 // it, so this kernel is bound by HBM bandwidth; 4-bit codes cut that traffic
@@ -11,9 +12,13 @@
 // multiplies pairs with x into an fp32 sum.  The group scale is applied in
 // fp32 once per 32 codes.
 //
-// Mapping: a wave owns R output rows; lane l streams the 16-byte chunks
-// l, l+64, ... (32 codes each, inside one 128-channel group) of every one of
-// its rows, so a wave's loads of one row are 1 KB contiguous.
+// Mapping: a block owns R output rows and spans all of K; lane l of wave w
+// owns the 16-byte chunk c = 64 w + l (32 codes) of each of the R rows, so
+// every wave-wide load is 1 KB of one row, contiguous.  Each lane issues all
+// of its loads (R weight chunks, their scales and zero points, and its 64 B
+// of x per activation row) before the first use, so a block needs a single
+// round trip to memory.  Partial sums are reduced across the wave with DPP
+// and across the block's waves through LDS in a fixed order.
 #include "awq_common.h"
 #include "awq_internal.h"
 
@@ -25,12 +30,34 @@ __device__ inline float dot2_acc(f16x2 a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, a), __builtin_bit_cast(h16x2, b), c, false);
 }
 
+// DPP add: v + v[permuted lane]; lanes whose source row is masked off add 0.
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_add(float v) {
+  const int src = __builtin_bit_cast(int, v);
+  const int moved = __builtin_amdgcn_update_dpp(0, src, CTRL, ROW_MASK, 0xF, false);
+  return v + __builtin_bit_cast(float, moved);
+}
+
+// Sum over the 64 lanes; the total lands in lane 63.
+__device__ inline float wave_sum_to_lane63(float v) {
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xF>(v);  // row_half_mirror: 8-lane sums
+  v = dpp_add<0x140, 0xF>(v);  // row_mirror: 16-lane row sums
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+constexpr int kMaxWaves = 16;
+
 template <int MB, int R>
-__global__ __launch_bounds__(256) void gemv_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
-                                                   const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                                                   f16* __restrict__ y, int64_t N, int64_t K) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+__global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
+                                                    const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
+                                                    f16* __restrict__ y, int64_t N, int64_t K) {
+  __shared__ float red[kMaxWaves][R * MB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * R;
   const int64_t K8 = K / 8, G = K / kGroup, P = (G + 1) / 2;
   const int64_t nchunk = K / 32;
   float acc[R][MB];
@@ -39,29 +66,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(const f16* __restrict__ x, co
 #pragma unroll
     for (int m = 0; m < MB; ++m) acc[r][m] = 0.0f;
 
-  for (int64_t c = lane; c < nchunk; c += kWave) {
+  for (int64_t c = (int64_t)wave * kWave + lane; c < nchunk; c += (int64_t)nwaves * kWave) {
     const int64_t g = c >> 2;
+    u32x4 wv[R];
+    float sc[R];
+    uint32_t zr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = (row0 + r < N) ? row0 + r : N - 1;  // tail rows reload the last row; never stored
+      wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + row * K8 + c * 4));
+      sc[r] = (float)scales[row * G + g];
+      zr[r] = zero_of(zeros + row * P, (int)g);
+    }
     uint4 xv[MB][4];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int u = 0; u < 4; ++u) xv[m][u] = reinterpret_cast<const uint4*>(x + m * K + c * 32)[u];
-    uint4 wv[R];
-    float sc[R];
-    uint32_t zr[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t row = row0 + r;
-      if (row < N) {
-        wv[r] = *reinterpret_cast<const uint4*>(packed + row * K8 + c * 4);
-        sc[r] = (float)scales[row * G + g];
-        zr[r] = zero_of(zeros + row * P, (int)g);
-      } else {
-        wv[r] = make_uint4(0u, 0u, 0u, 0u);
-        sc[r] = 0.0f;
-        zr[r] = 0u;
-      }
-    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const f16x2 zb = zero_biased(zr[r]);
@@ -81,45 +102,50 @@ __global__ __launch_bounds__(256) void gemv_kernel(const f16* __restrict__ x, co
           }
         }
 #pragma unroll
-      for (int m = 0; m < MB; ++m) acc[r][m] += sc[r] * part[m];
+      for (int m = 0; m < MB; ++m) acc[r][m] = fmaf(sc[r], part[m], acc[r][m]);
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t row = row0 + r;
+  for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      const float v = wave_sum(acc[r][m]);
-      if (lane == 0 && row < N) y[m * N + row] = (f16)v;
+      const float v = wave_sum_to_lane63(acc[r][m]);
+      if (lane == 63) red[wave][r * MB + m] = v;
     }
+  __syncthreads();
+  if ((int)threadIdx.x < R * MB) {
+    const int r = threadIdx.x / MB, m = threadIdx.x % MB;
+    float v = 0.0f;
+    for (int w = 0; w < nwaves; ++w) v += red[w][threadIdx.x];
+    const int64_t row = row0 + r;
+    if (row < N) y[m * N + row] = (f16)v;
   }
 }
 
-template <int MB>
+template <int MB, int R>
 static hipError_t gemv_m(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                          int64_t N, int64_t K, hipStream_t st) {
-  constexpr int R = (MB <= 2) ? 4 : 2;
-  const int64_t rows_per_block = 4 * R;
-  dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block));
-  gemv_kernel<MB, R><<<grid, dim3(256), 0, st>>>(
+  const int64_t nchunk = K / 32;
+  int waves = (int)((nchunk + kWave - 1) / kWave);
+  waves = waves < 1 ? 1 : (waves > kMaxWaves ? kMaxWaves : waves);
+  dim3 grid((unsigned)((N + R - 1) / R));
+  gemv_kernel<MB, R><<<grid, dim3(waves * kWave), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
       reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), N, K);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
-                       int64_t N, int64_t K, hipStream_t st) {
-  switch (M) {
-    case 1: return gemv_m<1>(x, packed, scales, zeros, y, N, K, st);
-    case 2: return gemv_m<2>(x, packed, scales, zeros, y, N, K, st);
-    case 3: return gemv_m<3>(x, packed, scales, zeros, y, N, K, st);
-    case 4: return gemv_m<4>(x, packed, scales, zeros, y, N, K, st);
-    case 5: return gemv_m<5>(x, packed, scales, zeros, y, N, K, st);
-    case 6: return gemv_m<6>(x, packed, scales, zeros, y, N, K, st);
-    case 7: return gemv_m<7>(x, packed, scales, zeros, y, N, K, st);
-    case 8: return gemv_m<8>(x, packed, scales, zeros, y, N, K, st);
-    default: return hipErrorInvalidValue;
-  }
+bool gemv_dot2_supported(int64_t M, int64_t K) { return M >= 1 && M <= 2 && K / 32 <= (int64_t)kMaxWaves * kWave; }
+
+// Rows per block: 2 keeps more blocks in flight on the smaller layers; 4 gives
+// each lane more loads in flight when K is long (measured on the Llama-2
+// 7B/70B decode shapes).
+hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                            int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const bool longk = K >= 11008;
+  if (M == 1) return longk ? gemv_m<1, 4>(x, packed, scales, zeros, y, N, K, st) : gemv_m<1, 2>(x, packed, scales, zeros, y, N, K, st);
+  if (M == 2) return longk ? gemv_m<2, 4>(x, packed, scales, zeros, y, N, K, st) : gemv_m<2, 2>(x, packed, scales, zeros, y, N, K, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace awq

@@ -1,0 +1,174 @@
+// W4A16 product for M <= 16 activation rows (decode): y[m][n] = sum_k x[m][k] * w_hat[n][k].
+//
+// Decoding reads every weight once per token and does little arithmetic with
+// it, so this kernel is bound by HBM bandwidth; 4-bit codes cut that traffic
+// about 4x ("AWQ: Activation-aware Weight Quantization for On-Device LLM
+// Compression and Acceleration", fdeinterviews.com/papers/awq, paragraphs 1
+// and 6).  Codes are dequantized on the fly in registers (OpenAlex record of
+// the GetMobile AWQ article, abstract).
+//
+// Design for gfx950: the dot products run on the matrix cores
+// (v_mfma_f32_16x16x32_f16) with the activations as the A operand (rows m,
+// zero beyond M) and the weights as the B operand.  The B operand of one lane
+// is 8 consecutive input channels of one weight row -- exactly one packed
+// word -- so a lane unpacks its word in registers: one shift and one and-or
+// per channel pair give fp16 1024 + code (the packed nibble order puts
+// channels 2j and 2j+1 in the two halves of (word >> 4j) & 0x000F000F) and one
+// packed fp16 subtraction of 1024 + zero gives (code - zero) exactly.  The
+// matrix core accumulates a 128-channel group in fp32; the group's fp16 scale
+// is then applied in fp32.  No cross-lane reduction is needed, and the vector
+// ALU work per weight does not grow with M.
+//
+// Mapping: a block owns 16*RW weight rows and all of K; its W waves split the
+// K groups (wave w takes groups w, w+W, ...).  For one group a wave loads 16 B
+// per lane: lane l reads the (l/16)-th 16-byte quarter of the group's 64 B in
+// row l%16, so one load instruction fetches 16 rows x 64 B.  All loads of a
+// batch of P groups are issued before any is used.  x is staged once per
+// block in LDS when it fits.  The waves' partial tiles are summed through LDS
+// in a fixed order, so results are deterministic.
+#include "awq_common.h"
+#include "awq_internal.h"
+
+namespace awq {
+
+constexpr int kSkinnyMaxWaves = 8;
+constexpr size_t kSkinnyLdsBudget = 64 * 1024;
+
+template <int RW, int P, bool XLDS>
+__global__ __launch_bounds__(1024) void skinny_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
+                                                      const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
+                                                      f16* __restrict__ y, int M, int64_t N, int64_t K,
+                                                      int64_t red_offset) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int nl = lane & 15, kq = lane >> 4;  // row within a 16-row tile; quarter of a group
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * RW);
+  const int64_t K8 = K / 8, G = K / kGroup, P2 = (G + 1) / 2;
+  const bool mlive = nl < M;  // this lane's A-operand row is a real activation row
+
+  int64_t rowi[RW];
+#pragma unroll
+  for (int t = 0; t < RW; ++t) {
+    const int64_t n = n0 + 16 * t + nl;
+    rowi[t] = n < N ? n : N - 1;  // tail rows reload the last row; never stored
+  }
+  f32x4 acc[RW];
+#pragma unroll
+  for (int t = 0; t < RW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  f16* xs = reinterpret_cast<f16*>(smem);
+  bool staged = false;
+
+  for (int64_t gb = wave; gb < G; gb += (int64_t)W * P) {
+    u32x4 wv[P][RW];
+    f16 sc[P][RW];
+    uint32_t zz[P][RW];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int64_t g = gb + (int64_t)p * W;
+      const int64_t gg = g < G ? g : G - 1;
+#pragma unroll
+      for (int t = 0; t < RW; ++t) {
+        wv[p][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + rowi[t] * K8 + gg * 16 + kq * 4));
+        sc[p][t] = scales[rowi[t] * G + gg];
+        zz[p][t] = (zeros[rowi[t] * P2 + (gg >> 1)] >> (4 * (gg & 1))) & 0xFu;
+      }
+    }
+    if (XLDS && !staged) {
+      // copy x into LDS while this wave's weight loads are in flight
+      const int64_t n16 = (int64_t)M * K / 8;
+      for (int64_t i = threadIdx.x; i < n16; i += blockDim.x)
+        reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
+      __syncthreads();
+      staged = true;
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int64_t g = gb + (int64_t)p * W;
+      if (g >= G) break;
+      const int64_t k0 = g * kGroup + kq * 32;
+      f16x8 a[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (mlive)
+          a[s] = XLDS ? *reinterpret_cast<const f16x8*>(xs + (int64_t)nl * K + k0 + 8 * s)
+                      : *reinterpret_cast<const f16x8*>(x + (int64_t)nl * K + k0 + 8 * s);
+        else
+          a[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int t = 0; t < RW; ++t) {
+        const f16x2 zb = zero_biased(zz[p][t]);
+        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t word = wv[p][t][s];
+          const f16x2 q0 = pair_biased(word, 0) - zb, q1 = pair_biased(word, 1) - zb;
+          const f16x2 q2 = pair_biased(word, 2) - zb, q3 = pair_biased(word, 3) - zb;
+          const f16x8 b = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], b, d, 0, 0, 0);
+        }
+        const float scf = (float)sc[p][t];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(scf, d[r], acc[t][r]);
+      }
+    }
+  }
+  if (XLDS && !staged) __syncthreads();  // a wave without groups still meets the staging barrier
+
+  // sum the waves' tiles: lane holds y[m = 4*kq + r][n0 + 16t + nl]
+  float* red = reinterpret_cast<float*>(smem + red_offset);
+#pragma unroll
+  for (int t = 0; t < RW; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * kq + r;
+      if (m < M) red[((wave * RW + t) * 16 + m) * 16 + nl] = acc[t][r];
+    }
+  __syncthreads();
+  for (int i = threadIdx.x; i < RW * 16 * M; i += blockDim.x) {
+    const int t = i / (16 * M), rem = i - t * 16 * M, m = rem >> 4, nn = rem & 15;
+    float v = 0.f;
+    for (int w = 0; w < W; ++w) v += red[((w * RW + t) * 16 + m) * 16 + nn];
+    const int64_t n = n0 + 16 * t + nn;
+    if (n < N) y[(int64_t)m * N + n] = (f16)v;
+  }
+}
+
+template <int RW, int P>
+static hipError_t skinny_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                                int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t G = K / kGroup;
+  int W = (int)((G + P - 1) / P);  // about P groups per wave
+  W = W < 1 ? 1 : (W > kSkinnyMaxWaves ? kSkinnyMaxWaves : W);
+  const size_t red_bytes = (size_t)W * RW * 16 * 16 * sizeof(float);
+  const size_t xbytes = (size_t)M * (size_t)K * 2;
+  const bool xlds = xbytes + red_bytes <= kSkinnyLdsBudget;
+  const size_t red_offset = xlds ? xbytes : 0;
+  const size_t lds = red_offset + red_bytes;
+  dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW))), block((unsigned)(W * kWave));
+  auto xp = reinterpret_cast<const f16*>(x);
+  auto pp = reinterpret_cast<const uint32_t*>(packed);
+  auto sp = reinterpret_cast<const f16*>(scales);
+  auto zp = reinterpret_cast<const uint8_t*>(zeros);
+  auto yp = reinterpret_cast<f16*>(y);
+  if (xlds)
+    skinny_kernel<RW, P, true><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, N, K, (int64_t)red_offset);
+  else
+    skinny_kernel<RW, P, false><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, N, K, (int64_t)red_offset);
+  return hipGetLastError();
+}
+
+// Tile shape, measured on the Llama-2 7B/70B decode shapes at M = 2..16:
+// at most 8 waves per block (more leaves one block per compute unit with no
+// overlap between blocks), and two 16-row tiles per wave when M > 8 and K is
+// long enough that the reuse of x outweighs the halved block count.
+hipError_t launch_gemv(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
+                       int64_t N, int64_t K, hipStream_t st) {
+  if (M < 1 || M > 16) return hipErrorInvalidValue;
+  if (gemv_dot2_supported(M, K)) return launch_gemv_dot2(x, packed, scales, zeros, y, M, N, K, st);
+  if (M > 8 && K >= 8192) return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
+  return skinny_launch<1, 4>(x, packed, scales, zeros, y, M, N, K, st);
+}
+
+}  // namespace awq
