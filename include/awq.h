@@ -141,9 +141,15 @@ int awq_pack(const void* W, const float* s, int64_t N, int64_t K, int32_t group,
  *
  * For each alpha_i: a = awq_channel_mean_abs(X); s_k = fp32(a_k ^ alpha_i)
  * evaluated in fp64 (s_k = 1 where a_k = 0); quantize W diag(s) as awq_pack;
- * E = w_hat / s - w in fp64; L_i = ||X E^T||_F^2 / (M N), the mean squared
- * change of the layer's output on the calibration rows, evaluated as
- * sum_n E_n G E_n^T / (M N) with G = X^T X.  alpha* is the first index with
+ * E = w_hat / s - w; L_i = ||X E^T||_F^2 / (M N), the mean squared change of
+ * the layer's output on the calibration rows.  For M < K it is evaluated
+ * directly (Y = X E^T with E in fp32 on the fp32 matrix cores); for M >= K
+ * through G = X^T X as sum_n E_n G E_n^T (G accumulated in fp64, then both
+ * factors rescaled per channel by powers of two and split into fp16 hi + lo
+ * pairs for the fp16 matrix cores).  Partial sums are reduced in fp64 in a
+ * fixed order; L agrees with an fp64 evaluation to about 1e-7 relative.  The
+ * Gram form assumes |E_nk| * sqrt(G_kk) < 2^15 (far above any 4-bit
+ * quantization error of realistic weights).  alpha* is the first index with
  * the smallest L.  The caller then feeds x / s (rounded to fp16) to awq_gemm.
  * Requires 1 <= n_alpha <= AWQ_MAX_ALPHAS, 1 <= M <= AWQ_MAX_CALIB_ROWS,
  * group == AWQ_GROUP, K % group == 0.

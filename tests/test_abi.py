@@ -76,8 +76,12 @@ def test_workspace_query():
     assert awq.awq_quantize_workspace_bytes(512, 500, 64, 128, 20) == 0
     assert awq.awq_quantize_workspace_bytes(512, 512, 64, 64, 20) == 0
     assert awq.awq_quantize_workspace_bytes(512, 512, 64, 128, 65) == 0
+    # Gram form (M >= K): X^T fp16, G fp32 + fp16 hi/lo, E' fp16 hi/lo
     big = awq.awq_quantize_workspace_bytes(4096, 11008, 65536, 128, 20)
-    assert big >= 8 * 11008 * 11008 + 2 * 11008 * 65536 + 8 * 4096 * 11008
+    assert big >= 2 * 11008 * 65536 + 8 * 11008 * 11008 + 4 * 4096 * 11008
+    # direct form (M < K): E in fp32, no Gram buffers
+    small = awq.awq_quantize_workspace_bytes(4096, 11008, 64, 128, 20)
+    assert 4 * 4096 * 11008 <= small < 4 * 4096 * 11008 + (1 << 20)
 
 
 def _lib_():

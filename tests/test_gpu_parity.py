@@ -277,3 +277,43 @@ def test_gemm_determinism():
         a = host(awq.awq_gemm(x, p, scd, zd))
         b = host(awq.awq_gemm(x, p, scd, zd))
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+# ------------------------------------------------------------------ full-size search (stored oracle results)
+def test_search_llama2_7b_block_full():
+    """The 7B-block search workload at full size (65,536 calibration rows per input, seven
+    layers) against the oracle's results stored by tests/golden/make_search_llama2_7b_block.py:
+    alpha index within the tie rule, losses within 1e-5, and the packed layer at alpha*
+    bit-exact against the oracle's quantizer (recomputed here; it needs no loss)."""
+    import json
+    import os
+    from gen.workloads import layer_inputs_7b_block
+    golden = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "search_llama2_7b_block.json")))
+    sys.path.insert(0, os.path.join(os.path.dirname(__file__), "golden"))
+    import make_search_llama2_7b_block as mk
+    alphas = np.array(golden["alphas"], dtype=np.float32)
+    assert np.array_equal(alphas, ALPHAS)
+    cache = {}
+    for li, (lname, src) in enumerate(layer_inputs_7b_block()):
+        ref = golden["layers"][lname]
+        K, N = ref["K"], ref["N"]
+        note(f"7B block search {lname} K={K} N={N} M={golden['calib_rows']}")
+        if src not in cache:
+            cache.clear()
+            Xh = mk.calib_input(src)
+            cache[src] = (Xh, dev(Xh), oracle.channel_mean_abs(Xh))
+        Xh, Xd, a = cache[src]
+        W = mk.layer_weight(li, K, N)
+        r = awq.awq_quantize(dev(W), Xd, ALPHAS)
+        best = int(host(r["best_alpha"])[0])
+        L = np.array(ref["losses"])
+        Lg = host(r["loss"])
+        assert L[best] <= (1 + 1e-6) * L.min(), (lname, best, ref["alpha_index"])
+        assert np.all(np.abs(Lg - L) <= 1e-5 * L), (lname, np.max(np.abs(Lg - L) / L))
+        q, z, sc, s = oracle.quantize_at(W, a, ALPHAS[best])
+        assert np.array_equal(host(r["s"]), s), lname
+        assert np.array_equal(decode_codes(host(r["packed"]), K), q), lname
+        assert np.array_equal(decode_zeros(host(r["zeros"]), K // 128), z), lname
+        assert np.array_equal(host(r["scales"]).view(np.uint16), sc.view(np.uint16)), lname
+        del r
+        torch.cuda.empty_cache()

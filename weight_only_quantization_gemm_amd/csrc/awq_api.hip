@@ -62,15 +62,19 @@ int check_layer(int64_t N, int64_t K, int32_t group) {
 }
 
 // Workspace of awq_quantize, carved in this order (each piece 256-byte aligned).
+// M < K uses the direct form of the loss (E in fp32); M >= K the Gram form
+// (X^T, G in fp32 and as scaled fp16 hi/lo, channel exponents, E' hi/lo).
 struct QuantizeWorkspace {
-  size_t a, s_all, xt, g, e, partial, loss, total;
+  bool direct;
+  size_t a, s_all, xt, g, gh, gl, ex, eh, el, e32, partial, loss, total;
   int64_t mp, partials;
 };
 
 QuantizeWorkspace quantize_workspace(int64_t N, int64_t K, int64_t M, int32_t n_alpha) {
   QuantizeWorkspace w{};
+  w.direct = M < K;
   w.mp = (M + 63) / 64 * 64;
-  w.partials = awq::loss_partial_count(N, K);
+  w.partials = w.direct ? awq::loss_direct_partial_count(M, N) : awq::loss_partial_count(N, K);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -79,9 +83,17 @@ QuantizeWorkspace quantize_workspace(int64_t N, int64_t K, int64_t M, int32_t n_
   };
   w.a = take(sizeof(double) * (size_t)K);
   w.s_all = take(sizeof(float) * (size_t)n_alpha * (size_t)K);
-  w.xt = take(2 * (size_t)K * (size_t)w.mp);
-  w.g = take(sizeof(double) * (size_t)K * (size_t)K);
-  w.e = take(sizeof(double) * (size_t)N * (size_t)K);
+  if (w.direct) {
+    w.e32 = take(sizeof(float) * (size_t)N * (size_t)K);
+  } else {
+    w.xt = take(2 * (size_t)K * (size_t)w.mp);
+    w.g = take(sizeof(float) * (size_t)K * (size_t)K);
+    w.gh = take(2 * (size_t)K * (size_t)K);
+    w.gl = take(2 * (size_t)K * (size_t)K);
+    w.ex = take(sizeof(int32_t) * (size_t)K);
+    w.eh = take(2 * (size_t)N * (size_t)K);
+    w.el = take(2 * (size_t)N * (size_t)K);
+  }
   w.partial = take(sizeof(double) * (size_t)w.partials);
   w.loss = take(sizeof(double) * (size_t)n_alpha);
   w.total = off;
@@ -179,22 +191,36 @@ int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, 
   char* base = static_cast<char*>(workspace);
   double* a = reinterpret_cast<double*>(base + w.a);
   float* s_all = reinterpret_cast<float*>(base + w.s_all);
-  void* xt = base + w.xt;
-  double* G = reinterpret_cast<double*>(base + w.g);
-  double* E = reinterpret_cast<double*>(base + w.e);
   double* partial = reinterpret_cast<double*>(base + w.partial);
   double* L = loss ? loss : reinterpret_cast<double*>(base + w.loss);
   hipStream_t hs = as_stream(stream);
+  const double mn = (double)M * (double)N;
 
   hipError_t e = awq::launch_channel_mean_abs(X, M, K, a, hs);
   if (e == hipSuccess) e = awq::launch_scales(a, grid, n_alpha, K, s_all, hs);
-  if (e == hipSuccess) e = awq::launch_transpose(X, M, K, w.mp, xt, hs);
-  if (e == hipSuccess) e = awq::launch_gram(xt, w.mp, K, G, hs);
-  const double mn = (double)M * (double)N;
-  for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
-    e = awq::launch_quant_error(W, s_all + (size_t)i * (size_t)K, N, K, E, hs);
-    if (e == hipSuccess) e = awq::launch_loss_partials(E, G, N, K, partial, hs);
-    if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, L + i, hs);
+  if (w.direct) {
+    float* E = reinterpret_cast<float*>(base + w.e32);
+    for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
+      e = awq::launch_quant_error32(W, s_all + (size_t)i * (size_t)K, N, K, E, hs);
+      if (e == hipSuccess) e = awq::launch_loss_direct(X, E, M, N, K, partial, hs);
+      if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, L + i, hs);
+    }
+  } else {
+    void* xt = base + w.xt;
+    float* G = reinterpret_cast<float*>(base + w.g);
+    void* Ghi = base + w.gh;
+    void* Glo = base + w.gl;
+    int32_t* ex = reinterpret_cast<int32_t*>(base + w.ex);
+    void* Ehi = base + w.eh;
+    void* Elo = base + w.el;
+    if (e == hipSuccess) e = awq::launch_transpose(X, M, K, w.mp, xt, hs);
+    if (e == hipSuccess) e = awq::launch_gram(xt, w.mp, K, G, hs);
+    if (e == hipSuccess) e = awq::launch_gram_split(G, K, ex, Ghi, Glo, hs);
+    for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
+      e = awq::launch_quant_error(W, s_all + (size_t)i * (size_t)K, ex, N, K, Ehi, Elo, hs);
+      if (e == hipSuccess) e = awq::launch_loss_partials(Ehi, Elo, Ghi, Glo, N, K, partial, hs);
+      if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, L + i, hs);
+    }
   }
   if (e == hipSuccess) e = awq::launch_argmin(L, n_alpha, best_alpha, hs);
   if (e == hipSuccess) e = awq::launch_select_scale(s_all, best_alpha, K, s, hs);

@@ -10,6 +10,7 @@ typedef _Float16 f16;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -39,6 +40,19 @@ __device__ inline f16x2 zero_biased(uint32_t zero) {
 
 __device__ inline uint32_t zero_of(const uint8_t* zeros_row, int g) {
   return (zeros_row[g >> 1] >> (4 * (g & 1))) & 0xFu;
+}
+
+// Block barrier for LDS hand-offs only.  __syncthreads() also waits for every
+// outstanding global load of the wave (vmcnt(0)), which would drain the
+// prefetches of later pipeline stages; this waits for the wave's LDS
+// operations (lgkmcnt(0)) and then meets the other waves at s_barrier.
+// s_waitcnt immediate on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] in bits 15:14, so 0xC07F leaves vmcnt and expcnt at their maxima.
+__device__ inline void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 template <typename T>

@@ -18,23 +18,30 @@ struct AlphaGrid {
 hipError_t launch_channel_mean_abs(const void* X, int64_t M, int64_t K, double* a, hipStream_t st);
 hipError_t launch_transpose(const void* X, int64_t M, int64_t K, int64_t Mp, void* Xt, hipStream_t st);
 
-// gram.hip: G = Xt Xt^T (fp64 [K][K]) from Xt fp16 [K][Mp], Mp % 64 == 0, K % 64 == 0.
-hipError_t launch_gram(const void* Xt, int64_t Mp, int64_t K, double* G, hipStream_t st);
+// gram.hip: G = Xt Xt^T (fp32 [K][K], fp64 accumulation) from Xt fp16 [K][Mp], Mp % 64 == 0, K % 64 == 0.
+hipError_t launch_gram(const void* Xt, int64_t Mp, int64_t K, float* G, hipStream_t st);
 
 // quant.hip
 hipError_t launch_scales(const double* a, const AlphaGrid& al, int n_alpha, int64_t K, float* s_all,
                          hipStream_t st);
-hipError_t launch_quant_error(const void* W, const float* s, int64_t N, int64_t K, double* E, hipStream_t st);
+hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, int64_t N, int64_t K, void* Ehi,
+                              void* Elo, hipStream_t st);
+hipError_t launch_quant_error32(const void* W, const float* s, int64_t N, int64_t K, float* E, hipStream_t st);
 hipError_t launch_pack(const void* W, const float* s, int64_t N, int64_t K, void* packed, void* scales,
                        void* zeros, hipStream_t st);
 hipError_t launch_select_scale(const float* s_all, const int32_t* best, int64_t K, float* s_out, hipStream_t st);
 hipError_t launch_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, uint8_t* codes,
                          uint8_t* zeros_u8, hipStream_t st);
 
-// loss.hip: partials of sum_n E_n G E_n^T; reduce + argmin.
+// loss.hip: channel exponents and the fp16 split of the scaled Gram matrix;
+// partials of sum_n E'_n G' E'_n^T; reduce + argmin.
+hipError_t launch_gram_split(const float* G, int64_t K, int32_t* e, void* Ghi, void* Glo, hipStream_t st);
 int64_t loss_partial_count(int64_t N, int64_t K);
-hipError_t launch_loss_partials(const double* E, const double* G, int64_t N, int64_t K, double* partial,
-                                hipStream_t st);
+hipError_t launch_loss_partials(const void* Ehi, const void* Elo, const void* Ghi, const void* Glo, int64_t N,
+                                int64_t K, double* partial, hipStream_t st);
+int64_t loss_direct_partial_count(int64_t M, int64_t N);
+hipError_t launch_loss_direct(const void* X, const float* E, int64_t M, int64_t N, int64_t K, double* partial,
+                              hipStream_t st);
 hipError_t launch_loss_reduce(const double* partial, int64_t count, double mn, double* loss, hipStream_t st);
 hipError_t launch_argmin(const double* loss, int n, int32_t* best, hipStream_t st);
 

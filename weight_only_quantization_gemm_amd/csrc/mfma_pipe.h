@@ -1,0 +1,87 @@
+// Building blocks of the pipelined fp16 matrix-core kernels (gfx950): tiles
+// of 64 fp16 values per row copied from global memory straight into LDS with
+// global_load_lds_dwordx4 (no registers in between, so several pipeline
+// stages can be in flight), and conflict-free 16-byte fragment reads.
+//
+// LDS tile layout: [rows][8 chunks of 16 B]; chunk c of row r sits in slot
+// c ^ (r & 7).  A direct load writes 1 KB per wave instruction (lane i to
+// bytes 16i..16i+15), i.e. 8 rows; lane i therefore fetches the global chunk
+// (i & 7) ^ (row & 7) of row (i >> 3).  A 32x32x16 fragment read touches 32
+// consecutive rows at one logical chunk, which the XOR spreads over all
+// eight slots of every group of eight rows.
+#pragma once
+
+#include "awq_common.h"
+
+namespace awq {
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (lgkmcnt and expcnt left at their maxima).
+__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+  __asm__ volatile("" ::: "memory");
+}
+
+typedef void __attribute__((address_space(3))) * lds_ptr_t;
+typedef const void __attribute__((address_space(1))) * global_ptr_t;
+
+// Copies rows [row0, row0 + ROWS) x columns [k0, k0 + 64) of a row-major fp16
+// matrix (row stride ld elements) into an LDS tile of ROWS x 64, with the
+// block's NW waves sharing the ROWS / 8 load instructions.  Rows at or past
+// row_end are read from row_end - 1 (valid memory); callers mask them later.
+// Issues ROWS / 8 / NW vector-memory operations per wave.
+template <int ROWS, int NW>
+__device__ __forceinline__ void dl_tile(f16* lds_tile, const f16* __restrict__ g, int64_t ld, int64_t row0,
+                                        int64_t row_end, int64_t k0, int wave, int lane) {
+  static_assert(ROWS % (8 * NW) == 0, "tile rows must split evenly over the waves");
+  constexpr int PER_WAVE = ROWS / 8 / NW;
+  wave = __builtin_amdgcn_readfirstlane(wave);  // the LDS destination must be wave-uniform
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int blk = wave * PER_WAVE + j;  // 8-row block written by this instruction
+    const int row = blk * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    int64_t r = row0 + row;
+    r = r < row_end ? r : row_end - 1;
+    const f16* src = g + r * ld + k0 + chunk * 8;
+    __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)(lds_tile + blk * 8 * 64), 16, 0, 0);
+  }
+}
+
+// The 16-byte fragment holding logical chunk c of row r of an LDS tile.
+__device__ __forceinline__ f16x8 frag(const f16* lds_tile, int r, int c) {
+  return *reinterpret_cast<const f16x8*>(lds_tile + r * 64 + ((c ^ (r & 7)) << 3));
+}
+
+// Narrow tiles: 32 fp16 values (4 chunks) per row.  One direct load covers 16
+// rows; chunk c of row r sits in slot c ^ ((r >> 1) & 3), which keeps the 8
+// rows a fragment read serves per cycle on distinct LDS banks (two 64-byte
+// rows share a 128-byte bank line).
+template <int ROWS, int NW>
+__device__ __forceinline__ void dl_tile32(f16* lds_tile, const f16* __restrict__ g, int64_t ld, int64_t row0,
+                                          int64_t row_end, int64_t k0, int wave, int lane) {
+  static_assert(ROWS % (16 * NW) == 0, "tile rows must split evenly over the waves");
+  constexpr int PER_WAVE = ROWS / 16 / NW;
+  wave = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int blk = wave * PER_WAVE + j;  // 16-row block written by this instruction
+    const int row = blk * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    int64_t r = row0 + row;
+    r = r < row_end ? r : row_end - 1;
+    const f16* src = g + r * ld + k0 + chunk * 8;
+    __builtin_amdgcn_global_load_lds((global_ptr_t)src, (lds_ptr_t)(lds_tile + blk * 16 * 32), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ f16x8 frag32(const f16* lds_tile, int r, int c) {
+  return *reinterpret_cast<const f16x8*>(lds_tile + r * 32 + ((c ^ ((r >> 1) & 3)) << 3));
+}
+
+}  // namespace awq

@@ -1,4 +1,4 @@
-// Per-channel scales s = a^alpha, the group-wise int4 quantizer, the fp64
+// Per-channel scales s = a^alpha, the group-wise int4 quantizer, the
 // weight error used by the search loss, and the packer.
 //
 // Method: a weight channel is multiplied by s and its input divided by s,
@@ -91,9 +91,13 @@ __device__ inline void quantize8(const float w[8], const float s[8], Quant8& r) 
   for (int i = 0; i < 8; ++i) r.q[i] = fminf(fmaxf(rintf(r.v[i] / r.sc) + r.z, 0.0f), 15.0f);
 }
 
-// E[n][k] = (q - z) * sc / s - w in fp64, one thread per 8 channels.
+// Weight error of the search, pre-scaled for the loss contraction:
+// E'[n][k] = ((q - z) * sc / s - w) * 2^e_k, evaluated in fp64, rounded to
+// fp32 and stored as an fp16 pair hi = fp16(E'), lo = fp16(E' - hi).  One
+// thread per 8 channels.
 __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
-                                                          int64_t N, int64_t K, double* __restrict__ E) {
+                                                          const int32_t* __restrict__ ex, int64_t N, int64_t K,
+                                                          f16* __restrict__ Ehi, f16* __restrict__ Elo) {
   const int64_t K8 = K / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // word index over N*K/8
   // K8 is a multiple of 16, so a 16-lane segment never straddles rows; the
@@ -105,19 +109,59 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restric
   load_s8(s, w * 8, sf);
   Quant8 r;
   quantize8(wf, sf, r);
-  double e[8];
   const double scd = (double)r.sc;
+  uint32_t hw[4], lw[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) e[i] = ((double)(r.q[i] - r.z) * scd) / (double)sf[i] - (double)wf[i];
-  double2* out = reinterpret_cast<double2*>(E + n * K + w * 8);
+  for (int i = 0; i < 8; i += 2) {
+    f16x2 h, l;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = make_double2(e[2 * i], e[2 * i + 1]);
+    for (int u = 0; u < 2; ++u) {
+      const double e = ((double)(r.q[i + u] - r.z) * scd) / (double)sf[i + u] - (double)wf[i + u];
+      const float v = (float)ldexp(e, ex[w * 8 + i + u]);
+      const f16 hi = (f16)v;
+      h[u] = hi;
+      l[u] = (f16)(v - (float)hi);
+    }
+    hw[i / 2] = as_u32(h);
+    lw[i / 2] = as_u32(l);
+  }
+  *reinterpret_cast<uint4*>(Ehi + n * K + w * 8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  *reinterpret_cast<uint4*>(Elo + n * K + w * 8) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
 }
 
-hipError_t launch_quant_error(const void* W, const float* s, int64_t N, int64_t K, double* E, hipStream_t st) {
+// Unscaled weight error in fp32 for the direct form of the loss.
+__global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
+                                                            int64_t N, int64_t K, float* __restrict__ E) {
+  const int64_t K8 = K / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= N * K8) return;  // whole 16-lane segments, as above
+  const int64_t n = idx / K8, w = idx - n * K8;
+  float wf[8], sf[8];
+  load_w8(W, idx, wf);
+  load_s8(s, w * 8, sf);
+  Quant8 r;
+  quantize8(wf, sf, r);
+  const double scd = (double)r.sc;
+  float e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = (float)(((double)(r.q[i] - r.z) * scd) / (double)sf[i] - (double)wf[i]);
+  float4* out = reinterpret_cast<float4*>(E + n * K + w * 8);
+  out[0] = make_float4(e[0], e[1], e[2], e[3]);
+  out[1] = make_float4(e[4], e[5], e[6], e[7]);
+}
+
+hipError_t launch_quant_error32(const void* W, const float* s, int64_t N, int64_t K, float* E, hipStream_t st) {
+  const int64_t words = N * (K / 8);
+  quant_error32_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st>>>(
+      reinterpret_cast<const uint4*>(W), s, N, K, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, int64_t N, int64_t K, void* Ehi,
+                              void* Elo, hipStream_t st) {
   const int64_t words = N * (K / 8);
   quant_error_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st>>>(
-      reinterpret_cast<const uint4*>(W), s, N, K, E);
+      reinterpret_cast<const uint4*>(W), s, ex, N, K, reinterpret_cast<f16*>(Ehi), reinterpret_cast<f16*>(Elo));
   return hipGetLastError();
 }
 
