@@ -192,6 +192,19 @@ def test_gemm_parity_ragged(M):
     assert_y_close(y, oracle.gemm(x, q, z, sc), f"M={M}")
 
 
+@pytest.mark.parametrize("N,K,M", [(77, 384, 17), (77, 384, 64), (77, 384, 65), (77, 384, 130), (131, 640, 200),
+                                   (200, 16640, 70), (136, 16640, 40)])
+def test_gemm_parity_block_tails(N, K, M):
+    """Weight-row counts that leave a partial 128-row block, odd group counts (the block's
+    scales and zeros end off a 16-byte boundary), and K = 16640 (130 groups, more than the
+    three-stage layout holds, so the two-stage one runs)."""
+    note(f"gemm tails N={N} K={K} M={M}")
+    q, z, sc, p, scd, zd = _random_packed(N, K, seed=N + K + M)
+    x = activations_fp16(M, K, seed=40 + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    assert_y_close(y, oracle.gemm(x, q, z, sc), f"N={N} K={K} M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 4, 8, 16])
 def test_gemm_one_hot_reproduces_dequantized_column(M):
     note(f"gemm one-hot M={M}")

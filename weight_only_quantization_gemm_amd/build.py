@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq.so")
 
-SOURCES = ["awq_api.hip", "stats.hip", "gram.hip", "quant.hip", "loss.hip", "gemv.hip", "skinny.hip", "gemm.hip"]
+SOURCES = ["awq_api.hip", "stats.hip", "gram.hip", "quant.hip", "loss.hip", "gemv.hip", "skinny.hip", "gemm.hip", "gemm_pipe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -26,11 +26,19 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source extras.  The W4A16 GEMM keeps its matrix-core accumulators in
+# ordinary vector registers, so the per-group scale is one FMA per element
+# (accumulators in AGPRs would need a register move before each FMA).
+FILE_FLAGS = {"gemm_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
+def flags_for(src: str) -> list:
+    return FLAGS + FILE_FLAGS.get(os.path.basename(src).replace("_probe", ""), [])
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *flags_for(src), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -362,6 +362,9 @@ __global__ __launch_bounds__(256) void gemm_mfma32_kernel(const f16* __restrict_
 
 hipError_t launch_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
                        int64_t N, int64_t K, hipStream_t st) {
+#ifndef AWQ_GEMM_LEGACY
+  if (gemm_pipe_supported(M, K)) return launch_gemm_pipe(x, packed, scales, zeros, y, M, N, K, st);
+#endif
 #ifndef AWQ_GEMM_OLD_BIG
   if (M > 64) {
     dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));

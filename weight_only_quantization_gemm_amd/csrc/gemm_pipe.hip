@@ -1,0 +1,271 @@
+// W4A16 GEMM for M > 16 activation rows on the fp16 matrix cores.
+//
+// With more activation rows each weight is reused M times and the product
+// turns compute-bound ("AWQ: Activation-aware Weight Quantization for On-Device
+// LLM Compression and Acceleration", fdeinterviews.com/papers/awq, paragraph 9:
+// under large batches serving becomes more compute-bound).  The codes are
+// still dequantized on the fly, never written back as fp16 weights (OpenAlex
+// record of the GetMobile AWQ article, abstract).
+//
+// Design for gfx950 (v_mfma_f32_32x32x16_f16, 160 KB LDS per compute unit):
+// the pipeline stage is one 128-channel group.  Both operands of a stage go
+// from global memory straight into LDS with global_load_lds_dwordx4 -- the x
+// tile [BM][128] fp16 as two 64-channel halves and the packed weight tile
+// [128 rows][64 B] -- two or three stages deep, so one or two stages of loads
+// are in flight while the matrix cores work.  The block's group scales and
+// zeros are copied to LDS once, up front.  A lane's B operand is 8 consecutive channels
+// of one weight row, i.e. one packed word: it is unpacked in registers to fp16
+// (1024 + code) - (1024 + zero) = code - zero, exactly.  The matrix core sums
+// one group in fp32 and the group's fp16 scale is then applied in fp32, so the
+// weights are never rounded (the same arithmetic as the decode kernels).
+//
+// Within a group, the MFMA lanes of half h (l / 32) take channels 64h + 8s ..
+// 64h + 8s + 7 at step s = 0..7 in both operands; a lane's 8 B-operand words
+// are then contiguous (words 8h .. 8h + 7 of its row).
+//
+// Blocks: 256 threads = 4 waves in 2 x 2, output tile BM x 128, wave tile
+// (BM / 2) x 64.  Consecutive block ids are dispatched to the 8 XCDs in turn,
+// so the block order puts the BM-row tiles that share a weight panel on the
+// same XCD (block b and b + 8), where they share that XCD's L2.
+#include "awq_common.h"
+#include "awq_internal.h"
+#include "mfma_pipe.h"
+
+#include <type_traits>
+
+namespace awq {
+
+constexpr int kPBN = 128;     // output columns (weight rows) per block
+constexpr int kXcds = 8;
+constexpr int kLdsBytes = 160 * 1024;
+
+template <int BM, int STAGES, int LDS_BYTES>
+struct PipeShape {
+  static constexpr int AB = BM / 64;                 // 32-row A blocks per wave
+  static constexpr int A_HALF = BM * 64;             // halfs in one 64-channel half of the x tile
+  static constexpr int B_TILE = kPBN * 32;           // halfs in the packed tile (64 B per row)
+  static constexpr int STAGE = 2 * A_HALF + B_TILE;  // halfs per stage
+  static constexpr int LOADS = 2 * (BM / 8 / 4) + kPBN / 16 / 4;  // direct loads per wave per stage
+  static constexpr int PIPE_BYTES = STAGES * STAGE * 2;
+  static constexpr int META_BYTES = LDS_BYTES - PIPE_BYTES;  // the block's scales and zeros
+  static_assert(META_BYTES > 0 && META_BYTES % 16 == 0, "LDS split");
+};
+
+// LDS bytes the block's scales ([128][G] fp16) and zeros ([128][ceil(G/2)]) take.
+__host__ __device__ constexpr int64_t pipe_meta_bytes(int64_t G) {
+  return ((int64_t)kPBN * G * 2 + 15) / 16 * 16 + (int64_t)kPBN * ((G + 1) / 2);
+}
+
+// Copies bytes [0, len) of src (16-byte aligned) to LDS dst (16-byte
+// aligned): whole 16-byte chunks straight into LDS by the block's 4 waves
+// (wave w takes chunks 64(w + 4j) .. +63), the tail bytes (len % 16) by plain
+// loads, which are issued first.
+__device__ __forceinline__ void dma_blob(unsigned char* dst, const unsigned char* __restrict__ src, int64_t len,
+                                         int wave, int lane, int tid) {
+  const int64_t n16 = len / 16;
+  if (tid < len - n16 * 16) dst[n16 * 16 + tid] = src[n16 * 16 + tid];
+  __asm__ volatile("" ::: "memory");
+  wave = __builtin_amdgcn_readfirstlane(wave);
+  for (int64_t base = (int64_t)wave * 64; base < n16; base += 256) {
+    const int64_t i = base + lane;
+    if (i < n16)
+      __builtin_amdgcn_global_load_lds((global_ptr_t)(src + 16 * i), (lds_ptr_t)(dst + 16 * base), 16, 0, 0);
+  }
+}
+
+template <int BM, int STAGES, int LDS_BYTES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(163840 / LDS_BYTES, 163840 / LDS_BYTES)))
+void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
+                                                        const f16* __restrict__ scales,
+                                                        const uint8_t* __restrict__ zeros, f16* __restrict__ y,
+                                                        int64_t M, int64_t N, int64_t K, int mt, int nt) {
+  using S = PipeShape<BM, STAGES, LDS_BYTES>;
+  constexpr int D = STAGES - 1;  // stages in flight ahead of the one being computed
+  __shared__ __attribute__((aligned(16))) f16 lds[LDS_BYTES / 2];
+
+  // block id -> (m tile, n tile): ids b and b + 8 land on one XCD and share n
+  const int b = (int)blockIdx.x;
+  const int chunk = b / (kXcds * mt), rem = b - chunk * kXcds * mt;
+  const int nb = chunk * kXcds + rem % kXcds, mb = rem / kXcds;
+  if (nb >= nt) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
+  const int64_t m0 = (int64_t)mb * BM, n0 = (int64_t)nb * kPBN;
+  const int64_t G = K / kGroup, P2 = (G + 1) / 2;
+  const int64_t rows = (N - n0) < kPBN ? (N - n0) : kPBN;  // weight rows of this block
+  const f16* packed_h = reinterpret_cast<const f16*>(packed);  // a row is K / 4 halfs
+
+  // Stage slot of group t is t % STAGES; past the last group the tail re-reads
+  // group G - 1 into the free slot, so every step issues the same loads and
+  // the in-order wait counts below hold on every path.
+  TilePlan<BM, 4, 64> xplan;
+  TilePlan<kPBN, 4, 32> wplan;
+  xplan.init(x, K, m0, M, wave, lane);
+  wplan.init(packed_h, K / 4, n0, N, wave, lane);
+  auto issue = [&](int64_t t) {
+    f16* st = lds + (t % STAGES) * S::STAGE;
+    const int64_t g = t < G ? t : G - 1;
+    xplan.issue(st, g * kGroup);
+    xplan.issue(st + S::A_HALF, g * kGroup + 64);
+    wplan.issue(st + 2 * S::A_HALF, g * 32);
+  };
+
+  // The block's scales and zeros are two contiguous byte ranges (rows
+  // n0 .. n0 + rows - 1 are adjacent); they go to LDS once, ahead of the first
+  // stage, so the loop issues no register loads (those would make the
+  // in-order vector-memory count unusable for the direct loads).
+  unsigned char* meta = reinterpret_cast<unsigned char*>(lds) + S::PIPE_BYTES;
+  const int64_t soff = (kPBN * G * 2 + 15) / 16 * 16;
+  dma_blob(meta, reinterpret_cast<const unsigned char*>(scales) + n0 * G * 2, rows * G * 2, wave, lane, tid);
+  dma_blob(meta + soff, zeros + n0 * P2, rows * P2, wave, lane, tid);
+  const uint16_t* msc = reinterpret_cast<const uint16_t*>(meta);
+  const uint8_t* mz = meta + soff;
+
+  for (int t = 0; t < D; ++t) issue(t);
+
+  int mrow[2];  // LDS meta row of the lane's two weight rows (clamped to the block's rows)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = wn * 64 + j * 32 + l32;
+    mrow[j] = r < rows ? r : (int)rows - 1;
+  }
+  // fp16x2 (1024, 1024) bit pattern kept in a vector register, so that each
+  // channel pair unpacks with one and-or (a VOP3 operand may not be a literal)
+  uint32_t magic;
+  __asm__ volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+  // acc += scale(g) * d(g) is applied one group late, after the next group's
+  // loads are issued, where it fills the wait for that group's LDS reads.
+  f32x16 acc[S::AB][2], d[S::AB][2];
+#pragma unroll
+  for (int a = 0; a < S::AB; ++a)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][j][r] = d[a][j][r] = 0.f;
+  float scf_prev[2] = {0.f, 0.f};
+
+  for (int64_t g = 0; g < G; ++g) {
+    wait_vmcnt<(D - 1) * S::LOADS>();  // stage g has landed; stages g+1 .. g+D-1 may be pending
+    lds_barrier();  // stage g is in LDS for every wave; stage g - 1 is no longer read
+    issue(g + D);
+
+    const f16* st = lds + (g % STAGES) * S::STAGE;
+    const f16* Ah = st + h * S::A_HALF;
+    const f16* Bt = st + 2 * S::A_HALF;
+    u32x4 wlo[2], whi[2];
+    f16x2 zb[2];
+    float scf[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = wn * 64 + j * 32 + l32;
+      const int sw = (row >> 1) & 3;  // the tile's chunk swizzle
+      wlo[j] = *reinterpret_cast<const u32x4*>(Bt + row * 32 + (((2 * h) ^ sw) << 3));
+      whi[j] = *reinterpret_cast<const u32x4*>(Bt + row * 32 + (((2 * h + 1) ^ sw) << 3));
+      zb[j] = zero_biased((mz[mrow[j] * P2 + (g >> 1)] >> (4 * (g & 1))) & 0xFu);
+      scf[j] = (float)as_f16x2((uint32_t)msc[mrow[j] * G + g]).x;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int a = 0; a < S::AB; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][j][r] = fmaf(scf_prev[j], d[a][j][r], acc[a][j][r]);
+    // Software-pipelined over the 8 MFMA steps of the group: the A fragments
+    // and unpacked B operands of step s + 1 are produced while the matrix
+    // cores run step s (a scheduling fence closes each step).
+    auto unpack = [&](int st_, f16x8(&bq)[2]) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t word = st_ < 4 ? wlo[j][st_ & 3] : whi[j][st_ & 3];
+        const f16x2 q0 = as_f16x2((word & 0x000F000Fu) | magic) - zb[j];
+        const f16x2 q1 = as_f16x2(((word >> 4) & 0x000F000Fu) | magic) - zb[j];
+        const f16x2 q2 = as_f16x2(((word >> 8) & 0x000F000Fu) | magic) - zb[j];
+        const f16x2 q3 = as_f16x2(((word >> 12) & 0x000F000Fu) | magic) - zb[j];
+        bq[j] = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+      }
+    };
+    f16x8 av[2][S::AB], bq[2][2];
+#pragma unroll
+    for (int a = 0; a < S::AB; ++a) av[0][a] = frag(Ah, wm * (BM / 2) + a * 32 + l32, 0);
+    unpack(0, bq[0]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int c = s & 1, n = c ^ 1;
+      if (s < 7) {
+#pragma unroll
+        for (int a = 0; a < S::AB; ++a) av[n][a] = frag(Ah, wm * (BM / 2) + a * 32 + l32, s + 1);
+      }
+#pragma unroll
+      for (int a = 0; a < S::AB; ++a)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          d[a][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[c][a], bq[c][j], s == 0 ? f32x16{} : d[a][j], 0, 0, 0);
+      if (s < 7) unpack(s + 1, bq[n]);
+      __builtin_amdgcn_sched_barrier(0);  // keep each step's work within the step
+    }
+    scf_prev[0] = scf[0];
+    scf_prev[1] = scf[1];
+  }
+  wait_vmcnt<0>();  // the tail's redundant LDS loads land before the block can exit
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int a = 0; a < S::AB; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][j][r] = fmaf(scf_prev[j], d[a][j][r], acc[a][j][r]);
+
+  // D register r of lane l: row 8(r/4) + 4(l/32) + r%4, column l%32 of a 32 x 32 block
+#pragma unroll
+  for (int a = 0; a < S::AB; ++a)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = n0 + wn * 64 + j * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * (BM / 2) + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < M && n < N) y[m * N + n] = (f16)acc[a][j][r];
+      }
+    }
+}
+
+template <int BM, int STAGES, int LDS_BYTES>
+static hipError_t pipe_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                              int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int mt = (int)((M + BM - 1) / BM), nt = (int)((N + kPBN - 1) / kPBN);
+  const int64_t blocks = (int64_t)((nt + kXcds - 1) / kXcds) * kXcds * mt;
+  gemm_pipe_kernel<BM, STAGES, LDS_BYTES><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+      reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),
+      reinterpret_cast<const f16*>(scales), reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), M, N,
+      K, mt, nt);
+  return hipGetLastError();
+}
+
+template <int BM, int STAGES, int LDS_BYTES>
+static bool pipe_fits(int64_t G) {
+  return pipe_meta_bytes(G) <= PipeShape<BM, STAGES, LDS_BYTES>::META_BYTES;
+}
+
+// Shapes: 128-row x tiles for M > 64, 64-row tiles (two blocks per compute
+// unit) below; fewer stages where the block's scales and zeros need the LDS.
+bool gemm_pipe_supported(int64_t M, int64_t K) {
+  const int64_t G = K / kGroup;
+  if (M > 64) return pipe_fits<128, 2, kLdsBytes>(G);
+  return pipe_fits<64, 2, kLdsBytes / 2>(G) || pipe_fits<64, 3, kLdsBytes>(G);
+}
+
+hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                            int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t G = K / kGroup;
+  if (M > 64) {
+    if (pipe_fits<128, 3, kLdsBytes>(G)) return pipe_launch<128, 3, kLdsBytes>(x, packed, scales, zeros, y, M, N, K, st);
+    if (pipe_fits<128, 2, kLdsBytes>(G)) return pipe_launch<128, 2, kLdsBytes>(x, packed, scales, zeros, y, M, N, K, st);
+    return hipErrorInvalidValue;
+  }
+  if (pipe_fits<64, 2, kLdsBytes / 2>(G)) return pipe_launch<64, 2, kLdsBytes / 2>(x, packed, scales, zeros, y, M, N, K, st);
+  if (pipe_fits<64, 3, kLdsBytes>(G)) return pipe_launch<64, 3, kLdsBytes>(x, packed, scales, zeros, y, M, N, K, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace awq

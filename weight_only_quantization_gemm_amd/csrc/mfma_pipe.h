@@ -84,4 +84,46 @@ __device__ __forceinline__ f16x8 frag32(const f16* lds_tile, int r, int c) {
   return *reinterpret_cast<const f16x8*>(lds_tile + r * 32 + ((c ^ ((r >> 1) & 3)) << 3));
 }
 
+// The same copies with the per-lane source addresses computed once: a tile
+// that moves along k by a uniform offset each stage costs one 64-bit add per
+// load instruction.  WIDTH is 64 (layout of dl_tile) or 32 (dl_tile32).
+template <int ROWS, int NW, int WIDTH>
+struct TilePlan {
+  static_assert(WIDTH == 64 || WIDTH == 32, "tile width");
+  static constexpr int ROWS_PER_LOAD = WIDTH == 64 ? 8 : 16;
+  static constexpr int PER_WAVE = ROWS / ROWS_PER_LOAD / NW;
+  static_assert(ROWS % (ROWS_PER_LOAD * NW) == 0, "tile rows must split evenly over the waves");
+  const f16* src[PER_WAVE];
+  int lds_off;  // halfs from the tile start to this wave's first load
+
+  __device__ __forceinline__ void init(const f16* __restrict__ g, int64_t ld, int64_t row0, int64_t row_end, int wave,
+                                       int lane) {
+    wave = __builtin_amdgcn_readfirstlane(wave);
+    lds_off = wave * PER_WAVE * ROWS_PER_LOAD * WIDTH;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = wave * PER_WAVE + j;
+      int row, chunk;
+      if (WIDTH == 64) {
+        row = blk * 8 + (lane >> 3);
+        chunk = (lane & 7) ^ (row & 7);
+      } else {
+        row = blk * 16 + (lane >> 2);
+        chunk = (lane & 3) ^ ((row >> 1) & 3);
+      }
+      int64_t r = row0 + row;
+      r = r < row_end ? r : row_end - 1;
+      src[j] = g + r * ld + chunk * 8;
+    }
+  }
+
+  // Columns [k0, k0 + WIDTH) of the planned rows into lds_tile.
+  __device__ __forceinline__ void issue(f16* lds_tile, int64_t k0) const {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j)
+      __builtin_amdgcn_global_load_lds((global_ptr_t)(src[j] + k0),
+                                       (lds_ptr_t)(lds_tile + lds_off + j * ROWS_PER_LOAD * WIDTH), 16, 0, 0);
+  }
+};
+
 }  // namespace awq
