@@ -170,11 +170,13 @@ int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, 
  *   packed, scales, zeros       device, format above
  *   y       device fp16 [M][N]  out: y[m][n] = sum_k x[m][k] * w_hat[n][k]
  *
- * Accumulation is fp32; y is rounded to fp16 once.  M <= 16 runs the decode
- * kernel: (code - zero) exact in fp16 on the matrix cores, fp32 sums per
- * 128-channel group, scale applied per group in fp32.  Larger M runs the MFMA
- * GEMM, which rounds w_hat = (code - zero) * scale to fp16 before the matrix
- * core.
+ * Accumulation is fp32; y is rounded to fp16 once, and no kernel rounds a
+ * dequantized weight.  M <= 2: vector-ALU GEMV; every product x * code is
+ * exact in fp32 and the zero point enters once per 32 codes as zero * sum(x)
+ * (so y is 0 only up to fp32 rounding when every code equals its zero).
+ * 3 <= M <= 16 and M > 16: matrix-core kernels on (code - zero), exact in
+ * fp16, with fp32 sums per 128-channel group and the group scale applied in
+ * fp32.
  * Requires M >= 1, N >= 1, K % group == 0, group == AWQ_GROUP.
  */
 int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y,

@@ -6,11 +6,20 @@
 // about 4x ("AWQ: Activation-aware Weight Quantization for On-Device LLM
 // Compression and Acceleration", fdeinterviews.com/papers/awq, paragraphs 1
 // and 6).  Codes are dequantized on the fly in registers (OpenAlex record of
-// the GetMobile AWQ article, abstract), using the packed nibble order: one
-// shift and one and-or turn a word into two fp16 values 1024 + code, one
-// packed fp16 subtraction gives (code - zero) exactly, and v_dot2_f32_f16
-// multiplies pairs with x into an fp32 sum.  The group scale is applied in
-// fp32 once per 32 codes.
+// the GetMobile AWQ article, abstract).
+//
+// Arithmetic, designed for few vector instructions per code: a code q in the
+// low mantissa bits of an fp16 with a zero exponent field is the subnormal
+// q * 2^-24, exactly.  The packed nibble order puts channels 2j and 2j + 1 of
+// a word in bits 4j and 16 + 4j, so with one shift (w8 = w >> 8) the four
+// channel pairs of a word are w & 0x000F000F (q units), w & 0x00F000F0 (16 q
+// units), and the same two masks of w8: four and-operations, no bias to add
+// or subtract.  v_dot2_f32_f16 multiplies each pair with x exactly (an fp16
+// times a 4-bit integer times 2^-24 fits fp32) into two fp32 sums (q units and
+// 16 q units).  The zero point enters once per 32 codes as z * sum(x), with
+// sum(x) over the lane's 32 channels computed once per lane; the group scale
+// then multiplies the 32-code partial sum in fp32, and the final 2^24 is an
+// exact rescale.
 //
 // Mapping: a block owns R output rows and spans all of K; lane l of wave w
 // owns the 16-byte chunk c = 64 w + l (32 codes) of each of the R rows, so
@@ -69,40 +78,59 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
   for (int64_t c = (int64_t)wave * kWave + lane; c < nchunk; c += (int64_t)nwaves * kWave) {
     const int64_t g = c >> 2;
     u32x4 wv[R];
-    float sc[R];
-    uint32_t zr[R];
+    uint32_t sr[R], zr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t row = (row0 + r < N) ? row0 + r : N - 1;  // tail rows reload the last row; never stored
       wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + row * K8 + c * 4));
-      sc[r] = (float)scales[row * G + g];
-      zr[r] = zero_of(zeros + row * P, (int)g);
+      sr[r] = reinterpret_cast<const uint16_t*>(scales)[row * G + g];
+      zr[r] = zeros[row * P + (g >> 1)];
     }
     uint4 xv[MB][4];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int u = 0; u < 4; ++u) xv[m][u] = reinterpret_cast<const uint4*>(x + m * K + c * 32)[u];
+    // 2^-24 * (sum of the lane's 32 x values), per activation row
+    float xs[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      float t = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t xw[4] = {xv[m][u].x, xv[m][u].y, xv[m][u].z, xv[m][u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t = dot2_acc(as_f16x2(0x3C003C00u), xw[q], t);  // (1, 1) . x pair
+      }
+      xs[m] = t * 0x1p-24f;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const f16x2 zb = zero_biased(zr[r]);
       const uint32_t words[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
-      float part[MB];
+      float lo[MB], hi[MB];
 #pragma unroll
-      for (int m = 0; m < MB; ++m) part[m] = 0.0f;
+      for (int m = 0; m < MB; ++m) lo[m] = hi[m] = 0.0f;
 #pragma unroll
-      for (int wi = 0; wi < 4; ++wi)
+      for (int wi = 0; wi < 4; ++wi) {
+        const uint32_t w = words[wi], w8 = w >> 8;
+        const f16x2 p0 = as_f16x2(w & 0x000F000Fu), p1 = as_f16x2(w & 0x00F000F0u);
+        const f16x2 p2 = as_f16x2(w8 & 0x000F000Fu), p3 = as_f16x2(w8 & 0x00F000F0u);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f16x2 d = pair_biased(words[wi], j) - zb;  // (code - zero), exact
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            const uint32_t xw = (j == 0) ? xv[m][wi].x : (j == 1) ? xv[m][wi].y : (j == 2) ? xv[m][wi].z : xv[m][wi].w;
-            part[m] = dot2_acc(d, xw, part[m]);
-          }
+        for (int m = 0; m < MB; ++m) {
+          lo[m] = dot2_acc(p0, xv[m][wi].x, lo[m]);
+          hi[m] = dot2_acc(p1, xv[m][wi].y, hi[m]);
+          lo[m] = dot2_acc(p2, xv[m][wi].z, lo[m]);
+          hi[m] = dot2_acc(p3, xv[m][wi].w, hi[m]);
         }
+      }
+      const float z = (float)((zr[r] >> (4 * (g & 1))) & 0xFu);
+      const float sc = (float)as_f16x2(sr[r]).x;
 #pragma unroll
-      for (int m = 0; m < MB; ++m) acc[r][m] = fmaf(sc[r], part[m], acc[r][m]);
+      for (int m = 0; m < MB; ++m) {
+        float t = fmaf(hi[m], 0.0625f, lo[m]);  // 2^-24 * sum x q
+        t = fmaf(-z, xs[m], t);                  // 2^-24 * sum x (q - z)
+        acc[r][m] = fmaf(sc, t, acc[r][m]);
+      }
     }
   }
 #pragma unroll
@@ -118,7 +146,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
     float v = 0.0f;
     for (int w = 0; w < nwaves; ++w) v += red[w][threadIdx.x];
     const int64_t row = row0 + r;
-    if (row < N) y[m * N + row] = (f16)v;
+    if (row < N) y[m * N + row] = (f16)(v * 0x1p24f);
   }
 }
 
@@ -137,14 +165,29 @@ static hipError_t gemv_m(const void* x, const void* packed, const void* scales, 
 
 bool gemv_dot2_supported(int64_t M, int64_t K) { return M >= 1 && M <= 2 && K / 32 <= (int64_t)kMaxWaves * kWave; }
 
-// Rows per block: 2 keeps more blocks in flight on the smaller layers; 4 gives
-// each lane more loads in flight when K is long (measured on the Llama-2
-// 7B/70B decode shapes).
+// Rows per block, measured on the Llama-2 7B/70B decode shapes: 2 keeps more
+// blocks in flight on a 4096 x 4096 layer; 4 amortizes each lane's x chunk
+// over more weight rows elsewhere; 8 on the widest layers (N >= 16384 with
+// K <= 8192).
+static int gemv_rows(int64_t N, int64_t K) {
+  if (N * K <= (int64_t)4096 * 4096) return 2;
+  if (K <= 8192 && N >= 16384) return 8;
+  return 4;
+}
+
 hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const bool longk = K >= 11008;
-  if (M == 1) return longk ? gemv_m<1, 4>(x, packed, scales, zeros, y, N, K, st) : gemv_m<1, 2>(x, packed, scales, zeros, y, N, K, st);
-  if (M == 2) return longk ? gemv_m<2, 4>(x, packed, scales, zeros, y, N, K, st) : gemv_m<2, 2>(x, packed, scales, zeros, y, N, K, st);
+  const int R = gemv_rows(N, K);
+  if (M == 1) {
+    if (R == 2) return gemv_m<1, 2>(x, packed, scales, zeros, y, N, K, st);
+    if (R == 8) return gemv_m<1, 8>(x, packed, scales, zeros, y, N, K, st);
+    return gemv_m<1, 4>(x, packed, scales, zeros, y, N, K, st);
+  }
+  if (M == 2) {
+    if (R == 2) return gemv_m<2, 2>(x, packed, scales, zeros, y, N, K, st);
+    if (R == 8) return gemv_m<2, 8>(x, packed, scales, zeros, y, N, K, st);
+    return gemv_m<2, 4>(x, packed, scales, zeros, y, N, K, st);
+  }
   return hipErrorInvalidValue;
 }
 
