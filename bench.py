@@ -15,7 +15,9 @@ Also reported in the same JSON line:
                  current kernel source exists under profiles/;
   cpu_baseline   the CPU oracle's W4A16 product on the same layers, timed on the
                  host cores (bounded sample);
-  legs           the M = 256 GEMM on the (4096, 11008) layer (TFLOP/s against the
+  legs           the same decode step with q/k/v and gate/up stored as one packed
+                 matrix each (4 launches instead of 7; same weight bytes), the M = 256
+                 GEMM on the (4096, 11008) layer (TFLOP/s against the
                  2.5 PFLOP/s dense fp16 peak), the batch sweep M = 1..1024 on that
                  layer, and awq_quantize over the 7 layers of a 7B block with 65,536
                  calibration rows (seconds per layer).
@@ -156,6 +158,32 @@ def run_decode(args, torch, awq, dev):
     return dict(step_bytes=step_bytes, copies=copies, ms_per_step=ms_per_step, wall_s=wall,
                 kern_ms=kern_ms, achieved=achieved, bytes_per_launch=bytes_per_launch, per_layer=detail,
                 layers=layers)
+
+
+LAYERS_7B_FUSED = [("qkv_proj", 4096, 3 * 4096), ("o_proj", 4096, 4096), ("gate_up_proj", 4096, 2 * 11008),
+                   ("down_proj", 11008, 4096)]
+
+
+def run_decode_fused(args, torch, awq, dev):
+    """The same 7 weight matrices with q/k/v and gate/up stored as one packed matrix each
+    (rows concatenated), so a decode step is 4 launches; same weight bytes, x read once
+    per fused launch."""
+    step_bytes = sum(gemv_bytes(1, K, N) for _, K, N in LAYERS_7B_FUSED)
+    copies = max(2, int(np.ceil((1 << 30) / step_bytes)) + 1)
+    layers = [Layer(n, K, N, torch, awq, copies, dev) for n, K, N in LAYERS_7B_FUSED]
+    torch.cuda.synchronize()
+
+    def step(c):
+        for L in layers:
+            p, s, z = L.copies[c]
+            awq.awq_gemm(L.x, p, s, z, out=L.y)
+
+    graphs = [graph_of(torch, lambda c=c: step(c)) for c in range(copies)]
+    ms = time_replays(torch, graphs, args.steps, args.warmup)
+    del graphs, layers
+    return dict(us_per_step=round(ms * 1e3, 3), GBs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                hbm_frac=round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_per_step=step_bytes,
+                launches=len(LAYERS_7B_FUSED), layers_KN=[[K, N] for _, K, N in LAYERS_7B_FUSED])
 
 
 def run_sweep(args, torch, awq, dev):
@@ -304,6 +332,9 @@ def main():
     torch.cuda.empty_cache()
 
     legs = {}
+    log("decode, q/k/v and gate/up fused by concatenated rows (4 launches)")
+    legs["decode_fused_qkv_gateup"] = run_decode_fused(args, torch, awq, dev)
+    torch.cuda.empty_cache()
     if not args.no_sweep:
         log("sweep: (4096, 11008) at M = 1..1024")
         legs["batch_sweep_4096x11008"] = run_sweep(args, torch, awq, dev)

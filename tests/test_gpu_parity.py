@@ -290,6 +290,21 @@ def test_batch_sweep_4096x11008(M):
     assert_y_close(y, oracle.gemm(x, q, z, sc), f"M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 2, 8, 64])
+def test_gemm_fused_rows_equal_separate_layers(M):
+    """q/k/v (or gate/up) stored as one packed matrix with their rows concatenated give, bit for
+    bit, the outputs of the separate layers side by side: every output row is computed from its
+    own weight row alone, whatever the kernel's row blocking."""
+    note(f"fused rows M={M}")
+    K = 1024
+    parts = [_random_packed(N, K, seed=70 + N) for N in (384, 256, 320)]
+    x = dev(activations_fp16(M, K, seed=71 + M))
+    ys = [host(awq.awq_gemm(x, p, scd, zd)) for (_, _, _, p, scd, zd) in parts]
+    cat = [torch.cat([part[i] for part in parts], dim=0) for i in (3, 4, 5)]
+    yf = host(awq.awq_gemm(x, *cat))
+    assert np.array_equal(yf.view(np.uint16), np.concatenate(ys, axis=1).view(np.uint16))
+
+
 def test_gemm_determinism():
     note("gemm determinism")
     q, z, sc, p, scd, zd = _random_packed(1000, 2048, seed=8)

@@ -39,16 +39,21 @@ constexpr int kPBN = 128;     // output columns (weight rows) per block
 constexpr int kXcds = 8;
 constexpr int kLdsBytes = 160 * 1024;
 
-template <int BM, int STAGES, int LDS_BYTES>
+template <int BM, int STAGES, int LDS_BYTES, int KS>
 struct PipeShape {
+  static constexpr int NW = 4 * KS;                  // waves: KS sets of 4, set i takes channel slice i of a group
+  static constexpr int C = kGroup / KS;              // channels of a group per set
+  static constexpr int STEPS = C / 16;               // MFMA steps per group per wave
   static constexpr int AB = BM / 64;                 // 32-row A blocks per wave
   static constexpr int A_HALF = BM * 64;             // halfs in one 64-channel half of the x tile
   static constexpr int B_TILE = kPBN * 32;           // halfs in the packed tile (64 B per row)
   static constexpr int STAGE = 2 * A_HALF + B_TILE;  // halfs per stage
-  static constexpr int LOADS = 2 * (BM / 8 / 4) + kPBN / 16 / 4;  // direct loads per wave per stage
+  static constexpr int LOADS = 2 * (BM / 8 / NW) + kPBN / 16 / NW;  // direct loads per wave per stage
   static constexpr int PIPE_BYTES = STAGES * STAGE * 2;
   static constexpr int META_BYTES = LDS_BYTES - PIPE_BYTES;  // the block's scales and zeros
   static_assert(META_BYTES > 0 && META_BYTES % 16 == 0, "LDS split");
+  static_assert(KS == 1 || KS == 2, "channel split");
+  static_assert(KS == 1 || BM * (kPBN + 1) * 4 <= PIPE_BYTES, "set reduction tile must fit the stage buffers");
 };
 
 // LDS bytes the block's scales ([128][G] fp16) and zeros ([128][ceil(G/2)]) take.
@@ -57,29 +62,36 @@ __host__ __device__ constexpr int64_t pipe_meta_bytes(int64_t G) {
 }
 
 // Copies bytes [0, len) of src (16-byte aligned) to LDS dst (16-byte
-// aligned): whole 16-byte chunks straight into LDS by the block's 4 waves
-// (wave w takes chunks 64(w + 4j) .. +63), the tail bytes (len % 16) by plain
-// loads, which are issued first.
+// aligned): whole 16-byte chunks straight into LDS by the block's NW waves
+// (wave w takes chunks 64(w + NW j) .. +63), the tail bytes (len % 16) by
+// plain loads, which are issued first.
+template <int NW>
 __device__ __forceinline__ void dma_blob(unsigned char* dst, const unsigned char* __restrict__ src, int64_t len,
                                          int wave, int lane, int tid) {
   const int64_t n16 = len / 16;
   if (tid < len - n16 * 16) dst[n16 * 16 + tid] = src[n16 * 16 + tid];
   __asm__ volatile("" ::: "memory");
   wave = __builtin_amdgcn_readfirstlane(wave);
-  for (int64_t base = (int64_t)wave * 64; base < n16; base += 256) {
+  for (int64_t base = (int64_t)wave * 64; base < n16; base += 64 * NW) {
     const int64_t i = base + lane;
     if (i < n16)
       __builtin_amdgcn_global_load_lds((global_ptr_t)(src + 16 * i), (lds_ptr_t)(dst + 16 * base), 16, 0, 0);
   }
 }
 
-template <int BM, int STAGES, int LDS_BYTES>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(163840 / LDS_BYTES, 163840 / LDS_BYTES)))
-void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
-                                                        const f16* __restrict__ scales,
-                                                        const uint8_t* __restrict__ zeros, f16* __restrict__ y,
-                                                        int64_t M, int64_t N, int64_t K, int mt, int nt) {
-  using S = PipeShape<BM, STAGES, LDS_BYTES>;
+// KS = 1: 4 waves in 2 x 2, wave tile (BM / 2) x 64, MFMA lanes of half h take
+// channels 64h + 8s of a group at step s = 0..7.  KS = 2 (two waves per
+// SIMD): 8 waves; waves 4i .. 4i + 3 form set i, which covers the same output
+// tile as KS = 1 over channels 64i .. 64i + 63 of every group (lane half h:
+// channels 64i + 32h + 8s, s = 0..3); the two sets' fp32 partials are summed
+// through LDS at the end, in a fixed order.
+template <int BM, int STAGES, int LDS_BYTES, int KS>
+__global__ __launch_bounds__(256 * KS)
+__attribute__((amdgpu_waves_per_eu(KS * 163840 / LDS_BYTES, KS * 163840 / LDS_BYTES)))
+void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed, const f16* __restrict__ scales,
+                      const uint8_t* __restrict__ zeros, f16* __restrict__ y, int64_t M, int64_t N, int64_t K, int mt,
+                      int nt) {
+  using S = PipeShape<BM, STAGES, LDS_BYTES, KS>;
   constexpr int D = STAGES - 1;  // stages in flight ahead of the one being computed
   __shared__ __attribute__((aligned(16))) f16 lds[LDS_BYTES / 2];
 
@@ -90,7 +102,8 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
   if (nb >= nt) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
+  const int set = wave >> 2, wq = wave & 3;
+  const int wm = wq >> 1, wn = wq & 1, h = lane >> 5, l32 = lane & 31;
   const int64_t m0 = (int64_t)mb * BM, n0 = (int64_t)nb * kPBN;
   const int64_t G = K / kGroup, P2 = (G + 1) / 2;
   const int64_t rows = (N - n0) < kPBN ? (N - n0) : kPBN;  // weight rows of this block
@@ -99,8 +112,8 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
   // Stage slot of group t is t % STAGES; past the last group the tail re-reads
   // group G - 1 into the free slot, so every step issues the same loads and
   // the in-order wait counts below hold on every path.
-  TilePlan<BM, 4, 64> xplan;
-  TilePlan<kPBN, 4, 32> wplan;
+  TilePlan<BM, S::NW, 64> xplan;
+  TilePlan<kPBN, S::NW, 32> wplan;
   xplan.init(x, K, m0, M, wave, lane);
   wplan.init(packed_h, K / 4, n0, N, wave, lane);
   auto issue = [&](int64_t t) {
@@ -117,8 +130,8 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
   // in-order vector-memory count unusable for the direct loads).
   unsigned char* meta = reinterpret_cast<unsigned char*>(lds) + S::PIPE_BYTES;
   const int64_t soff = (kPBN * G * 2 + 15) / 16 * 16;
-  dma_blob(meta, reinterpret_cast<const unsigned char*>(scales) + n0 * G * 2, rows * G * 2, wave, lane, tid);
-  dma_blob(meta + soff, zeros + n0 * P2, rows * P2, wave, lane, tid);
+  dma_blob<S::NW>(meta, reinterpret_cast<const unsigned char*>(scales) + n0 * G * 2, rows * G * 2, wave, lane, tid);
+  dma_blob<S::NW>(meta + soff, zeros + n0 * P2, rows * P2, wave, lane, tid);
   const uint16_t* msc = reinterpret_cast<const uint16_t*>(meta);
   const uint8_t* mz = meta + soff;
 
@@ -130,6 +143,9 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     const int r = wn * 64 + j * 32 + l32;
     mrow[j] = r < rows ? r : (int)rows - 1;
   }
+  // this lane's channel slice of a group: x half-tile, first 8-channel chunk, first packed word
+  const int c0 = set * S::C + h * (S::C / 2);
+  const int ahalf = c0 >> 6, achunk = (c0 & 63) >> 3, bchunk = c0 >> 5;
   // fp16x2 (1024, 1024) bit pattern kept in a vector register, so that each
   // channel pair unpacks with one and-or (a VOP3 operand may not be a literal)
   uint32_t magic;
@@ -152,17 +168,18 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     issue(g + D);
 
     const f16* st = lds + (g % STAGES) * S::STAGE;
-    const f16* Ah = st + h * S::A_HALF;
+    const f16* Ah = st + ahalf * S::A_HALF;
     const f16* Bt = st + 2 * S::A_HALF;
-    u32x4 wlo[2], whi[2];
+    u32x4 wv[2][S::STEPS / 4];
     f16x2 zb[2];
     float scf[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int row = wn * 64 + j * 32 + l32;
-      const int sw = (row >> 1) & 3;  // the tile's chunk swizzle
-      wlo[j] = *reinterpret_cast<const u32x4*>(Bt + row * 32 + (((2 * h) ^ sw) << 3));
-      whi[j] = *reinterpret_cast<const u32x4*>(Bt + row * 32 + (((2 * h + 1) ^ sw) << 3));
+      const int sw = (row >> 2) & 3;  // the tile's chunk swizzle (as frag32)
+#pragma unroll
+      for (int q = 0; q < S::STEPS / 4; ++q)
+        wv[j][q] = *reinterpret_cast<const u32x4*>(Bt + row * 32 + (((bchunk + q) ^ sw) << 3));
       zb[j] = zero_biased((mz[mrow[j] * P2 + (g >> 1)] >> (4 * (g & 1))) & 0xFu);
       scf[j] = (float)as_f16x2((uint32_t)msc[mrow[j] * G + g]).x;
     }
@@ -172,13 +189,13 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
       for (int a = 0; a < S::AB; ++a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][j][r] = fmaf(scf_prev[j], d[a][j][r], acc[a][j][r]);
-    // Software-pipelined over the 8 MFMA steps of the group: the A fragments
+    // Software-pipelined over the MFMA steps of the group: the A fragments
     // and unpacked B operands of step s + 1 are produced while the matrix
     // cores run step s (a scheduling fence closes each step).
     auto unpack = [&](int st_, f16x8(&bq)[2]) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t word = st_ < 4 ? wlo[j][st_ & 3] : whi[j][st_ & 3];
+        const uint32_t word = wv[j][st_ >> 2][st_ & 3];
         const f16x2 q0 = as_f16x2((word & 0x000F000Fu) | magic) - zb[j];
         const f16x2 q1 = as_f16x2(((word >> 4) & 0x000F000Fu) | magic) - zb[j];
         const f16x2 q2 = as_f16x2(((word >> 8) & 0x000F000Fu) | magic) - zb[j];
@@ -188,21 +205,21 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     };
     f16x8 av[2][S::AB], bq[2][2];
 #pragma unroll
-    for (int a = 0; a < S::AB; ++a) av[0][a] = frag(Ah, wm * (BM / 2) + a * 32 + l32, 0);
+    for (int a = 0; a < S::AB; ++a) av[0][a] = frag(Ah, wm * (BM / 2) + a * 32 + l32, achunk);
     unpack(0, bq[0]);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < S::STEPS; ++s) {
       const int c = s & 1, n = c ^ 1;
-      if (s < 7) {
+      if (s + 1 < S::STEPS) {
 #pragma unroll
-        for (int a = 0; a < S::AB; ++a) av[n][a] = frag(Ah, wm * (BM / 2) + a * 32 + l32, s + 1);
+        for (int a = 0; a < S::AB; ++a) av[n][a] = frag(Ah, wm * (BM / 2) + a * 32 + l32, achunk + s + 1);
       }
 #pragma unroll
       for (int a = 0; a < S::AB; ++a)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           d[a][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[c][a], bq[c][j], s == 0 ? f32x16{} : d[a][j], 0, 0, 0);
-      if (s < 7) unpack(s + 1, bq[n]);
+      if (s + 1 < S::STEPS) unpack(s + 1, bq[n]);
       __builtin_amdgcn_sched_barrier(0);  // keep each step's work within the step
     }
     scf_prev[0] = scf[0];
@@ -217,6 +234,29 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
       for (int r = 0; r < 16; ++r) acc[a][j][r] = fmaf(scf_prev[j], d[a][j][r], acc[a][j][r]);
 
   // D register r of lane l: row 8(r/4) + 4(l/32) + r%4, column l%32 of a 32 x 32 block
+  if (KS == 2) {  // set 1 hands its partial tile to set 0 through LDS
+    float* red = reinterpret_cast<float*>(lds);
+    lds_barrier();  // every wave is past its last LDS read of the stage buffers
+    if (set == 1) {
+#pragma unroll
+      for (int a = 0; a < S::AB; ++a)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            red[(wm * (BM / 2) + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * (kPBN + 1) + wn * 64 + j * 32 + l32] =
+                acc[a][j][r];
+    }
+    lds_barrier();
+    if (set == 1) return;
+#pragma unroll
+    for (int a = 0; a < S::AB; ++a)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[a][j][r] += red[(wm * (BM / 2) + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * (kPBN + 1) + wn * 64 + j * 32 + l32];
+  }
 #pragma unroll
   for (int a = 0; a < S::AB; ++a)
 #pragma unroll
@@ -230,12 +270,12 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     }
 }
 
-template <int BM, int STAGES, int LDS_BYTES>
+template <int BM, int STAGES, int LDS_BYTES, int KS>
 static hipError_t pipe_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                               int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int mt = (int)((M + BM - 1) / BM), nt = (int)((N + kPBN - 1) / kPBN);
   const int64_t blocks = (int64_t)((nt + kXcds - 1) / kXcds) * kXcds * mt;
-  gemm_pipe_kernel<BM, STAGES, LDS_BYTES><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+  gemm_pipe_kernel<BM, STAGES, LDS_BYTES, KS><<<dim3((unsigned)blocks), dim3(256 * KS), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),
       reinterpret_cast<const f16*>(scales), reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), M, N,
       K, mt, nt);
@@ -244,11 +284,16 @@ static hipError_t pipe_launch(const void* x, const void* packed, const void* sca
 
 template <int BM, int STAGES, int LDS_BYTES>
 static bool pipe_fits(int64_t G) {
-  return pipe_meta_bytes(G) <= PipeShape<BM, STAGES, LDS_BYTES>::META_BYTES;
+  return pipe_meta_bytes(G) <= PipeShape<BM, STAGES, LDS_BYTES, 1>::META_BYTES;
 }
 
-// Shapes: 128-row x tiles for M > 64, 64-row tiles (two blocks per compute
-// unit) below; fewer stages where the block's scales and zeros need the LDS.
+#ifndef AWQ_PIPE_KS
+#define AWQ_PIPE_KS 2
+#endif
+
+// Shapes: 128-row x tiles for M > 64 (8 waves, two per SIMD, when three
+// stages fit), 64-row tiles (two blocks per compute unit) below; fewer stages
+// where the block's scales and zeros need the LDS.
 bool gemm_pipe_supported(int64_t M, int64_t K) {
   const int64_t G = K / kGroup;
   if (M > 64) return pipe_fits<128, 2, kLdsBytes>(G);
@@ -259,12 +304,14 @@ hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scale
                             int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t G = K / kGroup;
   if (M > 64) {
-    if (pipe_fits<128, 3, kLdsBytes>(G)) return pipe_launch<128, 3, kLdsBytes>(x, packed, scales, zeros, y, M, N, K, st);
-    if (pipe_fits<128, 2, kLdsBytes>(G)) return pipe_launch<128, 2, kLdsBytes>(x, packed, scales, zeros, y, M, N, K, st);
+    if (pipe_fits<128, 3, kLdsBytes>(G))
+      return pipe_launch<128, 3, kLdsBytes, AWQ_PIPE_KS>(x, packed, scales, zeros, y, M, N, K, st);
+    if (pipe_fits<128, 2, kLdsBytes>(G)) return pipe_launch<128, 2, kLdsBytes, 1>(x, packed, scales, zeros, y, M, N, K, st);
     return hipErrorInvalidValue;
   }
-  if (pipe_fits<64, 2, kLdsBytes / 2>(G)) return pipe_launch<64, 2, kLdsBytes / 2>(x, packed, scales, zeros, y, M, N, K, st);
-  if (pipe_fits<64, 3, kLdsBytes>(G)) return pipe_launch<64, 3, kLdsBytes>(x, packed, scales, zeros, y, M, N, K, st);
+  if (pipe_fits<64, 2, kLdsBytes / 2>(G))
+    return pipe_launch<64, 2, kLdsBytes / 2, 1>(x, packed, scales, zeros, y, M, N, K, st);
+  if (pipe_fits<64, 3, kLdsBytes>(G)) return pipe_launch<64, 3, kLdsBytes, 1>(x, packed, scales, zeros, y, M, N, K, st);
   return hipErrorInvalidValue;
 }
 

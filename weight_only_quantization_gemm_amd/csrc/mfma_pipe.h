@@ -4,11 +4,15 @@
 // stages can be in flight), and conflict-free 16-byte fragment reads.
 //
 // LDS tile layout: [rows][8 chunks of 16 B]; chunk c of row r sits in slot
-// c ^ (r & 7).  A direct load writes 1 KB per wave instruction (lane i to
-// bytes 16i..16i+15), i.e. 8 rows; lane i therefore fetches the global chunk
-// (i & 7) ^ (row & 7) of row (i >> 3).  A 32x32x16 fragment read touches 32
-// consecutive rows at one logical chunk, which the XOR spreads over all
-// eight slots of every group of eight rows.
+// c ^ ((r >> 1) & 7).  A direct load writes 1 KB per wave instruction (lane i
+// to bytes 16i..16i+15), i.e. 8 rows; lane i therefore fetches the global
+// chunk (i & 7) ^ ((row >> 1) & 7) of row (i >> 3).  A 32x32x16 fragment read
+// touches 32 consecutive rows at one logical chunk.  The gfx950 LDS serves a
+// 16-byte read for 16 lanes per cycle across 64 four-byte banks (256 B): two
+// rows of 128 B per bank line, so the 8 even and the 8 odd rows of any 16
+// consecutive rows must each cover the 8 slots; the swizzle period of 16 rows
+// does that (measured: 160 B/clk per compute unit, against 120 for a period
+// of 8 rows and 32 unswizzled).
 #pragma once
 
 #include "awq_common.h"
@@ -45,7 +49,7 @@ __device__ __forceinline__ void dl_tile(f16* lds_tile, const f16* __restrict__ g
   for (int j = 0; j < PER_WAVE; ++j) {
     const int blk = wave * PER_WAVE + j;  // 8-row block written by this instruction
     const int row = blk * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ (row & 7);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     int64_t r = row0 + row;
     r = r < row_end ? r : row_end - 1;
     const f16* src = g + r * ld + k0 + chunk * 8;
@@ -55,13 +59,14 @@ __device__ __forceinline__ void dl_tile(f16* lds_tile, const f16* __restrict__ g
 
 // The 16-byte fragment holding logical chunk c of row r of an LDS tile.
 __device__ __forceinline__ f16x8 frag(const f16* lds_tile, int r, int c) {
-  return *reinterpret_cast<const f16x8*>(lds_tile + r * 64 + ((c ^ (r & 7)) << 3));
+  return *reinterpret_cast<const f16x8*>(lds_tile + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
 }
 
 // Narrow tiles: 32 fp16 values (4 chunks) per row.  One direct load covers 16
-// rows; chunk c of row r sits in slot c ^ ((r >> 1) & 3), which keeps the 8
-// rows a fragment read serves per cycle on distinct LDS banks (two 64-byte
-// rows share a 128-byte bank line).
+// rows; chunk c of row r sits in slot c ^ ((r >> 2) & 3): four 64-byte rows
+// share a 256-byte bank line, so each residue of r mod 4 among 16 consecutive
+// rows must cover the 4 slots (measured: 150 B/clk per compute unit, against
+// 117 for c ^ ((r >> 1) & 3)).
 template <int ROWS, int NW>
 __device__ __forceinline__ void dl_tile32(f16* lds_tile, const f16* __restrict__ g, int64_t ld, int64_t row0,
                                           int64_t row_end, int64_t k0, int wave, int lane) {
@@ -72,7 +77,7 @@ __device__ __forceinline__ void dl_tile32(f16* lds_tile, const f16* __restrict__
   for (int j = 0; j < PER_WAVE; ++j) {
     const int blk = wave * PER_WAVE + j;  // 16-row block written by this instruction
     const int row = blk * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
     int64_t r = row0 + row;
     r = r < row_end ? r : row_end - 1;
     const f16* src = g + r * ld + k0 + chunk * 8;
@@ -81,7 +86,7 @@ __device__ __forceinline__ void dl_tile32(f16* lds_tile, const f16* __restrict__
 }
 
 __device__ __forceinline__ f16x8 frag32(const f16* lds_tile, int r, int c) {
-  return *reinterpret_cast<const f16x8*>(lds_tile + r * 32 + ((c ^ ((r >> 1) & 3)) << 3));
+  return *reinterpret_cast<const f16x8*>(lds_tile + r * 32 + ((c ^ ((r >> 2) & 3)) << 3));
 }
 
 // The same copies with the per-lane source addresses computed once: a tile
@@ -106,10 +111,10 @@ struct TilePlan {
       int row, chunk;
       if (WIDTH == 64) {
         row = blk * 8 + (lane >> 3);
-        chunk = (lane & 7) ^ (row & 7);
+        chunk = (lane & 7) ^ ((row >> 1) & 7);
       } else {
         row = blk * 16 + (lane >> 2);
-        chunk = (lane & 3) ^ ((row >> 1) & 3);
+        chunk = (lane & 3) ^ ((row >> 2) & 3);
       }
       int64_t r = row0 + row;
       r = r < row_end ? r : row_end - 1;
