@@ -23,8 +23,10 @@
 // 64h + 8s + 7 at step s = 0..7 in both operands; a lane's 8 B-operand words
 // are then contiguous (words 8h .. 8h + 7 of its row).
 //
-// Blocks: 256 threads = 4 waves in 2 x 2, output tile BM x 128, wave tile
-// (BM / 2) x 64.  Consecutive block ids are dispatched to the 8 XCDs in turn,
+// Blocks: output tile BM x 128 over one or two sets of 4 waves; a set's waves
+// sit 2 x 2 (wave tile (BM / 2) x 64) or 1 x 4 (wave tile BM x 32, each
+// unpacked weight operand then feeds BM / 32 MFMAs).  Consecutive block ids
+// are dispatched to the 8 XCDs in turn,
 // so the block order puts the BM-row tiles that share a weight panel on the
 // same XCD (block b and b + 8), where they share that XCD's L2.
 #include "awq_common.h"
@@ -39,12 +41,16 @@ constexpr int kPBN = 128;     // output columns (weight rows) per block
 constexpr int kXcds = 8;
 constexpr int kLdsBytes = 160 * 1024;
 
-template <int BM, int STAGES, int LDS_BYTES, int KS>
+template <int BM, int STAGES, int LDS_BYTES, int KS, int WN_ = 2>
 struct PipeShape {
   static constexpr int NW = 4 * KS;                  // waves: KS sets of 4, set i takes channel slice i of a group
   static constexpr int C = kGroup / KS;              // channels of a group per set
   static constexpr int STEPS = C / 16;               // MFMA steps per group per wave
-  static constexpr int AB = BM / 64;                 // 32-row A blocks per wave
+  static constexpr int WN = WN_;                     // a set's 4 waves: 4 / WN along M, WN along N
+  static constexpr int WM = 4 / WN;
+  static constexpr int TM = BM / WM, TN = kPBN / WN;  // wave tile
+  static constexpr int AB = TM / 32;                 // 32-row A blocks per wave
+  static constexpr int JB = TN / 32;                 // 32-column B blocks per wave
   static constexpr int A_HALF = BM * 64;             // halfs in one 64-channel half of the x tile
   static constexpr int B_TILE = kPBN * 32;           // halfs in the packed tile (64 B per row)
   static constexpr int STAGE = 2 * A_HALF + B_TILE;  // halfs per stage
@@ -79,19 +85,19 @@ __device__ __forceinline__ void dma_blob(unsigned char* dst, const unsigned char
   }
 }
 
-// KS = 1: 4 waves in 2 x 2, wave tile (BM / 2) x 64, MFMA lanes of half h take
-// channels 64h + 8s of a group at step s = 0..7.  KS = 2 (two waves per
-// SIMD): 8 waves; waves 4i .. 4i + 3 form set i, which covers the same output
-// tile as KS = 1 over channels 64i .. 64i + 63 of every group (lane half h:
-// channels 64i + 32h + 8s, s = 0..3); the two sets' fp32 partials are summed
-// through LDS at the end, in a fixed order.
-template <int BM, int STAGES, int LDS_BYTES, int KS>
+// KS = 1: one set of 4 waves; MFMA lanes of half h take channels 64h + 8s of
+// a group at step s = 0..7.  KS = 2 (two waves per SIMD): 8 waves; waves
+// 4i .. 4i + 3 form set i, which covers the whole output tile over channels
+// 64i .. 64i + 63 of every group (lane half h: channels 64i + 32h + 8s,
+// s = 0..3); the two sets' fp32 partials are summed through LDS at the end,
+// in a fixed order.  WN: waves of a set along N (2: 2 x 2, 4: 1 x 4).
+template <int BM, int STAGES, int LDS_BYTES, int KS, int WN>
 __global__ __launch_bounds__(256 * KS)
 __attribute__((amdgpu_waves_per_eu(KS * 163840 / LDS_BYTES, KS * 163840 / LDS_BYTES)))
 void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed, const f16* __restrict__ scales,
                       const uint8_t* __restrict__ zeros, f16* __restrict__ y, int64_t M, int64_t N, int64_t K, int mt,
                       int nt) {
-  using S = PipeShape<BM, STAGES, LDS_BYTES, KS>;
+  using S = PipeShape<BM, STAGES, LDS_BYTES, KS, WN>;
   constexpr int D = STAGES - 1;  // stages in flight ahead of the one being computed
   __shared__ __attribute__((aligned(16))) f16 lds[LDS_BYTES / 2];
 
@@ -103,7 +109,7 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int set = wave >> 2, wq = wave & 3;
-  const int wm = wq >> 1, wn = wq & 1, h = lane >> 5, l32 = lane & 31;
+  const int wm = wq / WN, wn = wq % WN, h = lane >> 5, l32 = lane & 31;
   const int64_t m0 = (int64_t)mb * BM, n0 = (int64_t)nb * kPBN;
   const int64_t G = K / kGroup, P2 = (G + 1) / 2;
   const int64_t rows = (N - n0) < kPBN ? (N - n0) : kPBN;  // weight rows of this block
@@ -137,10 +143,10 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
 
   for (int t = 0; t < D; ++t) issue(t);
 
-  int mrow[2];  // LDS meta row of the lane's two weight rows (clamped to the block's rows)
+  int mrow[S::JB];  // LDS meta row of the lane's weight rows (clamped to the block's rows)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = wn * 64 + j * 32 + l32;
+  for (int j = 0; j < S::JB; ++j) {
+    const int r = wn * S::TN + j * 32 + l32;
     mrow[j] = r < rows ? r : (int)rows - 1;
   }
   // this lane's channel slice of a group: x half-tile, first 8-channel chunk, first packed word
@@ -153,14 +159,16 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
 
   // acc += scale(g) * d(g) is applied one group late, after the next group's
   // loads are issued, where it fills the wait for that group's LDS reads.
-  f32x16 acc[S::AB][2], d[S::AB][2];
+  f32x16 acc[S::AB][S::JB], d[S::AB][S::JB];
 #pragma unroll
   for (int a = 0; a < S::AB; ++a)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < S::JB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][j][r] = d[a][j][r] = 0.f;
-  float scf_prev[2] = {0.f, 0.f};
+  float scf_prev[S::JB];
+#pragma unroll
+  for (int j = 0; j < S::JB; ++j) scf_prev[j] = 0.f;
 
   for (int64_t g = 0; g < G; ++g) {
     wait_vmcnt<(D - 1) * S::LOADS>();  // stage g has landed; stages g+1 .. g+D-1 may be pending
@@ -170,12 +178,12 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     const f16* st = lds + (g % STAGES) * S::STAGE;
     const f16* Ah = st + ahalf * S::A_HALF;
     const f16* Bt = st + 2 * S::A_HALF;
-    u32x4 wv[2][S::STEPS / 4];
-    f16x2 zb[2];
-    float scf[2];
+    u32x4 wv[S::JB][S::STEPS / 4];
+    f16x2 zb[S::JB];
+    float scf[S::JB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = wn * 64 + j * 32 + l32;
+    for (int j = 0; j < S::JB; ++j) {
+      const int row = wn * S::TN + j * 32 + l32;
       const int sw = (row >> 2) & 3;  // the tile's chunk swizzle (as frag32)
 #pragma unroll
       for (int q = 0; q < S::STEPS / 4; ++q)
@@ -184,7 +192,7 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
       scf[j] = (float)as_f16x2((uint32_t)msc[mrow[j] * G + g]).x;
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < S::JB; ++j)
 #pragma unroll
       for (int a = 0; a < S::AB; ++a)
 #pragma unroll
@@ -192,9 +200,9 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     // Software-pipelined over the MFMA steps of the group: the A fragments
     // and unpacked B operands of step s + 1 are produced while the matrix
     // cores run step s (a scheduling fence closes each step).
-    auto unpack = [&](int st_, f16x8(&bq)[2]) {
+    auto unpack = [&](int st_, f16x8(&bq)[S::JB]) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < S::JB; ++j) {
         const uint32_t word = wv[j][st_ >> 2][st_ & 3];
         const f16x2 q0 = as_f16x2((word & 0x000F000Fu) | magic) - zb[j];
         const f16x2 q1 = as_f16x2(((word >> 4) & 0x000F000Fu) | magic) - zb[j];
@@ -203,31 +211,31 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
         bq[j] = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
       }
     };
-    f16x8 av[2][S::AB], bq[2][2];
+    f16x8 av[2][S::AB], bq[2][S::JB];
 #pragma unroll
-    for (int a = 0; a < S::AB; ++a) av[0][a] = frag(Ah, wm * (BM / 2) + a * 32 + l32, achunk);
+    for (int a = 0; a < S::AB; ++a) av[0][a] = frag(Ah, wm * S::TM + a * 32 + l32, achunk);
     unpack(0, bq[0]);
 #pragma unroll
     for (int s = 0; s < S::STEPS; ++s) {
       const int c = s & 1, n = c ^ 1;
       if (s + 1 < S::STEPS) {
 #pragma unroll
-        for (int a = 0; a < S::AB; ++a) av[n][a] = frag(Ah, wm * (BM / 2) + a * 32 + l32, achunk + s + 1);
+        for (int a = 0; a < S::AB; ++a) av[n][a] = frag(Ah, wm * S::TM + a * 32 + l32, achunk + s + 1);
       }
 #pragma unroll
       for (int a = 0; a < S::AB; ++a)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < S::JB; ++j)
           d[a][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[c][a], bq[c][j], s == 0 ? f32x16{} : d[a][j], 0, 0, 0);
       if (s + 1 < S::STEPS) unpack(s + 1, bq[n]);
       __builtin_amdgcn_sched_barrier(0);  // keep each step's work within the step
     }
-    scf_prev[0] = scf[0];
-    scf_prev[1] = scf[1];
+#pragma unroll
+    for (int j = 0; j < S::JB; ++j) scf_prev[j] = scf[j];
   }
   wait_vmcnt<0>();  // the tail's redundant LDS loads land before the block can exit
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < S::JB; ++j)
 #pragma unroll
     for (int a = 0; a < S::AB; ++a)
 #pragma unroll
@@ -241,10 +249,10 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
 #pragma unroll
       for (int a = 0; a < S::AB; ++a)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < S::JB; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            red[(wm * (BM / 2) + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * (kPBN + 1) + wn * 64 + j * 32 + l32] =
+            red[(wm * S::TM + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * (kPBN + 1) + wn * S::TN + j * 32 + l32] =
                 acc[a][j][r];
     }
     lds_barrier();
@@ -252,30 +260,30 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
 #pragma unroll
     for (int a = 0; a < S::AB; ++a)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < S::JB; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          acc[a][j][r] += red[(wm * (BM / 2) + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * (kPBN + 1) + wn * 64 + j * 32 + l32];
+          acc[a][j][r] += red[(wm * S::TM + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * (kPBN + 1) + wn * S::TN + j * 32 + l32];
   }
 #pragma unroll
   for (int a = 0; a < S::AB; ++a)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 32 + l32;
+    for (int j = 0; j < S::JB; ++j) {
+      const int64_t n = n0 + wn * S::TN + j * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * (BM / 2) + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t m = m0 + wm * S::TM + a * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < M && n < N) y[m * N + n] = (f16)acc[a][j][r];
       }
     }
 }
 
-template <int BM, int STAGES, int LDS_BYTES, int KS>
+template <int BM, int STAGES, int LDS_BYTES, int KS, int WN>
 static hipError_t pipe_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                               int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int mt = (int)((M + BM - 1) / BM), nt = (int)((N + kPBN - 1) / kPBN);
   const int64_t blocks = (int64_t)((nt + kXcds - 1) / kXcds) * kXcds * mt;
-  gemm_pipe_kernel<BM, STAGES, LDS_BYTES, KS><<<dim3((unsigned)blocks), dim3(256 * KS), 0, st>>>(
+  gemm_pipe_kernel<BM, STAGES, LDS_BYTES, KS, WN><<<dim3((unsigned)blocks), dim3(256 * KS), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),
       reinterpret_cast<const f16*>(scales), reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), M, N,
       K, mt, nt);
@@ -287,8 +295,15 @@ static bool pipe_fits(int64_t G) {
   return pipe_meta_bytes(G) <= PipeShape<BM, STAGES, LDS_BYTES, 1>::META_BYTES;
 }
 
+// Measured on the (4096, 11008) and (8192, 28672) layers at M = 128..1024:
+// the 1 x 4 wave layout (wave tile 128 x 32: each unpacked weight operand
+// feeds four MFMAs) beats 2 x 2 by 10-15 %; two wave sets per block add ~3 %
+// at K = 4096 and are neutral at K = 8192.
 #ifndef AWQ_PIPE_KS
 #define AWQ_PIPE_KS 2
+#endif
+#ifndef AWQ_PIPE_WN
+#define AWQ_PIPE_WN 4
 #endif
 
 // Shapes: 128-row x tiles for M > 64 (8 waves, two per SIMD, when three
@@ -305,13 +320,14 @@ hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scale
   const int64_t G = K / kGroup;
   if (M > 64) {
     if (pipe_fits<128, 3, kLdsBytes>(G))
-      return pipe_launch<128, 3, kLdsBytes, AWQ_PIPE_KS>(x, packed, scales, zeros, y, M, N, K, st);
-    if (pipe_fits<128, 2, kLdsBytes>(G)) return pipe_launch<128, 2, kLdsBytes, 1>(x, packed, scales, zeros, y, M, N, K, st);
+      return pipe_launch<128, 3, kLdsBytes, AWQ_PIPE_KS, AWQ_PIPE_WN>(x, packed, scales, zeros, y, M, N, K, st);
+    if (pipe_fits<128, 2, kLdsBytes>(G))
+      return pipe_launch<128, 2, kLdsBytes, 1, AWQ_PIPE_WN>(x, packed, scales, zeros, y, M, N, K, st);
     return hipErrorInvalidValue;
   }
   if (pipe_fits<64, 2, kLdsBytes / 2>(G))
-    return pipe_launch<64, 2, kLdsBytes / 2, 1>(x, packed, scales, zeros, y, M, N, K, st);
-  if (pipe_fits<64, 3, kLdsBytes>(G)) return pipe_launch<64, 3, kLdsBytes, 1>(x, packed, scales, zeros, y, M, N, K, st);
+    return pipe_launch<64, 2, kLdsBytes / 2, 1, 2>(x, packed, scales, zeros, y, M, N, K, st);
+  if (pipe_fits<64, 3, kLdsBytes>(G)) return pipe_launch<64, 3, kLdsBytes, 1, 2>(x, packed, scales, zeros, y, M, N, K, st);
   return hipErrorInvalidValue;
 }
 
