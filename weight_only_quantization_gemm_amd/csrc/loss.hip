@@ -18,19 +18,29 @@
 //
 // This Gram form is used when M >= K; for M < K see the direct form below.
 //
-// G is symmetric: with channels in 128-wide blocks I, J,
-//   sum_n E'_n G' E'_n^T = sum_n [ sum_J E'_nJ G'_JJ E'_nJ^T + 2 sum_{I<J} E'_nI G'_IJ E'_nJ^T ],
-// so a block (rows n, column block J) contracts over channel blocks I <= J
-// only and doubles (exactly) its accumulator before the diagonal block.
+// Blocking: 256 x 256 tiles of T = E' G' (rows n, columns j) over all K
+// channels.  Every tile has the same work, so the blocks of a launch run
+// side by side and stay in step, and the tiles are ordered so that the 32
+// blocks an XCD runs at once cover 4 E' panels x 8 G' panels: each operand
+// chunk is then fetched into that XCD's L2 once and read by 8 (or 4) blocks.
+// (Contracting only the channel blocks I <= J of the symmetric G' halves the
+// flops but gives blocks of unequal length, which drift apart and lose that
+// reuse; measured slower.)
 #include "awq_common.h"
 #include "awq_internal.h"
 #include "mfma_pipe.h"
 
 namespace awq {
 
-constexpr int kLT = 128;           // block tile: 128 rows n x 128 columns j
+constexpr int kFT = 256;     // tile of T: 256 rows n x 256 columns j
+constexpr int kFKS = 32;     // channels per pipeline stage
+constexpr int kFStages = 2;
+constexpr int kFLoads = 4 * (kFT / 16 / 8);  // direct loads per wave per stage
 
-int64_t loss_partial_count(int64_t N, int64_t K) { return ((N + kLT - 1) / kLT) * (K / kLT); }
+static int64_t full_tiles_n(int64_t N) { return (N + kFT - 1) / kFT; }
+static int64_t full_tiles_j(int64_t K) { return (K + kFT - 1) / kFT; }
+
+int64_t loss_partial_count(int64_t N, int64_t K) { return full_tiles_n(N) * full_tiles_j(K); }
 
 // e_k = floor(log2(G_kk) / 2), 0 where G_kk is 0 (a channel that is zero in every row).
 __global__ void channel_exponent_kernel(const float* __restrict__ G, int64_t K, int32_t* __restrict__ e) {
@@ -60,122 +70,134 @@ hipError_t launch_gram_split(const float* G, int64_t K, int32_t* e, void* Ghi, v
   return hipGetLastError();
 }
 
-// Block: 256 threads = 4 waves in 2 x 2, each a 64 x 64 tile of 2 x 2
-// v_mfma_f32_32x32x16_f16 (D register r of lane l is
-// D[8*(r/4) + 4*(l/32) + r%4][l%32]).  Channels are consumed 32 at a time; the
-// four operand tiles of a stage (E' hi/lo rows n, G' hi/lo rows j, 128 x 32
-// each) go straight from global memory into LDS, four stages deep.
-constexpr int kLKS = 32;
-constexpr int kLStages = 4;
-constexpr int kLLoadsPerWave = 4 * kLT / 16 / 4;  // direct loads per wave per stage
+// Tile of block b: XCD x = b % 8 takes the contiguous range of tile indices
+// [x * per, (x + 1) * per), and tile indices walk 4 n-tiles before advancing j.
+struct FullTile {
+  int t, jb, nb;
+};
+__device__ inline FullTile full_tile(int b, int nt, int jt) {
+  const int T = nt * jt, per = (T + 7) / 8;
+  const int t = (b & 7) * per + (b >> 3);
+  if (t >= T) return FullTile{-1, 0, 0};
+  const int g = t / (4 * jt);  // group of (up to) 4 n-tiles
+  const int gn = (nt - 4 * g) < 4 ? (nt - 4 * g) : 4;
+  const int w = t - g * 4 * jt;
+  return FullTile{t, w / gn, 4 * g + w % gn};
+}
 
-__global__ __launch_bounds__(256) void loss_partial_kernel(const f16* __restrict__ Ehi, const f16* __restrict__ Elo,
-                                                           const f16* __restrict__ Ghi, const f16* __restrict__ Glo,
-                                                           int64_t N, int64_t K, double* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) f16 lds[kLStages][4][kLT * kLKS];  // 131,072 B
-  __shared__ double red[4];
+// Block: 512 threads = 8 waves (two per SIMD) in 2 (j) x 4 (n), wave tile
+// 128 j x 64 n.  The matrix cores form D[j][n] = sum_k G'[j][k] E'[n][k] =
+// T[n][j] (G' is symmetric): A operand = rows j of G', B operand = rows n of
+// E', three MFMAs (hi.hi, hi.lo, lo.hi) per fragment pair.  D register r of
+// lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32], so a lane's registers 4q..4q+3
+// are 4 consecutive j of one n and the epilogue reads E'[n][j..j+3] with one
+// 8-byte load per fp16 half.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void loss_full_kernel(const f16* __restrict__ Ehi, const f16* __restrict__ Elo, const f16* __restrict__ Ghi,
+                      const f16* __restrict__ Glo, int64_t N, int64_t K, int nt, int jt, double* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) f16 lds[kFStages][4][kFT * kFKS];  // 131,072 B
+  __shared__ double red[8];
+  const FullTile ft = full_tile((int)blockIdx.x, nt, jt);
+  if (ft.t < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t n0 = (int64_t)blockIdx.y * kLT;
-  const int64_t j0 = (int64_t)blockIdx.x * kLT;
-  const int64_t S = (j0 + kLT) / kLKS;  // channel blocks I <= J
+  const int wj = wave >> 2, wn = wave & 3, l32 = lane & 31;
+  const int64_t j0 = (int64_t)ft.jb * kFT, n0 = (int64_t)ft.nb * kFT;
+  const int64_t S = K / kFKS;
 
+  TilePlan<kFT, 8, 32> pgh, pgl, peh, pel;
+  pgh.init(Ghi, K, j0, K, wave, lane);
+  pgl.init(Glo, K, j0, K, wave, lane);
+  peh.init(Ehi, K, n0, N, wave, lane);
+  pel.init(Elo, K, n0, N, wave, lane);
+  // past the last stage the tail re-reads stage S - 1 into the free slot
   auto issue = [&](int64_t s) {
-    const int64_t k0 = s * kLKS;
-    dl_tile32<kLT, 4>(lds[s % kLStages][0], Ehi, K, n0, N, k0, wave, lane);
-    dl_tile32<kLT, 4>(lds[s % kLStages][1], Elo, K, n0, N, k0, wave, lane);
-    dl_tile32<kLT, 4>(lds[s % kLStages][2], Ghi, K, j0, K, k0, wave, lane);
-    dl_tile32<kLT, 4>(lds[s % kLStages][3], Glo, K, j0, K, k0, wave, lane);
+    const int64_t k0 = (s < S ? s : S - 1) * kFKS;
+    pgh.issue(lds[s & 1][0], k0);
+    pgl.issue(lds[s & 1][1], k0);
+    peh.issue(lds[s & 1][2], k0);
+    pel.issue(lds[s & 1][3], k0);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // E' rows n >= N are read from row N - 1; mask their A fragments to zero.
-  bool arow_live[2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a) arow_live[a] = n0 + wm * 64 + a * 32 + (lane & 31) < N;
-
-  for (int64_t s = 0; s < kLStages - 1 && s < S; ++s) issue(s);
+  issue(0);
   for (int64_t s = 0; s < S; ++s) {
-    const int64_t ahead = (S - 1 - s) < (kLStages - 2) ? (S - 1 - s) : (kLStages - 2);
-    if (ahead >= 2) wait_vmcnt<2 * kLLoadsPerWave>();
-    else if (ahead == 1) wait_vmcnt<kLLoadsPerWave>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (s + kLStages - 1 < S) issue(s + kLStages - 1);
-    if (s * kLKS == j0) {  // entering the diagonal block: off-diagonal blocks count twice
+    wait_vmcnt<0>();  // stage s has landed (the only one in flight)
+    lds_barrier();    // ... for every wave; stage s - 1 is no longer read
+    issue(s + 1);
+    const f16* Gh = lds[s & 1][0];
+    const f16* Gl = lds[s & 1][1];
+    const f16* Eh = lds[s & 1][2];
+    const f16* El = lds[s & 1][3];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[a][b][r] *= 2.0f;
-    }
-    const f16* Ah = lds[s % kLStages][0];
-    const f16* Al = lds[s % kLStages][1];
-    const f16* Bh = lds[s % kLStages][2];
-    const f16* Bl = lds[s % kLStages][3];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 2 * h + (lane >> 5);
-      f16x8 ah[2], al[2], bh[2], bl[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int row = wm * 64 + a * 32 + (lane & 31);
-        const f16x8 zero8 = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        ah[a] = arow_live[a] ? frag32(Ah, row, c) : zero8;
-        al[a] = arow_live[a] ? frag32(Al, row, c) : zero8;
-      }
+    for (int hk = 0; hk < 2; ++hk) {
+      const int c = 2 * hk + (lane >> 5);
+      f16x8 eh[2], el[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int row = wn * 64 + b * 32 + (lane & 31);
-        bh[b] = frag32(Bh, row, c);
-        bl[b] = frag32(Bl, row, c);
+        eh[b] = frag32(Eh, wn * 64 + b * 32 + l32, c);
+        el[b] = frag32(El, wn * 64 + b * 32 + l32, c);
       }
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 4; ++a) {
+        const f16x8 gh = frag32(Gh, wj * 128 + a * 32 + l32, c);
+        const f16x8 gl = frag32(Gl, wj * 128 + a * 32 + l32, c);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[a], bh[b], acc[a][b], 0, 0, 0);
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[a], bl[b], acc[a][b], 0, 0, 0);
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[a], bh[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gh, eh[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gh, el[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gl, eh[b], acc[a][b], 0, 0, 0);
         }
+      }
     }
   }
+  wait_vmcnt<0>();  // the tail's redundant loads land before the block can exit
 
   // partial = sum over the tile of E'[n][j] * T[n][j], E' = hi + lo in fp32
   double sum = 0.0;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int b = 0; b < 2; ++b) {
+    const int64_t n = n0 + wn * 64 + b * 32 + l32;
+    if (n >= N) continue;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t n = n0 + wm * 64 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t j = j0 + wn * 64 + b * 32 + (lane & 31);
-        if (n < N) {
-          const float e = (float)Ehi[n * K + j] + (float)Elo[n * K + j];
-          sum += (double)e * (double)acc[a][b][r];
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int64_t j = j0 + wj * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
+        if (j >= K) continue;  // K % 128 == 0: the 4 channels j .. j + 3 are all in range or all out
+        const uint2 hv = *reinterpret_cast<const uint2*>(Ehi + n * K + j);
+        const uint2 lv = *reinterpret_cast<const uint2*>(Elo + n * K + j);
+        const f16x2 h01 = as_f16x2(hv.x), h23 = as_f16x2(hv.y), l01 = as_f16x2(lv.x), l23 = as_f16x2(lv.y);
+        const float e[4] = {(float)h01.x + (float)l01.x, (float)h01.y + (float)l01.y, (float)h23.x + (float)l23.x,
+                            (float)h23.y + (float)l23.y};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sum += (double)e[u] * (double)acc[a][b][4 * q + u];
       }
+  }
   sum = wave_sum(sum);
   if (lane == 0) red[wave] = sum;
   __syncthreads();
-  if (tid == 0) partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid == 0) {
+    double v = 0.0;
+    for (int w = 0; w < 8; ++w) v += red[w];
+    partial[ft.t] = v;
+  }
 }
 
 hipError_t launch_loss_partials(const void* Ehi, const void* Elo, const void* Ghi, const void* Glo, int64_t N,
                                 int64_t K, double* partial, hipStream_t st) {
-  dim3 grid((unsigned)(K / kLT), (unsigned)((N + kLT - 1) / kLT));
-  loss_partial_kernel<<<grid, dim3(256), 0, st>>>(
+  const int nt = (int)full_tiles_n(N), jt = (int)full_tiles_j(K);
+  const int64_t T = (int64_t)nt * jt;
+  const int64_t blocks = (T + 7) / 8 * 8;
+  loss_full_kernel<<<dim3((unsigned)blocks), dim3(512), 0, st>>>(
       reinterpret_cast<const f16*>(Ehi), reinterpret_cast<const f16*>(Elo), reinterpret_cast<const f16*>(Ghi),
-      reinterpret_cast<const f16*>(Glo), N, K, partial);
+      reinterpret_cast<const f16*>(Glo), N, K, nt, jt, partial);
   return hipGetLastError();
 }
 
