@@ -24,6 +24,66 @@ constexpr int kGStages = 4;       // pipeline depth
 constexpr int kGFlush = 4;        // stages (x 64 rows) per fp32 partial
 constexpr int kGLoadsPerWave = 2 * kGT / 8 / 4;  // direct loads per wave per stage (A and B)
 
+// Tile order.  The upper-triangle tiles (I <= J) are grouped into 4 x 4
+// super-tiles (SI, SJ), SI <= SJ, numbered row by row; XCD x (block ids b with
+// b % 8 == x, which the dispatcher places on XCD x) works through super-tiles
+// x, x + 8, x + 16, ..., each one's tiles in turn, so the 32 blocks an XCD
+// runs at once read about 8 distinct row panels of X^T and its L2 serves each
+// panel chunk to several blocks.
+constexpr int kGS = 4;
+
+__host__ __device__ inline int gram_super_tiles(int nb) { return (nb + kGS - 1) / kGS; }
+
+// tiles of super-tile (si, sj) that lie on or above the diagonal
+__host__ __device__ inline int gram_super_count(int si, int sj, int nb) {
+  const int ni = (nb - kGS * si) < kGS ? (nb - kGS * si) : kGS;
+  const int nj = (nb - kGS * sj) < kGS ? (nb - kGS * sj) : kGS;
+  return si == sj ? ni * (ni + 1) / 2 : ni * nj;
+}
+
+// (I, J) of the q-th tile on XCD x; false past the XCD's last tile
+__host__ __device__ inline bool gram_tile(int x, int q, int nb, int& I, int& J) {
+  const int ns = gram_super_tiles(nb);
+  int si = 0, sj = 0, s = 0;  // super-tile s = (si, sj), row-major over si <= sj
+  auto advance = [&](int steps) {
+    for (int k = 0; k < steps; ++k) {
+      if (++sj == ns) {
+        ++si;
+        sj = si;
+      }
+      ++s;
+    }
+  };
+  advance(x);
+  const int total = ns * (ns + 1) / 2;
+  while (s < total) {
+    const int c = gram_super_count(si, sj, nb);
+    if (q < c) {
+      const int ni = (nb - kGS * si) < kGS ? (nb - kGS * si) : kGS;
+      const int nj = (nb - kGS * sj) < kGS ? (nb - kGS * sj) : kGS;
+      int i = 0, j = 0;
+      if (si == sj) {  // row i holds ni - i tiles (j = i .. ni - 1)
+        int r = q;
+        while (r >= ni - i) {
+          r -= ni - i;
+          ++i;
+        }
+        j = i + r;
+      } else {
+        i = q / nj;
+        j = q - i * nj;
+      }
+      (void)ni;
+      I = kGS * si + i;
+      J = kGS * sj + j;
+      return true;
+    }
+    q -= c;
+    advance(8);
+  }
+  return false;
+}
+
 // Xt: fp16 [K][Mp] (rows of X^T), Mp % 64 == 0, K % 128 == 0.  Block: 4 waves
 // in 2 x 2, each a 64 x 64 tile of 2 x 2 32x32x16 MFMAs; D register r of lane l
 // is D[8*(r/4) + 4*(l/32) + r%4][l%32].
@@ -31,12 +91,8 @@ __global__ __launch_bounds__(256) void gram_kernel(const f16* __restrict__ Xt, i
                                                    float* __restrict__ G) {
   __shared__ __attribute__((aligned(16))) f16 lds[kGStages][2][kGT * 64];  // 131,072 B
   const int nb = (int)(K / kGT);
-  int I = 0, rem = (int)blockIdx.x;
-  while (rem >= nb - I) {  // row I of the upper triangle holds nb - I tiles
-    rem -= nb - I;
-    ++I;
-  }
-  const int J = I + rem;
+  int I, J;
+  if (!gram_tile((int)(blockIdx.x & 7), (int)(blockIdx.x >> 3), nb, I, J)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t r0 = (int64_t)I * kGT, c0 = (int64_t)J * kGT;
@@ -120,8 +176,13 @@ __global__ __launch_bounds__(256) void gram_kernel(const f16* __restrict__ Xt, i
 }
 
 hipError_t launch_gram(const void* Xt, int64_t Mp, int64_t K, float* G, hipStream_t st) {
-  const int64_t nb = K / kGT;
-  const int64_t blocks = nb * (nb + 1) / 2;
+  const int nb = (int)(K / kGT), ns = gram_super_tiles(nb);
+  int per[8] = {0, 0, 0, 0, 0, 0, 0, 0}, s = 0;
+  for (int si = 0; si < ns; ++si)
+    for (int sj = si; sj < ns; ++sj, ++s) per[s % 8] += gram_super_count(si, sj, nb);
+  int most = 0;
+  for (int x = 0; x < 8; ++x) most = per[x] > most ? per[x] : most;
+  const int64_t blocks = 8 * (int64_t)most;
   gram_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(reinterpret_cast<const f16*>(Xt), Mp, K, G);
   return hipGetLastError();
 }

@@ -94,8 +94,8 @@ __device__ __forceinline__ f16x8 frag32(const f16* lds_tile, int r, int c) {
 // load instruction.  WIDTH is 64 (layout of dl_tile) or 32 (dl_tile32).
 template <int ROWS, int NW, int WIDTH>
 struct TilePlan {
-  static_assert(WIDTH == 64 || WIDTH == 32, "tile width");
-  static constexpr int ROWS_PER_LOAD = WIDTH == 64 ? 8 : 16;
+  static_assert(WIDTH == 64 || WIDTH == 32 || WIDTH == 16, "tile width");
+  static constexpr int ROWS_PER_LOAD = 512 / WIDTH;
   static constexpr int PER_WAVE = ROWS / ROWS_PER_LOAD / NW;
   static_assert(ROWS % (ROWS_PER_LOAD * NW) == 0, "tile rows must split evenly over the waves");
   const f16* src[PER_WAVE];
@@ -112,9 +112,12 @@ struct TilePlan {
       if (WIDTH == 64) {
         row = blk * 8 + (lane >> 3);
         chunk = (lane & 7) ^ ((row >> 1) & 7);
-      } else {
+      } else if (WIDTH == 32) {
         row = blk * 16 + (lane >> 2);
         chunk = (lane & 3) ^ ((row >> 2) & 3);
+      } else {
+        row = blk * 32 + (lane >> 1);
+        chunk = (lane & 1) ^ ((row >> 3) & 1);
       }
       int64_t r = row0 + row;
       r = r < row_end ? r : row_end - 1;
@@ -130,5 +133,11 @@ struct TilePlan {
                                        (lds_ptr_t)(lds_tile + lds_off + j * ROWS_PER_LOAD * WIDTH), 16, 0, 0);
   }
 };
+
+// 16-wide tiles (2 chunks of 16 B per row): eight 32-byte rows share a
+// 256-byte bank line, so chunk c of row r sits in slot c ^ ((r >> 3) & 1).
+__device__ __forceinline__ f16x8 frag16(const f16* lds_tile, int r, int c) {
+  return *reinterpret_cast<const f16x8*>(lds_tile + r * 16 + ((c ^ ((r >> 3) & 1)) << 3));
+}
 
 }  // namespace awq
