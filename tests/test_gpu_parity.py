@@ -221,7 +221,7 @@ def test_gemm_one_hot_reproduces_dequantized_column(M):
         assert np.array_equal(y[m], col.astype(np.float16)), (m, k)
 
 
-@pytest.mark.parametrize("M", [1, 8, 64])
+@pytest.mark.parametrize("M", [1, 5, 8, 9, 64])
 def test_gemm_codes_equal_zeros_gives_zero(M):
     note(f"gemm zero codes M={M}")
     N, K = 64, 256
@@ -235,7 +235,7 @@ def test_gemm_codes_equal_zeros_gives_zero(M):
     if M > 2:
         assert np.all(y == 0)  # the matrix-core kernels subtract the zero point per code, exactly
     else:
-        # the decode GEMV folds the zero point as z * sum(x): y is 0 up to fp32 rounding of
+        # the decode GEMV (M <= 2) folds the zero point as z * sum(x): y is 0 up to fp32 rounding of
         # sums of at most 32 * 15 * |x| (2^-24 relative per addition)
         bound = 1e-6 * np.abs(x.astype(np.float64)).sum(axis=1, keepdims=True) * 15 * 0.01
         assert np.all(np.abs(y) <= bound)

@@ -163,6 +163,9 @@ static hipError_t gemv_m(const void* x, const void* packed, const void* scales, 
   return hipGetLastError();
 }
 
+// M <= 2 only: every further activation row costs 4 more dot2 per packed
+// word and the kernel turns VALU-bound (measured at M = 3..8 on the 7B/70B
+// shapes: 1.1-2.4x slower than the matrix-core kernel).
 bool gemv_dot2_supported(int64_t M, int64_t K) { return M >= 1 && M <= 2 && K / 32 <= (int64_t)kMaxWaves * kWave; }
 
 // Rows per block, measured on the Llama-2 7B/70B decode shapes: 2 keeps more
@@ -175,19 +178,19 @@ static int gemv_rows(int64_t N, int64_t K) {
   return 4;
 }
 
+template <int MB>
+static hipError_t gemv_rows_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                                   int64_t N, int64_t K, hipStream_t st) {
+  const int R = gemv_rows(N, K);
+  if (R == 2) return gemv_m<MB, 2>(x, packed, scales, zeros, y, N, K, st);
+  if (R == 8) return gemv_m<MB, 8>(x, packed, scales, zeros, y, N, K, st);
+  return gemv_m<MB, 4>(x, packed, scales, zeros, y, N, K, st);
+}
+
 hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const int R = gemv_rows(N, K);
-  if (M == 1) {
-    if (R == 2) return gemv_m<1, 2>(x, packed, scales, zeros, y, N, K, st);
-    if (R == 8) return gemv_m<1, 8>(x, packed, scales, zeros, y, N, K, st);
-    return gemv_m<1, 4>(x, packed, scales, zeros, y, N, K, st);
-  }
-  if (M == 2) {
-    if (R == 2) return gemv_m<2, 2>(x, packed, scales, zeros, y, N, K, st);
-    if (R == 8) return gemv_m<2, 8>(x, packed, scales, zeros, y, N, K, st);
-    return gemv_m<2, 4>(x, packed, scales, zeros, y, N, K, st);
-  }
+  if (M == 1) return gemv_rows_launch<1>(x, packed, scales, zeros, y, N, K, st);
+  if (M == 2) return gemv_rows_launch<2>(x, packed, scales, zeros, y, N, K, st);
   return hipErrorInvalidValue;
 }
 

@@ -159,15 +159,21 @@ static hipError_t skinny_launch(const void* x, const void* packed, const void* s
   return hipGetLastError();
 }
 
-// Tile shape, measured on the Llama-2 7B/70B decode shapes at M = 2..16:
-// at most 8 waves per block (more leaves one block per compute unit with no
-// overlap between blocks), and two 16-row tiles per wave when M > 8 and K is
-// long enough that the reuse of x outweighs the halved block count.
+// Tile shape, measured on the Llama-2 7B/70B decode shapes at M = 4, 8, 16:
+// one 16-row tile per wave by default; on wide layers (N >= 16384, or
+// N >= 8192 with K = 4096 and M > 8) four tiles per wave in batches of two
+// groups share each x fragment over more weight rows (8192 x 28672: 59-68 us
+// against 74-81 us; 4096 x 11008 at M = 16: 18 us against 21 us); on long K
+// (>= 16384), and for M > 8 on 8192-wide layers with K >= 8192, two tiles per
+// wave, which still leaves at least 256 blocks (8192 x 8192 at M = 16: 24 us
+// against 37 us with four tiles).
 hipError_t launch_gemv(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
                        int64_t N, int64_t K, hipStream_t st) {
   if (M < 1 || M > 16) return hipErrorInvalidValue;
   if (gemv_dot2_supported(M, K)) return launch_gemv_dot2(x, packed, scales, zeros, y, M, N, K, st);
-  if (M > 8 && K >= 8192) return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
+  if (K >= 16384) return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
+  if (N >= 16384 || (M > 8 && N >= 8192 && K <= 4096)) return skinny_launch<4, 2>(x, packed, scales, zeros, y, M, N, K, st);
+  if (M > 8 && N >= 8192) return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
   return skinny_launch<1, 4>(x, packed, scales, zeros, y, M, N, K, st);
 }
 
