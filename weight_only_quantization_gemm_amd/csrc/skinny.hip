@@ -34,17 +34,19 @@ namespace awq {
 constexpr int kSkinnyMaxWaves = 8;
 constexpr size_t kSkinnyLdsBudget = 64 * 1024;
 
-template <int RW, int P, bool XLDS>
-__global__ __launch_bounds__(1024) void skinny_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
-                                                      const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                                                      f16* __restrict__ y, int M, int64_t N, int64_t K,
-                                                      int64_t red_offset) {
+template <int RW, int P, int MT, bool XLDS>
+__global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
+                                                     const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
+                                                     f16* __restrict__ y, int M, int64_t N, int64_t K,
+                                                     int64_t red_offset) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int nl = lane & 15, kq = lane >> 4;  // row within a 16-row tile; quarter of a group
   const int64_t n0 = (int64_t)blockIdx.x * (16 * RW);
   const int64_t K8 = K / 8, G = K / kGroup, P2 = (G + 1) / 2;
-  const bool mlive = nl < M;  // this lane's A-operand row is a real activation row
+  bool mlive[MT];  // this lane's A-operand row of m-tile mt is a real activation row
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) mlive[mt] = 16 * mt + nl < M;
 
   int64_t rowi[RW];
 #pragma unroll
@@ -52,9 +54,11 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const f16* __restrict__ x,
     const int64_t n = n0 + 16 * t + nl;
     rowi[t] = n < N ? n : N - 1;  // tail rows reload the last row; never stored
   }
-  f32x4 acc[RW];
+  f32x4 acc[RW][MT];
 #pragma unroll
-  for (int t = 0; t < RW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < RW; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   f16* xs = reinterpret_cast<f16*>(smem);
   bool staged = false;
@@ -87,61 +91,93 @@ __global__ __launch_bounds__(1024) void skinny_kernel(const f16* __restrict__ x,
       const int64_t g = gb + (int64_t)p * W;
       if (g >= G) break;
       const int64_t k0 = g * kGroup + kq * 32;
-      f16x8 a[4];
+      f16x8 a[MT][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (mlive)
-          a[s] = XLDS ? *reinterpret_cast<const f16x8*>(xs + (int64_t)nl * K + k0 + 8 * s)
-                      : *reinterpret_cast<const f16x8*>(x + (int64_t)nl * K + k0 + 8 * s);
-        else
-          a[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int64_t row = 16 * mt + nl;
+          if (mlive[mt])
+            a[mt][s] = XLDS ? *reinterpret_cast<const f16x8*>(xs + row * K + k0 + 8 * s)
+                            : *reinterpret_cast<const f16x8*>(x + row * K + k0 + 8 * s);
+          else
+            a[mt][s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
 #pragma unroll
       for (int t = 0; t < RW; ++t) {
         const f16x2 zb = zero_biased(zz[p][t]);
-        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 d[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) d[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const uint32_t word = wv[p][t][s];
           const f16x2 q0 = pair_biased(word, 0) - zb, q1 = pair_biased(word, 1) - zb;
           const f16x2 q2 = pair_biased(word, 2) - zb, q3 = pair_biased(word, 3) - zb;
           const f16x8 b = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], b, d, 0, 0, 0);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][s], b, d[mt], 0, 0, 0);
         }
         const float scf = (float)sc[p][t];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(scf, d[r], acc[t][r]);
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[t][mt][r] = fmaf(scf, d[mt][r], acc[t][mt][r]);
       }
     }
   }
   if (XLDS && !staged) __syncthreads();  // a wave without groups still meets the staging barrier
 
-  // sum the waves' tiles: lane holds y[m = 4*kq + r][n0 + 16t + nl]
+  // sum the waves' tiles: lane holds y[m = 16*mt + 4*kq + r][n0 + 16t + nl]
   float* red = reinterpret_cast<float*>(smem + red_offset);
+  if (MT == 1) {  // one slot per wave, then a fixed-order sum per output
 #pragma unroll
-  for (int t = 0; t < RW; ++t)
+    for (int t = 0; t < RW; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * kq + r;
-      if (m < M) red[((wave * RW + t) * 16 + m) * 16 + nl] = acc[t][r];
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kq + r;
+        if (m < M) red[((wave * RW + t) * 16 + m) * 16 + nl] = acc[t][0][r];
+      }
+    __syncthreads();
+    for (int i = threadIdx.x; i < RW * 16 * M; i += blockDim.x) {
+      const int t = i / (16 * M), rem = i - t * 16 * M, m = rem >> 4, nn = rem & 15;
+      float v = 0.f;
+      for (int w = 0; w < W; ++w) v += red[((w * RW + t) * 16 + m) * 16 + nn];
+      const int64_t n = n0 + 16 * t + nn;
+      if (n < N) y[(int64_t)m * N + n] = (f16)v;
     }
-  __syncthreads();
-  for (int i = threadIdx.x; i < RW * 16 * M; i += blockDim.x) {
-    const int t = i / (16 * M), rem = i - t * 16 * M, m = rem >> 4, nn = rem & 15;
-    float v = 0.f;
-    for (int w = 0; w < W; ++w) v += red[((w * RW + t) * 16 + m) * 16 + nn];
-    const int64_t n = n0 + 16 * t + nn;
-    if (n < N) y[(int64_t)m * N + n] = (f16)v;
+  } else {  // one tile, accumulated wave by wave in a fixed order
+    constexpr int MR = 16 * MT;
+    for (int w = 0; w < W; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int t = 0; t < RW; ++t)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int m = 16 * mt + 4 * kq + r;
+              float& dst = red[(t * MR + m) * 16 + nl];
+              dst = (w == 0 ? 0.f : dst) + acc[t][mt][r];
+            }
+      }
+      __syncthreads();
+    }
+    for (int i = threadIdx.x; i < RW * 16 * M; i += blockDim.x) {
+      const int t = i / (16 * M), rem = i - t * 16 * M, m = rem >> 4, nn = rem & 15;
+      const int64_t n = n0 + 16 * t + nn;
+      if (n < N) y[(int64_t)m * N + n] = (f16)red[(t * MR + m) * 16 + nn];
+    }
   }
 }
 
-template <int RW, int P>
+template <int RW, int P, int MT = 1>
 static hipError_t skinny_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                                 int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t G = K / kGroup;
   int W = (int)((G + P - 1) / P);  // about P groups per wave
   W = W < 1 ? 1 : (W > kSkinnyMaxWaves ? kSkinnyMaxWaves : W);
-  const size_t red_bytes = (size_t)W * RW * 16 * 16 * sizeof(float);
+  const size_t red_bytes = (size_t)(MT == 1 ? W : 1) * RW * 16 * MT * 16 * sizeof(float);
   const size_t xbytes = (size_t)M * (size_t)K * 2;
   const bool xlds = xbytes + red_bytes <= kSkinnyLdsBudget;
   const size_t red_offset = xlds ? xbytes : 0;
@@ -153,10 +189,37 @@ static hipError_t skinny_launch(const void* x, const void* packed, const void* s
   auto zp = reinterpret_cast<const uint8_t*>(zeros);
   auto yp = reinterpret_cast<f16*>(y);
   if (xlds)
-    skinny_kernel<RW, P, true><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, N, K, (int64_t)red_offset);
+    skinny_kernel<RW, P, MT, true><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, N, K, (int64_t)red_offset);
   else
-    skinny_kernel<RW, P, false><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, N, K, (int64_t)red_offset);
+    skinny_kernel<RW, P, MT, false><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, N, K, (int64_t)red_offset);
   return hipGetLastError();
+}
+
+// 17 <= M <= 64: the same kernel with M in up to four 16-row m-tiles; each
+// unpacked weight operand feeds one MFMA per m-tile.  Measured against the
+// pipelined GEMM (M = 17, 32, 48, 64 on the 7B/70B shapes) it wins on layers
+// up to 8192 wide (two tiles per wave: 4096 x 4096 at 15-27 us against 32 us,
+// 11008 x 4096 at 34-60 us against 72 us) and, with four tiles per wave in
+// batches of two groups, on wider K = 4096 layers up to M = 48 (4096 x 11008
+// at 22-30 us against 33 us); elsewhere the GEMM is faster.
+bool gemv_wide_preferred(int64_t M, int64_t N, int64_t K) {
+  if (M <= 16 || M > 64) return false;
+  return N <= 8192 || (M <= 48 && K <= 4096);
+}
+
+template <int RW, int P>
+static hipError_t wide_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                              int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  if (M <= 32) return skinny_launch<RW, P, 2>(x, packed, scales, zeros, y, M, N, K, st);
+  if (M <= 48) return skinny_launch<RW, P, 3>(x, packed, scales, zeros, y, M, N, K, st);
+  return skinny_launch<RW, P, 4>(x, packed, scales, zeros, y, M, N, K, st);
+}
+
+hipError_t launch_gemv_wide(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                            int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  if (M <= 16 || M > 64) return hipErrorInvalidValue;
+  if (N <= 8192) return wide_launch<2, 1>(x, packed, scales, zeros, y, M, N, K, st);
+  return wide_launch<4, 2>(x, packed, scales, zeros, y, M, N, K, st);
 }
 
 // Tile shape, measured on the Llama-2 7B/70B decode shapes at M = 4, 8, 16:
