@@ -19,8 +19,9 @@ Also reported in the same JSON line:
                  matrix each (4 launches instead of 7; same weight bytes), the M = 256
                  GEMM on the (4096, 11008) layer (TFLOP/s against the
                  2.5 PFLOP/s dense fp16 peak), the batch sweep M = 1..1024 on that
-                 layer, and awq_quantize over the 7 layers of a 7B block with 65,536
-                 calibration rows (seconds per layer).
+                 layer, awq_quantize over the 7 layers of a 7B block with 65,536
+                 calibration rows (seconds per layer), and the same block searched
+                 with one shared s per input (q/k/v and gate/up jointly).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        [--no-search] [--no-sweep] [--profile-mode gemv|copy]
@@ -251,6 +252,37 @@ def run_search(args, torch, awq, dev):
                 calib_rows=M, n_alpha=20)
 
 
+def run_search_joint(args, torch, awq, dev):
+    """The same block with one shared s per input: q/k/v and gate/up searched jointly as
+    row-concatenated weights (4 searches instead of 7; statistics and Gram matrix formed once
+    per input).  The packed outputs are the fused matrices of the 4-launch decode step."""
+    from gen import activations_fp16, normal_fp16, seed_for
+    M = 65536
+    specs = [("qkv_proj", "attn_in", 4096, 3 * 4096), ("o_proj", "o_in", 4096, 4096),
+             ("gate_up_proj", "mlp_in", 4096, 2 * 11008), ("down_proj", "down_in", 11008, 4096)]
+    res = {}
+    total_ms = 0.0
+    for li, (lname, src, K, N) in enumerate(specs):
+        X = torch.from_numpy(activations_fp16(M, K, seed=seed_for(5, 10 + li), lognormal=True)).to(dev)
+        W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=seed_for(5, 200 + li))).to(dev)
+        ws = torch.empty((awq.awq_quantize_workspace_bytes(N, K, M, 128, 20),), dtype=torch.uint8, device=dev)
+        awq.awq_quantize(W, X, None, workspace=ws)  # warm-up
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = awq.awq_quantize(W, X, None, workspace=ws)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        total_ms += ms
+        best = int(r["best_alpha"].item())
+        res[lname] = dict(K=K, N=N, ms=round(ms, 2), alpha_index=best)
+        del W, X, ws, r
+        torch.cuda.empty_cache()
+    return dict(layers=res, total_s=round(total_ms / 1e3, 3), s_per_linear=round(total_ms / 7 / 1e3, 4),
+                calib_rows=M, n_alpha=20)
+
+
 def run_cpu_baseline(layers_spec, budget_s: float):
     """The oracle's fp64 W4A16 product over the 7 decode layers, on the host cores."""
     import oracle
@@ -344,6 +376,9 @@ def main():
     if not args.no_search:
         log("search: awq_quantize over a 7B block, 65,536 calibration rows")
         legs["search_llama2_7b_block"] = run_search(args, torch, awq, dev)
+        torch.cuda.empty_cache()
+        log("search: joint (one s per input: q/k/v, o, gate/up, down)")
+        legs["search_llama2_7b_block_joint"] = run_search_joint(args, torch, awq, dev)
         torch.cuda.empty_cache()
 
     cpu = None

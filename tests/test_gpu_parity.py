@@ -162,6 +162,26 @@ def test_search_llama_shaped(N, K, M):
     note(f"  alpha*={ALPHAS[best]:.2f} L(alpha*)/L(0)={ref['losses'][best] / ref['losses'][0]:.4f}")
 
 
+@pytest.mark.parametrize("widths,K,M", [((192, 128, 128), 512, 1024), ((256, 256), 384, 200)])
+def test_search_joint_shared_input(widths, K, M):
+    """Layers reading the same input (q/k/v, gate/up) searched jointly for one s: awq_quantize on
+    their row-concatenated weights.  Its loss at every alpha is the row-weighted mean of the
+    layers' own output MSEs (checked against the oracle per layer), so alpha* minimizes their sum;
+    the packed result is the fused matrix the decode path multiplies, and it is checked against
+    the oracle's search on the concatenation like any other layer."""
+    note(f"joint search widths={widths} K={K} M={M}")
+    Ws = [normal_fp16((n, K), 0.02, seed=600 + i) for i, n in enumerate(widths)]
+    X = activations_fp16(M, K, seed=601, lognormal=True)
+    Wc = np.concatenate(Ws, axis=0)
+    r = awq.awq_quantize(dev(Wc), dev(X), ALPHAS)
+    ref = oracle.search(Wc, X, alphas=ALPHAS)
+    _check_search(Wc, X, r, ref)
+    parts = [oracle.search(W, X, alphas=ALPHAS)["losses"] for W in Ws]
+    mean = sum(n * L for n, L in zip(widths, parts)) / sum(widths)
+    assert np.allclose(ref["losses"], mean, rtol=1e-12, atol=0)
+    assert np.allclose(host(r["loss"]), mean, rtol=1e-5, atol=0)
+
+
 def test_search_determinism():
     note("search determinism")
     W = normal_fp16((256, 512), 0.02, seed=77)
