@@ -177,7 +177,7 @@ int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, 
  * 3 <= M <= 16 and M > 16: matrix-core kernels on (code - zero), exact in
  * fp16, with fp32 sums per 128-channel group and the group scale applied in
  * fp32.
- * Requires M >= 1, N >= 1, K % group == 0, group == AWQ_GROUP.
+ * Requires M >= 1, 1 <= N < 2^31, K % group == 0, K <= 2^20, group == AWQ_GROUP.
  */
 int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
              int64_t M, int64_t N, int64_t K, int32_t group, void* stream);

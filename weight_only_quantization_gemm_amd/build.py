@@ -29,7 +29,12 @@ FLAGS = [
 # Per-source extras.  The W4A16 GEMM keeps its matrix-core accumulators in
 # ordinary vector registers, so the per-group scale is one FMA per element
 # (accumulators in AGPRs would need a register move before each FMA).
-FILE_FLAGS = {"gemm_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# The decode kernels are short enough (a few microseconds) that the kernel-argument
+# load at each wave's start is on its critical path; gfx950 can preload the
+# arguments into SGPRs at dispatch instead.
+FILE_FLAGS = {"gemm_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+              "skinny.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def flags_for(src: str) -> list:

@@ -56,7 +56,7 @@ int check_layer(int64_t N, int64_t K, int32_t group) {
               (long long)K);
   AWQ_REQUIRE(group == AWQ_GROUP, AWQ_ERROR_INVALID_VALUE, "group must be %d (got %d)", AWQ_GROUP, group);
   AWQ_REQUIRE(K % group == 0, AWQ_ERROR_INVALID_VALUE, "K=%lld is not a multiple of group %d", (long long)K, group);
-  AWQ_REQUIRE(N <= (int64_t(1) << 31) && K <= (int64_t(1) << 20), AWQ_ERROR_INVALID_VALUE,
+  AWQ_REQUIRE(N < (int64_t(1) << 31) && K <= (int64_t(1) << 20), AWQ_ERROR_INVALID_VALUE,
               "N=%lld or K=%lld exceeds the supported range", (long long)N, (long long)K);
   return AWQ_OK;
 }

@@ -60,12 +60,19 @@ __device__ inline float wave_sum_to_lane63(float v) {
 
 constexpr int kMaxWaves = 16;
 
+// Waves per block: one 64-lane wave per 2048 channels (a lane takes 32).
+__host__ __device__ inline int gemv_waves(int64_t K) {
+  int w = (int)((K / 32 + kWave - 1) / kWave);
+  return w < 1 ? 1 : (w > kMaxWaves ? kMaxWaves : w);
+}
+
 template <int MB, int R>
 __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                     const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
                                                     f16* __restrict__ y, int64_t N, int64_t K) {
   __shared__ float red[kMaxWaves][R * MB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = gemv_waves(K);  // == blockDim.x / 64, from the arguments (all preloaded)
   const int64_t row0 = (int64_t)blockIdx.x * R;
   const int64_t K8 = K / 8, G = K / kGroup, P = (G + 1) / 2;
   const int64_t nchunk = K / 32;
@@ -153,9 +160,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
 template <int MB, int R>
 static hipError_t gemv_m(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                          int64_t N, int64_t K, hipStream_t st) {
-  const int64_t nchunk = K / 32;
-  int waves = (int)((nchunk + kWave - 1) / kWave);
-  waves = waves < 1 ? 1 : (waves > kMaxWaves ? kMaxWaves : waves);
+  const int waves = gemv_waves(K);
   dim3 grid((unsigned)((N + R - 1) / R));
   gemv_kernel<MB, R><<<grid, dim3(waves * kWave), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),

@@ -34,13 +34,23 @@ namespace awq {
 constexpr int kSkinnyMaxWaves = 8;
 constexpr size_t kSkinnyLdsBudget = 64 * 1024;
 
+// Waves per block: about P groups per wave, at most kSkinnyMaxWaves.  It is a
+// function of K alone, so the kernel derives it from its arguments (which the
+// hardware preloads into registers) instead of reading the dispatch packet.
+template <int P>
+__host__ __device__ inline int skinny_waves(int64_t K) {
+  const int64_t w = (K / kGroup + P - 1) / P;
+  return w < 1 ? 1 : (w > kSkinnyMaxWaves ? kSkinnyMaxWaves : (int)w);
+}
+
 template <int RW, int P, int MT, bool XLDS>
 __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                      const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                                                     f16* __restrict__ y, int M, int64_t N, int64_t K,
-                                                     int64_t red_offset) {
+                                                     f16* __restrict__ y, int M, int N32, int K32, int red_offset) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int64_t N = N32, K = K32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int W = skinny_waves<P>(K);  // == blockDim.x / 64
   const int nl = lane & 15, kq = lane >> 4;  // row within a 16-row tile; quarter of a group
   const int64_t n0 = (int64_t)blockIdx.x * (16 * RW);
   const int64_t K8 = K / 8, G = K / kGroup, P2 = (G + 1) / 2;
@@ -81,7 +91,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
     if (XLDS && !staged) {
       // copy x into LDS while this wave's weight loads are in flight
       const int64_t n16 = (int64_t)M * K / 8;
-      for (int64_t i = threadIdx.x; i < n16; i += blockDim.x)
+      for (int64_t i = threadIdx.x; i < n16; i += W * kWave)
         reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
       __syncthreads();
       staged = true;
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
         if (m < M) red[((wave * RW + t) * 16 + m) * 16 + nl] = acc[t][0][r];
       }
     __syncthreads();
-    for (int i = threadIdx.x; i < RW * 16 * M; i += blockDim.x) {
+    for (int i = threadIdx.x; i < RW * 16 * M; i += W * kWave) {
       const int t = i / (16 * M), rem = i - t * 16 * M, m = rem >> 4, nn = rem & 15;
       float v = 0.f;
       for (int w = 0; w < W; ++w) v += red[((w * RW + t) * 16 + m) * 16 + nn];
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
       }
       __syncthreads();
     }
-    for (int i = threadIdx.x; i < RW * 16 * M; i += blockDim.x) {
+    for (int i = threadIdx.x; i < RW * 16 * M; i += W * kWave) {
       const int t = i / (16 * M), rem = i - t * 16 * M, m = rem >> 4, nn = rem & 15;
       const int64_t n = n0 + 16 * t + nn;
       if (n < N) y[(int64_t)m * N + n] = (f16)red[(t * MR + m) * 16 + nn];
@@ -174,9 +184,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
 template <int RW, int P, int MT = 1>
 static hipError_t skinny_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                                 int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const int64_t G = K / kGroup;
-  int W = (int)((G + P - 1) / P);  // about P groups per wave
-  W = W < 1 ? 1 : (W > kSkinnyMaxWaves ? kSkinnyMaxWaves : W);
+  const int W = skinny_waves<P>(K);
   const size_t red_bytes = (size_t)(MT == 1 ? W : 1) * RW * 16 * MT * 16 * sizeof(float);
   const size_t xbytes = (size_t)M * (size_t)K * 2;
   const bool xlds = xbytes + red_bytes <= kSkinnyLdsBudget;
@@ -189,9 +197,9 @@ static hipError_t skinny_launch(const void* x, const void* packed, const void* s
   auto zp = reinterpret_cast<const uint8_t*>(zeros);
   auto yp = reinterpret_cast<f16*>(y);
   if (xlds)
-    skinny_kernel<RW, P, MT, true><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, N, K, (int64_t)red_offset);
+    skinny_kernel<RW, P, MT, true><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, (int)N, (int)K, (int)red_offset);
   else
-    skinny_kernel<RW, P, MT, false><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, N, K, (int64_t)red_offset);
+    skinny_kernel<RW, P, MT, false><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, (int)N, (int)K, (int)red_offset);
   return hipGetLastError();
 }
 
