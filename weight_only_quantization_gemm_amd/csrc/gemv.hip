@@ -23,11 +23,14 @@
 //
 // Mapping: a block owns R output rows and spans all of K; lane l of wave w
 // owns the 16-byte chunk c = 64 w + l (32 codes) of each of the R rows, so
-// every wave-wide load is 1 KB of one row, contiguous.  Each lane issues all
-// of its loads (R weight chunks, their scales and zero points, and its 64 B
-// of x per activation row) before the first use, so a block needs a single
-// round trip to memory.  Partial sums are reduced across the wave with DPP
-// and across the block's waves through LDS in a fixed order.
+// every wave-wide load is 1 KB of one row, contiguous.  The rows' base
+// addresses are wave-uniform and each lane adds a 32-bit offset.  Each lane
+// issues all of its loads (R weight chunks, their scales and zero points, and
+// its 64 B of x per activation row) before the first use, so a block makes a
+// single round trip to memory.  A lane's x chunk serves its R rows: the x
+// bytes a block moves from L2 are 4 / R times its weight bytes.  Partial sums
+// are reduced across the wave with DPP and across the block's waves through
+// LDS in a fixed order.
 #include "awq_common.h"
 #include "awq_internal.h"
 
@@ -62,93 +65,112 @@ constexpr int kMaxWaves = 16;
 
 // Waves per block: one 64-lane wave per 2048 channels (a lane takes 32).
 __host__ __device__ inline int gemv_waves(int64_t K) {
-  int w = (int)((K / 32 + kWave - 1) / kWave);
-  return w < 1 ? 1 : (w > kMaxWaves ? kMaxWaves : w);
+  const int64_t w = (K / 32 + kWave - 1) / kWave;
+  return w < 1 ? 1 : (int)w;
 }
 
+// K <= 32768 (at most 1024 chunks) keeps a block within 16 waves.
 template <int MB, int R>
 __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                     const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                                                    f16* __restrict__ y, int64_t N, int64_t K) {
+                                                    f16* __restrict__ y, int N, int K) {
   __shared__ float red[kMaxWaves][R * MB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = gemv_waves(K);  // == blockDim.x / 64, from the arguments (all preloaded)
-  const int64_t row0 = (int64_t)blockIdx.x * R;
-  const int64_t K8 = K / 8, G = K / kGroup, P = (G + 1) / 2;
-  const int64_t nchunk = K / 32;
+  const uint32_t nchunk = (uint32_t)K / 32, G = (uint32_t)K / kGroup, P = (G + 1) / 2;
+  const int row0 = blockIdx.x * R;
+
+  // A chunk past the end of the row (last wave) reloads the row's last chunk
+  // and is dropped from the sum; rows past N reload row N - 1 and are never
+  // stored.
+  const uint32_t c0 = (uint32_t)(wave * kWave + lane);
+  const bool live = c0 < nchunk;
+  const uint32_t c = live ? c0 : nchunk - 1, g = c >> 2;
+  const u32x4* wrow[R];
+  const uint16_t* srow[R];
+  const uint8_t* zrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r < N ? row0 + r : N - 1;
+    wrow[r] = reinterpret_cast<const u32x4*>(packed + row * (K / 8));
+    srow[r] = reinterpret_cast<const uint16_t*>(scales) + row * G;
+    zrow[r] = zeros + row * P;
+  }
+
+  // All loads are issued before the first wait: the rows' scales and zero
+  // points, x, then the weight chunks.  The scheduling barrier stops the
+  // compiler from sinking any of them below a wait, which would add a second
+  // round trip to memory (measured: up to 18% faster at M = 2 on the 7B/70B
+  // shapes than the order the compiler picked by itself).
+  uint32_t sr[R], zr[R];
+  uint4 xv[MB][4];
+  u32x4 wv[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    sr[r] = srow[r][g];
+    zr[r] = zrow[r][g >> 1];
+  }
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) xv[m][u] = reinterpret_cast<const uint4*>(x + (int64_t)m * K)[c * 4 + u];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wv[r] = __builtin_nontemporal_load(wrow[r] + c);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2^-24 * (sum of the lane's 32 x values), per activation row
+  float xs[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    float t = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t xw[4] = {xv[m][u].x, xv[m][u].y, xv[m][u].z, xv[m][u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) t = dot2_acc(as_f16x2(0x3C003C00u), xw[q], t);  // (1, 1) . x pair
+    }
+    xs[m] = t * 0x1p-24f;
+  }
+
   float acc[R][MB];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r) {
+    const uint32_t words[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
+    float lo[MB], hi[MB];
 #pragma unroll
-    for (int m = 0; m < MB; ++m) acc[r][m] = 0.0f;
-
-  for (int64_t c = (int64_t)wave * kWave + lane; c < nchunk; c += (int64_t)nwaves * kWave) {
-    const int64_t g = c >> 2;
-    u32x4 wv[R];
-    uint32_t sr[R], zr[R];
-    uint4 xv[MB][4];
-    // All loads are issued before the first wait: the rows' scales and zero
-    // points, x, then the weight chunks.  The scheduling barrier stops the
-    // compiler from sinking any of them below a wait, which would add a second
-    // round trip to memory (measured: up to 18% faster at M = 2 on the 7B/70B
-    // shapes than the order the compiler picked by itself).
+    for (int m = 0; m < MB; ++m) lo[m] = hi[m] = 0.0f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t row = (row0 + r < N) ? row0 + r : N - 1;  // tail rows reload the last row; never stored
-      sr[r] = reinterpret_cast<const uint16_t*>(scales)[row * G + g];
-      zr[r] = zeros[row * P + (g >> 1)];
-    }
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) xv[m][u] = reinterpret_cast<const uint4*>(x + m * K + c * 32)[u];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t row = (row0 + r < N) ? row0 + r : N - 1;
-      wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + row * K8 + c * 4));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // 2^-24 * (sum of the lane's 32 x values), per activation row
-    float xs[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      float t = 0.0f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t xw[4] = {xv[m][u].x, xv[m][u].y, xv[m][u].z, xv[m][u].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) t = dot2_acc(as_f16x2(0x3C003C00u), xw[q], t);  // (1, 1) . x pair
-      }
-      xs[m] = t * 0x1p-24f;
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t words[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
-      float lo[MB], hi[MB];
-#pragma unroll
-      for (int m = 0; m < MB; ++m) lo[m] = hi[m] = 0.0f;
-#pragma unroll
-      for (int wi = 0; wi < 4; ++wi) {
-        const uint32_t w = words[wi], w8 = w >> 8;
-        const f16x2 p0 = as_f16x2(w & 0x000F000Fu), p1 = as_f16x2(w & 0x00F000F0u);
-        const f16x2 p2 = as_f16x2(w8 & 0x000F000Fu), p3 = as_f16x2(w8 & 0x00F000F0u);
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          lo[m] = dot2_acc(p0, xv[m][wi].x, lo[m]);
-          hi[m] = dot2_acc(p1, xv[m][wi].y, hi[m]);
-          lo[m] = dot2_acc(p2, xv[m][wi].z, lo[m]);
-          hi[m] = dot2_acc(p3, xv[m][wi].w, hi[m]);
-        }
-      }
-      const float z = (float)((zr[r] >> (4 * (g & 1))) & 0xFu);
-      const float sc = (float)as_f16x2(sr[r]).x;
+    for (int wi = 0; wi < 4; ++wi) {
+      const uint32_t w = words[wi], w8 = w >> 8;
+      const f16x2 p0 = as_f16x2(w & 0x000F000Fu), p1 = as_f16x2(w & 0x00F000F0u);
+      const f16x2 p2 = as_f16x2(w8 & 0x000F000Fu), p3 = as_f16x2(w8 & 0x00F000F0u);
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
-        float t = fmaf(hi[m], 0.0625f, lo[m]);  // 2^-24 * sum x q
-        t = fmaf(-z, xs[m], t);                  // 2^-24 * sum x (q - z)
-        acc[r][m] = fmaf(sc, t, acc[r][m]);
+        lo[m] = dot2_acc(p0, xv[m][wi].x, lo[m]);
+        hi[m] = dot2_acc(p1, xv[m][wi].y, hi[m]);
+        lo[m] = dot2_acc(p2, xv[m][wi].z, lo[m]);
+        hi[m] = dot2_acc(p3, xv[m][wi].w, hi[m]);
       }
     }
+    const float z = (float)((zr[r] >> (4 * (g & 1))) & 0xFu);
+    const float sc = (float)as_f16x2(sr[r]).x;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      float t = fmaf(hi[m], 0.0625f, lo[m]);  // 2^-24 * sum x q
+      t = fmaf(-z, xs[m], t);                  // 2^-24 * sum x (q - z)
+      acc[r][m] = live ? sc * t : 0.0f;
+    }
+  }
+
+  if (nwaves == 1) {  // the whole row is in this wave: no cross-wave step
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const float v = wave_sum_to_lane63(acc[r][m]);
+        if (lane == 63 && row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)(v * 0x1p24f);
+      }
+    return;
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -162,19 +184,19 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
     const int r = threadIdx.x / MB, m = threadIdx.x % MB;
     float v = 0.0f;
     for (int w = 0; w < nwaves; ++w) v += red[w][threadIdx.x];
-    const int64_t row = row0 + r;
-    if (row < N) y[m * N + row] = (f16)(v * 0x1p24f);
+    if (row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)(v * 0x1p24f);
   }
 }
 
 template <int MB, int R>
-static hipError_t gemv_m(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                         int64_t N, int64_t K, hipStream_t st) {
+static hipError_t gemv_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                              int64_t N, int64_t K, hipStream_t st) {
   const int waves = gemv_waves(K);
+  if (waves > kMaxWaves) return hipErrorInvalidValue;
   dim3 grid((unsigned)((N + R - 1) / R));
   gemv_kernel<MB, R><<<grid, dim3(waves * kWave), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
-      reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), N, K);
+      reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -183,23 +205,18 @@ static hipError_t gemv_m(const void* x, const void* packed, const void* scales, 
 // shapes: 1.1-2.4x slower than the matrix-core kernel).
 bool gemv_dot2_supported(int64_t M, int64_t K) { return M >= 1 && M <= 2 && K / 32 <= (int64_t)kMaxWaves * kWave; }
 
-// Rows per block, measured on the Llama-2 7B/70B decode shapes: 2 keeps more
-// blocks in flight on a 4096 x 4096 layer; 4 amortizes each lane's x chunk
-// over more weight rows elsewhere; 8 on the widest layers (N >= 16384 with
-// K <= 8192).
-static int gemv_rows(int64_t N, int64_t K) {
-  if (N * K <= (int64_t)4096 * 4096) return 2;
-  if (K <= 8192 && N >= 16384) return 8;
-  return 4;
-}
-
+// Rows per block, measured on the Llama-2 7B/70B decode shapes: 8 when both K
+// and N are >= 8192 (x, reloaded per block, then costs half as much L2
+// traffic; 8192 x 8192 at 8.3 us against 8.6 us with 4, 28672 x 8192 at
+// 26.4 us against 27.4 us), and for two activation rows on the widest K = 4096
+// layer; 4 elsewhere, which keeps more blocks in flight (4096 x 11008 at
+// 6.1 us and 11008 x 4096 at 6.8 us, against 6.8 and 7.2 us with 8).  More
+// chunks per lane (fewer waves) measured slower on every shape.
 template <int MB>
-static hipError_t gemv_rows_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                                   int64_t N, int64_t K, hipStream_t st) {
-  const int R = gemv_rows(N, K);
-  if (R == 2) return gemv_m<MB, 2>(x, packed, scales, zeros, y, N, K, st);
-  if (R == 8) return gemv_m<MB, 8>(x, packed, scales, zeros, y, N, K, st);
-  return gemv_m<MB, 4>(x, packed, scales, zeros, y, N, K, st);
+static hipError_t gemv_rows_launch(const void* x, const void* packed, const void* scales, const void* zeros,
+                                   void* y, int64_t N, int64_t K, hipStream_t st) {
+  if ((K >= 8192 && N >= 8192) || (MB == 2 && N >= 16384)) return gemv_launch<MB, 8>(x, packed, scales, zeros, y, N, K, st);
+  return gemv_launch<MB, 4>(x, packed, scales, zeros, y, N, K, st);
 }
 
 hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
