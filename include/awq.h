@@ -170,13 +170,18 @@ int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, 
  *   packed, scales, zeros       device, format above
  *   y       device fp16 [M][N]  out: y[m][n] = sum_k x[m][k] * w_hat[n][k]
  *
- * Accumulation is fp32; y is rounded to fp16 once, and no kernel rounds a
- * dequantized weight.  M <= 2: vector-ALU GEMV; every product x * code is
- * exact in fp32 and the zero point enters once per 32 codes as zero * sum(x)
- * (so y is 0 only up to fp32 rounding when every code equals its zero).
- * 3 <= M <= 16 and M > 16: matrix-core kernels on (code - zero), exact in
- * fp16, with fp32 sums per 128-channel group and the group scale applied in
- * fp32.
+ * Accumulation is fp32 and y is rounded to fp16 once.  M <= 2: vector-ALU
+ * GEMV; every product x * code is exact in fp32 and the zero point enters
+ * once per 32 codes as zero * sum(x) (so y is 0 only up to fp32 rounding when
+ * every code equals its zero).  3 <= M <= 16, and 17 <= M <= 64 on the layer
+ * shapes the multi-row decode kernel serves: matrix-core kernels on
+ * (code - zero), exact in fp16, with fp32 sums per 128-channel group and the
+ * group scale applied in fp32, so no dequantized weight is rounded.  Other
+ * M >= 17: the pipelined matrix-core GEMM multiplies the dequantized weight
+ * (code - zero) * scale rounded once to fp16 (relative error <= 2^-11 per
+ * weight; a weight with |code - zero| * scale above 65504 overflows to inf),
+ * or, where the block's scales do not fit its LDS (K above about 32K), the
+ * general-shape kernel with the exact arithmetic above.
  * Requires M >= 1, 1 <= N < 2^31, K % group == 0, K <= 2^20, group == AWQ_GROUP.
  */
 int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y,

@@ -15,9 +15,12 @@
 // are in flight while the matrix cores work.  The block's group scales and
 // zeros are copied to LDS once, up front.  A lane's B operand is 8 consecutive channels
 // of one weight row, i.e. one packed word: it is unpacked in registers to fp16
-// (1024 + code) - (1024 + zero) = code - zero, exactly.  The matrix core sums
-// one group in fp32 and the group's fp16 scale is then applied in fp32, so the
-// weights are never rounded (the same arithmetic as the decode kernels).
+// (1024 + code) - (1024 + zero) = code - zero, exactly, and multiplied by the
+// group's fp16 scale, which rounds the dequantized weight once to fp16.  The
+// matrix core then accumulates all of K in fp32, with no per-group step.
+// (Applying the scale in fp32 after each group's MFMAs instead, exact, costs
+// 16 more vector instructions per 32 x 32 accumulator tile per group and
+// measured 1-3% slower.)
 //
 // Within a group, the MFMA lanes of half h (l / 32) take channels 64h + 8s ..
 // 64h + 8s + 7 at step s = 0..7 in both operands; a lane's 8 B-operand words
@@ -157,18 +160,13 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
   uint32_t magic;
   __asm__ volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-  // acc += scale(g) * d(g) is applied one group late, after the next group's
-  // loads are issued, where it fills the wait for that group's LDS reads.
-  f32x16 acc[S::AB][S::JB], d[S::AB][S::JB];
+  f32x16 acc[S::AB][S::JB];
 #pragma unroll
   for (int a = 0; a < S::AB; ++a)
 #pragma unroll
     for (int j = 0; j < S::JB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][j][r] = d[a][j][r] = 0.f;
-  float scf_prev[S::JB];
-#pragma unroll
-  for (int j = 0; j < S::JB; ++j) scf_prev[j] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[a][j][r] = 0.f;
 
   for (int64_t g = 0; g < G; ++g) {
     wait_vmcnt<(D - 1) * S::LOADS>();  // stage g has landed; stages g+1 .. g+D-1 may be pending
@@ -179,8 +177,7 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     const f16* Ah = st + ahalf * S::A_HALF;
     const f16* Bt = st + 2 * S::A_HALF;
     u32x4 wv[S::JB][S::STEPS / 4];
-    f16x2 zb[S::JB];
-    float scf[S::JB];
+    f16x2 zb[S::JB], sc2[S::JB];
 #pragma unroll
     for (int j = 0; j < S::JB; ++j) {
       const int row = wn * S::TN + j * 32 + l32;
@@ -189,14 +186,9 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
       for (int q = 0; q < S::STEPS / 4; ++q)
         wv[j][q] = *reinterpret_cast<const u32x4*>(Bt + row * 32 + (((bchunk + q) ^ sw) << 3));
       zb[j] = zero_biased((mz[mrow[j] * P2 + (g >> 1)] >> (4 * (g & 1))) & 0xFu);
-      scf[j] = (float)as_f16x2((uint32_t)msc[mrow[j] * G + g]).x;
+      const uint32_t sbits = msc[mrow[j] * G + g];
+      sc2[j] = as_f16x2(sbits | (sbits << 16));
     }
-#pragma unroll
-    for (int j = 0; j < S::JB; ++j)
-#pragma unroll
-      for (int a = 0; a < S::AB; ++a)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[a][j][r] = fmaf(scf_prev[j], d[a][j][r], acc[a][j][r]);
     // Software-pipelined over the MFMA steps of the group: the A fragments
     // and unpacked B operands of step s + 1 are produced while the matrix
     // cores run step s (a scheduling fence closes each step).
@@ -204,10 +196,10 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
 #pragma unroll
       for (int j = 0; j < S::JB; ++j) {
         const uint32_t word = wv[j][st_ >> 2][st_ & 3];
-        const f16x2 q0 = as_f16x2((word & 0x000F000Fu) | magic) - zb[j];
-        const f16x2 q1 = as_f16x2(((word >> 4) & 0x000F000Fu) | magic) - zb[j];
-        const f16x2 q2 = as_f16x2(((word >> 8) & 0x000F000Fu) | magic) - zb[j];
-        const f16x2 q3 = as_f16x2(((word >> 12) & 0x000F000Fu) | magic) - zb[j];
+        const f16x2 q0 = (as_f16x2((word & 0x000F000Fu) | magic) - zb[j]) * sc2[j];
+        const f16x2 q1 = (as_f16x2(((word >> 4) & 0x000F000Fu) | magic) - zb[j]) * sc2[j];
+        const f16x2 q2 = (as_f16x2(((word >> 8) & 0x000F000Fu) | magic) - zb[j]) * sc2[j];
+        const f16x2 q3 = (as_f16x2(((word >> 12) & 0x000F000Fu) | magic) - zb[j]) * sc2[j];
         bq[j] = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
       }
     };
@@ -226,20 +218,12 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
       for (int a = 0; a < S::AB; ++a)
 #pragma unroll
         for (int j = 0; j < S::JB; ++j)
-          d[a][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[c][a], bq[c][j], s == 0 ? f32x16{} : d[a][j], 0, 0, 0);
+          acc[a][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[c][a], bq[c][j], acc[a][j], 0, 0, 0);
       if (s + 1 < S::STEPS) unpack(s + 1, bq[n]);
       __builtin_amdgcn_sched_barrier(0);  // keep each step's work within the step
     }
-#pragma unroll
-    for (int j = 0; j < S::JB; ++j) scf_prev[j] = scf[j];
   }
   wait_vmcnt<0>();  // the tail's redundant LDS loads land before the block can exit
-#pragma unroll
-  for (int j = 0; j < S::JB; ++j)
-#pragma unroll
-    for (int a = 0; a < S::AB; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][j][r] = fmaf(scf_prev[j], d[a][j][r], acc[a][j][r]);
 
   // D register r of lane l: row 8(r/4) + 4(l/32) + r%4, column l%32 of a 32 x 32 block
   if (KS == 2) {  // set 1 hands its partial tile to set 0 through LDS
