@@ -23,6 +23,8 @@ MUTATIONS = {
     "tie_to_last": ("if losses[i] < losses[best]:", "if losses[i] <= losses[best]:"),
     "loss_per_row_only": ("/ (np.float64(M) * np.float64(N)))\n\n\ndef gram", "/ (np.float64(M)))\n\n\ndef gram"),
     "gram_perturbed": ("return X.T @ X", "return X.T @ X * 1.0000001"),
+    "levels_not_minus_one": ("qmax = np.float32(2 ** bits - 1)", "qmax = np.float32(2 ** bits)"),
+    "fixed_four_bit_range": ("qmax = np.float32(2 ** bits - 1)", "qmax = np.float32(15)"),
     "gemm_wrong_group": ("zz = np.repeat(np.asarray(z, dtype=np.float64), group, axis=1)",
                          "zz = np.tile(np.asarray(z, dtype=np.float64), (1, group))"),
 }

@@ -86,6 +86,21 @@ def test_quantizer_hand_worked_mixed_sign_group():
     assert np.all(q[0, 9:] == 5)
 
 
+def test_quantizer_hand_worked_three_bit_group():
+    # 3-bit codes (0..7): lo = -1.5, hi = 2.0, step = 3.5 / 7 = 0.5 exactly; z = rint(1.5 / 0.5) = 3.
+    # q = rint(2 v) + 3 clamped to [0, 7], halves to the even neighbour:
+    #  -1.5 -> 0    2.0 -> 4 + 3 = 7    0.25 -> 0 -> 3    0.75 -> 2 -> 5    1.25 -> 2 -> 5
+    #  -0.75 -> -2 -> 1    1.9 -> 3.8 -> 4 -> 7    0.0 -> 3    fill 1.0 -> 2 -> 5
+    V = _hand_group([-1.5, 2.0, 0.25, 0.75, 1.25, -0.75, 1.9, 0.0], 1.0)
+    q, z, sc = O.quantize_groups(V, bits=3)
+    assert sc[0, 0] == np.float16(0.5) and z[0, 0] == 3
+    assert list(q[0, :8]) == [0, 7, 3, 5, 5, 1, 7, 3]
+    assert np.all(q[0, 8:] == 5)
+    # the same values at 4 bits: step 3.5 / 15 rounds to an fp16 that is not 0.5
+    q4, z4, sc4 = O.quantize_groups(V, bits=4)
+    assert sc4[0, 0] != sc[0, 0] and q4.max() > 7
+
+
 def test_quantizer_hand_worked_positive_group_fp16_step():
     # lo = min(0, 1) = 0, hi = 3: step = fp32(0.2); the nearest fp16 is 1638 * 2**-13
     # = 0.199951171875 (0.2 / 2**-13 = 1638.4).  z = 0.  q = rint(v / 0.19995...):
@@ -113,51 +128,56 @@ def _fp16_neighbours(x16):
     return dn, up
 
 
+@pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("group", [8, 16, 128])
-def test_quantizer_brute_force_nearest(group):
-    g = np.random.default_rng(10 + group)
+def test_quantizer_brute_force_nearest(group, bits):
+    qmax = 2 ** bits - 1
+    g = np.random.default_rng(10 + group + bits)
     N, K = 6, group * 3
     V = (g.standard_normal((N, K)) * g.choice([0.01, 1.0, 50.0], size=(N, 1))).astype(np.float32)
     V[0, :group] = np.abs(V[0, :group])            # a one-signed group
     V[1, group:2 * group] = -np.abs(V[1, group:2 * group])
-    q, z, sc16 = O.quantize_groups(V, group)
+    q, z, sc16 = O.quantize_groups(V, group, bits)
+    assert q.max() <= qmax and z.max() <= qmax
     for n in range(N):
         for j in range(K // group):
             vs = V[n, j * group:(j + 1) * group]
             lo = min(0.0, float(vs.min()))
             hi = max(0.0, float(vs.max()))
-            step = max(F(np.float32(np.float32(hi) - np.float32(lo))) / 15, F(2.0 ** -14))
+            step = max(F(np.float32(np.float32(hi) - np.float32(lo))) / qmax, F(2.0 ** -14))
             sc = F(sc16[n, j])
             # sc is the fp16 nearest to the float32 step (ties to even mantissa)
             dn, up = _fp16_neighbours(sc16[n, j])
             d0 = abs(sc - step)
             assert d0 <= abs(F(dn) - step) and d0 <= abs(F(up) - step)
-            # z is the nearest integer in [0, 15] to -lo / sc (slack: one fp32 rounding)
+            # z is the nearest integer in [0, qmax] to -lo / sc (slack: one fp32 rounding)
             t = F(-lo) / sc
-            dz = [abs(t - c) for c in range(16)]
+            dz = [abs(t - c) for c in range(qmax + 1)]
             assert dz[z[n, j]] <= min(dz) + Fraction(1, 2 ** 19)
-            # every code is a nearest grid point (q - z) * sc over q in [0, 15]
+            # every code is a nearest grid point (q - z) * sc over q in [0, qmax]
             for i, v in enumerate(vs):
-                d = [abs(F(v) - (c - int(z[n, j])) * sc) for c in range(16)]
+                d = [abs(F(v) - (c - int(z[n, j])) * sc) for c in range(qmax + 1)]
                 assert d[q[n, j * group + i]] <= min(d) + sc / 2 ** 19
 
 
-def test_quantizer_error_bound_and_ranges():
+@pytest.mark.parametrize("bits", [3, 4])
+def test_quantizer_error_bound_and_ranges(bits):
+    qmax = 2 ** bits - 1
     W = normal_fp16((64, 1024), 0.02, seed=11)
     a = O.channel_mean_abs(activations_fp16(64, 1024, seed=12))
     for al in (0.0, 0.35, 0.9):
-        q, z, sc16, s = O.quantize_at(W, a, al)
+        q, z, sc16, s = O.quantize_at(W, a, al, bits=bits)
         V = O.scale_weights(W, s).astype(np.float64)
-        assert q.max() <= 15 and z.max() <= 15
+        assert q.max() <= qmax and z.max() <= qmax
         assert np.all(np.isfinite(sc16.astype(np.float32))) and np.all(sc16 > 0)
         Wh = O.dequantize(q, z, sc16)
         scf = np.repeat(sc16.astype(np.float64), 128, axis=1)
         zz = np.repeat(z.astype(np.float64), 128, axis=1)
-        unclamped = (np.rint(V / scf) + zz >= 0) & (np.rint(V / scf) + zz <= 15)
+        unclamped = (np.rint(V / scf) + zz >= 0) & (np.rint(V / scf) + zz <= qmax)
         err = np.abs(V - Wh)
         assert np.all(err[unclamped] <= scf[unclamped] * (0.5 + 2.0 ** -20))
         # clamped elements can only exist because fp16 rounding shrank the step
-        assert np.all(err <= scf * (0.5 + 16 * 2.0 ** -11))
+        assert np.all(err <= scf * (0.5 + (qmax + 1) * 2.0 ** -11))
 
 
 def test_quantizer_power_of_two_covariance():
@@ -189,6 +209,20 @@ def _on_grid_layer(N=8, K=256, M=16, seed=20):
     W = (V / 2.0 ** e[None, :]).astype(np.float16)
     assert np.array_equal(W.astype(np.float64) * 2.0 ** e[None, :], V)
     return W, X, c, z0
+
+
+def test_lossless_construction_three_bit():
+    """Codes in [0, 7] hitting both ends of every group, step 2**-5: exact at 3 bits."""
+    g = np.random.default_rng(21)
+    N, K = 8, 256
+    c = g.integers(0, 8, size=(N, K))
+    c[:, 0::128] = 0
+    c[:, 1::128] = 7
+    z0 = g.integers(0, 8, size=(N, K // 128))
+    W = ((c - np.repeat(z0, 128, axis=1)) * 2.0 ** -5).astype(np.float16)
+    q, z, sc16 = O.quantize_groups(W.astype(np.float32), bits=3)
+    assert np.array_equal(q, c) and np.array_equal(z, z0) and np.all(sc16 == np.float16(2.0 ** -5))
+    assert np.array_equal(O.dequantize(q, z, sc16), W.astype(np.float64))
 
 
 def test_lossless_construction_dequantizes_exactly():
