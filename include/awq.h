@@ -57,7 +57,9 @@ typedef enum awq_status {
   AWQ_ERROR_NOT_IMPLEMENTED = 5
 } awq_status;
 
-/* Supported quantization: 4-bit codes, group of 128 input channels. */
+/* Default quantization: 4-bit codes, group of 128 input channels.  The *_bits
+ * entry points also take 3-bit codes ([summary] paragraphs 4 and 10: the
+ * method is evaluated at 3 and 4 bits, 4 being the safer default). */
 #define AWQ_BITS 4
 #define AWQ_GROUP 128
 /* Most alpha values one search accepts. */
@@ -84,8 +86,22 @@ typedef enum awq_status {
  *
  * Dequantized weight: w_hat[n][k] = (code[n][k] - zero[n][k/g]) * scale[n][k/g].
  * At g = 128 this is 4 + 2.5*8/128 = 4.156 bits per weight.
+ *
+ * 3-bit format (bits = 3): codes 0..7, zeros and scales as above (a zero point
+ * is at most 7), and
+ *   packed  uint32 [N][K/32][3]  the 32 input channels 32c..32c+31 of row n
+ *                                are the words w0, w1, w2 at [n][c].  For a
+ *                                channel pair p = 0..14 (channels 2p, 2p+1 of
+ *                                the 32) with t = p/5, j = p%5: the code of
+ *                                channel 2p sits in bits 3j..3j+2 of word t,
+ *                                that of channel 2p+1 in bits 16+3j..16+3j+2.
+ *                                Bit b (b = 0, 1, 2) of the codes of channels
+ *                                30 and 31 sits in bits 15 and 31 of word b.
+ * 3 + 2.5*8/128 = 3.156 bits per weight; K must be a multiple of 128.
  * ------------------------------------------------------------------------ */
 size_t awq_packed_bytes(int64_t N, int64_t K);
+/* Packed bytes at 4 or 3 bits; 0 for other widths or sizes the format cannot hold. */
+size_t awq_packed_bytes_bits(int64_t N, int64_t K, int32_t bits);
 size_t awq_scales_bytes(int64_t N, int64_t K, int32_t group);
 size_t awq_zeros_bytes(int64_t N, int64_t K, int32_t group);
 
@@ -124,6 +140,10 @@ int awq_channel_mean_abs(const void* X, int64_t M, int64_t K, double* a, void* s
  */
 int awq_pack(const void* W, const float* s, int64_t N, int64_t K, int32_t group,
              void* packed, void* scales, void* zeros, void* stream);
+/* awq_pack at `bits` = 4 (as above) or 3 (15 in the formulas above becomes 7,
+ * and the 3-bit format is written).  Requires bits == 4 or 3. */
+int awq_pack_bits(const void* W, const float* s, int64_t N, int64_t K, int32_t group, int32_t bits,
+                  void* packed, void* scales, void* zeros, void* stream);
 
 /*
  * awq_quantize -- the activation-aware scale search of [summary] paragraph 3
@@ -159,6 +179,13 @@ int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, 
                  void* packed, void* scales, void* zeros, float* s,
                  int32_t* best_alpha, double* loss,
                  void* workspace, size_t workspace_bytes, void* stream);
+/* awq_quantize at `bits` = 4 (as above) or 3 (the quantizer and format of
+ * awq_pack_bits); the workspace does not depend on bits. */
+int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_t M, int32_t group,
+                      int32_t bits, const float* alphas, int32_t n_alpha,
+                      void* packed, void* scales, void* zeros, float* s,
+                      int32_t* best_alpha, double* loss,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * awq_gemm -- the W4A16 product that 4-bit decoding runs on ([summary]
@@ -186,6 +213,13 @@ int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, 
  */
 int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
              int64_t M, int64_t N, int64_t K, int32_t group, void* stream);
+/* awq_gemm on the format written at `bits` = 4 (awq_gemm itself) or 3.  At 3
+ * bits: M <= 2 runs the vector-ALU GEMV with the arithmetic stated above
+ * (every product exact in fp32, zero point as zero * sum(x)); M > 2 the
+ * general-shape matrix-core kernel on exact (code - zero) with the group scale
+ * applied in fp32.  Requires bits == 4 or 3 and M <= 65535 * 64 at 3 bits. */
+int awq_gemm_bits(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                  int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* stream);
 
 /*
  * awq_unpack -- logical view of the packed format, for checking it.
@@ -194,6 +228,9 @@ int awq_gemm(const void* x, const void* packed, const void* scales, const void* 
  */
 int awq_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, int32_t group,
                uint8_t* codes, uint8_t* zeros_u8, void* stream);
+/* awq_unpack of the format written at `bits` = 4 or 3. */
+int awq_unpack_bits(const void* packed, const void* zeros, int64_t N, int64_t K, int32_t group, int32_t bits,
+                    uint8_t* codes, uint8_t* zeros_u8, void* stream);
 
 /* Message for a status code; message for the calling thread's last failure. */
 const char* awq_status_string(int status);

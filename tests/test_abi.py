@@ -57,6 +57,15 @@ def test_size_queries(N, K):
     assert awq.awq_scales_bytes(N, K + 8) == 0  # K % group != 0
 
 
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 384), (4096, 4096), (4096, 11008), (28672, 8192)])
+def test_size_queries_three_bit(N, K):
+    assert awq.awq_packed_bytes(N, K, bits=3) == 3 * N * K // 8
+    assert _lib.load().awq_packed_bytes_bits(N, K, 4) == N * K // 2
+    assert _lib.load().awq_packed_bytes_bits(N, K, 5) == 0
+    assert _lib.load().awq_packed_bytes_bits(N, K + 16, 3) == 0  # K % 32 != 0
+    assert awq.packed_words(K, 3) * 4 * N == awq.awq_packed_bytes(N, K, bits=3)
+
+
 def test_byte_accounting_matches_page_figures():
     figs = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
     N, K = 4096, 4096
@@ -112,6 +121,20 @@ def test_pack_and_unpack_argument_errors_before_launch():
     assert lib.awq_channel_mean_abs(FAKE_MISALIGNED, 4, 16, FAKE, None) == MISALIGNED
 
 
+def test_bits_argument_errors_before_launch():
+    lib = _lib_()
+    for bits in (0, 2, 5, 8):
+        assert lib.awq_pack_bits(FAKE, None, 4, 128, 128, bits, FAKE, FAKE, FAKE, None) == INVALID
+        assert "bits" in awq.awq_last_error()
+        assert lib.awq_gemm_bits(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, bits, None) == INVALID
+        assert lib.awq_unpack_bits(FAKE, FAKE, 4, 128, 128, bits, FAKE, FAKE, None) == INVALID
+    al = np.arange(20, dtype=np.float32) / np.float32(20)
+    ws = awq.awq_quantize_workspace_bytes(64, 256, 32, 128, 20)
+    assert lib.awq_quantize_bits(FAKE, FAKE, 64, 256, 32, 128, 2, al.ctypes.data, 20, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, None, FAKE, ws, None) == INVALID
+    assert lib.awq_gemm_bits(FAKE_MISALIGNED, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 3, None) == MISALIGNED
+
+
 def test_quantize_argument_errors_before_launch():
     lib = _lib_()
     q = lib.awq_quantize
@@ -160,3 +183,26 @@ def test_host_layout_codec_roundtrip():
     c[0, 2] = 0x5
     p, _ = encode(c, np.zeros((1, 1), np.uint8))
     assert int(p.view(np.uint32)[0, 0]) == (0xA << 16) | (0x5 << 4)
+
+
+def test_host_layout_codec_roundtrip_three_bit():
+    from layout import decode_codes3, decode_zeros, encode3
+    g = np.random.default_rng(1)
+    for N, K in ((3, 128), (5, 384), (2, 1024)):
+        codes = g.integers(0, 8, size=(N, K)).astype(np.uint8)
+        zeros = g.integers(0, 8, size=(N, K // 128)).astype(np.uint8)
+        p, zb = encode3(codes, zeros)
+        assert p.shape == (N, 3 * K // 32)
+        assert np.array_equal(decode_codes3(p, K), codes)
+        assert np.array_equal(decode_zeros(zb, K // 128), zeros)
+    # word placement worked out from the format statement: channel 2 (pair 1, even) in
+    # bits 3..5 of word 0; channel 11 (pair 5: word 1, field 0, odd) in bits 16..18 of
+    # word 1; code 6 = 0b110 of channel 30 sets bit 15 of words 1 and 2; code 4 of
+    # channel 31 sets bit 31 of word 2.
+    c = np.zeros((1, 128), np.uint8)
+    c[0, 2], c[0, 11], c[0, 30], c[0, 31] = 5, 3, 6, 4
+    p, _ = encode3(c, np.zeros((1, 1), np.uint8))
+    w = p.view(np.uint32)[0, :3]
+    assert int(w[0]) == 5 << 3
+    assert int(w[1]) == (3 << 16) | (1 << 15)
+    assert int(w[2]) == (1 << 15) | (1 << 31)

@@ -1,0 +1,152 @@
+"""GPU parity of the 3-bit format against the oracle at bits=3, with the bars of the 4-bit
+path: codes, zero points, steps, s and the alpha index bit-exact (the index up to ties
+within 1e-6 relative loss); products within relative Frobenius error 1e-3 and
+max |dy| <= 1e-2 max |y_ref|."""
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_quantization_gemm_amd as awq
+from gen import activations_fp16, normal_fp16
+from layout import assert_y_close, decode_codes3, decode_zeros, encode3
+from test_gpu_parity import ALPHAS, dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ packer
+def _check_pack3(W, s, packed, scales, zeros):
+    N, K = W.shape
+    q, z, sc = oracle.quantize_groups(oracle.scale_weights(W, np.ones(K, np.float32) if s is None else s), bits=3)
+    assert tuple(packed.shape) == (N, 3 * K // 32)
+    assert np.array_equal(decode_codes3(host(packed), K), q)
+    assert np.array_equal(decode_zeros(host(zeros), K // 128), z)
+    assert np.array_equal(host(scales).view(np.uint16), sc.view(np.uint16))
+    codes, zz = awq.awq_unpack(packed, zeros, K)  # the width follows from the packed shape
+    assert np.array_equal(host(codes), q) and np.array_equal(host(zz), z)
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 384), (100, 512), (7, 4096), (64, 11008)])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_pack3_bit_exact(N, K, scaled):
+    note(f"pack3 N={N} K={K} scaled={scaled}")
+    W = normal_fp16((N, K), 0.02, seed=300 + N + K)
+    s = None
+    if scaled:
+        s = np.exp(np.random.default_rng(N + K).standard_normal(K) * 1.5).astype(np.float32)
+    packed, scales, zeros = awq.awq_pack(dev(W), None if s is None else dev(s), bits=3)
+    _check_pack3(W, s, packed, scales, zeros)
+
+
+def test_pack3_degenerate_groups():
+    note("pack3 degenerate groups")
+    K = 512
+    W = normal_fp16((6, K), 0.02, seed=56)
+    W[0] = 0
+    W[1] = np.float16(0.125)
+    W[2] = np.float16(-3.0)
+    W[3, :128] = np.float16(60000)
+    W[3, 128:256] = np.float16(-60000)
+    W[4] = np.float16(6e-8)
+    packed, scales, zeros = awq.awq_pack(dev(W), bits=3)
+    _check_pack3(W, None, packed, scales, zeros)
+
+
+# ------------------------------------------------------------------ search
+@pytest.mark.parametrize("N,K,M,lognormal", [(512, 512, 64, False), (100, 384, 50, False), (96, 640, 300, True),
+                                             (256, 1024, 2048, True)])
+def test_search3(N, K, M, lognormal):
+    """Direct (M < K) and Gram (M >= K) forms of the loss at 3 bits."""
+    note(f"search3 N={N} K={K} M={M}")
+    W = normal_fp16((N, K), 0.02, seed=700 + N + K)
+    X = activations_fp16(M, K, seed=701 + M, lognormal=lognormal)
+    r = awq.awq_quantize(dev(W), dev(X), ALPHAS, bits=3)
+    ref = oracle.search(W, X, alphas=ALPHAS, bits=3)
+    best = int(host(r["best_alpha"])[0])
+    L = ref["losses"]
+    Lg = host(r["loss"])
+    assert L[best] <= (1 + 1e-6) * L.min(), f"alpha index {best} vs oracle {ref['alpha_index']}"
+    assert np.all(np.abs(Lg - L) <= 1e-5 * L)
+    q, z, sc, s = oracle.quantize_at(W, ref["a"], ALPHAS[best], bits=3)
+    assert np.array_equal(host(r["s"]), s)
+    _check_pack3(W, s, r["packed"], r["scales"], r["zeros"])
+    # 3-bit codes lose more than 4-bit ones on the same layer
+    assert L.min() > oracle.search(W, X, alphas=ALPHAS, bits=4)["losses"].min()
+
+
+# ------------------------------------------------------------------ product
+def _random_packed3(N, K, seed, sigma=0.02):
+    g = np.random.default_rng(seed)
+    q = g.integers(0, 8, size=(N, K)).astype(np.uint8)
+    z = g.integers(0, 8, size=(N, K // 128)).astype(np.uint8)
+    sc = (np.abs(g.standard_normal((N, K // 128))) * sigma * 0.8 + 1e-4).astype(np.float16)
+    p, zb = encode3(q, z)
+    return q, z, sc, dev(p), dev(sc), dev(zb)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16, 33, 64, 100, 256])
+def test_gemm3_parity_ragged(M):
+    note(f"gemm3 M={M} N=300 K=1024")
+    q, z, sc, p, scd, zd = _random_packed3(300, 1024, seed=M)
+    x = activations_fp16(M, 1024, seed=950 + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    assert_y_close(y, oracle.gemm(x, q, z, sc), f"M={M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(77, 384, 1), (77, 384, 2), (77, 384, 17), (131, 640, 200), (200, 16640, 1),
+                                   (200, 16640, 70), (64, 36096, 2), (8200, 512, 40), (4096, 4096, 1),
+                                   (4096, 11008, 1), (11008, 4096, 2), (8192, 8192, 1)])
+def test_gemm3_parity_shapes(N, K, M):
+    """Partial row blocks, 130 groups, K beyond the GEMV's 32768 (the matrix-core kernel then
+    serves M = 2), and the 7B/70B decode shapes in full."""
+    note(f"gemm3 N={N} K={K} M={M}")
+    q, z, sc, p, scd, zd = _random_packed3(N, K, seed=N + K + M)
+    x = activations_fp16(M, K, seed=60 + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd, bits=3))
+    assert_y_close(y, oracle.gemm(x, q, z, sc), f"N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_gemm3_one_hot_reproduces_dequantized_column(M):
+    note(f"gemm3 one-hot M={M}")
+    N, K = 80, 512
+    q, z, sc, p, scd, zd = _random_packed3(N, K, seed=41 + M)
+    ks = [0, 1, 30, 31, 127, 128, 300, 511, 2, 29, 62, 63, 383, 384, 400, 510][:M]
+    x = np.zeros((M, K), np.float16)
+    for m, k in enumerate(ks):
+        x[m, k] = 1.0
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    for m, k in enumerate(ks):
+        col = (q[:, k].astype(np.float64) - z[:, k // 128]) * sc[:, k // 128].astype(np.float64)
+        assert np.array_equal(y[m], col.astype(np.float16)), (m, k)
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 64])
+def test_gemm3_codes_equal_zeros_gives_zero(M):
+    note(f"gemm3 zero codes M={M}")
+    N, K = 64, 256
+    z = np.random.default_rng(6).integers(0, 8, size=(N, K // 128)).astype(np.uint8)
+    q = np.repeat(z, 128, axis=1)
+    sc = np.full((N, K // 128), 0.01, np.float16)
+    p, zb = encode3(q, z)
+    x = activations_fp16(M, K, seed=7)
+    y = host(awq.awq_gemm(dev(x), dev(p), dev(sc), dev(zb))).astype(np.float64)
+    if M > 2:
+        assert np.all(y == 0)  # the matrix-core kernel subtracts the zero point per code, exactly
+    else:
+        bound = 1e-6 * np.abs(x.astype(np.float64)).sum(axis=1, keepdims=True) * 7 * 0.01
+        assert np.all(np.abs(y) <= bound)
+
+
+def test_gemm3_after_search_end_to_end():
+    """x / s through the 3-bit layer the search produced equals the oracle's product."""
+    note("gemm3 after search")
+    W = normal_fp16((512, 512), 0.02, seed=901)
+    X = activations_fp16(64, 512, seed=902)
+    r = awq.awq_quantize(dev(W), dev(X), ALPHAS, bits=3)
+    best = int(host(r["best_alpha"])[0])
+    q, z, sc, s = oracle.quantize_at(W, oracle.channel_mean_abs(X), ALPHAS[best], bits=3)
+    for M in (1, 4, 100):
+        x = (activations_fp16(M, 512, seed=903 + M).astype(np.float32) / s).astype(np.float16)
+        y = host(awq.awq_gemm(dev(x), r["packed"], r["scales"], r["zeros"]))
+        assert_y_close(y, oracle.gemm(x, q, z, sc), f"M={M}")

@@ -19,6 +19,8 @@ from .api import (  # noqa: F401
     awq_unpack,
     awq_version,
     awq_zeros_bytes,
+    bits_of,
     default_alpha_grid,
     empty_packed,
+    packed_words,
 )

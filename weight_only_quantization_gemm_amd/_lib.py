@@ -25,6 +25,12 @@ SIGNATURES = {
                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "awq_gemm": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp]),
     "awq_unpack": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]),
+    "awq_packed_bytes_bits": (c_size, [c_i64, c_i64, c_i32]),
+    "awq_pack_bits": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "awq_quantize_bits": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_i32,
+                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "awq_gemm_bits": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
+    "awq_unpack_bits": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "awq_last_error": (ctypes.c_char_p, []),
     "awq_version": (ctypes.c_int, []),

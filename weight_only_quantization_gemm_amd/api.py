@@ -15,6 +15,7 @@ from ._lib import AwqError, check, load
 
 GROUP = 128
 MAX_ALPHAS = 64
+BITS = (4, 3)  # code widths of the packed formats
 
 
 def _stream(dev: torch.device) -> int:
@@ -44,8 +45,8 @@ def default_alpha_grid(n: int = 20) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- size queries
-def awq_packed_bytes(N: int, K: int) -> int:
-    return int(load().awq_packed_bytes(N, K))
+def awq_packed_bytes(N: int, K: int, bits: int = 4) -> int:
+    return int(load().awq_packed_bytes_bits(N, K, bits))
 
 
 def awq_scales_bytes(N: int, K: int, group: int = GROUP) -> int:
@@ -72,11 +73,31 @@ def awq_version() -> int:
     return int(load().awq_version())
 
 
-def empty_packed(N: int, K: int, device, group: int = GROUP):
-    """Output buffers of the packed format: packed int32 [N][K/8], scales fp16 [N][K/g],
-    zeros uint8 [N][ceil(K/g/2)]."""
+def _check_bits(bits: int) -> None:
+    if bits not in BITS:
+        raise ValueError(f"bits must be one of {BITS}, got {bits}")
+
+
+def packed_words(K: int, bits: int = 4) -> int:
+    """int32 words per row of the packed format: K/8 at 4 bits, 3K/32 at 3 bits."""
+    _check_bits(bits)
+    return K // 8 if bits == 4 else 3 * (K // 32)
+
+
+def bits_of(packed: torch.Tensor, K: int) -> int:
+    """The code width a packed tensor of K input channels was written at (K/8 and 3K/32
+    words per row never coincide)."""
+    for b in BITS:
+        if packed.dim() == 2 and packed.shape[1] == packed_words(K, b):
+            return b
+    raise ValueError(f"packed {tuple(packed.shape)} matches no format for K={K}")
+
+
+def empty_packed(N: int, K: int, device, group: int = GROUP, bits: int = 4):
+    """Output buffers of the packed format: packed int32 [N][K/8] (4-bit) or [N][3K/32]
+    (3-bit), scales fp16 [N][K/g], zeros uint8 [N][ceil(K/g/2)]."""
     G = K // group
-    packed = torch.empty((N, K // 8), dtype=torch.int32, device=device)
+    packed = torch.empty((N, packed_words(K, bits)), dtype=torch.int32, device=device)
     scales = torch.empty((N, G), dtype=torch.float16, device=device)
     zeros = torch.empty((N, (G + 1) // 2), dtype=torch.uint8, device=device)
     return packed, scales, zeros
@@ -92,8 +113,9 @@ def awq_channel_mean_abs(X: torch.Tensor) -> torch.Tensor:
     return a
 
 
-def awq_pack(W: torch.Tensor, s: Optional[torch.Tensor] = None, group: int = GROUP):
+def awq_pack(W: torch.Tensor, s: Optional[torch.Tensor] = None, group: int = GROUP, bits: int = 4):
     _need(W, "W", torch.float16, 2)
+    _check_bits(bits)
     N, K = W.shape
     if s is not None:
         _need(s, "s", torch.float32, 1)
@@ -101,18 +123,19 @@ def awq_pack(W: torch.Tensor, s: Optional[torch.Tensor] = None, group: int = GRO
             raise ValueError("s must be float32 [K] on W's device")
     if K % group:
         raise ValueError(f"K={K} is not a multiple of group {group}")
-    packed, scales, zeros = empty_packed(N, K, W.device, group)
+    packed, scales, zeros = empty_packed(N, K, W.device, group, bits)
     with torch.cuda.device(W.device):
-        check(load().awq_pack(W.data_ptr(), _ptr(s), N, K, group, packed.data_ptr(), scales.data_ptr(),
-                              zeros.data_ptr(), _stream(W.device)))
+        check(load().awq_pack_bits(W.data_ptr(), _ptr(s), N, K, group, bits, packed.data_ptr(), scales.data_ptr(),
+                                   zeros.data_ptr(), _stream(W.device)))
     return packed, scales, zeros
 
 
 def awq_quantize(W: torch.Tensor, X: torch.Tensor, alphas: Optional[Sequence[float]] = None,
-                 group: int = GROUP, workspace: Optional[torch.Tensor] = None) -> dict:
+                 group: int = GROUP, workspace: Optional[torch.Tensor] = None, bits: int = 4) -> dict:
     """AWQ scale search for one linear layer; returns packed, scales, zeros, s,
     best_alpha (int32 [1] on device), loss (fp64 [n_alpha] on device)."""
     _need(W, "W", torch.float16, 2)
+    _check_bits(bits)
     _need(X, "X", torch.float16, 2)
     N, K = W.shape
     M = X.shape[0]
@@ -132,21 +155,22 @@ def awq_quantize(W: torch.Tensor, X: torch.Tensor, alphas: Optional[Sequence[flo
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
     elif workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_cuda:
         raise ValueError(f"workspace must be a GPU buffer of at least {ws_bytes} bytes")
-    packed, scales, zeros = empty_packed(N, K, W.device, group)
+    packed, scales, zeros = empty_packed(N, K, W.device, group, bits)
     s = torch.empty((K,), dtype=torch.float32, device=W.device)
     best = torch.empty((1,), dtype=torch.int32, device=W.device)
     loss = torch.empty((n_alpha,), dtype=torch.float64, device=W.device)
     with torch.cuda.device(W.device):
-        check(lib.awq_quantize(W.data_ptr(), X.data_ptr(), N, K, M, group, al.ctypes.data, n_alpha,
-                               packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), s.data_ptr(),
-                               best.data_ptr(), loss.data_ptr(), workspace.data_ptr(),
-                               workspace.numel() * workspace.element_size(), _stream(W.device)))
-    return dict(packed=packed, scales=scales, zeros=zeros, s=s, best_alpha=best, loss=loss, alphas=al)
+        check(lib.awq_quantize_bits(W.data_ptr(), X.data_ptr(), N, K, M, group, bits, al.ctypes.data, n_alpha,
+                                    packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), s.data_ptr(),
+                                    best.data_ptr(), loss.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(W.device)))
+    return dict(packed=packed, scales=scales, zeros=zeros, s=s, best_alpha=best, loss=loss, alphas=al, bits=bits)
 
 
 def awq_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
-             out: Optional[torch.Tensor] = None, group: int = GROUP) -> torch.Tensor:
-    """y = x @ w_hat^T with fp32 accumulation; x fp16 [M][K] (already divided by s)."""
+             out: Optional[torch.Tensor] = None, group: int = GROUP, bits: Optional[int] = None) -> torch.Tensor:
+    """y = x @ w_hat^T with fp32 accumulation; x fp16 [M][K] (already divided by s).  bits
+    (4 or 3) defaults to the width the packed tensor's shape says it was written at."""
     _need(x, "x", torch.float16, 2)
     _need(packed, "packed", torch.int32, 2)
     _need(scales, "scales", torch.float16, 2)
@@ -154,7 +178,10 @@ def awq_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros:
     M, K = x.shape
     N = packed.shape[0]
     G = K // group
-    if packed.shape[1] * 8 != K or tuple(scales.shape) != (N, G) or tuple(zeros.shape) != (N, (G + 1) // 2):
+    if bits is None:
+        bits = bits_of(packed, K)
+    if packed.shape[1] != packed_words(K, bits) or tuple(scales.shape) != (N, G) or \
+            tuple(zeros.shape) != (N, (G + 1) // 2):
         raise ValueError("packed/scales/zeros do not match x's K")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
@@ -163,22 +190,25 @@ def awq_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros:
         if tuple(out.shape) != (M, N):
             raise ValueError("out must be fp16 [M][N]")
     with torch.cuda.device(x.device):
-        check(load().awq_gemm(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
-                              out.data_ptr(), M, N, K, group, _stream(x.device)))
+        check(load().awq_gemm_bits(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                   out.data_ptr(), M, N, K, group, bits, _stream(x.device)))
     return out
 
 
-def awq_unpack(packed: torch.Tensor, zeros: torch.Tensor, K: int, group: int = GROUP):
+def awq_unpack(packed: torch.Tensor, zeros: torch.Tensor, K: int, group: int = GROUP, bits: Optional[int] = None):
     """Logical codes uint8 [N][K] and zero points uint8 [N][K/g] of a packed layer."""
     _need(packed, "packed", torch.int32, 2)
     _need(zeros, "zeros", torch.uint8, 2)
+    if bits is None:
+        bits = bits_of(packed, K)
     N = packed.shape[0]
     codes = torch.empty((N, K), dtype=torch.uint8, device=packed.device)
     z = torch.empty((N, K // group), dtype=torch.uint8, device=packed.device)
     with torch.cuda.device(packed.device):
-        check(load().awq_unpack(packed.data_ptr(), zeros.data_ptr(), N, K, group, codes.data_ptr(),
-                                z.data_ptr(), _stream(packed.device)))
+        check(load().awq_unpack_bits(packed.data_ptr(), zeros.data_ptr(), N, K, group, bits, codes.data_ptr(),
+                                     z.data_ptr(), _stream(packed.device)))
     return codes, z
 
 
-__all__ = [n for n in dir() if n.startswith("awq_")] + ["AwqError", "default_alpha_grid", "empty_packed"]
+__all__ = [n for n in dir() if n.startswith("awq_")] + ["AwqError", "default_alpha_grid", "empty_packed",
+                                                        "packed_words", "bits_of"]

@@ -51,6 +51,11 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+int check_bits(int32_t bits) {
+  AWQ_REQUIRE(bits == 4 || bits == 3, AWQ_ERROR_INVALID_VALUE, "bits must be 4 or 3 (got %d)", bits);
+  return AWQ_OK;
+}
+
 int check_layer(int64_t N, int64_t K, int32_t group) {
   AWQ_REQUIRE(N >= 1 && K >= 1, AWQ_ERROR_INVALID_VALUE, "N and K must be >= 1 (got N=%lld K=%lld)", (long long)N,
               (long long)K);
@@ -120,9 +125,13 @@ const char* awq_status_string(int status) {
 
 const char* awq_last_error(void) { return g_last_error.c_str(); }
 
-size_t awq_packed_bytes(int64_t N, int64_t K) {
-  if (N < 1 || K < 1 || K % 8 != 0) return 0;
-  return (size_t)N * (size_t)(K / 8) * 4;
+size_t awq_packed_bytes(int64_t N, int64_t K) { return awq_packed_bytes_bits(N, K, 4); }
+
+size_t awq_packed_bytes_bits(int64_t N, int64_t K, int32_t bits) {
+  if (N < 1 || K < 1) return 0;
+  if (bits == 4) return K % 8 == 0 ? (size_t)N * (size_t)(K / 8) * 4 : 0;
+  if (bits == 3) return K % 32 == 0 ? (size_t)N * (size_t)(K / 32) * 12 : 0;
+  return 0;
 }
 
 size_t awq_scales_bytes(int64_t N, int64_t K, int32_t group) {
@@ -154,23 +163,37 @@ int awq_channel_mean_abs(const void* X, int64_t M, int64_t K, double* a, void* s
 
 int awq_pack(const void* W, const float* s, int64_t N, int64_t K, int32_t group, void* packed, void* scales,
              void* zeros, void* stream) {
+  return awq_pack_bits(W, s, N, K, group, 4, packed, scales, zeros, stream);
+}
+
+int awq_pack_bits(const void* W, const float* s, int64_t N, int64_t K, int32_t group, int32_t bits, void* packed,
+                  void* scales, void* zeros, void* stream) {
   AWQ_GUARD_BEGIN
   AWQ_REQUIRE(W && packed && scales && zeros, AWQ_ERROR_INVALID_VALUE, "W, packed, scales, zeros must not be NULL");
   int st = check_layer(N, K, group);
+  if (st == AWQ_OK) st = check_bits(bits);
   if (st != AWQ_OK) return st;
   AWQ_REQUIRE(aligned16(W) && aligned16(packed) && (s == nullptr || aligned16(s)), AWQ_ERROR_MISALIGNED,
               "W, s and packed must be 16-byte aligned");
-  return device_status(awq::launch_pack(W, s, N, K, packed, scales, zeros, as_stream(stream)), "awq_pack");
+  return device_status(awq::launch_pack(W, s, N, K, bits, packed, scales, zeros, as_stream(stream)), "awq_pack");
   AWQ_GUARD_END
 }
 
 int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, int32_t group, const float* alphas,
                  int32_t n_alpha, void* packed, void* scales, void* zeros, float* s, int32_t* best_alpha,
                  double* loss, void* workspace, size_t workspace_bytes, void* stream) {
+  return awq_quantize_bits(W, X, N, K, M, group, 4, alphas, n_alpha, packed, scales, zeros, s, best_alpha, loss,
+                           workspace, workspace_bytes, stream);
+}
+
+int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_t M, int32_t group, int32_t bits,
+                      const float* alphas, int32_t n_alpha, void* packed, void* scales, void* zeros, float* s,
+                      int32_t* best_alpha, double* loss, void* workspace, size_t workspace_bytes, void* stream) {
   AWQ_GUARD_BEGIN
   AWQ_REQUIRE(W && X && alphas && packed && scales && zeros && s && best_alpha && workspace, AWQ_ERROR_INVALID_VALUE,
               "W, X, alphas, packed, scales, zeros, s, best_alpha and workspace must not be NULL");
   int st = check_layer(N, K, group);
+  if (st == AWQ_OK) st = check_bits(bits);
   if (st != AWQ_OK) return st;
   AWQ_REQUIRE(M >= 1 && M <= AWQ_MAX_CALIB_ROWS, AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^23]", (long long)M);
   AWQ_REQUIRE(n_alpha >= 1 && n_alpha <= AWQ_MAX_ALPHAS, AWQ_ERROR_INVALID_VALUE, "n_alpha=%d outside [1, %d]",
@@ -201,7 +224,7 @@ int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, 
   if (w.direct) {
     float* E = reinterpret_cast<float*>(base + w.e32);
     for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
-      e = awq::launch_quant_error32(W, s_all + (size_t)i * (size_t)K, N, K, E, hs);
+      e = awq::launch_quant_error32(W, s_all + (size_t)i * (size_t)K, N, K, bits, E, hs);
       if (e == hipSuccess) e = awq::launch_loss_direct(X, E, M, N, K, partial, hs);
       if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, L + i, hs);
     }
@@ -217,41 +240,56 @@ int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, 
     if (e == hipSuccess) e = awq::launch_gram(xt, w.mp, K, G, hs);
     if (e == hipSuccess) e = awq::launch_gram_split(G, K, ex, Ghi, Glo, hs);
     for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
-      e = awq::launch_quant_error(W, s_all + (size_t)i * (size_t)K, ex, N, K, Ehi, Elo, hs);
+      e = awq::launch_quant_error(W, s_all + (size_t)i * (size_t)K, ex, N, K, bits, Ehi, Elo, hs);
       if (e == hipSuccess) e = awq::launch_loss_partials(Ehi, Elo, Ghi, Glo, N, K, partial, hs);
       if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, L + i, hs);
     }
   }
   if (e == hipSuccess) e = awq::launch_argmin(L, n_alpha, best_alpha, hs);
   if (e == hipSuccess) e = awq::launch_select_scale(s_all, best_alpha, K, s, hs);
-  if (e == hipSuccess) e = awq::launch_pack(W, s, N, K, packed, scales, zeros, hs);
+  if (e == hipSuccess) e = awq::launch_pack(W, s, N, K, bits, packed, scales, zeros, hs);
   return device_status(e, "awq_quantize");
   AWQ_GUARD_END
 }
 
 int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M, int64_t N,
              int64_t K, int32_t group, void* stream) {
+  return awq_gemm_bits(x, packed, scales, zeros, y, M, N, K, group, 4, stream);
+}
+
+int awq_gemm_bits(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
+                  int64_t N, int64_t K, int32_t group, int32_t bits, void* stream) {
   AWQ_GUARD_BEGIN
   AWQ_REQUIRE(x && packed && scales && zeros && y, AWQ_ERROR_INVALID_VALUE,
               "x, packed, scales, zeros and y must not be NULL");
   int st = check_layer(N, K, group);
+  if (st == AWQ_OK) st = check_bits(bits);
   if (st != AWQ_OK) return st;
   AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
   AWQ_REQUIRE(aligned16(x) && aligned16(packed), AWQ_ERROR_MISALIGNED, "x and packed must be 16-byte aligned");
-  hipError_t e = (M <= 16) ? awq::launch_gemv(x, packed, scales, zeros, y, M, N, K, as_stream(stream))
-                           : awq::launch_gemm(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
+  hipError_t e;
+  if (bits == 3) e = awq::launch_gemm3(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
+  else if (M <= 16) e = awq::launch_gemv(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
+  else e = awq::launch_gemm(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
   return device_status(e, "awq_gemm");
   AWQ_GUARD_END
 }
 
 int awq_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, int32_t group, uint8_t* codes,
                uint8_t* zeros_u8, void* stream) {
+  return awq_unpack_bits(packed, zeros, N, K, group, 4, codes, zeros_u8, stream);
+}
+
+int awq_unpack_bits(const void* packed, const void* zeros, int64_t N, int64_t K, int32_t group, int32_t bits,
+                    uint8_t* codes, uint8_t* zeros_u8, void* stream) {
   AWQ_GUARD_BEGIN
   AWQ_REQUIRE(packed && zeros && codes && zeros_u8, AWQ_ERROR_INVALID_VALUE, "pointers must not be NULL");
   int st = check_layer(N, K, group);
+  if (st == AWQ_OK) st = check_bits(bits);
   if (st != AWQ_OK) return st;
   AWQ_REQUIRE(aligned16(packed), AWQ_ERROR_MISALIGNED, "packed must be 16-byte aligned");
-  return device_status(awq::launch_unpack(packed, zeros, N, K, codes, zeros_u8, as_stream(stream)), "awq_unpack");
+  return device_status(awq::launch_unpack(packed, zeros, N, K, bits, codes, zeros_u8, as_stream(stream)),
+                       "awq_unpack");
   AWQ_GUARD_END
 }
 

@@ -24,13 +24,15 @@ hipError_t launch_gram(const void* Xt, int64_t Mp, int64_t K, float* G, hipStrea
 // quant.hip
 hipError_t launch_scales(const double* a, const AlphaGrid& al, int n_alpha, int64_t K, float* s_all,
                          hipStream_t st);
-hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, int64_t N, int64_t K, void* Ehi,
-                              void* Elo, hipStream_t st);
-hipError_t launch_quant_error32(const void* W, const float* s, int64_t N, int64_t K, float* E, hipStream_t st);
-hipError_t launch_pack(const void* W, const float* s, int64_t N, int64_t K, void* packed, void* scales,
+// bits: 4 (16 levels) or 3 (8 levels)
+hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, int64_t N, int64_t K, int bits,
+                              void* Ehi, void* Elo, hipStream_t st);
+hipError_t launch_quant_error32(const void* W, const float* s, int64_t N, int64_t K, int bits, float* E,
+                                hipStream_t st);
+hipError_t launch_pack(const void* W, const float* s, int64_t N, int64_t K, int bits, void* packed, void* scales,
                        void* zeros, hipStream_t st);
 hipError_t launch_select_scale(const float* s_all, const int32_t* best, int64_t K, float* s_out, hipStream_t st);
-hipError_t launch_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, uint8_t* codes,
+hipError_t launch_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, int bits, uint8_t* codes,
                          uint8_t* zeros_u8, hipStream_t st);
 
 // loss.hip: channel exponents and the fp16 split of the scaled Gram matrix;
@@ -59,5 +61,11 @@ hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scale
                             int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st);
+// 3-bit format: GEMV for M <= 2 (gemv.hip), general-shape matrix-core kernel otherwise (gemm.hip)
+bool gemv3_supported(int64_t M, int64_t K);
+hipError_t launch_gemv3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                        int64_t M, int64_t N, int64_t K, hipStream_t st);
+hipError_t launch_gemm3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                        int64_t M, int64_t N, int64_t K, hipStream_t st);
 
 }  // namespace awq

@@ -1,6 +1,7 @@
 // W4A16 GEMM for M > 16 rows on the fp16 matrix cores: the general-shape
 // path, for the K the pipelined kernel cannot hold (its LDS keeps the block's
-// scales and zeros for all of K), and the dispatcher for M > 16.
+// scales and zeros for all of K), the dispatcher for M > 16, and the product
+// of the 3-bit format for M > 2.
 //
 // With more activation rows each weight is reused M times and the product
 // turns compute-bound ("AWQ: Activation-aware Weight Quantization for On-Device
@@ -21,6 +22,7 @@ constexpr int kLdsStride = kGroup + 8;  // halfs per LDS row (16-byte aligned, s
 // output tile as 2x2 MFMA tiles.  MFMA layouts: A lane l holds
 // A[l%16][8*(l/16) .. +8] (x rows), B lane l holds B[8*(l/16) .. +8][l%16]
 // (weight rows), D register r of lane l is D[4*(l/16)+r][l%16] = y[m][n].
+template <int BITS>
 __global__ __launch_bounds__(256) void gemm_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                    const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
                                                    f16* __restrict__ y, int64_t M, int64_t N, int64_t K) {
@@ -43,25 +45,39 @@ __global__ __launch_bounds__(256) void gemm_kernel(const f16* __restrict__ x, co
   for (int64_t g = 0; g < G; ++g) {
     const int64_t k0 = g * kGroup;
     uint4 xv[4];
-    uint4 wv = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t words[4] = {0u, 0u, 0u, 0u};  // the thread's 32 codes: 4 words (4-bit) or 3 (3-bit)
     f16 sc = (f16)0.0f;
     uint32_t z = 0u;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       xv[u] = xlive ? reinterpret_cast<const uint4*>(x + (m0 + lr) * K + k0 + lq * 32)[u] : make_uint4(0u, 0u, 0u, 0u);
     if (wlive) {
-      wv = *reinterpret_cast<const uint4*>(packed + (n0 + lr) * K8 + g * 16 + lq * 4);
+      if constexpr (BITS == 4) {
+        const uint4 wv = *reinterpret_cast<const uint4*>(packed + (n0 + lr) * K8 + g * 16 + lq * 4);
+        words[0] = wv.x, words[1] = wv.y, words[2] = wv.z, words[3] = wv.w;
+      } else {
+        const uint32_t* src = packed + ((n0 + lr) * (K / 32) + g * 4 + lq) * 3;
+        words[0] = src[0], words[1] = src[1], words[2] = src[2];
+      }
       sc = scales[(n0 + lr) * G + g];
       z = zero_of(zeros + (n0 + lr) * P, (int)g);
     }
-    // 32 codes as fp16 (code - zero), exact
+    // 32 codes as fp16 (code - zero), exact: channel pair p of the chunk in wh[p]
     const f16x2 zb = zero_biased(z);
-    const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
     uint32_t wh[16];
+    if constexpr (BITS == 4) {
 #pragma unroll
-    for (int wi2 = 0; wi2 < 4; ++wi2)
+      for (int wi2 = 0; wi2 < 4; ++wi2)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wh[wi2 * 4 + j] = as_u32(pair_biased(words[wi2], j) - zb);
+        for (int j = 0; j < 4; ++j) wh[wi2 * 4 + j] = as_u32(pair_biased(words[wi2], j) - zb);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 15; ++p)
+        wh[p] = as_u32(as_f16x2(((words[p / 5] >> (3 * (p % 5))) & 0x00070007u) | 0x64006400u) - zb);
+      const uint32_t p15 = ((words[0] >> 15) & 0x00010001u) | ((words[1] >> 14) & 0x00020002u) |
+                           ((words[2] >> 13) & 0x00040004u);
+      wh[15] = as_u32(as_f16x2(p15 | 0x64006400u) - zb);
+    }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -115,10 +131,22 @@ hipError_t launch_gemm(const void* x, const void* packed, const void* scales, co
                        int64_t N, int64_t K, hipStream_t st) {
   if (gemv_wide_preferred(M, N, K)) return launch_gemv_wide(x, packed, scales, zeros, y, M, N, K, st);
   if (gemm_pipe_supported(M, K)) return launch_gemm_pipe(x, packed, scales, zeros, y, M, N, K, st);
+  if ((M + kBM - 1) / kBM > 65535) return hipErrorInvalidValue;  // grid.y limit
   dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
-  gemm_kernel<<<grid, dim3(256), 0, st>>>(reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),
-                                          reinterpret_cast<const f16*>(scales), reinterpret_cast<const uint8_t*>(zeros),
-                                          reinterpret_cast<f16*>(y), M, N, K);
+  gemm_kernel<4><<<grid, dim3(256), 0, st>>>(reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),
+                                             reinterpret_cast<const f16*>(scales),
+                                             reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), M, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm3(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
+                        int64_t N, int64_t K, hipStream_t st) {
+  if (gemv3_supported(M, K)) return launch_gemv3(x, packed, scales, zeros, y, M, N, K, st);
+  if ((M + kBM - 1) / kBM > 65535) return hipErrorInvalidValue;  // grid.y limit
+  dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
+  gemm_kernel<3><<<grid, dim3(256), 0, st>>>(reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),
+                                             reinterpret_cast<const f16*>(scales),
+                                             reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), M, N, K);
   return hipGetLastError();
 }
 

@@ -219,6 +219,157 @@ static hipError_t gemv_rows_launch(const void* x, const void* packed, const void
   return gemv_launch<MB, 4>(x, packed, scales, zeros, y, N, K, st);
 }
 
+// 3-bit format (three words per 32 channels of a row; see the packer).  The
+// same mapping as above: lane l of wave w owns the chunk c = 64 w + l of each
+// of R rows, now 12 bytes.  In a 16-bit half, fields 0, 1, 2 (bits 0-2, 3-5,
+// 6-8) come out with one AND each as q, 8 q and 64 q units of 2^-24 -- all
+// below 2^10, so still exact fp16 subnormals -- and fields 3, 4 the same way
+// after one shift by 9; the pair in the spare bits takes three shifts and
+// ANDs.  Three fp32 sums (1, 8 and 64 q units) are combined with exact
+// power-of-two factors.  Pair p of the chunk multiplies x word p.
+template <int MB, int R>
+__global__ __launch_bounds__(1024) void gemv3_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
+                                                     const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
+                                                     f16* __restrict__ y, int N, int K) {
+  __shared__ float red[kMaxWaves][R * MB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = gemv_waves(K);  // == blockDim.x / 64
+  const uint32_t nchunk = (uint32_t)K / 32, G = (uint32_t)K / kGroup, P = (G + 1) / 2;
+  const int row0 = blockIdx.x * R;
+
+  const uint32_t c0 = (uint32_t)(wave * kWave + lane);
+  const bool live = c0 < nchunk;
+  const uint32_t c = live ? c0 : nchunk - 1, g = c >> 2;
+  const uint32_t* wrow[R];
+  const uint16_t* srow[R];
+  const uint8_t* zrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r < N ? row0 + r : N - 1;
+    wrow[r] = packed + row * (int64_t)(nchunk * 3);
+    srow[r] = reinterpret_cast<const uint16_t*>(scales) + row * G;
+    zrow[r] = zeros + row * P;
+  }
+  uint32_t sr[R], zr[R], wv[R][3];
+  uint4 xv[MB][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    sr[r] = srow[r][g];
+    zr[r] = zrow[r][g >> 1];
+  }
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) xv[m][u] = reinterpret_cast<const uint4*>(x + (int64_t)m * K)[c * 4 + u];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < 3; ++t) wv[r][t] = __builtin_nontemporal_load(wrow[r] + 3 * c + t);
+  __builtin_amdgcn_sched_barrier(0);  // every load before the first wait, as in the 4-bit kernel
+
+  float xs[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    float t = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t xw[4] = {xv[m][u].x, xv[m][u].y, xv[m][u].z, xv[m][u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) t = dot2_acc(as_f16x2(0x3C003C00u), xw[q], t);
+    }
+    xs[m] = t * 0x1p-24f;
+  }
+
+  float acc[R][MB];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float a1[MB], a8[MB], a64[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) a1[m] = a8[m] = a64[m] = 0.0f;
+    auto xword = [&](int m, int p) -> uint32_t {
+      const uint4 v = xv[m][p >> 2];
+      return (p & 3) == 0 ? v.x : (p & 3) == 1 ? v.y : (p & 3) == 2 ? v.z : v.w;
+    };
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const uint32_t w = wv[r][t], w9 = w >> 9;
+      const f16x2 p0 = as_f16x2(w & 0x00070007u), p1 = as_f16x2(w & 0x00380038u);
+      const f16x2 p2 = as_f16x2(w & 0x01C001C0u), p3 = as_f16x2(w9 & 0x00070007u);
+      const f16x2 p4 = as_f16x2(w9 & 0x00380038u);
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        a1[m] = dot2_acc(p0, xword(m, 5 * t), a1[m]);
+        a8[m] = dot2_acc(p1, xword(m, 5 * t + 1), a8[m]);
+        a64[m] = dot2_acc(p2, xword(m, 5 * t + 2), a64[m]);
+        a1[m] = dot2_acc(p3, xword(m, 5 * t + 3), a1[m]);
+        a8[m] = dot2_acc(p4, xword(m, 5 * t + 4), a8[m]);
+      }
+    }
+    const f16x2 p15 = as_f16x2(((wv[r][0] >> 15) & 0x00010001u) | ((wv[r][1] >> 14) & 0x00020002u) |
+                               ((wv[r][2] >> 13) & 0x00040004u));
+    const float z = (float)((zr[r] >> (4 * (g & 1))) & 0xFu);
+    const float sc = (float)as_f16x2(sr[r]).x;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      a1[m] = dot2_acc(p15, xword(m, 15), a1[m]);
+      float t = fmaf(a64[m], 0.015625f, fmaf(a8[m], 0.125f, a1[m]));  // 2^-24 * sum x q
+      t = fmaf(-z, xs[m], t);                                          // 2^-24 * sum x (q - z)
+      acc[r][m] = live ? sc * t : 0.0f;
+    }
+  }
+
+  if (nwaves == 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const float v = wave_sum_to_lane63(acc[r][m]);
+        if (lane == 63 && row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)(v * 0x1p24f);
+      }
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const float v = wave_sum_to_lane63(acc[r][m]);
+      if (lane == 63) red[wave][r * MB + m] = v;
+    }
+  __syncthreads();
+  if ((int)threadIdx.x < R * MB) {
+    const int r = threadIdx.x / MB, m = threadIdx.x % MB;
+    float v = 0.0f;
+    for (int w = 0; w < nwaves; ++w) v += red[w][threadIdx.x];
+    if (row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)(v * 0x1p24f);
+  }
+}
+
+template <int MB, int R>
+static hipError_t gemv3_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                               int64_t N, int64_t K, hipStream_t st) {
+  const int waves = gemv_waves(K);
+  if (waves > kMaxWaves) return hipErrorInvalidValue;
+  gemv3_kernel<MB, R><<<dim3((unsigned)((N + R - 1) / R)), dim3(waves * kWave), 0, st>>>(
+      reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
+      reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)N, (int)K);
+  return hipGetLastError();
+}
+
+bool gemv3_supported(int64_t M, int64_t K) { return gemv_dot2_supported(M, K); }
+
+// Rows per block as for the 4-bit kernel.
+hipError_t launch_gemv3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const bool wide = (K >= 8192 && N >= 8192) || (M == 2 && N >= 16384);
+  if (M == 1)
+    return wide ? gemv3_launch<1, 8>(x, packed, scales, zeros, y, N, K, st)
+                : gemv3_launch<1, 4>(x, packed, scales, zeros, y, N, K, st);
+  if (M == 2)
+    return wide ? gemv3_launch<2, 8>(x, packed, scales, zeros, y, N, K, st)
+                : gemv3_launch<2, 4>(x, packed, scales, zeros, y, N, K, st);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st) {
   if (M == 1) return gemv_rows_launch<1>(x, packed, scales, zeros, y, N, K, st);

@@ -1,5 +1,5 @@
-// Per-channel scales s = a^alpha, the group-wise int4 quantizer, the
-// weight error used by the search loss, and the packer.
+// Per-channel scales s = a^alpha, the group-wise int4 / int3 quantizer, the
+// weight error used by the search loss, and the packers.
 //
 // Method: a weight channel is multiplied by s and its input divided by s,
 // which leaves the layer's output unchanged in exact arithmetic while the
@@ -7,8 +7,10 @@
 // average activation magnitude raised to alpha ("AWQ: Activation-aware Weight
 // Quantization for On-Device LLM Compression and Acceleration",
 // fdeinterviews.com/papers/awq, paragraph 3).  The group quantizer (group 128,
-// min-max asymmetric, fp16 step, 4-bit zero point, round-half-even) is this
-// library's reading of the 4-bit weight-only format the pages name.
+// min-max asymmetric, fp16 step, integer zero point, round-half-even) is this
+// library's reading of the 4-bit weight-only format the pages name; the pages
+// also evaluate 3-bit weights (same page, paragraphs 4 and 10), which take the
+// same quantizer with 8 levels instead of 16.
 //
 // Every float operation below is an IEEE fp32/fp64 operation rounded to
 // nearest-even (the file is built with -ffp-contract=off and correctly
@@ -69,6 +71,7 @@ __device__ inline void load_s8(const float* s, int64_t k0, float out[8]) {
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+template <int QMAX>
 __device__ inline void quantize8(const float w[8], const float s[8], Quant8& r) {
   float mn = 0.0f, mx = 0.0f;  // the range always contains 0
 #pragma unroll
@@ -82,19 +85,21 @@ __device__ inline void quantize8(const float w[8], const float s[8], Quant8& r) 
     mn = fminf(mn, __shfl_xor(mn, off, 16));
     mx = fmaxf(mx, __shfl_xor(mx, off, 16));
   }
-  float step = (mx - mn) / 15.0f;
+  constexpr float qmax = (float)QMAX;
+  float step = (mx - mn) / qmax;
   step = fmaxf(step, 0x1p-14f);
   r.sc16 = (f16)step;
   r.sc = (float)r.sc16;
-  r.z = fminf(fmaxf(rintf(-mn / r.sc), 0.0f), 15.0f);
+  r.z = fminf(fmaxf(rintf(-mn / r.sc), 0.0f), qmax);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r.q[i] = fminf(fmaxf(rintf(r.v[i] / r.sc) + r.z, 0.0f), 15.0f);
+  for (int i = 0; i < 8; ++i) r.q[i] = fminf(fmaxf(rintf(r.v[i] / r.sc) + r.z, 0.0f), qmax);
 }
 
 // Weight error of the search, pre-scaled for the loss contraction:
 // E'[n][k] = ((q - z) * sc / s - w) * 2^e_k, evaluated in fp64, rounded to
 // fp32 and stored as an fp16 pair hi = fp16(E'), lo = fp16(E' - hi).  One
 // thread per 8 channels.
+template <int QMAX>
 __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
                                                           const int32_t* __restrict__ ex, int64_t N, int64_t K,
                                                           f16* __restrict__ Ehi, f16* __restrict__ Elo) {
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restric
   load_w8(W, idx, wf);
   load_s8(s, w * 8, sf);
   Quant8 r;
-  quantize8(wf, sf, r);
+  quantize8<QMAX>(wf, sf, r);
   const double scd = (double)r.sc;
   uint32_t hw[4], lw[4];
 #pragma unroll
@@ -130,6 +135,7 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restric
 }
 
 // Unscaled weight error in fp32 for the direct form of the loss.
+template <int QMAX>
 __global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
                                                             int64_t N, int64_t K, float* __restrict__ E) {
   const int64_t K8 = K / 8;
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restr
   load_w8(W, idx, wf);
   load_s8(s, w * 8, sf);
   Quant8 r;
-  quantize8(wf, sf, r);
+  quantize8<QMAX>(wf, sf, r);
   const double scd = (double)r.sc;
   float e[8];
 #pragma unroll
@@ -150,23 +156,59 @@ __global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restr
   out[1] = make_float4(e[4], e[5], e[6], e[7]);
 }
 
-hipError_t launch_quant_error32(const void* W, const float* s, int64_t N, int64_t K, float* E, hipStream_t st) {
-  const int64_t words = N * (K / 8);
-  quant_error32_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st>>>(
-      reinterpret_cast<const uint4*>(W), s, N, K, E);
+hipError_t launch_quant_error32(const void* W, const float* s, int64_t N, int64_t K, int bits, float* E,
+                                hipStream_t st) {
+  const dim3 grid((unsigned)((N * (K / 8) + 255) / 256)), block(256);
+  auto Wp = reinterpret_cast<const uint4*>(W);
+  if (bits == 3) quant_error32_kernel<7><<<grid, block, 0, st>>>(Wp, s, N, K, E);
+  else quant_error32_kernel<15><<<grid, block, 0, st>>>(Wp, s, N, K, E);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, int64_t N, int64_t K, void* Ehi,
-                              void* Elo, hipStream_t st) {
-  const int64_t words = N * (K / 8);
-  quant_error_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st>>>(
-      reinterpret_cast<const uint4*>(W), s, ex, N, K, reinterpret_cast<f16*>(Ehi), reinterpret_cast<f16*>(Elo));
+hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, int64_t N, int64_t K, int bits,
+                              void* Ehi, void* Elo, hipStream_t st) {
+  const dim3 grid((unsigned)((N * (K / 8) + 255) / 256)), block(256);
+  auto Wp = reinterpret_cast<const uint4*>(W);
+  auto hi = reinterpret_cast<f16*>(Ehi);
+  auto lo = reinterpret_cast<f16*>(Elo);
+  if (bits == 3) quant_error_kernel<7><<<grid, block, 0, st>>>(Wp, s, ex, N, K, hi, lo);
+  else quant_error_kernel<15><<<grid, block, 0, st>>>(Wp, s, ex, N, K, hi, lo);
   return hipGetLastError();
 }
 
-// Packer: a 32-lane segment handles the group pair (2p, 2p+1) of one row so
-// that the two zero points of a zeros byte are known to one lane.
+// Packers: a 32-lane segment handles the group pair (2p, 2p+1) of one row so
+// that the two zero points of a zeros byte are known to one lane; lane i of a
+// 16-lane half quantizes channels 8i .. 8i + 7 of its group.
+//
+// 4-bit words: the code of channel 8w + i of a row sits in nibble
+// 4 (i % 2) + i / 2 of word w.  3-bit: the 32 channels 32c .. 32c + 31 of a
+// row are the three words 3c .. 3c + 2; the code of channel 2p (p = 0..14)
+// sits in bits 3j .. 3j + 2 of word p / 5 (j = p % 5), that of channel 2p + 1
+// in bits 16 + 3j .. 16 + 3j + 2 of the same word, and bit b of the codes of
+// channels 30 and 31 in bits 15 and 31 of word b.  A chunk of 32 channels is
+// four lanes' codes, OR-ed together across the four lanes.
+template <int BITS>
+__device__ inline void pack3_bits(const float q[8], int sub, uint32_t w[3]) {
+  w[0] = w[1] = w[2] = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t code = (uint32_t)q[i];
+    const int ch = 8 * sub + i;  // channel within the 32-channel chunk
+    if (ch < 30) {
+      const int p = ch >> 1, t = p / 5, j = p - 5 * t;
+      const uint32_t bits = code << (3 * j + 16 * (ch & 1));
+      w[0] |= t == 0 ? bits : 0u;
+      w[1] |= t == 1 ? bits : 0u;
+      w[2] |= t == 2 ? bits : 0u;
+    } else {
+      const int at = ch == 30 ? 15 : 31;
+#pragma unroll
+      for (int b = 0; b < 3; ++b) w[b] |= ((code >> b) & 1u) << at;
+    }
+  }
+}
+
+template <int BITS>
 __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
                                                    int64_t N, int64_t K, uint32_t* __restrict__ packed,
                                                    f16* __restrict__ scales, uint8_t* __restrict__ zeros) {
@@ -178,7 +220,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ W, 
   const int64_t n = seg / P, p = seg - n * P;
   const int64_t g = 2 * p + (lane32 >> 4);
   const bool live = g < G;
-  const int64_t w = g * 16 + (lane32 & 15);  // word within the row
+  const int64_t w = g * 16 + (lane32 & 15);  // 8-channel word within the row
   float wf[8], sf[8];
   if (live) {
     load_w8(W, n * (K / 8) + w, wf);
@@ -188,13 +230,30 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ W, 
     for (int i = 0; i < 8; ++i) { wf[i] = 0.0f; sf[i] = 1.0f; }
   }
   Quant8 r;
-  quantize8(wf, sf, r);  // a dead half-segment quantizes zeros and is discarded
+  quantize8<(1 << BITS) - 1>(wf, sf, r);  // a dead half-segment quantizes zeros and is discarded
   uint32_t z_other = (uint32_t)__shfl_xor((int)r.z, 16, 32);
-  if (!live) return;
-  uint32_t word = 0;
+  if constexpr (BITS == 4) {
+    if (!live) return;
+    uint32_t word = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) word |= ((uint32_t)r.q[i]) << (4 * nibble_pos(i));
-  packed[n * (K / 8) + w] = word;
+    for (int i = 0; i < 8; ++i) word |= ((uint32_t)r.q[i]) << (4 * nibble_pos(i));
+    packed[n * (K / 8) + w] = word;
+  } else {
+    uint32_t cw[3];
+    pack3_bits<BITS>(r.q, lane32 & 3, cw);
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {  // OR over the chunk's four lanes (all lanes take part)
+      cw[b] |= (uint32_t)__shfl_xor((int)cw[b], 1, 32);
+      cw[b] |= (uint32_t)__shfl_xor((int)cw[b], 2, 32);
+    }
+    if (!live) return;
+    if ((lane32 & 3) == 0) {
+      uint32_t* dst = packed + (n * (K / 32) + (w >> 2)) * 3;
+      dst[0] = cw[0];
+      dst[1] = cw[1];
+      dst[2] = cw[2];
+    }
+  }
   if ((lane32 & 15) == 0) scales[n * G + g] = r.sc16;
   if (lane32 == 0) {
     uint32_t zlo = (uint32_t)r.z;
@@ -203,13 +262,17 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ W, 
   }
 }
 
-hipError_t launch_pack(const void* W, const float* s, int64_t N, int64_t K, void* packed, void* scales,
+hipError_t launch_pack(const void* W, const float* s, int64_t N, int64_t K, int bits, void* packed, void* scales,
                        void* zeros, hipStream_t st) {
   const int64_t G = K / kGroup, P = (G + 1) / 2;
   const int64_t threads = N * P * 32;
-  pack_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st>>>(
-      reinterpret_cast<const uint4*>(W), s, N, K, reinterpret_cast<uint32_t*>(packed),
-      reinterpret_cast<f16*>(scales), reinterpret_cast<uint8_t*>(zeros));
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  auto Wp = reinterpret_cast<const uint4*>(W);
+  auto pp = reinterpret_cast<uint32_t*>(packed);
+  auto sp = reinterpret_cast<f16*>(scales);
+  auto zp = reinterpret_cast<uint8_t*>(zeros);
+  if (bits == 3) pack_kernel<3><<<grid, block, 0, st>>>(Wp, s, N, K, pp, sp, zp);
+  else pack_kernel<4><<<grid, block, 0, st>>>(Wp, s, N, K, pp, sp, zp);
   return hipGetLastError();
 }
 
@@ -239,11 +302,40 @@ __global__ void unpack_kernel(const uint32_t* __restrict__ packed, const uint8_t
   }
 }
 
-hipError_t launch_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, uint8_t* codes,
+// One thread per 32-channel chunk of the 3-bit format.
+__global__ void unpack3_kernel(const uint32_t* __restrict__ packed, const uint8_t* __restrict__ zeros, int64_t N,
+                               int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ zeros_u8) {
+  const int64_t K32 = K / 32, G = K / kGroup, P = (G + 1) / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= N * K32) return;
+  const int64_t n = idx / K32, c = idx - n * K32;
+  const uint32_t w[3] = {packed[3 * idx], packed[3 * idx + 1], packed[3 * idx + 2]};
+  uint8_t* out = codes + n * K + c * 32;
+#pragma unroll
+  for (int p = 0; p < 15; ++p) {
+    const uint32_t v = w[p / 5] >> (3 * (p % 5));
+    out[2 * p] = (uint8_t)(v & 7u);
+    out[2 * p + 1] = (uint8_t)((v >> 16) & 7u);
+  }
+  out[30] = (uint8_t)(((w[0] >> 15) & 1u) | (((w[1] >> 15) & 1u) << 1) | (((w[2] >> 15) & 1u) << 2));
+  out[31] = (uint8_t)(((w[0] >> 31) & 1u) | (((w[1] >> 31) & 1u) << 1) | (((w[2] >> 31) & 1u) << 2));
+  if ((c & 3) == 0) {
+    const int64_t g = c >> 2;
+    zeros_u8[n * G + g] = (uint8_t)((zeros[n * P + (g >> 1)] >> (4 * (g & 1))) & 0xFu);
+  }
+}
+
+hipError_t launch_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, int bits, uint8_t* codes,
                          uint8_t* zeros_u8, hipStream_t st) {
-  const int64_t words = N * (K / 8);
-  unpack_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st>>>(
-      reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const uint8_t*>(zeros), N, K, codes, zeros_u8);
+  auto pp = reinterpret_cast<const uint32_t*>(packed);
+  auto zp = reinterpret_cast<const uint8_t*>(zeros);
+  if (bits == 3) {
+    const int64_t chunks = N * (K / 32);
+    unpack3_kernel<<<dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st>>>(pp, zp, N, K, codes, zeros_u8);
+  } else {
+    const int64_t words = N * (K / 8);
+    unpack_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st>>>(pp, zp, N, K, codes, zeros_u8);
+  }
   return hipGetLastError();
 }
 
