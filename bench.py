@@ -54,9 +54,11 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def gemv_bytes(M: int, K: int, N: int) -> int:
+def gemv_bytes(M: int, K: int, N: int, bits: int = 4) -> int:
+    """Algorithmic bytes of one product: codes (bits per weight), fp16 scales and 4-bit
+    zero points per 128-channel group, x and y once."""
     G = K // 128
-    return N * K // 2 + 2 * N * G + N * ((G + 1) // 2) + 2 * M * K + 2 * M * N
+    return N * K * bits // 8 + 2 * N * G + N * ((G + 1) // 2) + 2 * M * K + 2 * M * N
 
 
 def source_hash(paths) -> str:
@@ -80,16 +82,16 @@ def measured_traffic(per_launch_alg_bytes: float):
 
 
 class Layer:
-    def __init__(self, name, K, N, torch, awq, copies, dev):
+    def __init__(self, name, K, N, torch, awq, copies, dev, bits=4):
         from gen import activations_fp16, normal_fp16
         self.name, self.K, self.N = name, K, N
         W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=2000 + K + N)).to(dev)
-        p, s, z = awq.awq_pack(W)  # plain round-to-nearest; values do not change the speed
+        p, s, z = awq.awq_pack(W, bits=bits)  # plain round-to-nearest; values do not change the speed
         del W
         self.copies = [(p, s, z)] + [(p.clone(), s.clone(), z.clone()) for _ in range(copies - 1)]
         self.x = torch.from_numpy(activations_fp16(1, K, seed=2100 + K)).to(dev)
         self.y = torch.empty((1, N), dtype=torch.float16, device=dev)
-        self.bytes = gemv_bytes(1, K, N)
+        self.bytes = gemv_bytes(1, K, N, bits)
 
 
 def graph_of(torch, fn):
@@ -209,6 +211,26 @@ def run_decode_fused(args, torch, awq, dev):
     return dict(us_per_step=round(ms * 1e3, 3), GBs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
                 hbm_frac=round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_per_step=step_bytes,
                 launches=len(LAYERS_7B_FUSED), layers_KN=[[K, N] for _, K, N in LAYERS_7B_FUSED])
+
+
+def run_decode_3bit(args, torch, awq, dev):
+    """The 7-launch decode step of run_decode with the weights packed at 3 bits (the same
+    layers and inputs; 3.156 instead of 4.156 bits per weight)."""
+    step_bytes = sum(gemv_bytes(1, K, N, 3) for _, K, N in LAYERS_7B)
+    copies = max(2, int(np.ceil((1 << 30) / step_bytes)) + 1)
+    layers = [Layer(n, K, N, torch, awq, copies, dev, bits=3) for n, K, N in LAYERS_7B]
+    torch.cuda.synchronize()
+
+    def step(c):
+        for L in layers:
+            p, s, z = L.copies[c]
+            awq.awq_gemm(L.x, p, s, z, out=L.y)
+
+    ms = time_steps(torch, step, copies, args.steps, args.warmup)
+    del layers
+    return dict(us_per_step=round(ms * 1e3, 3), GBs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                hbm_frac=round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_per_step=step_bytes,
+                launches=len(LAYERS_7B), bits=3)
 
 
 def run_sweep(args, torch, awq, dev):
@@ -390,6 +412,9 @@ def main():
     legs = {}
     log("decode, q/k/v and gate/up fused by concatenated rows (4 launches)")
     legs["decode_fused_qkv_gateup"] = run_decode_fused(args, torch, awq, dev)
+    torch.cuda.empty_cache()
+    log("decode, 3-bit weights (7 launches)")
+    legs["decode_llama2_7b_3bit"] = run_decode_3bit(args, torch, awq, dev)
     torch.cuda.empty_cache()
     if not args.no_sweep:
         log("sweep: (4096, 11008) at M = 1..1024")
