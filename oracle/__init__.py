@@ -15,6 +15,10 @@ Parity status per function (what pins it is in the tests named here):
   search             pinned: alpha = 0 is round-to-nearest, L(alpha*) <= L(0),
                      forced tie, known-answer construction
   gemm               pinned: brute-force loops, one-hot inputs, codes = zeros
+  top_channels / keep_fp16_error / keep_fp16_ablation
+                     pinned: hand-built rankings with ties, keeping every channel gives 0,
+                     keeping none is the alpha = 0 search loss, brute-force loops with the
+                     kept columns removed, Gram form = direct form
 """
 from .awq_oracle import (  # noqa: F401
     SCALE_FLOOR,
@@ -32,4 +36,7 @@ from .awq_oracle import (  # noqa: F401
     quantize_at,
     search,
     gemm,
+    top_channels,
+    keep_fp16_error,
+    keep_fp16_ablation,
 )

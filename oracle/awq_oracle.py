@@ -29,6 +29,11 @@ notes of the repository):
   R4  the search objective is the mean squared error of the layer's output on
       the calibration rows, against the unquantized layer.
   R5  ties in the search are broken towards the smallest alpha.
+  R6  keep-fp16 ablation: the whole weight is rounded group-wise as usual (s = 1) and the
+      kept channels' weights are then restored exactly; they are not removed from their
+      groups' ranges, so every selection rule shares the same steps and codes.  The weight
+      magnitude of an input channel is the mean of |w| over the output rows.
+  R7  top channels: largest value first, equal values ordered by the lower index.
 """
 from __future__ import annotations
 
@@ -194,6 +199,48 @@ def search(W: np.ndarray, X: np.ndarray, group: int = 128, alphas=None, bits: in
     q, z, sc16, s = quantize_at(W, a, alphas[best], group, bits)
     return dict(alpha_index=best, alpha=float(alphas[best]), losses=losses, a=a,
                 q=q, z=z, scales=sc16, s=s)
+
+
+# --------------------------------------------------------------------------- keep-fp16 ablation
+def top_channels(v: np.ndarray, n_keep: int) -> np.ndarray:
+    """Indices of the n_keep largest entries of v, largest first; equal values are ordered
+    by the lower index (reading R7)."""
+    v = np.asarray(v, dtype=np.float64)
+    order = sorted(range(v.shape[0]), key=lambda k: (-v[k], k))
+    return np.array(order[:n_keep], dtype=np.int32)
+
+
+def keep_fp16_error(W: np.ndarray, keep, group: int = 128, bits: int = 4) -> np.ndarray:
+    """E = w_hat - w (float64) of plain group-wise rounding (s = 1), with the columns of the
+    kept input channels exact ([summary] P2: a few channels stay in 16-bit while the rest
+    are rounded).  The kept channels stay in their groups' ranges (reading R6)."""
+    q, z, sc16 = quantize_groups(np.asarray(W).astype(np.float32), group, bits)
+    E = dequantize(q, z, sc16, group) - np.asarray(W).astype(np.float64)
+    E[:, np.asarray(keep, dtype=np.int64)] = 0.0
+    return E
+
+
+def keep_fp16_ablation(W: np.ndarray, X: np.ndarray, n_keep: int, random_keep, group: int = 128,
+                       bits: int = 4, use_gram: bool | None = None) -> dict:
+    """Output MSE on X of plain rounding with n_keep input channels kept in fp16, for the
+    channels chosen by activation magnitude (largest mean |x|), by weight magnitude (largest
+    mean |w| over output rows) and by the caller's random choice, next to keeping none
+    ([summary] P2).  Losses in the order none, activation, weight, random."""
+    W = np.asarray(W)
+    X = np.asarray(X)
+    M, K = X.shape
+    if use_gram is None:
+        use_gram = M > K
+    a = channel_mean_abs(X)
+    b = channel_mean_abs(W)  # mean over output rows of |w| per input channel: the same reduction
+    sets = [np.zeros(0, np.int32), top_channels(a, n_keep), top_channels(b, n_keep),
+            np.asarray(random_keep, dtype=np.int32)]
+    G = gram(X) if use_gram else None
+    losses = np.zeros(4, dtype=np.float64)
+    for i, keep in enumerate(sets):
+        E = keep_fp16_error(W, keep, group, bits)
+        losses[i] = output_mse_gram(G, E, M) if use_gram else output_mse(X, E)
+    return dict(losses=losses, keep_activation=sets[1], keep_weight=sets[2], a=a, b=b)
 
 
 # --------------------------------------------------------------------------- A8/A9

@@ -25,6 +25,8 @@ MUTATIONS = {
     "gram_perturbed": ("return X.T @ X", "return X.T @ X * 1.0000001"),
     "levels_not_minus_one": ("qmax = np.float32(2 ** bits - 1)", "qmax = np.float32(2 ** bits)"),
     "fixed_four_bit_range": ("qmax = np.float32(2 ** bits - 1)", "qmax = np.float32(15)"),
+    "kept_columns_not_restored": ("    E[:, np.asarray(keep, dtype=np.int64)] = 0.0\n", "\n"),
+    "smallest_channels_kept": ("key=lambda k: (-v[k], k)", "key=lambda k: (v[k], k)"),
     "gemm_wrong_group": ("zz = np.repeat(np.asarray(z, dtype=np.float64), group, axis=1)",
                          "zz = np.tile(np.asarray(z, dtype=np.float64), (1, group))"),
 }

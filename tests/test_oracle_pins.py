@@ -343,3 +343,64 @@ def test_gemm_one_hot_and_zero_codes():
             assert y[n] == (int(q[n, k]) - int(z[n, k // 128])) * float(sc[n, k // 128])
     qz = np.repeat(z, 128, axis=1)
     assert np.all(O.gemm(g.standard_normal((2, K)).astype(np.float16), qz, z, sc) == 0.0)
+
+
+# ----------------------------------------------------------------- keep-fp16 ablation
+def test_top_channels_hand_ranking():
+    v = np.array([1.0, 3.0, 3.0, 2.0, 5.0, 0.0, 3.0])
+    assert list(O.top_channels(v, 4)) == [4, 1, 2, 6]  # 5, then the three 3s by index
+    assert list(O.top_channels(v, 0)) == []
+    assert sorted(O.top_channels(v, 7)) == list(range(7))
+
+
+def test_keep_fp16_extremes():
+    W = normal_fp16((16, 256), 0.02, seed=30)
+    X = activations_fp16(24, 256, seed=31)
+    r = O.keep_fp16_ablation(W, X, 256, np.arange(256))
+    assert np.all(r["losses"][1:] == 0.0)  # every channel kept: nothing is rounded
+    r0 = O.keep_fp16_ablation(W, X, 0, np.zeros(0, np.int32))
+    L0 = O.search(W, X, alphas=np.zeros(1, np.float32))["losses"][0]
+    assert np.all(r0["losses"] == L0) and L0 > 0  # nothing kept: plain rounding
+
+
+def test_keep_fp16_loss_brute_force_loops():
+    W = normal_fp16((4, 128), 0.05, seed=32)
+    X = activations_fp16(5, 128, seed=33)
+    keep = np.array([3, 70], np.int32)
+    q, z, sc = O.quantize_groups(W.astype(np.float32))
+    L = 0.0
+    for t in range(5):
+        for n in range(4):
+            acc = 0.0
+            for k in range(128):
+                if k in (3, 70):
+                    continue
+                w_hat = (int(q[n, k]) - int(z[n, 0])) * float(sc[n, 0])
+                acc += float(X[t, k]) * (w_hat - float(W[n, k]))
+            L += acc * acc
+    L /= 20.0
+    r = O.keep_fp16_ablation(W, X, 2, keep)
+    assert abs(r["losses"][3] - L) <= 1e-12 * L
+
+
+def test_keep_fp16_gram_equals_direct():
+    W = normal_fp16((32, 256), 0.02, seed=34)
+    X = activations_fp16(300, 256, seed=35, lognormal=True)
+    rnd = np.random.default_rng(36).permutation(256)[:3].astype(np.int32)
+    d = O.keep_fp16_ablation(W, X, 3, rnd, use_gram=False)["losses"]
+    g = O.keep_fp16_ablation(W, X, 3, rnd, use_gram=True)["losses"]
+    assert np.all(np.abs(d - g) <= 1e-10 * d)
+
+
+def test_keep_fp16_activation_channels_are_the_outliers():
+    """With a few input channels scaled x20 (the synthetic salient channels), keeping the
+    channels of largest mean |x| keeps exactly those, and removes their error terms."""
+    K = 512
+    W = normal_fp16((64, K), 0.02, seed=37)
+    X = activations_fp16(256, K, seed=38)  # 1% of channels (5) carry x20 outliers
+    a = O.channel_mean_abs(X)
+    outliers = np.sort(np.argsort(-a)[:5])
+    assert np.all(a[outliers] > 10 * np.median(a))
+    r = O.keep_fp16_ablation(W, X, 5, np.arange(5, dtype=np.int32))
+    assert np.array_equal(np.sort(r["keep_activation"]), outliers)
+    assert r["losses"][1] < r["losses"][0]
