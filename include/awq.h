@@ -10,6 +10,8 @@
  *   [profile]  "AWQ: Activation-aware Weight Quantization for On-Device LLM
  *              Compression", aiexpertsdirectory.org, "Execution Profile &
  *              Computation Stack".
+ *   [proof page] the same aiexpertsdirectory.org page, "Methodological &
+ *              Architectural Deep-Dive".
  *
  * Notation.  A linear layer maps an input row x[K] to y[N] = W x, with W an
  * fp16 [N][K] row-major matrix (row n = output channel, like a torch Linear
@@ -231,6 +233,41 @@ int awq_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, int3
 /* awq_unpack of the format written at `bits` = 4 or 3. */
 int awq_unpack_bits(const void* packed, const void* zeros, int64_t N, int64_t K, int32_t group, int32_t bits,
                     uint8_t* codes, uint8_t* zeros_u8, void* stream);
+
+/*
+ * awq_keep_fp16_ablation -- the observation AWQ starts from ([summary]
+ * paragraph 2; [proof page], methodological paragraph): keeping a few input
+ * channels of a layer in 16-bit while rounding the rest recovers most of the
+ * rounding loss, but only when the channels are chosen by activation
+ * magnitude; chosen by weight magnitude they do about as well as at random.
+ *
+ *   W, X        device fp16 [N][K] weight and [M][K] calibration rows
+ *   bits        4 or 3
+ *   n_keep      channels kept, 0 <= n_keep <= K
+ *   random_keep device int32 [n_keep]   the caller's random choice of channels
+ *                                       (entries outside [0, K) are ignored)
+ *   keep_act    device int32 [n_keep]   out: channels of largest mean |x| over
+ *                                       X's rows, largest first
+ *   keep_wt     device int32 [n_keep]   out: channels of largest mean |w| over
+ *                                       W's rows, largest first
+ *   loss        device fp64 [4]         out: output MSE on X with no channel
+ *                                       kept, keep_act, keep_wt, random_keep
+ *   workspace   device, >= awq_ablation_workspace_bytes(N, K, M, group)
+ *
+ * W is quantized group-wise exactly as awq_pack with s = NULL (plain
+ * round-to-nearest); the kept channels' weights are then used unrounded (they
+ * stay in their groups' ranges, so every choice shares the same steps).  The
+ * loss is that of awq_quantize, L = ||X E^T||_F^2 / (M N) with E = w_hat - w
+ * and E = 0 on the kept channels, in the same direct or Gram form.  Equal
+ * magnitudes are ordered by the lower channel index; the magnitudes are exact
+ * sums (as awq_channel_mean_abs), so the choice is reproducible.
+ * Requires 1 <= M, N <= AWQ_MAX_CALIB_ROWS, group == AWQ_GROUP, K % group == 0.
+ */
+size_t awq_ablation_workspace_bytes(int64_t N, int64_t K, int64_t M, int32_t group);
+int awq_keep_fp16_ablation(const void* W, const void* X, int64_t N, int64_t K, int64_t M, int32_t group,
+                           int32_t bits, int32_t n_keep, const int32_t* random_keep,
+                           int32_t* keep_act, int32_t* keep_wt, double* loss,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for a status code; message for the calling thread's last failure. */
 const char* awq_status_string(int status);

@@ -135,6 +135,24 @@ def test_bits_argument_errors_before_launch():
     assert lib.awq_gemm_bits(FAKE_MISALIGNED, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 3, None) == MISALIGNED
 
 
+def test_ablation_argument_errors_before_launch():
+    lib = _lib_()
+    f = lib.awq_keep_fp16_ablation
+    ws = awq.awq_ablation_workspace_bytes(64, 256, 32)
+    assert ws >= awq.awq_quantize_workspace_bytes(64, 256, 32, 128, 1) + 9 * 256 > 0
+    base = dict(W=FAKE, X=FAKE, N=64, K=256, M=32, g=128, bits=4, nk=3, rk=FAKE, ka=FAKE, kw=FAKE, loss=FAKE,
+                ws=FAKE, wsb=ws, st=None)
+    call = lambda **kw: f(*dict(base, **kw).values())
+    assert call(nk=257) == INVALID and "n_keep" in awq.awq_last_error()
+    assert call(nk=-1) == INVALID
+    assert call(rk=None) == INVALID
+    assert call(bits=2) == INVALID
+    assert call(M=0) == INVALID
+    assert call(N=(1 << 23) + 1) == INVALID
+    assert call(wsb=ws - 1) == WS_SMALL
+    assert call(X=FAKE_MISALIGNED) == MISALIGNED
+
+
 def test_quantize_argument_errors_before_launch():
     lib = _lib_()
     q = lib.awq_quantize

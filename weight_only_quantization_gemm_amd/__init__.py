@@ -5,10 +5,13 @@ allocates device memory and provides streams; every step runs in the library.
 """
 from ._lib import LIB_PATH, AwqError, load  # noqa: F401
 from .api import (  # noqa: F401
+    ABLATION_ORDER,
     GROUP,
     MAX_ALPHAS,
+    awq_ablation_workspace_bytes,
     awq_channel_mean_abs,
     awq_gemm,
+    awq_keep_fp16_ablation,
     awq_last_error,
     awq_pack,
     awq_packed_bytes,

@@ -31,6 +31,9 @@ SIGNATURES = {
                                          c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "awq_gemm_bits": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
     "awq_unpack_bits": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "awq_ablation_workspace_bytes": (c_size, [c_i64, c_i64, c_i64, c_i32]),
+    "awq_keep_fp16_ablation": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp,
+                                              c_vp, c_vp, c_vp, c_size, c_vp]),
     "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "awq_last_error": (ctypes.c_char_p, []),
     "awq_version": (ctypes.c_int, []),

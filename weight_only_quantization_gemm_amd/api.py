@@ -195,6 +195,52 @@ def awq_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros:
     return out
 
 
+ABLATION_ORDER = ("none", "activation", "weight", "random")
+
+
+def awq_ablation_workspace_bytes(N: int, K: int, M: int, group: int = GROUP) -> int:
+    return int(load().awq_ablation_workspace_bytes(N, K, M, group))
+
+
+def awq_keep_fp16_ablation(W: torch.Tensor, X: torch.Tensor, n_keep: int, random_keep: Optional[torch.Tensor] = None,
+                           group: int = GROUP, bits: int = 4, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Output MSE of plain rounding with n_keep input channels kept in fp16, chosen by
+    activation magnitude, by weight magnitude and at random (random_keep: int32 [n_keep] on
+    W's device, the caller's draw); loss fp64 [4] in ABLATION_ORDER."""
+    _need(W, "W", torch.float16, 2)
+    _need(X, "X", torch.float16, 2)
+    _check_bits(bits)
+    N, K = W.shape
+    M = X.shape[0]
+    if X.shape[1] != K or X.device != W.device:
+        raise ValueError("X must be fp16 [M][K] on W's device")
+    if not 0 <= n_keep <= K:
+        raise ValueError(f"n_keep={n_keep} outside [0, {K}]")
+    if n_keep > 0:
+        if random_keep is None:
+            raise ValueError("random_keep is required when n_keep > 0")
+        _need(random_keep, "random_keep", torch.int32, 1)
+        if random_keep.shape[0] != n_keep or random_keep.device != W.device:
+            raise ValueError("random_keep must be int32 [n_keep] on W's device")
+    lib = load()
+    ws_bytes = int(lib.awq_ablation_workspace_bytes(N, K, M, group))
+    if ws_bytes == 0:
+        raise ValueError("unsupported sizes for awq_keep_fp16_ablation")
+    if workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
+    elif workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_cuda:
+        raise ValueError(f"workspace must be a GPU buffer of at least {ws_bytes} bytes")
+    keep_act = torch.empty((n_keep,), dtype=torch.int32, device=W.device)
+    keep_wt = torch.empty((n_keep,), dtype=torch.int32, device=W.device)
+    loss = torch.empty((4,), dtype=torch.float64, device=W.device)
+    with torch.cuda.device(W.device):
+        check(lib.awq_keep_fp16_ablation(W.data_ptr(), X.data_ptr(), N, K, M, group, bits, n_keep,
+                                         _ptr(random_keep) if n_keep > 0 else None, keep_act.data_ptr(),
+                                         keep_wt.data_ptr(), loss.data_ptr(), workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), _stream(W.device)))
+    return dict(loss=loss, keep_activation=keep_act, keep_weight=keep_wt, order=ABLATION_ORDER)
+
+
 def awq_unpack(packed: torch.Tensor, zeros: torch.Tensor, K: int, group: int = GROUP, bits: Optional[int] = None):
     """Logical codes uint8 [N][K] and zero points uint8 [N][K/g] of a packed layer."""
     _need(packed, "packed", torch.int32, 2)
@@ -211,4 +257,4 @@ def awq_unpack(packed: torch.Tensor, zeros: torch.Tensor, K: int, group: int = G
 
 
 __all__ = [n for n in dir() if n.startswith("awq_")] + ["AwqError", "default_alpha_grid", "empty_packed",
-                                                        "packed_words", "bits_of"]
+                                                        "packed_words", "bits_of", "ABLATION_ORDER"]

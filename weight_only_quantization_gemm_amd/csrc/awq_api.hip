@@ -71,11 +71,12 @@ int check_layer(int64_t N, int64_t K, int32_t group) {
 // (X^T, G in fp32 and as scaled fp16 hi/lo, channel exponents, E' hi/lo).
 struct QuantizeWorkspace {
   bool direct;
-  size_t a, s_all, xt, g, gh, gl, ex, eh, el, e32, partial, loss, total;
+  size_t a, s_all, xt, g, gh, gl, ex, eh, el, e32, partial, loss, b, mask, total;
   int64_t mp, partials;
 };
 
-QuantizeWorkspace quantize_workspace(int64_t N, int64_t K, int64_t M, int32_t n_alpha) {
+// The keep-fp16 ablation adds the weight magnitudes b [K] and a channel mask [K].
+QuantizeWorkspace quantize_workspace(int64_t N, int64_t K, int64_t M, int32_t n_alpha, bool ablation = false) {
   QuantizeWorkspace w{};
   w.direct = M < K;
   w.mp = (M + 63) / 64 * 64;
@@ -101,6 +102,10 @@ QuantizeWorkspace quantize_workspace(int64_t N, int64_t K, int64_t M, int32_t n_
   }
   w.partial = take(sizeof(double) * (size_t)w.partials);
   w.loss = take(sizeof(double) * (size_t)n_alpha);
+  if (ablation) {
+    w.b = take(sizeof(double) * (size_t)K);
+    w.mask = take((size_t)K);
+  }
   w.total = off;
   return w;
 }
@@ -224,7 +229,7 @@ int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_
   if (w.direct) {
     float* E = reinterpret_cast<float*>(base + w.e32);
     for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
-      e = awq::launch_quant_error32(W, s_all + (size_t)i * (size_t)K, N, K, bits, E, hs);
+      e = awq::launch_quant_error32(W, s_all + (size_t)i * (size_t)K, nullptr, N, K, bits, E, hs);
       if (e == hipSuccess) e = awq::launch_loss_direct(X, E, M, N, K, partial, hs);
       if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, L + i, hs);
     }
@@ -240,7 +245,7 @@ int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_
     if (e == hipSuccess) e = awq::launch_gram(xt, w.mp, K, G, hs);
     if (e == hipSuccess) e = awq::launch_gram_split(G, K, ex, Ghi, Glo, hs);
     for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
-      e = awq::launch_quant_error(W, s_all + (size_t)i * (size_t)K, ex, N, K, bits, Ehi, Elo, hs);
+      e = awq::launch_quant_error(W, s_all + (size_t)i * (size_t)K, ex, nullptr, N, K, bits, Ehi, Elo, hs);
       if (e == hipSuccess) e = awq::launch_loss_partials(Ehi, Elo, Ghi, Glo, N, K, partial, hs);
       if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, L + i, hs);
     }
@@ -249,6 +254,67 @@ int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_
   if (e == hipSuccess) e = awq::launch_select_scale(s_all, best_alpha, K, s, hs);
   if (e == hipSuccess) e = awq::launch_pack(W, s, N, K, bits, packed, scales, zeros, hs);
   return device_status(e, "awq_quantize");
+  AWQ_GUARD_END
+}
+
+size_t awq_ablation_workspace_bytes(int64_t N, int64_t K, int64_t M, int32_t group) {
+  if (N < 1 || K < 1 || M < 1 || group != AWQ_GROUP || K % group != 0) return 0;
+  return quantize_workspace(N, K, M, 1, true).total;
+}
+
+int awq_keep_fp16_ablation(const void* W, const void* X, int64_t N, int64_t K, int64_t M, int32_t group, int32_t bits,
+                           int32_t n_keep, const int32_t* random_keep, int32_t* keep_act, int32_t* keep_wt,
+                           double* loss, void* workspace, size_t workspace_bytes, void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(W && X && loss && workspace && (n_keep == 0 || (random_keep && keep_act && keep_wt)),
+              AWQ_ERROR_INVALID_VALUE, "W, X, loss, workspace (and the keep lists when n_keep > 0) must not be NULL");
+  int st = check_layer(N, K, group);
+  if (st == AWQ_OK) st = check_bits(bits);
+  if (st != AWQ_OK) return st;
+  AWQ_REQUIRE(M >= 1 && M <= AWQ_MAX_CALIB_ROWS && N <= AWQ_MAX_CALIB_ROWS, AWQ_ERROR_INVALID_VALUE,
+              "M=%lld and N=%lld must be in [1, 2^23]", (long long)M, (long long)N);
+  AWQ_REQUIRE(n_keep >= 0 && n_keep <= K, AWQ_ERROR_INVALID_VALUE, "n_keep=%d outside [0, K]", n_keep);
+  AWQ_REQUIRE(aligned16(W) && aligned16(X) && aligned16(workspace), AWQ_ERROR_MISALIGNED,
+              "W, X and workspace must be 16-byte aligned");
+  const QuantizeWorkspace w = quantize_workspace(N, K, M, 1, true);
+  AWQ_REQUIRE(workspace_bytes >= w.total, AWQ_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu",
+              workspace_bytes, w.total);
+  char* base = static_cast<char*>(workspace);
+  double* a = reinterpret_cast<double*>(base + w.a);
+  double* b = reinterpret_cast<double*>(base + w.b);
+  uint8_t* mask = reinterpret_cast<uint8_t*>(base + w.mask);
+  double* partial = reinterpret_cast<double*>(base + w.partial);
+  hipStream_t hs = as_stream(stream);
+  const double mn = (double)M * (double)N;
+
+  // activation magnitude of each input channel, and weight magnitude: the same
+  // exact mean of |.| over the rows of W [N][K]
+  hipError_t e = awq::launch_channel_mean_abs(X, M, K, a, hs);
+  if (e == hipSuccess) e = awq::launch_channel_mean_abs(W, N, K, b, hs);
+  if (e == hipSuccess && n_keep > 0) e = awq::launch_top_channels(a, K, n_keep, keep_act, hs);
+  if (e == hipSuccess && n_keep > 0) e = awq::launch_top_channels(b, K, n_keep, keep_wt, hs);
+  int32_t* ex = reinterpret_cast<int32_t*>(base + w.ex);
+  if (!w.direct) {
+    if (e == hipSuccess) e = awq::launch_transpose(X, M, K, w.mp, base + w.xt, hs);
+    if (e == hipSuccess) e = awq::launch_gram(base + w.xt, w.mp, K, reinterpret_cast<float*>(base + w.g), hs);
+    if (e == hipSuccess)
+      e = awq::launch_gram_split(reinterpret_cast<float*>(base + w.g), K, ex, base + w.gh, base + w.gl, hs);
+  }
+  const int32_t* sets[4] = {nullptr, keep_act, keep_wt, random_keep};
+  for (int i = 0; i < 4 && e == hipSuccess; ++i) {
+    e = awq::launch_keep_mask(sets[i], i == 0 ? 0 : n_keep, K, mask, hs);
+    if (w.direct) {
+      float* E = reinterpret_cast<float*>(base + w.e32);
+      if (e == hipSuccess) e = awq::launch_quant_error32(W, nullptr, mask, N, K, bits, E, hs);
+      if (e == hipSuccess) e = awq::launch_loss_direct(X, E, M, N, K, partial, hs);
+    } else {
+      if (e == hipSuccess) e = awq::launch_quant_error(W, nullptr, ex, mask, N, K, bits, base + w.eh, base + w.el, hs);
+      if (e == hipSuccess) e = awq::launch_loss_partials(base + w.eh, base + w.el, base + w.gh, base + w.gl, N, K,
+                                                         partial, hs);
+    }
+    if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, loss + i, hs);
+  }
+  return device_status(e, "awq_keep_fp16_ablation");
   AWQ_GUARD_END
 }
 

@@ -25,10 +25,13 @@ hipError_t launch_gram(const void* Xt, int64_t Mp, int64_t K, float* G, hipStrea
 hipError_t launch_scales(const double* a, const AlphaGrid& al, int n_alpha, int64_t K, float* s_all,
                          hipStream_t st);
 // bits: 4 (16 levels) or 3 (8 levels)
-hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, int64_t N, int64_t K, int bits,
-                              void* Ehi, void* Elo, hipStream_t st);
-hipError_t launch_quant_error32(const void* W, const float* s, int64_t N, int64_t K, int bits, float* E,
-                                hipStream_t st);
+// keep: NULL, or uint8 [K] marking channels whose error is 0 (kept exact)
+hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, const uint8_t* keep, int64_t N,
+                              int64_t K, int bits, void* Ehi, void* Elo, hipStream_t st);
+hipError_t launch_quant_error32(const void* W, const float* s, const uint8_t* keep, int64_t N, int64_t K, int bits,
+                                float* E, hipStream_t st);
+hipError_t launch_top_channels(const double* v, int64_t K, int n_keep, int32_t* out, hipStream_t st);
+hipError_t launch_keep_mask(const int32_t* keep, int n_keep, int64_t K, uint8_t* mask, hipStream_t st);
 hipError_t launch_pack(const void* W, const float* s, int64_t N, int64_t K, int bits, void* packed, void* scales,
                        void* zeros, hipStream_t st);
 hipError_t launch_select_scale(const float* s_all, const int32_t* best, int64_t K, float* s_out, hipStream_t st);

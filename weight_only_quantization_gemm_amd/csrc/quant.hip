@@ -98,10 +98,12 @@ __device__ inline void quantize8(const float w[8], const float s[8], Quant8& r) 
 // Weight error of the search, pre-scaled for the loss contraction:
 // E'[n][k] = ((q - z) * sc / s - w) * 2^e_k, evaluated in fp64, rounded to
 // fp32 and stored as an fp16 pair hi = fp16(E'), lo = fp16(E' - hi).  One
-// thread per 8 channels.
+// thread per 8 channels.  Channels with keep[k] != 0 (keep may be NULL) stay
+// exact: their error is 0.
 template <int QMAX>
 __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
-                                                          const int32_t* __restrict__ ex, int64_t N, int64_t K,
+                                                          const int32_t* __restrict__ ex,
+                                                          const uint8_t* __restrict__ keep, int64_t N, int64_t K,
                                                           f16* __restrict__ Ehi, f16* __restrict__ Elo) {
   const int64_t K8 = K / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // word index over N*K/8
@@ -121,7 +123,8 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restric
     f16x2 h, l;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const double e = ((double)(r.q[i + u] - r.z) * scd) / (double)sf[i + u] - (double)wf[i + u];
+      double e = ((double)(r.q[i + u] - r.z) * scd) / (double)sf[i + u] - (double)wf[i + u];
+      if (keep != nullptr && keep[w * 8 + i + u]) e = 0.0;
       const float v = (float)ldexp(e, ex[w * 8 + i + u]);
       const f16 hi = (f16)v;
       h[u] = hi;
@@ -137,7 +140,8 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restric
 // Unscaled weight error in fp32 for the direct form of the loss.
 template <int QMAX>
 __global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
-                                                            int64_t N, int64_t K, float* __restrict__ E) {
+                                                            const uint8_t* __restrict__ keep, int64_t N, int64_t K,
+                                                            float* __restrict__ E) {
   const int64_t K8 = K / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= N * K8) return;  // whole 16-lane segments, as above
@@ -150,29 +154,81 @@ __global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restr
   const double scd = (double)r.sc;
   float e[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) e[i] = (float)(((double)(r.q[i] - r.z) * scd) / (double)sf[i] - (double)wf[i]);
+  for (int i = 0; i < 8; ++i) {
+    e[i] = (float)(((double)(r.q[i] - r.z) * scd) / (double)sf[i] - (double)wf[i]);
+    if (keep != nullptr && keep[w * 8 + i]) e[i] = 0.0f;
+  }
   float4* out = reinterpret_cast<float4*>(E + n * K + w * 8);
   out[0] = make_float4(e[0], e[1], e[2], e[3]);
   out[1] = make_float4(e[4], e[5], e[6], e[7]);
 }
 
-hipError_t launch_quant_error32(const void* W, const float* s, int64_t N, int64_t K, int bits, float* E,
-                                hipStream_t st) {
+hipError_t launch_quant_error32(const void* W, const float* s, const uint8_t* keep, int64_t N, int64_t K, int bits,
+                                float* E, hipStream_t st) {
   const dim3 grid((unsigned)((N * (K / 8) + 255) / 256)), block(256);
   auto Wp = reinterpret_cast<const uint4*>(W);
-  if (bits == 3) quant_error32_kernel<7><<<grid, block, 0, st>>>(Wp, s, N, K, E);
-  else quant_error32_kernel<15><<<grid, block, 0, st>>>(Wp, s, N, K, E);
+  if (bits == 3) quant_error32_kernel<7><<<grid, block, 0, st>>>(Wp, s, keep, N, K, E);
+  else quant_error32_kernel<15><<<grid, block, 0, st>>>(Wp, s, keep, N, K, E);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, int64_t N, int64_t K, int bits,
-                              void* Ehi, void* Elo, hipStream_t st) {
+hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, const uint8_t* keep, int64_t N,
+                              int64_t K, int bits, void* Ehi, void* Elo, hipStream_t st) {
   const dim3 grid((unsigned)((N * (K / 8) + 255) / 256)), block(256);
   auto Wp = reinterpret_cast<const uint4*>(W);
   auto hi = reinterpret_cast<f16*>(Ehi);
   auto lo = reinterpret_cast<f16*>(Elo);
-  if (bits == 3) quant_error_kernel<7><<<grid, block, 0, st>>>(Wp, s, ex, N, K, hi, lo);
-  else quant_error_kernel<15><<<grid, block, 0, st>>>(Wp, s, ex, N, K, hi, lo);
+  if (bits == 3) quant_error_kernel<7><<<grid, block, 0, st>>>(Wp, s, ex, keep, N, K, hi, lo);
+  else quant_error_kernel<15><<<grid, block, 0, st>>>(Wp, s, ex, keep, N, K, hi, lo);
+  return hipGetLastError();
+}
+
+// Top channels: out[r] = k for the channel k of rank r < n_keep, the rank being
+// the number of channels with a larger value plus those with an equal value
+// and a lower index (largest first, ties to the lower index).  Every value is
+// compared exactly, so the choice is reproducible bit for bit.
+__global__ __launch_bounds__(256) void top_channels_kernel(const double* __restrict__ v, int K, int n_keep,
+                                                           int32_t* __restrict__ out) {
+  __shared__ double tile[256];
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  const double vk = k < K ? v[k] : 0.0;
+  int rank = 0;
+  for (int j0 = 0; j0 < K; j0 += 256) {
+    __syncthreads();
+    if (j0 + (int)threadIdx.x < K) tile[threadIdx.x] = v[j0 + threadIdx.x];
+    __syncthreads();
+    const int jn = K - j0 < 256 ? K - j0 : 256;
+    for (int j = 0; j < jn; ++j) {
+      const double vj = tile[j];
+      rank += (vj > vk) || (vj == vk && j0 + j < k);
+    }
+  }
+  if (k < K && rank < n_keep) out[rank] = k;
+}
+
+hipError_t launch_top_channels(const double* v, int64_t K, int n_keep, int32_t* out, hipStream_t st) {
+  top_channels_kernel<<<dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st>>>(v, (int)K, n_keep, out);
+  return hipGetLastError();
+}
+
+__global__ void keep_mask_clear_kernel(uint8_t* __restrict__ mask, int64_t K) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < K) mask[k] = 0;
+}
+
+__global__ void keep_mask_set_kernel(const int32_t* __restrict__ keep, int n_keep, int64_t K,
+                                     uint8_t* __restrict__ mask) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_keep) {
+    const int32_t k = keep[i];
+    if (k >= 0 && k < K) mask[k] = 1;  // out-of-range entries are ignored
+  }
+}
+
+hipError_t launch_keep_mask(const int32_t* keep, int n_keep, int64_t K, uint8_t* mask, hipStream_t st) {
+  keep_mask_clear_kernel<<<dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st>>>(mask, K);
+  if (n_keep > 0)
+    keep_mask_set_kernel<<<dim3((unsigned)((n_keep + 255) / 256)), dim3(256), 0, st>>>(keep, n_keep, K, mask);
   return hipGetLastError();
 }
 
