@@ -263,6 +263,27 @@ def run_sweep(args, torch, awq, dev):
     return out
 
 
+def run_ablation(torch, awq, dev, W, X, search_loss):
+    """Keep 1% of the input channels in fp16 and round the rest (s = 1): output MSE on the
+    calibration rows, relative to plain rounding, for channels chosen by activation, by weight
+    magnitude and at random, next to the searched scales' loss."""
+    N, K = W.shape
+    n_keep = round(0.01 * K)
+    rnd = torch.from_numpy(np.random.default_rng(5150).permutation(K)[:n_keep].astype(np.int32)).to(dev)
+    awq.awq_keep_fp16_ablation(W, X, n_keep, rnd)  # warm-up
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    r = awq.awq_keep_fp16_ablation(W, X, n_keep, rnd)
+    b.record()
+    torch.cuda.synchronize()
+    L = r["loss"].cpu().numpy()
+    assert L[0] == search_loss[0], "plain rounding must give the search's alpha = 0 loss"
+    return dict(n_keep=n_keep, ms=round(a.elapsed_time(b), 2),
+                mse_ratio_vs_rtn={k: float(L[i] / L[0]) for i, k in enumerate(r["order"]) if i > 0},
+                awq_search_ratio_vs_rtn=float(search_loss.min() / search_loss[0]))
+
+
 def run_search(args, torch, awq, dev):
     """awq_quantize on the 7 linears of a 7B block, 65,536 calibration rows per input."""
     from gen import activations_fp16, normal_fp16, seed_for
@@ -292,6 +313,8 @@ def run_search(args, torch, awq, dev):
         best = int(r["best_alpha"].item())
         res[lname] = dict(K=K, N=N, ms=round(ms, 2), alpha_index=best, alpha=float(r["alphas"][best]),
                           mse_ratio_vs_rtn=float(loss[best] / loss[0]))
+        if lname == "q_proj":
+            res[lname]["keep_fp16_ablation"] = run_ablation(torch, awq, dev, W, inputs[src], loss)
         del W, ws, r
         torch.cuda.empty_cache()
     return dict(layers=res, s_per_layer=round(total_ms / 7 / 1e3, 4), total_s=round(total_ms / 1e3, 3),
