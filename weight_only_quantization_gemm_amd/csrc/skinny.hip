@@ -23,8 +23,9 @@
 // K groups (wave w takes groups w, w+W, ...).  For one group a wave loads 16 B
 // per lane: lane l reads the (l/16)-th 16-byte quarter of the group's 64 B in
 // row l%16, so one load instruction fetches 16 rows x 64 B.  All loads of a
-// batch of P groups are issued before any is used.  x is staged once per
-// block in LDS when it fits.  The waves' partial tiles are summed through LDS
+// batch of P groups (and, without LDS staging, their x fragments) are issued
+// before any is used.  x is staged once per block in LDS when it fits, before
+// the first weight load.  The waves' partial tiles are summed through LDS
 // in a fixed order, so results are deterministic.
 #include "awq_common.h"
 #include "awq_internal.h"
@@ -54,9 +55,11 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
   const int nl = lane & 15, kq = lane >> 4;  // row within a 16-row tile; quarter of a group
   const int64_t n0 = (int64_t)blockIdx.x * (16 * RW);
   const int64_t K8 = K / 8, G = K / kGroup, P2 = (G + 1) / 2;
-  bool mlive[MT];  // this lane's A-operand row of m-tile mt is a real activation row
+  // A-operand rows past M read row M - 1 (valid memory): MFMA output rows are
+  // independent and those rows are never stored.
+  int64_t xrow[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) mlive[mt] = 16 * mt + nl < M;
+  for (int mt = 0; mt < MT; ++mt) xrow[mt] = 16 * mt + nl < M ? 16 * mt + nl : M - 1;
 
   int64_t rowi[RW];
 #pragma unroll
@@ -70,17 +73,35 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // x goes into LDS before any weight load is issued: vector-memory loads
+  // complete in order, so waiting for the copy must not include them.
   f16* xs = reinterpret_cast<f16*>(smem);
-  bool staged = false;
+  if (XLDS) {
+    const int64_t n16 = (int64_t)M * K / 8;
+    for (int64_t i = threadIdx.x; i < n16; i += W * kWave)
+      reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
+    __syncthreads();
+  }
+  // Without LDS staging the batch's x fragments are loaded together with its
+  // weights, before the first wait, when they fit in registers; otherwise per group.
+  constexpr bool XPRE = !XLDS && P * MT <= 4;
 
   for (int64_t gb = wave; gb < G; gb += (int64_t)W * P) {
     u32x4 wv[P][RW];
     f16 sc[P][RW];
     uint32_t zz[P][RW];
+    f16x8 ap[XPRE ? P : 1][MT][4];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int64_t g = gb + (int64_t)p * W;
-      const int64_t gg = g < G ? g : G - 1;
+      const int64_t gg = g < G ? g : G - 1;  // past the last group: reloaded, never used
+      if constexpr (XPRE) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            ap[p][mt][s] = *reinterpret_cast<const f16x8*>(x + xrow[mt] * K + gg * kGroup + kq * 32 + 8 * s);
+      }
 #pragma unroll
       for (int t = 0; t < RW; ++t) {
         wv[p][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + rowi[t] * K8 + gg * 16 + kq * 4));
@@ -88,30 +109,23 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
         zz[p][t] = (zeros[rowi[t] * P2 + (gg >> 1)] >> (4 * (gg & 1))) & 0xFu;
       }
     }
-    if (XLDS && !staged) {
-      // copy x into LDS while this wave's weight loads are in flight
-      const int64_t n16 = (int64_t)M * K / 8;
-      for (int64_t i = threadIdx.x; i < n16; i += W * kWave)
-        reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
-      __syncthreads();
-      staged = true;
-    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch before the first wait
 #pragma unroll
     for (int p = 0; p < P; ++p) {
+      // branch-free: a group past the last one recomputes the last and adds 0
+      // (a branch here would let the compiler sink this group's loads below
+      // the previous group's wait)
       const int64_t g = gb + (int64_t)p * W;
-      if (g >= G) break;
-      const int64_t k0 = g * kGroup + kq * 32;
+      const bool live = g < G;
+      const int64_t k0 = (live ? g : G - 1) * kGroup + kq * 32;
       f16x8 a[MT][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int64_t row = 16 * mt + nl;
-          if (mlive[mt])
-            a[mt][s] = XLDS ? *reinterpret_cast<const f16x8*>(xs + row * K + k0 + 8 * s)
-                            : *reinterpret_cast<const f16x8*>(x + row * K + k0 + 8 * s);
-          else
-            a[mt][s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+          if constexpr (XPRE) a[mt][s] = ap[p][mt][s];
+          else if constexpr (XLDS) a[mt][s] = *reinterpret_cast<const f16x8*>(xs + xrow[mt] * K + k0 + 8 * s);
+          else a[mt][s] = *reinterpret_cast<const f16x8*>(x + xrow[mt] * K + k0 + 8 * s);
         }
 #pragma unroll
       for (int t = 0; t < RW; ++t) {
@@ -128,7 +142,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][s], b, d[mt], 0, 0, 0);
         }
-        const float scf = (float)sc[p][t];
+        const float scf = live ? (float)sc[p][t] : 0.0f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -136,7 +150,6 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
       }
     }
   }
-  if (XLDS && !staged) __syncthreads();  // a wave without groups still meets the staging barrier
 
   // sum the waves' tiles: lane holds y[m = 16*mt + 4*kq + r][n0 + 16t + nl]
   float* red = reinterpret_cast<float*>(smem + red_offset);
