@@ -26,9 +26,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]
-# Per-source extras.  The W4A16 GEMM keeps its matrix-core accumulators in
-# ordinary vector registers, so the per-group scale is one FMA per element
-# (accumulators in AGPRs would need a register move before each FMA).
+# Per-source extras.  The pipelined W4A16 GEMM keeps its matrix-core
+# accumulators in ordinary vector registers (measured faster than the
+# accumulation-register form).
 # The decode kernels are short enough (a few microseconds) that the kernel-argument
 # load at each wave's start is on its critical path; gfx950 can preload the
 # arguments into SGPRs at dispatch instead.
