@@ -1,0 +1,70 @@
+"""GPU parity of the matrix-core decode path (3 <= M <= 16) against the oracle, with the
+bars of the other product tests (relative Frobenius error <= 1e-3, max |dy| <= 1e-2 max
+|y_ref|), at shapes that select each ring layout: one or two 16-row tiles per wave, four
+or eight waves per block.  Row counts leave a partial last block (which stages its scales
+and zeros one by one instead of by DMA), group counts are odd or smaller than the wave
+count, and one K is long enough that the block's scales and zeros no longer fit in LDS
+beside the rings at M = 16, so the register-staged kernel runs instead."""
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_quantization_gemm_amd as awq
+from gen import activations_fp16
+from layout import assert_y_close
+from test_gpu_parity import _random_packed, dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(N, K, M, seed, sample=None):
+    q, z, sc, p, scd, zd = _random_packed(N, K, seed=seed)
+    x = activations_fp16(M, K, seed=seed + 1)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    if sample is None:
+        assert_y_close(y, oracle.gemm(x, q, z, sc), f"N={N} K={K} M={M}")
+        return y
+    g = np.random.default_rng(seed + 2)
+    rows = np.union1d(g.choice(N, size=sample, replace=False), np.arange(N - 40, N))  # always the last block
+    assert_y_close(y[:, rows], oracle.gemm(x, q[rows], z[rows], sc[rows]), f"N={N} K={K} M={M}")
+    return y
+
+
+@pytest.mark.parametrize("N,K,M", [
+    (300, 384, 3), (300, 384, 6), (300, 384, 12), (300, 384, 16),  # 3 groups: 3 waves, ragged last block
+    (47, 128, 5), (47, 128, 16),                                     # one group: one wave, one partial block
+    (4090, 2176, 9),                                                 # one tile, eight waves; 17 groups
+    (4100, 640, 7),                                                  # K <= 4096 on a wider layer: four waves
+])
+def test_ring_small_layers(N, K, M):
+    note(f"ring N={N} K={K} M={M}")
+    _check(N, K, M, seed=N * 3 + K + M)
+
+
+@pytest.mark.parametrize("N,K,M", [
+    (8190, 4224, 8), (8190, 4224, 13),  # two tiles, eight waves; 33 groups; 8190 = 255 * 32 + 30
+    (9000, 4352, 6),                    # 8192 < N < 16384: one tile, four waves
+    (16400, 4480, 9),                   # N >= 16384: two tiles, four waves; 16400 = 512 * 32 + 16
+    (16400, 4480, 4),                   # M <= 4: one tile, eight waves
+])
+def test_ring_wide_layers_sampled_rows(N, K, M):
+    note(f"ring N={N} K={K} M={M}")
+    _check(N, K, M, seed=N + K * 5 + M, sample=256)
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_ring_long_k(M):
+    """K = 270336 (2112 groups): at M = 4 the block's scales and zeros (85 KB) still fit
+    beside the rings; at M = 16 they do not, and the register-staged kernel runs."""
+    note(f"ring long K M={M}")
+    _check(64, 270336, M, seed=77 + M)
+
+
+def test_ring_determinism():
+    note("ring determinism")
+    q, z, sc, p, scd, zd = _random_packed(8190, 4224, seed=12)
+    for M in (3, 8, 16):
+        x = dev(activations_fp16(M, 4224, seed=13 + M))
+        a = host(awq.awq_gemm(x, p, scd, zd))
+        b = host(awq.awq_gemm(x, p, scd, zd))
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), M

@@ -50,7 +50,7 @@ hipError_t launch_loss_direct(const void* X, const float* E, int64_t M, int64_t 
 hipError_t launch_loss_reduce(const double* partial, int64_t count, double mn, double* loss, hipStream_t st);
 hipError_t launch_argmin(const double* loss, int n, int32_t* best, hipStream_t st);
 
-// gemv.hip (vector-ALU GEMV, M <= 2), skinny.hip (matrix-core decode kernel, M <= 16, and up to
+// gemv.hip (vector-ALU GEMV, M <= 2), skinny.hip (matrix-core decode kernels: LDS-ring kernel for M <= 16, register-staged up to
 // 64 where it beats the GEMM), gemm.hip / gemm_pipe.hip (matrix-core GEMM)
 bool gemv_dot2_supported(int64_t M, int64_t K);
 hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scales, const void* zeros, void* y,

@@ -19,14 +19,20 @@
 // is then applied in fp32.  No cross-lane reduction is needed, and the vector
 // ALU work per weight does not grow with M.
 //
-// Mapping: a block owns 16*RW weight rows and all of K; its W waves split the
-// K groups (wave w takes groups w, w+W, ...).  For one group a wave loads 16 B
-// per lane: lane l reads the (l/16)-th 16-byte quarter of the group's 64 B in
-// row l%16, so one load instruction fetches 16 rows x 64 B.  All loads of a
-// batch of P groups (and, without LDS staging, their x fragments) are issued
-// before any is used.  x is staged once per block in LDS when it fits, before
-// the first weight load.  The waves' partial tiles are summed through LDS
-// in a fixed order, so results are deterministic.
+// Two kernels share that arithmetic.  In both, a block owns 16*RW weight rows
+// and all of K, its W waves split the K groups, and the waves' partial tiles
+// are summed through LDS in a fixed order, so results are deterministic.
+//
+// The register-staged kernel (skinny_kernel): wave w takes groups w, w+W, ....
+// For one group a wave loads 16 B per lane: lane l reads the (l/16)-th 16-byte
+// quarter of the group's 64 B in row l%16, so one load instruction fetches 16
+// rows x 64 B.  All loads of a batch of P groups (and, without LDS staging,
+// their x fragments) are issued before any is used.  x is staged once per
+// block in LDS when it fits, before the first weight load.  It serves
+// 17 <= M <= 64, and 3 <= M <= 16 where the ring kernel's LDS does not fit.
+//
+// The ring kernel (ring_kernel, 3 <= M <= 16) moves weights and x fragments
+// from memory straight into per-wave LDS rings; it is described with its code.
 #include "awq_common.h"
 #include "awq_internal.h"
 
@@ -216,6 +222,272 @@ static hipError_t skinny_launch(const void* x, const void* packed, const void* s
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Ring kernel, 3 <= M <= 16.  The register-staged kernel holds a batch's
+// weight loads in registers until they land, so the bytes a CU keeps in flight
+// are capped by its register file (about 64 KB at one block of eight waves per
+// CU), and it streams the 70B-sized layers at a third of what the GEMV
+// reaches.  Here weights and x fragments go from memory straight into LDS
+// (global_load_lds_dwordx4, new in gfx950), which costs no registers while in
+// flight: each wave owns a ring of S stages in LDS and keeps S - 1 of them
+// loading while it computes on one.  A block's scales and zeros are staged in
+// LDS once, before the first stage.
+//
+// A stage is one chunk of P consecutive groups for the block's RW tiles of 16
+// rows (64 P bytes of each weight row) and for MX rows of x (256 P bytes
+// each).  One DMA instruction fills 1 KB of LDS; each lane fetches the 16-byte
+// piece (slot ^ swizzle(row)) of its row, so a row's reads stay contiguous in
+// memory while the fragment reads of 16 rows (one piece each) hit 16 distinct
+// bank groups.  Waves take chunks wave, wave + W, ....  Vector-memory
+// operations complete in issue order, so one wait per stage, on the number of
+// DMA instructions issued after the stage's own, says it has landed; the
+// compiler tracks no LDS-DMA dependences, so these waits are explicit.  x rows
+// past M hold row M - 1: MFMA output rows are independent and never stored.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_void;
+
+// s_waitcnt immediates: vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLds = 15 | (3 << 14) | (7 << 4);
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
+
+template <int P>
+__device__ inline int ring_swizzle(int r) {
+  return (r / (4 / P)) & (4 * P - 1);
+}
+
+template <int RW, int P, int S, int MX>
+__global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
+                                                   const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
+                                                   f16* __restrict__ y, int M, int N32, int K32, int W) {
+  static_assert((P == 1 || P == 2) && S >= 2 && S <= 4 && MX % 4 == 0 && MX <= 16, "ring shape");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int ROWB = 64 * P, RPI = 1024 / ROWB, NI = 16 / RPI, SLOTS = 4 * P, TILE = 16 * ROWB;
+  constexpr int XROWB = 256 * P, XRPI = 1024 / XROWB, NXI = MX / XRPI, XSLOTS = 16 * P;
+  constexpr int STAGE = RW * TILE + MX * XROWB;
+  constexpr int NIS = RW * NI + NXI;  // DMA instructions per stage
+  const int64_t N = N32, K = K32, K8 = K / 8, G = K / kGroup, P2 = (G + 1) / 2, NC = (G + P - 1) / P;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, kq = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * RW);
+  const int T = (int)((NC + W - 1) / W);  // stages per wave; chunks past the last are reloaded, scaled by 0
+  unsigned char* ring = smem + (size_t)wave * (S * STAGE);
+  // the block's scales and zeros, staged once after the rings (each padded to whole KB)
+  const int SCB = (int)(32 * RW * G), ZB = (int)(16 * RW * P2);
+  f16* sl = reinterpret_cast<f16*>(smem + (size_t)W * S * STAGE);
+  uint8_t* zl = reinterpret_cast<uint8_t*>(smem + (size_t)W * S * STAGE + ((SCB + 1023) & ~1023));
+
+  int64_t dsrc[RW][NI];  // weight DMA source of this lane, less the group: row start + quarter
+  int dgi[NI];           // and its group within the chunk
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int r = q * RPI + lane / SLOTS, piece = (lane % SLOTS) ^ ring_swizzle<P>(r);
+    dgi[q] = piece >> 2;
+#pragma unroll
+    for (int t = 0; t < RW; ++t) {
+      const int64_t n = n0 + 16 * t + r;
+      dsrc[t][q] = (n < N ? n : N - 1) * K8 + (piece & 3) * 4;  // tail rows reload the last row; never stored
+    }
+  }
+  // x DMA: LDS row r of a stage holds x row min(r, M - 1); piece slot ^ (r & 15) of it
+  int64_t xsrc[NXI];
+  int xgi[NXI];
+#pragma unroll
+  for (int q = 0; q < NXI; ++q) {
+    const int r = q * XRPI + lane / XSLOTS, piece = (lane % XSLOTS) ^ (r & 15);
+    xgi[q] = piece >> 4;
+    xsrc[q] = (int64_t)(r < M ? r : M - 1) * K + (piece & 15) * 8;
+  }
+
+  f32x4 acc[RW];
+#pragma unroll
+  for (int t = 0; t < RW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto issue = [&](int j) {
+    int64_t c = (int64_t)j * W + wave;
+    c = c < NC ? c : NC - 1;
+    unsigned char* dst = ring + (j % S) * STAGE;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      int64_t g = c * P + dgi[q];
+      g = g < G ? g : G - 1;
+#pragma unroll
+      for (int t = 0; t < RW; ++t)
+        __builtin_amdgcn_global_load_lds((global_void*)(packed + dsrc[t][q] + g * 16), (lds_void*)(dst + t * TILE + q * 1024),
+                                         16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < NXI; ++q) {
+      int64_t g = c * P + xgi[q];
+      g = g < G ? g : G - 1;
+      __builtin_amdgcn_global_load_lds((global_void*)(x + xsrc[q] + g * kGroup), (lds_void*)(dst + RW * TILE + q * 1024), 16,
+                                       0, 0);
+    }
+  };
+
+  // A full block's rows are consecutive, so its scales and zeros are two contiguous
+  // runs of whole 16-byte pieces: DMA them; a ragged last block copies them one by one.
+  if (n0 + 16 * RW <= N) {
+    const unsigned char* gs = reinterpret_cast<const unsigned char*>(scales) + n0 * G * 2;
+    const unsigned char* gz = zeros + n0 * P2;
+    for (int b = wave * kWave; b < SCB / 16; b += W * kWave) {
+      const int v = b + lane < SCB / 16 ? b + lane : SCB / 16 - 1;  // lanes past the end land in the padding
+      __builtin_amdgcn_global_load_lds((global_void*)(gs + v * 16), (lds_void*)(reinterpret_cast<unsigned char*>(sl) + b * 16),
+                                       16, 0, 0);
+    }
+    for (int b = wave * kWave; b < ZB / 16; b += W * kWave) {
+      const int v = b + lane < ZB / 16 ? b + lane : ZB / 16 - 1;
+      __builtin_amdgcn_global_load_lds((global_void*)(gz + v * 16), (lds_void*)(zl + b * 16), 16, 0, 0);
+    }
+  } else {
+    for (int i = threadIdx.x; i < 16 * RW * G; i += W * kWave) {
+      const int r = (int)(i / G);
+      const int64_t n = n0 + r;
+      sl[i] = scales[(n < N ? n : N - 1) * G + (i - (int64_t)r * G)];
+    }
+    for (int i = threadIdx.x; i < ZB; i += W * kWave) {
+      const int r = (int)(i / P2);
+      const int64_t n = n0 + r;
+      zl[i] = zeros[(n < N ? n : N - 1) * P2 + (i - (int64_t)r * P2)];
+    }
+  }
+  for (int j = 0; j < S - 1 && j < T; ++j) issue(j);
+  // the staged scales and zeros are read by every wave: all of this wave's loads land, then the barrier
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  const int xr = nl < MX ? nl : MX - 1;
+  for (int j = 0; j < T; ++j) {
+    // the slot refilled here was read by the previous stage, whose LDS reads are done
+    __builtin_amdgcn_s_waitcnt(kWaitLds);
+    __builtin_amdgcn_sched_barrier(0);
+    const int ahead = T - 1 - j;  // stages issued after this one
+    if (ahead >= S - 1) {
+      issue(j + S - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 1) * NIS));
+    } else if (S > 3 && ahead == 2) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NIS));
+    } else if (S > 2 && ahead == 1) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(NIS));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t c = (int64_t)j * W + wave;  // past NC only in the last stage of some waves
+    const unsigned char* src = ring + (j % S) * STAGE;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int64_t g = c * P + i;
+      const bool live = g < G;
+      const int gc = (int)(live ? g : G - 1);
+      f16x8 a[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        a[s] = *reinterpret_cast<const f16x8*>(src + RW * TILE + xr * XROWB + ((i * 16 + kq * 4 + s) ^ xr) * 16);
+#pragma unroll
+      for (int t = 0; t < RW; ++t) {
+        const u32x4 w =
+            *reinterpret_cast<const u32x4*>(src + t * TILE + nl * ROWB + ((i * 4 + kq) ^ ring_swizzle<P>(nl)) * 16);
+        const int r = 16 * t + nl;
+        const f16x2 zb = zero_biased((zl[r * P2 + (gc >> 1)] >> (4 * (gc & 1))) & 0xFu);
+        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f16x2 q0 = pair_biased(w[s], 0) - zb, q1 = pair_biased(w[s], 1) - zb;
+          const f16x2 q2 = pair_biased(w[s], 2) - zb, q3 = pair_biased(w[s], 3) - zb;
+          const f16x8 b = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], b, d, 0, 0, 0);
+        }
+        const float scf = live ? (float)sl[r * G + gc] : 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[t][rr] = fmaf(scf, d[rr], acc[t][rr]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // every wave's DMA has landed (the last stage waited for all); the rings become the
+  // reduction buffer: lane holds y[m = 4*kq + r][n0 + 16t + nl]
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int t = 0; t < RW; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * kq + r;
+      if (m < M) red[((wave * RW + t) * 16 + m) * 16 + nl] = acc[t][r];
+    }
+  __syncthreads();
+  for (int i = threadIdx.x; i < RW * 16 * M; i += W * kWave) {
+    const int t = i / (16 * M), rem = i - t * 16 * M, m = rem >> 4, nn = rem & 15;
+    float v = 0.f;
+    for (int w = 0; w < W; ++w) v += red[((w * RW + t) * 16 + m) * 16 + nn];
+    const int64_t n = n0 + 16 * t + nn;
+    if (n < N) y[(int64_t)m * N + n] = (f16)v;
+  }
+}
+
+template <int RW, int P, int S, int MX>
+static size_t ring_lds_bytes(int W, int64_t K) {
+  const int64_t G = K / kGroup;
+  const size_t sc = (size_t)32 * RW * G, z = (size_t)16 * RW * ((G + 1) / 2);
+  return (size_t)W * S * (RW * 1024 * P + MX * 256 * P) + ((sc + 1023) & ~(size_t)1023) + ((z + 1023) & ~(size_t)1023);
+}
+
+template <int RW, int P, int S, int MX>
+static int ring_waves(int max_waves, int64_t K) {
+  const int64_t NC = (K / kGroup + P - 1) / P;
+  return (int)(NC < max_waves ? NC : max_waves);
+}
+
+template <int RW, int P, int S, int MX>
+static hipError_t ring_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
+                              int64_t N, int64_t K, int max_waves, hipStream_t st) {
+  const int W = ring_waves<RW, P, S, MX>(max_waves, K);
+  const size_t lds = ring_lds_bytes<RW, P, S, MX>(W, K);
+  if (lds > kLdsBytes) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW))), block((unsigned)(W * kWave));
+  ring_kernel<RW, P, S, MX><<<grid, block, lds, st>>>(
+      reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
+      reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)M, (int)N, (int)K, W);
+  return hipGetLastError();
+}
+
+// Ring shape: one-group chunks in a two-stage ring (deeper rings cost blocks per
+// CU and measured slower); 16-row tiles per wave and waves per block by layer
+// shape, measured on the Llama-2 7B/70B decode shapes at M = 4, 8, 16.  The
+// choice mostly sets how evenly the blocks fill 256 CUs: one tile and eight
+// waves for M <= 4 and on layers up to 4096 wide; one tile and four waves on
+// K <= 4096 (4096 x 11008 at M = 16: 11.6 us against 14.8) and on layers up
+// to 16384 wide; two tiles and four waves on wider ones (8192 x 28672 at
+// M = 16: 44 us against 58 with eight waves); two tiles and eight waves on
+// the rest (8192 x 8192, 28672 x 8192).
+constexpr int kRingP = 1, kRingStages = 2;
+
+struct RingShape {
+  int rw, waves;
+};
+
+static RingShape ring_shape(int64_t M, int64_t N, int64_t K) {
+  if (M <= 4 || N <= 4096) return {1, 8};
+  if (K <= 4096 || (N > 8192 && N < 16384)) return {1, 4};
+  if (N >= 16384) return {2, 4};
+  return {2, 8};
+}
+
+template <int MX>
+static bool ring_fits(const RingShape& r, int64_t K) {
+  if (r.rw == 1)
+    return ring_lds_bytes<1, kRingP, kRingStages, MX>(ring_waves<1, kRingP, kRingStages, MX>(r.waves, K), K) <= kLdsBytes;
+  return ring_lds_bytes<2, kRingP, kRingStages, MX>(ring_waves<2, kRingP, kRingStages, MX>(r.waves, K), K) <= kLdsBytes;
+}
+
+template <int MX>
+static hipError_t ring_dispatch(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
+                                int64_t N, int64_t K, const RingShape& r, hipStream_t st) {
+  if (r.rw == 1) return ring_launch<1, kRingP, kRingStages, MX>(x, packed, scales, zeros, y, M, N, K, r.waves, st);
+  return ring_launch<2, kRingP, kRingStages, MX>(x, packed, scales, zeros, y, M, N, K, r.waves, st);
+}
+
 // 17 <= M <= 64: the same kernel with M in up to four 16-row m-tiles; each
 // unpacked weight operand feeds one MFMA per m-tile.  Measured against the
 // pipelined GEMM (M = 17, 32, 48, 64 on the 7B/70B shapes) it wins on layers
@@ -243,18 +515,20 @@ hipError_t launch_gemv_wide(const void* x, const void* packed, const void* scale
   return wide_launch<4, 2>(x, packed, scales, zeros, y, M, N, K, st);
 }
 
-// Tile shape, measured on the Llama-2 7B/70B decode shapes at M = 4, 8, 16:
-// one 16-row tile per wave by default; on wide layers (N >= 16384, or
-// N >= 8192 with K = 4096 and M > 8) four tiles per wave in batches of two
-// groups share each x fragment over more weight rows (8192 x 28672: 59-68 us
-// against 74-81 us; 4096 x 11008 at M = 16: 18 us against 21 us); on long K
-// (>= 16384), and for M > 8 on 8192-wide layers with K >= 8192, two tiles per
-// wave, which still leaves at least 256 blocks (8192 x 8192 at M = 16: 24 us
-// against 37 us with four tiles).
+// 3 <= M <= 16 runs on the ring kernel.  The register-staged kernel above
+// serves the layers whose scales and zeros do not fit in LDS beside the rings
+// (K beyond about 260000), with its tile shape measured on the same layers:
+// one 16-row tile per wave by default; four tiles per wave in batches of two
+// groups on wide layers (N >= 16384, or N >= 8192 with K = 4096 and M > 8);
+// two tiles per wave on long K (>= 16384) and for M > 8 on 8192-wide layers.
 hipError_t launch_gemv(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
                        int64_t N, int64_t K, hipStream_t st) {
   if (M < 1 || M > 16) return hipErrorInvalidValue;
   if (gemv_dot2_supported(M, K)) return launch_gemv_dot2(x, packed, scales, zeros, y, M, N, K, st);
+  const RingShape r = ring_shape(M, N, K);
+  if (M <= 4 && ring_fits<4>(r, K)) return ring_dispatch<4>(x, packed, scales, zeros, y, M, N, K, r, st);
+  if (M > 4 && M <= 8 && ring_fits<8>(r, K)) return ring_dispatch<8>(x, packed, scales, zeros, y, M, N, K, r, st);
+  if (M > 8 && ring_fits<16>(r, K)) return ring_dispatch<16>(x, packed, scales, zeros, y, M, N, K, r, st);
   if (K >= 16384) return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
   if (N >= 16384 || (M > 8 && N >= 8192 && K <= 4096)) return skinny_launch<4, 2>(x, packed, scales, zeros, y, M, N, K, st);
   if (M > 8 && N >= 8192) return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
