@@ -259,7 +259,51 @@ def run_sweep(args, torch, awq, dev):
         out[str(M)] = dict(us=round(us, 3), GBs=round(nbytes / us / 1e3, 1),
                            hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                            TFLOPs=round(flops / us / 1e6, 2), mfma_frac=round(flops / us / 1e6 / FP16_PEAK_TFLOPS, 4),
-                           kernel="gemv_dot2" if M <= 2 else ("skinny_mfma" if M <= 16 else "mfma_gemm"))
+                           kernel="gemv_dot2" if M <= 2 else ("ring_mfma" if M <= 16 else "mfma_gemm"))
+    return out
+
+
+LAYERS_70B = [("qkv", 8192, 10240), ("o", 8192, 8192), ("gate", 8192, 28672), ("up", 8192, 28672),
+              ("down", 28672, 8192)]
+
+
+def run_70b(args, torch, awq, dev):
+    """awq_gemm on the Llama-2 70B linears (fused q/k/v with grouped K/V heads, o, gate, up,
+    down) at M = 1, 8, 16, each layer on rotating weight copies (> 1 GiB per layer shape), and
+    the five launches of one block's decode step summed."""
+    from gen import activations_fp16, normal_fp16
+    out = {}
+    packs = {}
+    for _, K, N in LAYERS_70B:
+        if (K, N) in packs:
+            continue
+        W = torch.from_numpy(normal_fp16((N, K), 0.015, seed=7000 + K + N)).to(dev)
+        base = awq.awq_pack(W)
+        del W
+        copies = max(3, -(-int(1.2e9) // gemv_bytes(1, K, N)))
+        packs[(K, N)] = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
+    for M in (1, 8, 16):
+        per, step_us, step_bytes = {}, 0.0, 0
+        for name, K, N in LAYERS_70B:
+            cp = packs[(K, N)]
+            x = torch.from_numpy(activations_fp16(M, K, seed=7100 + M + K)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+            def run(x=x, y=y, cp=cp):
+                for c in cp:
+                    awq.awq_gemm(x, *c, out=y)
+            g = graph_of(torch, run)
+            us = time_replays(torch, [g], max(3, args.steps // len(cp)), 1) / len(cp) * 1e3
+            del g
+            nbytes = gemv_bytes(M, K, N)
+            per[name] = dict(K=K, N=N, us=round(us, 3), GBs=round(nbytes / us / 1e3, 1),
+                             hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4))
+            step_us += us
+            step_bytes += nbytes
+        out[str(M)] = dict(step_us=round(step_us, 3), GBs=round(step_bytes / step_us / 1e3, 1),
+                           hbm_frac=round(step_bytes / step_us / 1e3 / HBM_PEAK_GBS, 4),
+                           kernel="gemv_dot2" if M <= 2 else "ring_mfma", layers=per)
+    del packs
     return out
 
 
@@ -444,6 +488,9 @@ def main():
         legs["batch_sweep_4096x11008"] = run_sweep(args, torch, awq, dev)
         m256 = legs["batch_sweep_4096x11008"]["256"]
         legs["gemm_m256_4096x11008"] = dict(TFLOPs=m256["TFLOPs"], mfma_frac=m256["mfma_frac"], us=m256["us"])
+        torch.cuda.empty_cache()
+        log("70B layers: q/k/v, o, gate, up, down at M = 1, 8, 16")
+        legs["llama2_70b_layers"] = run_70b(args, torch, awq, dev)
         torch.cuda.empty_cache()
     if not args.no_search:
         log("search: awq_quantize over a 7B block, 65,536 calibration rows")
