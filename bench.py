@@ -263,6 +263,34 @@ def run_sweep(args, torch, awq, dev):
     return out
 
 
+def run_sweep3(args, torch, awq, dev):
+    """The same (K=4096, N=11008) layer with 3-bit codes at M = 1..16 (decode batch sizes)."""
+    from gen import activations_fp16, normal_fp16
+    K, N = 4096, 11008
+    W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=3001)).to(dev)
+    base = awq.awq_pack(W, bits=3)
+    del W
+    copies = 64  # 64 x 17.6 MB > 1 GiB
+    packs = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
+    out = {}
+    for M in (1, 2, 4, 8, 16):
+        x = torch.from_numpy(activations_fp16(M, K, seed=3100 + M)).to(dev)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+        def run(x=x, y=y):
+            for c in range(copies):
+                awq.awq_gemm(x, *packs[c], out=y)
+        g = graph_of(torch, run)
+        us = time_replays(torch, [g], max(3, args.steps // copies), 1) / copies * 1e3
+        del g
+        nbytes = gemv_bytes(M, K, N, bits=3)
+        out[str(M)] = dict(us=round(us, 3), GBs=round(nbytes / us / 1e3, 1),
+                           hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                           kernel="gemv3_dot2" if M <= 2 else "ring_mfma")
+    del packs
+    return out
+
+
 LAYERS_70B = [("qkv", 8192, 10240), ("o", 8192, 8192), ("gate", 8192, 28672), ("up", 8192, 28672),
               ("down", 28672, 8192)]
 
@@ -488,6 +516,9 @@ def main():
         legs["batch_sweep_4096x11008"] = run_sweep(args, torch, awq, dev)
         m256 = legs["batch_sweep_4096x11008"]["256"]
         legs["gemm_m256_4096x11008"] = dict(TFLOPs=m256["TFLOPs"], mfma_frac=m256["mfma_frac"], us=m256["us"])
+        torch.cuda.empty_cache()
+        log("sweep: (4096, 11008) with 3-bit codes at M = 1..16")
+        legs["batch_sweep_4096x11008_3bit"] = run_sweep3(args, torch, awq, dev)
         torch.cuda.empty_cache()
         log("70B layers: q/k/v, o, gate, up, down at M = 1, 8, 16")
         legs["llama2_70b_layers"] = run_70b(args, torch, awq, dev)

@@ -217,9 +217,10 @@ int awq_gemm(const void* x, const void* packed, const void* scales, const void* 
              int64_t M, int64_t N, int64_t K, int32_t group, void* stream);
 /* awq_gemm on the format written at `bits` = 4 (awq_gemm itself) or 3.  At 3
  * bits: M <= 2 runs the vector-ALU GEMV with the arithmetic stated above
- * (every product exact in fp32, zero point as zero * sum(x)); M > 2 the
- * general-shape matrix-core kernel on exact (code - zero) with the group scale
- * applied in fp32.  Requires bits == 4 or 3 and M <= 65535 * 64 at 3 bits. */
+ * (every product exact in fp32, zero point as zero * sum(x)); 3 <= M <= 16 the
+ * matrix-core decode kernel and other M > 2 the general-shape matrix-core
+ * kernel, both on exact (code - zero) with the group scale applied in fp32.
+ * Requires bits == 4 or 3 and M <= 65535 * 64 at 3 bits. */
 int awq_gemm_bits(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                   int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* stream);
 

@@ -150,3 +150,30 @@ def test_gemm3_after_search_end_to_end():
         x = (activations_fp16(M, 512, seed=903 + M).astype(np.float32) / s).astype(np.float16)
         y = host(awq.awq_gemm(dev(x), r["packed"], r["scales"], r["zeros"]))
         assert_y_close(y, oracle.gemm(x, q, z, sc), f"M={M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(300, 384, 3), (300, 384, 16), (47, 128, 5), (4090, 2176, 9), (4100, 640, 7),
+                                   (64, 270336, 4), (64, 270336, 16)])
+def test_gemm3_decode_ring(N, K, M):
+    """3 <= M <= 16 on the LDS-ring decode kernel with 48-byte rows: 1, 3 and 17 groups
+    (fewer chunks than waves), ragged last blocks, one- and four-wave layouts, and a long K
+    where the block's scales no longer fit beside the rings at M = 16 (the general
+    matrix-core kernel then runs)."""
+    note(f"gemm3 ring N={N} K={K} M={M}")
+    q, z, sc, p, scd, zd = _random_packed3(N, K, seed=N * 5 + K + M)
+    x = activations_fp16(M, K, seed=70 + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd, bits=3))
+    assert_y_close(y, oracle.gemm(x, q, z, sc), f"N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(8190, 4224, 8), (9000, 4352, 6), (16400, 4480, 9), (16400, 4480, 4)])
+def test_gemm3_decode_ring_wide_sampled_rows(N, K, M):
+    """Two tiles per wave with eight or four waves, and one tile with four, on wide layers
+    with a partial last block (sampled rows, always including the last block's)."""
+    note(f"gemm3 ring N={N} K={K} M={M}")
+    q, z, sc, p, scd, zd = _random_packed3(N, K, seed=N + 3 * K + M)
+    x = activations_fp16(M, K, seed=71 + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd, bits=3))
+    g = np.random.default_rng(N + M)
+    rows = np.union1d(g.choice(N, size=256, replace=False), np.arange(N - 40, N))
+    assert_y_close(y[:, rows], oracle.gemm(x, q[rows], z[rows], sc[rows]), f"N={N} K={K} M={M}")

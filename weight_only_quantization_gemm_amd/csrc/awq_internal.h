@@ -55,6 +55,9 @@ hipError_t launch_argmin(const double* loss, int n, int32_t* best, hipStream_t s
 bool gemv_dot2_supported(int64_t M, int64_t K);
 hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st);
+bool ring3_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_ring3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                        int64_t M, int64_t N, int64_t K, hipStream_t st);
 bool gemv_wide_preferred(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_wide(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st);

@@ -142,6 +142,7 @@ hipError_t launch_gemm(const void* x, const void* packed, const void* scales, co
 hipError_t launch_gemm3(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
                         int64_t N, int64_t K, hipStream_t st) {
   if (gemv3_supported(M, K)) return launch_gemv3(x, packed, scales, zeros, y, M, N, K, st);
+  if (ring3_supported(M, N, K)) return launch_ring3(x, packed, scales, zeros, y, M, N, K, st);
   if ((M + kBM - 1) / kBM > 65535) return hipErrorInvalidValue;  // grid.y limit
   dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
   gemm_kernel<3><<<grid, dim3(256), 0, st>>>(reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),

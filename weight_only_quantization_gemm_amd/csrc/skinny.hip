@@ -256,17 +256,24 @@ __device__ inline int ring_swizzle(int r) {
   return (r / (4 / P)) & (4 * P - 1);
 }
 
-template <int RW, int P, int S, int MX>
+template <int BITS, int RW, int P, int S, int MX>
 __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                    const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
                                                    f16* __restrict__ y, int M, int N32, int K32, int W) {
   static_assert((P == 1 || P == 2) && S >= 2 && S <= 4 && MX % 4 == 0 && MX <= 16, "ring shape");
+  static_assert(BITS == 4 || (BITS == 3 && P == 1), "4-bit, or 3-bit in one-group chunks");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int ROWB = 64 * P, RPI = 1024 / ROWB, NI = 16 / RPI, SLOTS = 4 * P, TILE = 16 * ROWB;
+  constexpr int ROWB = 64 * P, RPI = 1024 / ROWB, SLOTS = 4 * P;
+  // 4-bit: 16 rows x 64 P bytes per tile, NI instructions of 1 KB each; 3-bit: rows of
+  // 48 bytes (three 16-byte pieces) back to back over the RW tiles, in NI instructions.
+  constexpr int NI = BITS == 4 ? RW * (16 / RPI) : (48 * RW + 63) / 64;
+  constexpr int TILE = BITS == 4 ? 16 * ROWB : 16 * 48;
   constexpr int XROWB = 256 * P, XRPI = 1024 / XROWB, NXI = MX / XRPI, XSLOTS = 16 * P;
-  constexpr int STAGE = RW * TILE + MX * XROWB;
-  constexpr int NIS = RW * NI + NXI;  // DMA instructions per stage
+  constexpr int WBYTES = NI * 1024;  // the weights of a stage, padded to whole instructions
+  constexpr int STAGE = WBYTES + MX * XROWB;
+  constexpr int NIS = NI + NXI;  // DMA instructions per stage
   const int64_t N = N32, K = K32, K8 = K / 8, G = K / kGroup, P2 = (G + 1) / 2, NC = (G + P - 1) / P;
+  const int64_t RW3 = 3 * K / 32;  // 3-bit: words per row
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, kq = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * (16 * RW);
   const int T = (int)((NC + W - 1) / W);  // stages per wave; chunks past the last are reloaded, scaled by 0
@@ -276,16 +283,24 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
   f16* sl = reinterpret_cast<f16*>(smem + (size_t)W * S * STAGE);
   uint8_t* zl = reinterpret_cast<uint8_t*>(smem + (size_t)W * S * STAGE + ((SCB + 1023) & ~1023));
 
-  int64_t dsrc[RW][NI];  // weight DMA source of this lane, less the group: row start + quarter
-  int dgi[NI];           // and its group within the chunk
+  // Weight DMA source of this lane per instruction, less the group's offset (4-bit:
+  // row start + quarter, and the piece's group within the chunk in dgi; 3-bit: row
+  // start + piece, for piece q * 64 + lane of the stage, clamped to the last).
+  int64_t dsrc[NI];
+  int dgi[NI];
 #pragma unroll
   for (int q = 0; q < NI; ++q) {
-    const int r = q * RPI + lane / SLOTS, piece = (lane % SLOTS) ^ ring_swizzle<P>(r);
-    dgi[q] = piece >> 2;
-#pragma unroll
-    for (int t = 0; t < RW; ++t) {
+    if constexpr (BITS == 4) {
+      const int t = q / (16 / RPI), qq = q % (16 / RPI);
+      const int r = qq * RPI + lane / SLOTS, piece = (lane % SLOTS) ^ ring_swizzle<P>(r);
+      dgi[q] = piece >> 2;
       const int64_t n = n0 + 16 * t + r;
-      dsrc[t][q] = (n < N ? n : N - 1) * K8 + (piece & 3) * 4;  // tail rows reload the last row; never stored
+      dsrc[q] = (n < N ? n : N - 1) * K8 + (piece & 3) * 4;  // tail rows reload the last row; never stored
+    } else {
+      const int pc = q * 64 + lane < 48 * RW ? q * 64 + lane : 48 * RW - 1;
+      const int64_t n = n0 + pc / 3;
+      dgi[q] = 0;
+      dsrc[q] = (n < N ? n : N - 1) * RW3 + (pc % 3) * 4;
     }
   }
   // x DMA: LDS row r of a stage holds x row min(r, M - 1); piece slot ^ (r & 15) of it
@@ -310,17 +325,15 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
     for (int q = 0; q < NI; ++q) {
       int64_t g = c * P + dgi[q];
       g = g < G ? g : G - 1;
-#pragma unroll
-      for (int t = 0; t < RW; ++t)
-        __builtin_amdgcn_global_load_lds((global_void*)(packed + dsrc[t][q] + g * 16), (lds_void*)(dst + t * TILE + q * 1024),
-                                         16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)(packed + dsrc[q] + g * (BITS == 4 ? 16 : 12)),
+                                       (lds_void*)(dst + q * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < NXI; ++q) {
       int64_t g = c * P + xgi[q];
       g = g < G ? g : G - 1;
-      __builtin_amdgcn_global_load_lds((global_void*)(x + xsrc[q] + g * kGroup), (lds_void*)(dst + RW * TILE + q * 1024), 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)(x + xsrc[q] + g * kGroup), (lds_void*)(dst + WBYTES + q * 1024), 16, 0,
+                                       0);
     }
   };
 
@@ -382,20 +395,39 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
       f16x8 a[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        a[s] = *reinterpret_cast<const f16x8*>(src + RW * TILE + xr * XROWB + ((i * 16 + kq * 4 + s) ^ xr) * 16);
+        a[s] = *reinterpret_cast<const f16x8*>(src + WBYTES + xr * XROWB + ((i * 16 + kq * 4 + s) ^ xr) * 16);
 #pragma unroll
       for (int t = 0; t < RW; ++t) {
-        const u32x4 w =
-            *reinterpret_cast<const u32x4*>(src + t * TILE + nl * ROWB + ((i * 4 + kq) ^ ring_swizzle<P>(nl)) * 16);
         const int r = 16 * t + nl;
         const f16x2 zb = zero_biased((zl[r * P2 + (gc >> 1)] >> (4 * (gc & 1))) & 0xFu);
         f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (BITS == 4) {
+          const u32x4 w =
+              *reinterpret_cast<const u32x4*>(src + t * TILE + nl * ROWB + ((i * 4 + kq) ^ ring_swizzle<P>(nl)) * 16);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const f16x2 q0 = pair_biased(w[s], 0) - zb, q1 = pair_biased(w[s], 1) - zb;
-          const f16x2 q2 = pair_biased(w[s], 2) - zb, q3 = pair_biased(w[s], 3) - zb;
-          const f16x8 b = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], b, d, 0, 0, 0);
+          for (int s = 0; s < 4; ++s) {
+            const f16x2 q0 = pair_biased(w[s], 0) - zb, q1 = pair_biased(w[s], 1) - zb;
+            const f16x2 q2 = pair_biased(w[s], 2) - zb, q3 = pair_biased(w[s], 3) - zb;
+            const f16x8 b = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], b, d, 0, 0, 0);
+          }
+        } else {
+          // the three words of the lane's 32 channels (rows of 48 bytes: 16 rows on
+          // distinct banks); channel pair p of the chunk, as fp16 (1024 + code) pairs
+          const uint32_t* wp = reinterpret_cast<const uint32_t*>(src + r * 48 + kq * 12);
+          const uint32_t w[3] = {wp[0], wp[1], wp[2]};
+          f16x2 q[16];
+#pragma unroll
+          for (int pp = 0; pp < 15; ++pp) q[pp] = as_f16x2(((w[pp / 5] >> (3 * (pp % 5))) & 0x00070007u) | 0x64006400u) - zb;
+          q[15] = as_f16x2(((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) | ((w[2] >> 13) & 0x00040004u) |
+                           0x64006400u) -
+                  zb;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const f16x8 b = f16x8{q[4 * s].x,     q[4 * s].y,     q[4 * s + 1].x, q[4 * s + 1].y,
+                                  q[4 * s + 2].x, q[4 * s + 2].y, q[4 * s + 3].x, q[4 * s + 3].y};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], b, d, 0, 0, 0);
+          }
         }
         const float scf = live ? (float)sl[r * G + gc] : 0.0f;
 #pragma unroll
@@ -426,27 +458,28 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
   }
 }
 
-template <int RW, int P, int S, int MX>
+template <int BITS, int RW, int P, int S, int MX>
 static size_t ring_lds_bytes(int W, int64_t K) {
   const int64_t G = K / kGroup;
   const size_t sc = (size_t)32 * RW * G, z = (size_t)16 * RW * ((G + 1) / 2);
-  return (size_t)W * S * (RW * 1024 * P + MX * 256 * P) + ((sc + 1023) & ~(size_t)1023) + ((z + 1023) & ~(size_t)1023);
+  const size_t wbytes = BITS == 4 ? (size_t)RW * 1024 * P : (size_t)(48 * RW + 63) / 64 * 1024;
+  return (size_t)W * S * (wbytes + MX * 256 * P) + ((sc + 1023) & ~(size_t)1023) + ((z + 1023) & ~(size_t)1023);
 }
 
-template <int RW, int P, int S, int MX>
+template <int P>
 static int ring_waves(int max_waves, int64_t K) {
   const int64_t NC = (K / kGroup + P - 1) / P;
   return (int)(NC < max_waves ? NC : max_waves);
 }
 
-template <int RW, int P, int S, int MX>
+template <int BITS, int RW, int P, int S, int MX>
 static hipError_t ring_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
                               int64_t N, int64_t K, int max_waves, hipStream_t st) {
-  const int W = ring_waves<RW, P, S, MX>(max_waves, K);
-  const size_t lds = ring_lds_bytes<RW, P, S, MX>(W, K);
+  const int W = ring_waves<P>(max_waves, K);
+  const size_t lds = ring_lds_bytes<BITS, RW, P, S, MX>(W, K);
   if (lds > kLdsBytes) return hipErrorInvalidValue;
   dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW))), block((unsigned)(W * kWave));
-  ring_kernel<RW, P, S, MX><<<grid, block, lds, st>>>(
+  ring_kernel<BITS, RW, P, S, MX><<<grid, block, lds, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
       reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)M, (int)N, (int)K, W);
   return hipGetLastError();
@@ -474,18 +507,48 @@ static RingShape ring_shape(int64_t M, int64_t N, int64_t K) {
   return {2, 8};
 }
 
-template <int MX>
+template <int BITS, int MX>
 static bool ring_fits(const RingShape& r, int64_t K) {
-  if (r.rw == 1)
-    return ring_lds_bytes<1, kRingP, kRingStages, MX>(ring_waves<1, kRingP, kRingStages, MX>(r.waves, K), K) <= kLdsBytes;
-  return ring_lds_bytes<2, kRingP, kRingStages, MX>(ring_waves<2, kRingP, kRingStages, MX>(r.waves, K), K) <= kLdsBytes;
+  const int W = ring_waves<kRingP>(r.waves, K);
+  if (r.rw == 1) return ring_lds_bytes<BITS, 1, kRingP, kRingStages, MX>(W, K) <= kLdsBytes;
+  return ring_lds_bytes<BITS, 2, kRingP, kRingStages, MX>(W, K) <= kLdsBytes;
 }
 
-template <int MX>
+template <int BITS, int MX>
 static hipError_t ring_dispatch(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
                                 int64_t N, int64_t K, const RingShape& r, hipStream_t st) {
-  if (r.rw == 1) return ring_launch<1, kRingP, kRingStages, MX>(x, packed, scales, zeros, y, M, N, K, r.waves, st);
-  return ring_launch<2, kRingP, kRingStages, MX>(x, packed, scales, zeros, y, M, N, K, r.waves, st);
+  if (r.rw == 1) return ring_launch<BITS, 1, kRingP, kRingStages, MX>(x, packed, scales, zeros, y, M, N, K, r.waves, st);
+  return ring_launch<BITS, 2, kRingP, kRingStages, MX>(x, packed, scales, zeros, y, M, N, K, r.waves, st);
+}
+
+template <int BITS>
+static bool ring_select(int64_t M, int64_t K, const RingShape& r, int* mx) {
+  *mx = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
+  if (M < 3 || M > 16) return false;
+  return *mx == 4 ? ring_fits<BITS, 4>(r, K) : (*mx == 8 ? ring_fits<BITS, 8>(r, K) : ring_fits<BITS, 16>(r, K));
+}
+
+template <int BITS>
+static hipError_t ring_run(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
+                           int64_t N, int64_t K, const RingShape& r, int mx, hipStream_t st) {
+  if (mx == 4) return ring_dispatch<BITS, 4>(x, packed, scales, zeros, y, M, N, K, r, st);
+  if (mx == 8) return ring_dispatch<BITS, 8>(x, packed, scales, zeros, y, M, N, K, r, st);
+  return ring_dispatch<BITS, 16>(x, packed, scales, zeros, y, M, N, K, r, st);
+}
+
+// 3-bit codes, 3 <= M <= 16: the ring kernel with rows of 48 bytes, tile and
+// wave shape as at 4 bits.
+bool ring3_supported(int64_t M, int64_t N, int64_t K) {
+  int mx;
+  return ring_select<3>(M, K, ring_shape(M, N, K), &mx);
+}
+
+hipError_t launch_ring3(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
+                        int64_t N, int64_t K, hipStream_t st) {
+  const RingShape r = ring_shape(M, N, K);
+  int mx;
+  if (!ring_select<3>(M, K, r, &mx)) return hipErrorInvalidValue;
+  return ring_run<3>(x, packed, scales, zeros, y, M, N, K, r, mx, st);
 }
 
 // 17 <= M <= 64: the same kernel with M in up to four 16-row m-tiles; each
@@ -526,9 +589,8 @@ hipError_t launch_gemv(const void* x, const void* packed, const void* scales, co
   if (M < 1 || M > 16) return hipErrorInvalidValue;
   if (gemv_dot2_supported(M, K)) return launch_gemv_dot2(x, packed, scales, zeros, y, M, N, K, st);
   const RingShape r = ring_shape(M, N, K);
-  if (M <= 4 && ring_fits<4>(r, K)) return ring_dispatch<4>(x, packed, scales, zeros, y, M, N, K, r, st);
-  if (M > 4 && M <= 8 && ring_fits<8>(r, K)) return ring_dispatch<8>(x, packed, scales, zeros, y, M, N, K, r, st);
-  if (M > 8 && ring_fits<16>(r, K)) return ring_dispatch<16>(x, packed, scales, zeros, y, M, N, K, r, st);
+  int mx;
+  if (ring_select<4>(M, K, r, &mx)) return ring_run<4>(x, packed, scales, zeros, y, M, N, K, r, mx, st);
   if (K >= 16384) return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
   if (N >= 16384 || (M > 8 && N >= 8192 && K <= 4096)) return skinny_launch<4, 2>(x, packed, scales, zeros, y, M, N, K, st);
   if (M > 8 && N >= 8192) return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
