@@ -33,6 +33,7 @@ def _check(N, K, M, seed, sample=None):
 @pytest.mark.parametrize("N,K,M", [
     (300, 384, 3), (300, 384, 6), (300, 384, 12), (300, 384, 16),  # 3 groups: 3 waves, ragged last block
     (47, 128, 5), (47, 128, 16),                                     # one group: one wave, one partial block
+    (5, 256, 3), (5, 256, 16),                                       # fewer rows than one tile
     (4090, 2176, 9),                                                 # one tile, eight waves; 17 groups
     (4100, 640, 7),                                                  # K <= 4096 on a wider layer: four waves
 ])

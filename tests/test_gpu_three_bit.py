@@ -152,7 +152,7 @@ def test_gemm3_after_search_end_to_end():
         assert_y_close(y, oracle.gemm(x, q, z, sc), f"M={M}")
 
 
-@pytest.mark.parametrize("N,K,M", [(300, 384, 3), (300, 384, 16), (47, 128, 5), (4090, 2176, 9), (4100, 640, 7),
+@pytest.mark.parametrize("N,K,M", [(300, 384, 3), (300, 384, 16), (47, 128, 5), (5, 256, 12), (4090, 2176, 9), (4100, 640, 7),
                                    (64, 270336, 4), (64, 270336, 16)])
 def test_gemm3_decode_ring(N, K, M):
     """3 <= M <= 16 on the LDS-ring decode kernel with 48-byte rows: 1, 3 and 17 groups
