@@ -238,7 +238,10 @@ static hipError_t skinny_launch(const void* x, const void* packed, const void* s
 // each).  One DMA instruction fills 1 KB of LDS; each lane fetches the 16-byte
 // piece (slot ^ swizzle(row)) of its row, so a row's reads stay contiguous in
 // memory while the fragment reads of 16 rows (one piece each) hit 16 distinct
-// bank groups.  Waves take chunks wave, wave + W, ....  Vector-memory
+// bank groups.  3-bit codes (P = 1) take 48 bytes of a row per group: the
+// rows go back to back as 16-byte pieces, and a lane reads the three words of
+// its 32 channels (a 12-word row stride already spreads 16 rows over distinct
+// banks).  Waves take chunks wave, wave + W, ....  Vector-memory
 // operations complete in issue order, so one wait per stage, on the number of
 // DMA instructions issued after the stage's own, says it has landed; the
 // compiler tracks no LDS-DMA dependences, so these waits are explicit.  x rows
