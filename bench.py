@@ -456,7 +456,7 @@ def run_cpu_baseline(layers_spec, budget_s: float):
 
 
 def profile_mode(args, torch, awq, dev):
-    """Short runs for rocprofv3 counter passes: the decode GEMVs, or a plain copy."""
+    """Short runs for rocprofv3 counter passes: the decode GEMVs, a plain copy, or one GEMM / decode layer."""
     if args.profile_mode == "copy":
         n = 256 << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -465,6 +465,21 @@ def profile_mode(args, torch, awq, dev):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps(dict(profile_mode="copy", bytes_per_copy=n, launches=5)))
+        return
+    if args.profile_mode in ("gemm", "ring"):
+        # one layer, 20 launches: the M = 256 GEMM on (4096, 11008), or the M = 16 decode
+        # ring kernel on (8192, 28672)
+        from gen import activations_fp16, normal_fp16
+        K, N, M = (4096, 11008, 256) if args.profile_mode == "gemm" else (8192, 28672, 16)
+        W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=K + N)).to(dev)
+        p, sc, z = awq.awq_pack(W)
+        del W
+        x = torch.from_numpy(activations_fp16(M, K, seed=K)).to(dev)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        for _ in range(20):
+            awq.awq_gemm(x, p, sc, z, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(profile_mode=args.profile_mode, K=K, N=N, M=M, launches=20)))
         return
     r = run_decode(args, torch, awq, dev)
     print(json.dumps(dict(profile_mode="gemv", alg_bytes_per_launch=r["bytes_per_launch"], kern_ms=r["kern_ms"],
@@ -480,7 +495,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-search", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--profile-mode", choices=["gemv", "copy"], default=None)
+    ap.add_argument("--profile-mode", choices=["gemv", "copy", "gemm", "ring"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the W4A16 kernels are measured on one MI355X; "

@@ -33,6 +33,20 @@ __device__ inline f16x2 pair_biased(uint32_t word, int j) {
   return as_f16x2(((word >> (4 * j)) & 0x000F000Fu) | 0x64006400u);
 }
 
+// The fp16x2 (1024, 1024) bit pattern in a vector register.  A VOP3 operand
+// may not be a literal, so with the pattern in a register (and the mask in a
+// scalar one) each pair unpacks with one and-or instead of an and and an or.
+__device__ inline uint32_t bias_in_vgpr() {
+  uint32_t v;
+  __asm__ volatile("v_mov_b32 %0, 0x64006400" : "=v"(v));
+  return v;
+}
+
+// pair_biased with the bias pattern from bias_in_vgpr().
+__device__ inline f16x2 pair_biased(uint32_t word, int j, uint32_t bias) {
+  return as_f16x2(((word >> (4 * j)) & 0x000F000Fu) | bias);
+}
+
 // fp16x2 (1024 + zero, 1024 + zero) for subtracting the zero point exactly.
 __device__ inline f16x2 zero_biased(uint32_t zero) {
   return as_f16x2(0x64006400u | zero | (zero << 16));

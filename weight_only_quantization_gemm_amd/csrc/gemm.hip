@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const f16* __restrict__ x, co
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const uint32_t bias = bias_in_vgpr();
   for (int64_t g = 0; g < G; ++g) {
     const int64_t k0 = g * kGroup;
     uint4 xv[4];
@@ -69,14 +70,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const f16* __restrict__ x, co
 #pragma unroll
       for (int wi2 = 0; wi2 < 4; ++wi2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) wh[wi2 * 4 + j] = as_u32(pair_biased(words[wi2], j) - zb);
+        for (int j = 0; j < 4; ++j) wh[wi2 * 4 + j] = as_u32(pair_biased(words[wi2], j, bias) - zb);
     } else {
 #pragma unroll
       for (int p = 0; p < 15; ++p)
-        wh[p] = as_u32(as_f16x2(((words[p / 5] >> (3 * (p % 5))) & 0x00070007u) | 0x64006400u) - zb);
+        wh[p] = as_u32(as_f16x2(((words[p / 5] >> (3 * (p % 5))) & 0x00070007u) | bias) - zb);
       const uint32_t p15 = ((words[0] >> 15) & 0x00010001u) | ((words[1] >> 14) & 0x00020002u) |
                            ((words[2] >> 13) & 0x00040004u);
-      wh[15] = as_u32(as_f16x2(p15 | 0x64006400u) - zb);
+      wh[15] = as_u32(as_f16x2(p15 | bias) - zb);
     }
     __syncthreads();
 #pragma unroll

@@ -91,6 +91,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
   // Without LDS staging the batch's x fragments are loaded together with its
   // weights, before the first wait, when they fit in registers; otherwise per group.
   constexpr bool XPRE = !XLDS && P * MT <= 4;
+  const uint32_t bias = bias_in_vgpr();
 
   for (int64_t gb = wave; gb < G; gb += (int64_t)W * P) {
     u32x4 wv[P][RW];
@@ -142,8 +143,8 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const uint32_t word = wv[p][t][s];
-          const f16x2 q0 = pair_biased(word, 0) - zb, q1 = pair_biased(word, 1) - zb;
-          const f16x2 q2 = pair_biased(word, 2) - zb, q3 = pair_biased(word, 3) - zb;
+          const f16x2 q0 = pair_biased(word, 0, bias) - zb, q1 = pair_biased(word, 1, bias) - zb;
+          const f16x2 q2 = pair_biased(word, 2, bias) - zb, q3 = pair_biased(word, 3, bias) - zb;
           const f16x8 b = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][s], b, d[mt], 0, 0, 0);
@@ -371,6 +372,7 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
   const int xr = nl < MX ? nl : MX - 1;
+  const uint32_t bias = bias_in_vgpr();
   for (int j = 0; j < T; ++j) {
     // the slot refilled here was read by the previous stage, whose LDS reads are done
     __builtin_amdgcn_s_waitcnt(kWaitLds);
@@ -409,8 +411,8 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
               *reinterpret_cast<const u32x4*>(src + t * TILE + nl * ROWB + ((i * 4 + kq) ^ ring_swizzle<P>(nl)) * 16);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const f16x2 q0 = pair_biased(w[s], 0) - zb, q1 = pair_biased(w[s], 1) - zb;
-            const f16x2 q2 = pair_biased(w[s], 2) - zb, q3 = pair_biased(w[s], 3) - zb;
+            const f16x2 q0 = pair_biased(w[s], 0, bias) - zb, q1 = pair_biased(w[s], 1, bias) - zb;
+            const f16x2 q2 = pair_biased(w[s], 2, bias) - zb, q3 = pair_biased(w[s], 3, bias) - zb;
             const f16x8 b = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], b, d, 0, 0, 0);
           }
@@ -421,9 +423,9 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
           const uint32_t w[3] = {wp[0], wp[1], wp[2]};
           f16x2 q[16];
 #pragma unroll
-          for (int pp = 0; pp < 15; ++pp) q[pp] = as_f16x2(((w[pp / 5] >> (3 * (pp % 5))) & 0x00070007u) | 0x64006400u) - zb;
+          for (int pp = 0; pp < 15; ++pp) q[pp] = as_f16x2(((w[pp / 5] >> (3 * (pp % 5))) & 0x00070007u) | bias) - zb;
           q[15] = as_f16x2(((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) | ((w[2] >> 13) & 0x00040004u) |
-                           0x64006400u) -
+                           bias) -
                   zb;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
