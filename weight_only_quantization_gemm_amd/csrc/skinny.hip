@@ -56,7 +56,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
                                                      f16* __restrict__ y, int M, int N32, int K32, int red_offset) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int64_t N = N32, K = K32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = skinny_waves<P>(K);  // == blockDim.x / 64
   const int nl = lane & 15, kq = lane >> 4;  // row within a 16-row tile; quarter of a group
   const int64_t n0 = (int64_t)blockIdx.x * (16 * RW);
@@ -278,7 +278,9 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
   constexpr int NIS = NI + NXI;  // DMA instructions per stage
   const int64_t N = N32, K = K32, K8 = K / 8, G = K / kGroup, P2 = (G + 1) / 2, NC = (G + P - 1) / P;
   const int64_t RW3 = 3 * K / 32;  // 3-bit: words per row
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, kq = lane >> 4;
+  const int lane = threadIdx.x & 63, nl = lane & 15, kq = lane >> 4;
+  // wave-uniform, so the chunk index, its clamps and the LDS destinations stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t n0 = (int64_t)blockIdx.x * (16 * RW);
   const int T = (int)((NC + W - 1) / W);  // stages per wave; chunks past the last are reloaded, scaled by 0
   unsigned char* ring = smem + (size_t)wave * (S * STAGE);
