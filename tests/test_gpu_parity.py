@@ -213,14 +213,17 @@ def test_gemm_parity_ragged(M):
 
 
 @pytest.mark.parametrize("N,K,M", [(77, 384, 17), (77, 384, 64), (77, 384, 65), (77, 384, 130), (131, 640, 200),
-                                   (200, 16640, 70), (136, 16640, 40), (72, 33280, 70), (64, 36096, 20),
-                                   (8200, 512, 17), (8200, 512, 40), (8200, 512, 50)])
+                                   (200, 16640, 70), (136, 16640, 40), (72, 33280, 70), (72, 36096, 70),
+                                   (64, 36096, 20), (8200, 512, 17), (8200, 512, 40), (8200, 512, 50),
+                                   (28672, 512, 128)])
 def test_gemm_parity_block_tails(N, K, M):
     """Weight-row counts that leave a partial 128-row block, odd group counts (the block's
-    scales and zeros end off a 16-byte boundary), K = 16640 (130 groups, more than the
-    three-stage layout holds, so the two-stage one runs), and K = 33280 / 36096 (more groups
-    than any pipelined layout holds, so the general-shape kernel runs); N = 8200 with
-    17 <= M <= 48 takes the multi-m-tile decode kernel with four tiles per wave."""
+    scales and zeros end off a 16-byte boundary), K = 16640 (130 groups: 64-row tiles over
+    four stages), K = 33280 (260 groups: 64-row tiles over three stages, one channel set),
+    K = 36096 (282 groups, more than any pipelined layout holds, so the general-shape kernel
+    runs), 28672 rows at M = 128 (128-row tiles, which fill the chip there); N = 8200 with
+    17 <= M <= 32 takes the multi-m-tile decode kernel with four tiles per wave, larger M
+    the GEMM's 64-row tiles."""
     note(f"gemm tails N={N} K={K} M={M}")
     q, z, sc, p, scd, zd = _random_packed(N, K, seed=N + K + M)
     x = activations_fp16(M, K, seed=40 + M)

@@ -290,25 +290,37 @@ static bool pipe_fits(int64_t G) {
 #define AWQ_PIPE_WN 4
 #endif
 
-// Shapes: 128-row x tiles for M > 64 (8 waves, two per SIMD, when three
-// stages fit), 64-row tiles (two blocks per compute unit) below; fewer stages
-// where the block's scales and zeros need the LDS.
-bool gemm_pipe_supported(int64_t M, int64_t K) {
+// Shapes.  64-row x tiles in two channel sets (8 waves) over four stages for
+// M <= 64, and for larger M where 128-row tiles would number fewer than 128
+// (most compute units idle): measured on the 7B/70B layers, 4096 x 11008 at
+// M = 64 takes 26 us against 37 with one set of 4 waves, and at M = 80..128
+// 28 us against 39 with 128-row tiles (11008 x 4096: 52 against 81 us), while
+// 8192 x 28672 (224 tiles of 128 rows at M = 128) is faster with 128-row tiles
+// (98 against 123 us).  128-row tiles elsewhere (8 waves, two per SIMD, when
+// three stages fit); fewer stages where the block's scales and zeros need the
+// LDS.
+static bool pipe_rows64(int64_t M, int64_t N) {
+  if (M <= 64) return true;
+  return ((M + 127) / 128) * ((N + kPBN - 1) / kPBN) < 128;
+}
+
+bool gemm_pipe_supported(int64_t M, int64_t N, int64_t K) {
   const int64_t G = K / kGroup;
-  if (M > 64) return pipe_fits<128, 2, kLdsBytes>(G);
-  return pipe_fits<64, 2, kLdsBytes / 2>(G) || pipe_fits<64, 3, kLdsBytes>(G);
+  if (!pipe_rows64(M, N)) return pipe_fits<128, 2, kLdsBytes>(G);
+  return pipe_fits<64, 4, kLdsBytes>(G) || pipe_fits<64, 2, kLdsBytes / 2>(G) || pipe_fits<64, 3, kLdsBytes>(G);
 }
 
 hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t G = K / kGroup;
-  if (M > 64) {
+  if (!pipe_rows64(M, N)) {
     if (pipe_fits<128, 3, kLdsBytes>(G))
       return pipe_launch<128, 3, kLdsBytes, AWQ_PIPE_KS, AWQ_PIPE_WN>(x, packed, scales, zeros, y, M, N, K, st);
     if (pipe_fits<128, 2, kLdsBytes>(G))
       return pipe_launch<128, 2, kLdsBytes, 1, AWQ_PIPE_WN>(x, packed, scales, zeros, y, M, N, K, st);
     return hipErrorInvalidValue;
   }
+  if (pipe_fits<64, 4, kLdsBytes>(G)) return pipe_launch<64, 4, kLdsBytes, 2, 4>(x, packed, scales, zeros, y, M, N, K, st);
   if (pipe_fits<64, 2, kLdsBytes / 2>(G))
     return pipe_launch<64, 2, kLdsBytes / 2, 1, 2>(x, packed, scales, zeros, y, M, N, K, st);
   if (pipe_fits<64, 3, kLdsBytes>(G)) return pipe_launch<64, 3, kLdsBytes, 1, 2>(x, packed, scales, zeros, y, M, N, K, st);

@@ -558,16 +558,17 @@ hipError_t launch_ring3(const void* x, const void* packed, const void* scales, c
   return ring_run<3>(x, packed, scales, zeros, y, M, N, K, r, mx, st);
 }
 
-// 17 <= M <= 64: the same kernel with M in up to four 16-row m-tiles; each
-// unpacked weight operand feeds one MFMA per m-tile.  Measured against the
-// pipelined GEMM (M = 17, 32, 48, 64 on the 7B/70B shapes) it wins on layers
-// up to 8192 wide (two tiles per wave: 4096 x 4096 at 15-27 us against 32 us,
-// 11008 x 4096 at 34-60 us against 72 us) and, with four tiles per wave in
-// batches of two groups, on wider K = 4096 layers up to M = 48 (4096 x 11008
-// at 22-30 us against 33 us); elsewhere the GEMM is faster.
+// 17 <= M <= 64: the register-staged kernel with M in up to four 16-row
+// m-tiles; each unpacked weight operand feeds one MFMA per m-tile.  Measured
+// against the pipelined GEMM (M = 24, 32, 48, 64 on the 7B/70B shapes) it wins
+// on layers up to 8192 wide (4096 x 4096 at 14-25 us against 24 us, 8192 x
+// 8192 at 27-46 us against 53 us, 28672 x 8192 at 81-139 us against 239 us)
+// and, with four tiles per wave in batches of two groups, on wider K = 4096
+// layers up to M = 32 (4096 x 11008 at 22-24 us against 25 us; at M = 48 the
+// GEMM takes 25.5 us against 29); elsewhere the GEMM is faster.
 bool gemv_wide_preferred(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 || M > 64) return false;
-  return N <= 8192 || (M <= 48 && K <= 4096);
+  return N <= 8192 || (M <= 32 && K <= 4096);
 }
 
 template <int RW, int P>
