@@ -291,29 +291,37 @@ static bool pipe_fits(int64_t G) {
 #endif
 
 // Shapes.  64-row x tiles in two channel sets (8 waves) over four stages for
-// M <= 64, and for larger M where 128-row tiles would number fewer than 128
-// (most compute units idle): measured on the 7B/70B layers, 4096 x 11008 at
-// M = 64 takes 26 us against 37 with one set of 4 waves, and at M = 80..128
-// 28 us against 39 with 128-row tiles (11008 x 4096: 52 against 81 us), while
-// 8192 x 28672 (224 tiles of 128 rows at M = 128) is faster with 128-row tiles
-// (98 against 123 us).  128-row tiles elsewhere (8 waves, two per SIMD, when
+// M <= 64, and for larger M when their rounds over the 256 compute units cost
+// less than those of 128-row tiles, a 64-row tile taking ~2/3 of a 128-row
+// one.  Measured on the 7B/70B layers: 4096 x 11008 at M = 64 takes 26 us
+// against 37 with one set of 4 waves, and at M = 96..128 28 us against 39 with
+// 128-row tiles (86 of them: one round either way); 8192 x 8192 at M = 256
+// 69 against 79 us (256 tiles of 64 rows against 128 of 128: one round each);
+// 8192 x 10240 at M = 256 85 against 111 us the other way (320 tiles of 64
+// rows: two rounds), and at M = 512 159 against 174 us (three rounds of 64-row
+// tiles against two).  128-row tiles elsewhere (8 waves, two per SIMD, when
 // three stages fit); fewer stages where the block's scales and zeros need the
 // LDS.
-static bool pipe_rows64(int64_t M, int64_t N) {
+constexpr int64_t kCUs = 256;
+
+static bool pipe_rows64(int64_t M, int64_t N, int64_t G) {
   if (M <= 64) return true;
-  return ((M + 127) / 128) * ((N + kPBN - 1) / kPBN) < 128;
+  if (!pipe_fits<64, 4, kLdsBytes>(G)) return false;
+  const int64_t nt = (N + kPBN - 1) / kPBN;
+  const int64_t r64 = ((M + 63) / 64 * nt + kCUs - 1) / kCUs, r128 = ((M + 127) / 128 * nt + kCUs - 1) / kCUs;
+  return 2 * r64 < 3 * r128;
 }
 
 bool gemm_pipe_supported(int64_t M, int64_t N, int64_t K) {
   const int64_t G = K / kGroup;
-  if (!pipe_rows64(M, N)) return pipe_fits<128, 2, kLdsBytes>(G);
+  if (!pipe_rows64(M, N, G)) return pipe_fits<128, 2, kLdsBytes>(G);
   return pipe_fits<64, 4, kLdsBytes>(G) || pipe_fits<64, 2, kLdsBytes / 2>(G) || pipe_fits<64, 3, kLdsBytes>(G);
 }
 
 hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t G = K / kGroup;
-  if (!pipe_rows64(M, N)) {
+  if (!pipe_rows64(M, N, G)) {
     if (pipe_fits<128, 3, kLdsBytes>(G))
       return pipe_launch<128, 3, kLdsBytes, AWQ_PIPE_KS, AWQ_PIPE_WN>(x, packed, scales, zeros, y, M, N, K, st);
     if (pipe_fits<128, 2, kLdsBytes>(G))
