@@ -199,13 +199,14 @@ int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_
  *   packed, scales, zeros       device, format above
  *   y       device fp16 [M][N]  out: y[m][n] = sum_k x[m][k] * w_hat[n][k]
  *
- * Accumulation is fp32 and y is rounded to fp16 once.  M <= 2: vector-ALU
- * GEMV; every product x * code is exact in fp32 and the zero point enters
- * once per 32 codes as zero * sum(x) (so y is 0 only up to fp32 rounding when
- * every code equals its zero).  3 <= M <= 16, and 17 <= M <= 64 on the layer
- * shapes the multi-row decode kernel serves: matrix-core kernels on
- * (code - zero), exact in fp16, with fp32 sums per 128-channel group and the
- * group scale applied in fp32, so no dequantized weight is rounded.  Other
+ * Accumulation is fp32 and y is rounded to fp16 once.  M = 1, and M = 2 with
+ * K < 16384: vector-ALU GEMV; every product x * code is exact in fp32 and the
+ * zero point enters once per 32 codes as zero * sum(x) (so y is 0 only up to
+ * fp32 rounding when every code equals its zero).  Other M <= 16, and
+ * 17 <= M <= 64 on the layer shapes the multi-row decode kernel serves:
+ * matrix-core kernels on (code - zero), exact in fp16, with fp32 sums per
+ * 128-channel group and the group scale applied in fp32, so no dequantized
+ * weight is rounded.  Other
  * M >= 17: the pipelined matrix-core GEMM multiplies the dequantized weight
  * (code - zero) * scale rounded once to fp16 (relative error <= 2^-11 per
  * weight; a weight with |code - zero| * scale above 65504 overflows to inf),
@@ -216,11 +217,12 @@ int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_
 int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
              int64_t M, int64_t N, int64_t K, int32_t group, void* stream);
 /* awq_gemm on the format written at `bits` = 4 (awq_gemm itself) or 3.  At 3
- * bits: M <= 2 runs the vector-ALU GEMV with the arithmetic stated above
- * (every product exact in fp32, zero point as zero * sum(x)); 3 <= M <= 16 the
- * matrix-core decode kernel and other M > 2 the general-shape matrix-core
- * kernel, both on exact (code - zero) with the group scale applied in fp32.
- * Requires bits == 4 or 3 and M <= 65535 * 64 at 3 bits. */
+ * bits: M = 1, and M = 2 with K < 16384, run the vector-ALU GEMV with the
+ * arithmetic stated above (every product exact in fp32, zero point as
+ * zero * sum(x)); other M <= 16 the matrix-core decode kernel and M > 16 the
+ * general-shape matrix-core kernel, both on exact (code - zero) with the group
+ * scale applied in fp32.  Requires bits == 4 or 3 and M <= 65535 * 64 at 3
+ * bits. */
 int awq_gemm_bits(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                   int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* stream);
 

@@ -34,6 +34,7 @@ def _check(N, K, M, seed, sample=None):
     (300, 384, 3), (300, 384, 6), (300, 384, 12), (300, 384, 16),  # 3 groups: 3 waves, ragged last block
     (47, 128, 5), (47, 128, 16),                                     # one group: one wave, one partial block
     (5, 256, 3), (5, 256, 16),                                       # fewer rows than one tile
+    (300, 16640, 2), (64, 36096, 2),                                 # M = 2 on long rows
     (4090, 2176, 9),                                                 # one tile, eight waves; 17 groups
     (4100, 640, 7),                                                  # K <= 4096 on a wider layer: four waves
 ])

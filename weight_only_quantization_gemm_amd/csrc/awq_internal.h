@@ -68,7 +68,8 @@ hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scale
                             int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st);
-// 3-bit format: GEMV for M <= 2 (gemv.hip), general-shape matrix-core kernel otherwise (gemm.hip)
+// 3-bit format: GEMV for M = 1 and short-row M = 2 (gemv.hip), the ring kernel up to M = 16 (skinny.hip),
+// the general-shape matrix-core kernel otherwise (gemm.hip)
 bool gemv3_supported(int64_t M, int64_t K);
 hipError_t launch_gemv3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                         int64_t M, int64_t N, int64_t K, hipStream_t st);

@@ -200,10 +200,15 @@ static hipError_t gemv_launch(const void* x, const void* packed, const void* sca
   return hipGetLastError();
 }
 
-// M <= 2 only: every further activation row costs 4 more dot2 per packed
-// word and the kernel turns VALU-bound (measured at M = 3..8 on the 7B/70B
-// shapes: 1.1-2.4x slower than the matrix-core kernel).
-bool gemv_dot2_supported(int64_t M, int64_t K) { return M >= 1 && M <= 2 && K / 32 <= (int64_t)kMaxWaves * kWave; }
+// M = 1, and M = 2 on rows shorter than 16384 channels: every further
+// activation row costs 4 more dot2 per packed word and the kernel turns
+// VALU-bound (measured at M = 3..8 on the 7B/70B shapes: 1.1-2.4x slower than
+// the matrix-core kernel; at M = 2 the matrix-core ring kernel is faster on
+// long rows, 28672 x 8192 at 29 us against 36, and slower on the others, 8192
+// x 28672 at 31 us against 27).
+bool gemv_dot2_supported(int64_t M, int64_t K) {
+  return (M == 1 || (M == 2 && K < 16384)) && K / 32 <= (int64_t)kMaxWaves * kWave;
+}
 
 // Rows per block, measured on the Llama-2 7B/70B decode shapes: 8 when both K
 // and N are >= 8192 (x, reloaded per block, then costs half as much L2

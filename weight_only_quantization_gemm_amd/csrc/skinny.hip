@@ -29,9 +29,10 @@
 // rows x 64 B.  All loads of a batch of P groups (and, without LDS staging,
 // their x fragments) are issued before any is used.  x is staged once per
 // block in LDS when it fits, before the first weight load.  It serves
-// 17 <= M <= 64, and 3 <= M <= 16 where the ring kernel's LDS does not fit.
+// 17 <= M <= 64, and 2 <= M <= 16 where the ring kernel's LDS does not fit.
 //
-// The ring kernel (ring_kernel, 3 <= M <= 16) moves weights and x fragments
+// The ring kernel (ring_kernel, 3 <= M <= 16, and M = 2 on rows of 16384
+// channels or more) moves weights and x fragments
 // from memory straight into per-wave LDS rings; it is described with its code.
 #include "awq_common.h"
 #include "awq_internal.h"
@@ -224,7 +225,7 @@ static hipError_t skinny_launch(const void* x, const void* packed, const void* s
 }
 
 // ---------------------------------------------------------------------------
-// Ring kernel, 3 <= M <= 16.  The register-staged kernel holds a batch's
+// Ring kernel, 2 <= M <= 16.  The register-staged kernel holds a batch's
 // weight loads in registers until they land, so the bytes a CU keeps in flight
 // are capped by its register file (about 64 KB at one block of eight waves per
 // CU), and it streams the 70B-sized layers at a third of what the GEMV
@@ -531,7 +532,7 @@ static hipError_t ring_dispatch(const void* x, const void* packed, const void* s
 template <int BITS>
 static bool ring_select(int64_t M, int64_t K, const RingShape& r, int* mx) {
   *mx = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
-  if (M < 3 || M > 16) return false;
+  if (M < 2 || M > 16) return false;
   return *mx == 4 ? ring_fits<BITS, 4>(r, K) : (*mx == 8 ? ring_fits<BITS, 8>(r, K) : ring_fits<BITS, 16>(r, K));
 }
 
@@ -543,7 +544,7 @@ static hipError_t ring_run(const void* x, const void* packed, const void* scales
   return ring_dispatch<BITS, 16>(x, packed, scales, zeros, y, M, N, K, r, st);
 }
 
-// 3-bit codes, 3 <= M <= 16: the ring kernel with rows of 48 bytes, tile and
+// 3-bit codes, 2 <= M <= 16: the ring kernel with rows of 48 bytes, tile and
 // wave shape as at 4 bits.
 bool ring3_supported(int64_t M, int64_t N, int64_t K) {
   int mx;
@@ -586,7 +587,7 @@ hipError_t launch_gemv_wide(const void* x, const void* packed, const void* scale
   return wide_launch<4, 2>(x, packed, scales, zeros, y, M, N, K, st);
 }
 
-// 3 <= M <= 16 runs on the ring kernel.  The register-staged kernel above
+// M <= 16 beyond the GEMV's range runs on the ring kernel.  The register-staged kernel above
 // serves the layers whose scales and zeros do not fit in LDS beside the rings
 // (K beyond about 260000), with its tile shape measured on the same layers:
 // one 16-row tile per wave by default; four tiles per wave in batches of two
