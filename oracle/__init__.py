@@ -15,6 +15,8 @@ Parity status per function (what pins it is in the tests named here):
   search             pinned: alpha = 0 is round-to-nearest, L(alpha*) <= L(0),
                      forced tie, known-answer construction
   gemm               pinned: brute-force loops, one-hot inputs, codes = zeros
+  scaled_input       pinned: s = 1 identity, powers of two exact, nearest fp16 to the exact
+                     quotient (brute force), product = unscaled layer within the rounding bound
   top_channels / keep_fp16_error / keep_fp16_ablation
                      pinned: hand-built rankings with ties, keeping every channel gives 0,
                      keeping none is the alpha = 0 search loss, brute-force loops with the
@@ -28,6 +30,7 @@ from .awq_oracle import (  # noqa: F401
     scale_weights,
     quantize_groups,
     dequantize,
+    scaled_input,
     effective_weight,
     weight_error,
     output_mse,

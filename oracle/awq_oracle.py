@@ -34,6 +34,7 @@ notes of the repository):
       groups' ranges, so every selection rule shares the same steps and codes.  The weight
       magnitude of an input channel is the mean of |w| over the output rows.
   R7  top channels: largest value first, equal values ordered by the lower index.
+  R11 the scaled input x / s is one float32 division per value, rounded once to fp16.
 """
 from __future__ import annotations
 
@@ -241,6 +242,15 @@ def keep_fp16_ablation(W: np.ndarray, X: np.ndarray, n_keep: int, random_keep, g
         E = keep_fp16_error(W, keep, group, bits)
         losses[i] = output_mse_gram(G, E, M) if use_gram else output_mse(X, E)
     return dict(losses=losses, keep_activation=sets[1], keep_weight=sets[2], a=a, b=b)
+
+
+# --------------------------------------------------------------------------- NEXT-2
+def scaled_input(x: np.ndarray, s) -> np.ndarray:
+    """The fp16 input the W4A16 product takes: each channel of x divided by its s
+    ([summary] P3: a channel scaled up by s in the weight has its input divided by s),
+    as one float32 division rounded once to fp16 (reading R11)."""
+    x32 = np.asarray(x, dtype=np.float16).astype(np.float32)
+    return (x32 / np.asarray(s, dtype=np.float32)[None, :]).astype(np.float16)
 
 
 # --------------------------------------------------------------------------- A8/A9

@@ -27,6 +27,10 @@ MUTATIONS = {
     "fixed_four_bit_range": ("qmax = np.float32(2 ** bits - 1)", "qmax = np.float32(15)"),
     "kept_columns_not_restored": ("    E[:, np.asarray(keep, dtype=np.int64)] = 0.0\n", "\n"),
     "smallest_channels_kept": ("key=lambda k: (-v[k], k)", "key=lambda k: (v[k], k)"),
+    "scaled_input_multiplies": ("return (x32 / np.asarray(s, dtype=np.float32)[None, :])",
+                                "return (x32 * np.asarray(s, dtype=np.float32)[None, :])"),
+    "scaled_input_in_fp16": ("return (x32 / np.asarray(s, dtype=np.float32)[None, :]).astype(np.float16)",
+                             "return (x32.astype(np.float16) / np.asarray(s, dtype=np.float16)[None, :])"),
     "gemm_wrong_group": ("zz = np.repeat(np.asarray(z, dtype=np.float64), group, axis=1)",
                          "zz = np.tile(np.asarray(z, dtype=np.float64), (1, group))"),
 }

@@ -258,6 +258,40 @@ def test_scaling_invariance_fp64():
         1e-12 * np.max(np.abs(xl @ Wl.astype(np.float64).T))
 
 
+def test_scaled_input_special_cases():
+    # s = 1 leaves x unchanged; s = 2^e is an exact exponent shift (no value here underflows)
+    x = activations_fp16(6, 256, seed=31)
+    assert np.array_equal(O.scaled_input(x, np.ones(256, np.float32)).view(np.uint16), x.view(np.uint16))
+    e = np.random.default_rng(32).integers(-6, 7, 256)
+    s = np.ldexp(np.ones(256, np.float32), e).astype(np.float32)
+    assert np.array_equal(O.scaled_input(x, s), np.ldexp(x.astype(np.float64), -e[None, :]).astype(np.float16))
+    # one rounding: every value is the fp16 nearest to the exact quotient, or ties to it within half an fp16 ulp
+    s = np.random.default_rng(33).uniform(0.2, 9.0, 256).astype(np.float32)
+    xs = O.scaled_input(x, s).astype(np.float64)
+    exact = x.astype(np.float64) / s.astype(np.float64)[None, :]
+    ulp = np.spacing(np.abs(exact).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(xs - exact) <= 0.5 * ulp * (1 + 2.0 ** -20))
+    for i, j in [(0, 0), (3, 17), (5, 255)]:  # brute force: the nearer of the two fp16 neighbours
+        q = Fraction(float(x[i, j])) / Fraction(float(s[j]))
+        lo = np.float16(float(q))
+        cands = {float(lo), float(np.nextafter(lo, np.float16(np.inf))), float(np.nextafter(lo, np.float16(-np.inf)))}
+        best = min(abs(Fraction(c) - q) for c in cands)
+        assert abs(Fraction(float(O.scaled_input(x, s)[i, j])) - q) == best
+
+
+def test_scaled_input_product_matches_unscaled_layer():
+    # (x / s) w_hat^T = x (w_hat / s)^T up to the fp16 rounding of x / s, whose effect is
+    # bounded by sum_k |x_k / s_k| 2^-11 |w_hat_nk|.
+    W = normal_fp16((48, 512), 0.02, seed=34)
+    X = activations_fp16(64, 512, seed=35)
+    q, z, sc16, s = O.quantize_at(W, O.channel_mean_abs(X), 0.5)
+    x = activations_fp16(4, 512, seed=36)
+    y = O.gemm(O.scaled_input(x, s), q, z, sc16)
+    ref = x.astype(np.float64) @ O.effective_weight(q, z, sc16, s).T
+    bound = (np.abs(x.astype(np.float64) / s.astype(np.float64)[None, :]) * 2.0 ** -11) @ np.abs(O.dequantize(q, z, sc16)).T
+    assert np.all(np.abs(y - ref) <= bound * (1 + 1e-9)) and np.max(np.abs(y - ref)) > 0
+
+
 # ----------------------------------------------------------------- loss
 def test_loss_brute_force_loops():
     g = np.random.default_rng(30)
