@@ -233,6 +233,32 @@ def run_decode_3bit(args, torch, awq, dev):
                 launches=len(LAYERS_7B), bits=3)
 
 
+def run_decode_scaled(args, torch, awq, dev):
+    """The 7-launch decode step of run_decode with x not yet divided by s: awq_gemm_scaled
+    divides it (as x * inv_s, inv_s = 1/s from awq_inverse_scale) inside the GEMV's x load.
+    Bytes per step add inv_s (4 K per layer).  s is a^0.5 of a lognormal channel profile."""
+    from gen import activations_fp16
+    step_bytes = sum(gemv_bytes(1, K, N) + 4 * K for _, K, N in LAYERS_7B)
+    copies = max(2, int(np.ceil((1 << 30) / step_bytes)) + 1)
+    layers = [Layer(n, K, N, torch, awq, copies, dev) for n, K, N in LAYERS_7B]
+    for L in layers:
+        g = np.random.default_rng(2200 + L.K)
+        sv = np.sqrt(np.exp(g.normal(0.0, 0.8, L.K))).astype(np.float32)
+        L.inv = awq.awq_inverse_scale(torch.from_numpy(sv).to(dev))
+    torch.cuda.synchronize()
+
+    def step(c):
+        for L in layers:
+            p, s, z = L.copies[c]
+            awq.awq_gemm_scaled(L.x, L.inv, p, s, z, out=L.y)
+
+    ms = time_steps(torch, step, copies, args.steps, args.warmup)
+    del layers
+    return dict(us_per_step=round(ms * 1e3, 3), GBs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                hbm_frac=round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_per_step=step_bytes,
+                launches=len(LAYERS_7B))
+
+
 def run_sweep(args, torch, awq, dev):
     """awq_gemm on the (K=4096, N=11008) layer at M = 1..1024, rotating weight copies."""
     from gen import activations_fp16, normal_fp16
@@ -522,6 +548,9 @@ def main():
     legs = {}
     log("decode, q/k/v and gate/up fused by concatenated rows (4 launches)")
     legs["decode_fused_qkv_gateup"] = run_decode_fused(args, torch, awq, dev)
+    torch.cuda.empty_cache()
+    log("decode, x divided by s inside the GEMV (7 launches)")
+    legs["decode_llama2_7b_scaled_input"] = run_decode_scaled(args, torch, awq, dev)
     torch.cuda.empty_cache()
     log("decode, 3-bit weights (7 launches)")
     legs["decode_llama2_7b_3bit"] = run_decode_3bit(args, torch, awq, dev)

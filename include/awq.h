@@ -227,6 +227,50 @@ int awq_gemm_bits(const void* x, const void* packed, const void* scales, const v
                   int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* stream);
 
 /*
+ * The input side of the per-channel scaling ([summary] paragraph 3: a weight
+ * channel scaled up by s has its input divided by s, so the product keeps its
+ * value).  awq_gemm takes x already divided; these calls do the division on
+ * the device, fused into the decode GEMV where that kernel serves M.
+ *
+ * awq_inverse_scale -- inv_s[k] = 1 / s[k], IEEE fp32 division (correctly
+ * rounded), once per layer.
+ *   s      device fp32 [K]   the s written by awq_quantize
+ *   inv_s  device fp32 [K]   out
+ * Requires 1 <= K <= 2^20.
+ */
+int awq_inverse_scale(const float* s, int64_t K, float* inv_s, void* stream);
+
+/*
+ * awq_scale_input -- xs[m][k] = fp16(fp32(x[m][k]) * inv_s[k]): one fp32
+ * product, rounded once to fp16 (round to nearest even).  It equals the
+ * correctly rounded x / s except where x * fl(1/s) and x / s (at most 1.5 fp32
+ * ulp apart) round to neighbouring fp16 values.
+ *   x      device fp16 [M][K]
+ *   inv_s  device fp32 [K]   from awq_inverse_scale
+ *   xs     device fp16 [M][K]   out (may not overlap x)
+ * Requires 1 <= M <= 2^22, K % 8 == 0, 8 <= K <= 2^20.
+ */
+int awq_scale_input(const void* x, const float* inv_s, int64_t M, int64_t K, void* xs, void* stream);
+
+/*
+ * awq_gemm_scaled -- y = awq_scale_input(x, inv_s) times w_hat^T: the product
+ * of awq_gemm_bits on the scaled input, bit for bit.  At 4 bits with M = 1, and
+ * M = 2 with K < 16384 (the vector-ALU GEMV), the scaling happens in the
+ * GEMV's own x load: one launch, no intermediate, and
+ * awq_gemm_scaled_workspace_bytes is 0 (workspace may be NULL).  Otherwise
+ * the scaled input goes through `workspace` (device, M * K * 2 bytes rounded up
+ * to 256) and awq_gemm_bits runs on it.
+ *   x      device fp16 [M][K]   activations, not divided by s
+ *   inv_s  device fp32 [K]      from awq_inverse_scale
+ *   other arguments as awq_gemm_bits
+ * Requires what awq_gemm_bits requires.
+ */
+size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t K, int32_t bits);
+int awq_gemm_scaled(const void* x, const float* inv_s, const void* packed, const void* scales, const void* zeros,
+                    void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * awq_unpack -- logical view of the packed format, for checking it.
  *   codes     device uint8 [N][K]     out: code of every weight
  *   zeros_u8  device uint8 [N][K/g]   out: zero point of every group

@@ -109,6 +109,30 @@ def test_gemm_argument_errors_before_launch():
     assert f(FAKE_MISALIGNED, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, None) == MISALIGNED
 
 
+def test_input_scaling_queries_and_errors_before_launch():
+    lib = _lib_()
+    ws = lib.awq_gemm_scaled_workspace_bytes
+    assert ws(1, 4096, 4) == 0 and ws(2, 4096, 4) == 0          # fused into the GEMV's x load
+    assert ws(2, 16384, 4) == 2 * 16384 * 2                      # M = 2 on long rows: another kernel
+    assert ws(3, 4096, 4) == 3 * 4096 * 2 and ws(1, 4096, 3) == 4096 * 2
+    assert ws(5, 136, 4) == (5 * 136 * 2 + 255) // 256 * 256
+    assert ws(0, 4096, 4) == 0 and ws(1, 4096, 5) == 0
+    assert lib.awq_inverse_scale(None, 128, FAKE, None) == INVALID
+    assert lib.awq_inverse_scale(FAKE, 0, FAKE, None) == INVALID
+    assert lib.awq_inverse_scale(FAKE_MISALIGNED, 128, FAKE, None) == MISALIGNED
+    assert lib.awq_scale_input(FAKE, FAKE, 1, 12, FAKE, None) == INVALID       # K % 8
+    assert lib.awq_scale_input(FAKE, FAKE, 0, 128, FAKE, None) == INVALID
+    assert lib.awq_scale_input(FAKE, FAKE_MISALIGNED, 1, 128, FAKE, None) == MISALIGNED
+    f = lib.awq_gemm_scaled
+    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 4, None, 0, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 128, 4, None, 0, None) == INVALID   # K % group
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 5, None, 0, None) == INVALID   # bits
+    assert f(FAKE, FAKE_MISALIGNED, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 4, None, 0, None) == MISALIGNED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, None, 0, None) == WS_SMALL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE, 767, None) == WS_SMALL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE_MISALIGNED, 768, None) == MISALIGNED
+
+
 def test_pack_and_unpack_argument_errors_before_launch():
     lib = _lib_()
     assert lib.awq_pack(None, None, 4, 128, 128, FAKE, FAKE, FAKE, None) == INVALID

@@ -195,6 +195,72 @@ def awq_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros:
     return out
 
 
+def awq_inverse_scale(s: torch.Tensor) -> torch.Tensor:
+    """inv_s = 1 / s (fp32 [K], IEEE division on the device), once per layer."""
+    _need(s, "s", torch.float32, 1)
+    inv = torch.empty_like(s)
+    with torch.cuda.device(s.device):
+        check(load().awq_inverse_scale(s.data_ptr(), s.shape[0], inv.data_ptr(), _stream(s.device)))
+    return inv
+
+
+def awq_scale_input(x: torch.Tensor, inv_s: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """xs = fp16(fp32(x) * inv_s) per input channel; x fp16 [M][K]."""
+    _need(x, "x", torch.float16, 2)
+    _need(inv_s, "inv_s", torch.float32, 1)
+    M, K = x.shape
+    if inv_s.shape[0] != K:
+        raise ValueError("inv_s must have K entries")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (M, K):
+            raise ValueError("out must be fp16 [M][K]")
+    with torch.cuda.device(x.device):
+        check(load().awq_scale_input(x.data_ptr(), inv_s.data_ptr(), M, K, out.data_ptr(), _stream(x.device)))
+    return out
+
+
+def awq_gemm_scaled_workspace_bytes(M: int, K: int, bits: int = 4) -> int:
+    return int(load().awq_gemm_scaled_workspace_bytes(M, K, bits))
+
+
+def awq_gemm_scaled(x: torch.Tensor, inv_s: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                    zeros: torch.Tensor, out: Optional[torch.Tensor] = None, group: int = GROUP,
+                    bits: Optional[int] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = awq_scale_input(x, inv_s) @ w_hat^T; x fp16 [M][K] not divided by s.  At 4 bits
+    and M <= 2 the division happens inside the GEMV's x load (no workspace); otherwise a
+    workspace of awq_gemm_scaled_workspace_bytes bytes is taken from `workspace` or allocated."""
+    _need(x, "x", torch.float16, 2)
+    _need(inv_s, "inv_s", torch.float32, 1)
+    _need(packed, "packed", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    _need(zeros, "zeros", torch.uint8, 2)
+    M, K = x.shape
+    N = packed.shape[0]
+    G = K // group
+    if bits is None:
+        bits = bits_of(packed, K)
+    if inv_s.shape[0] != K or packed.shape[1] != packed_words(K, bits) or tuple(scales.shape) != (N, G) or \
+            tuple(zeros.shape) != (N, (G + 1) // 2):
+        raise ValueError("inv_s/packed/scales/zeros do not match x's K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be fp16 [M][N]")
+    need = awq_gemm_scaled_workspace_bytes(M, K, bits)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        check(load().awq_gemm_scaled(x.data_ptr(), inv_s.data_ptr(), packed.data_ptr(), scales.data_ptr(),
+                                     zeros.data_ptr(), out.data_ptr(), M, N, K, group, bits, _ptr(workspace),
+                                     need if need else 0, _stream(x.device)))
+    return out
+
+
 ABLATION_ORDER = ("none", "activation", "weight", "random")
 
 

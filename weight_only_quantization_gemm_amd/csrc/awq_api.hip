@@ -341,6 +341,63 @@ int awq_gemm_bits(const void* x, const void* packed, const void* scales, const v
   AWQ_GUARD_END
 }
 
+int awq_inverse_scale(const float* s, int64_t K, float* inv_s, void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(s && inv_s, AWQ_ERROR_INVALID_VALUE, "s and inv_s must not be NULL");
+  AWQ_REQUIRE(K >= 1 && K <= (int64_t(1) << 20), AWQ_ERROR_INVALID_VALUE, "K=%lld outside [1, 2^20]", (long long)K);
+  AWQ_REQUIRE(aligned16(s) && aligned16(inv_s), AWQ_ERROR_MISALIGNED, "s and inv_s must be 16-byte aligned");
+  return device_status(awq::launch_inverse_scale(s, K, inv_s, as_stream(stream)), "awq_inverse_scale");
+  AWQ_GUARD_END
+}
+
+int awq_scale_input(const void* x, const float* inv_s, int64_t M, int64_t K, void* xs, void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(x && inv_s && xs, AWQ_ERROR_INVALID_VALUE, "x, inv_s and xs must not be NULL");
+  AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
+  AWQ_REQUIRE(K >= 8 && K % 8 == 0 && K <= (int64_t(1) << 20), AWQ_ERROR_INVALID_VALUE,
+              "K=%lld must be a positive multiple of 8, at most 2^20", (long long)K);
+  AWQ_REQUIRE(aligned16(x) && aligned16(inv_s) && aligned16(xs), AWQ_ERROR_MISALIGNED,
+              "x, inv_s and xs must be 16-byte aligned");
+  return device_status(awq::launch_scale_input(x, inv_s, M, K, xs, as_stream(stream)), "awq_scale_input");
+  AWQ_GUARD_END
+}
+
+size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t K, int32_t bits) {
+  if (M < 1 || K < 1 || (bits != 4 && bits != 3)) return 0;
+  if (bits == 4 && awq::gemv_dot2_supported(M, K)) return 0;  // fused: no intermediate
+  return (size_t)((M * K * 2 + 255) / 256 * 256);
+}
+
+int awq_gemm_scaled(const void* x, const float* inv_s, const void* packed, const void* scales, const void* zeros,
+                    void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(x && inv_s && packed && scales && zeros && y, AWQ_ERROR_INVALID_VALUE,
+              "x, inv_s, packed, scales, zeros and y must not be NULL");
+  int st = check_layer(N, K, group);
+  if (st == AWQ_OK) st = check_bits(bits);
+  if (st != AWQ_OK) return st;
+  AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
+  AWQ_REQUIRE(aligned16(x) && aligned16(inv_s) && aligned16(packed), AWQ_ERROR_MISALIGNED,
+              "x, inv_s and packed must be 16-byte aligned");
+  const size_t need = awq_gemm_scaled_workspace_bytes(M, K, bits);
+  const hipStream_t hs = as_stream(stream);
+  if (need == 0)
+    return device_status(awq::launch_gemv_dot2_scaled(x, inv_s, packed, scales, zeros, y, M, N, K, hs),
+                         "awq_gemm_scaled");
+  AWQ_REQUIRE(workspace && workspace_bytes >= need, AWQ_ERROR_WORKSPACE_TOO_SMALL,
+              "workspace_bytes=%zu below awq_gemm_scaled_workspace_bytes=%zu", workspace_bytes, need);
+  AWQ_REQUIRE(aligned16(workspace), AWQ_ERROR_MISALIGNED, "workspace must be 16-byte aligned");
+  hipError_t e = awq::launch_scale_input(x, inv_s, M, K, workspace, hs);
+  if (e == hipSuccess) {
+    if (bits == 3) e = awq::launch_gemm3(workspace, packed, scales, zeros, y, M, N, K, hs);
+    else if (M <= 16) e = awq::launch_gemv(workspace, packed, scales, zeros, y, M, N, K, hs);
+    else e = awq::launch_gemm(workspace, packed, scales, zeros, y, M, N, K, hs);
+  }
+  return device_status(e, "awq_gemm_scaled");
+  AWQ_GUARD_END
+}
+
 int awq_unpack(const void* packed, const void* zeros, int64_t N, int64_t K, int32_t group, uint8_t* codes,
                uint8_t* zeros_u8, void* stream) {
   return awq_unpack_bits(packed, zeros, N, K, group, 4, codes, zeros_u8, stream);

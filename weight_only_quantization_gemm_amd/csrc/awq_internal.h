@@ -53,6 +53,12 @@ hipError_t launch_argmin(const double* loss, int n, int32_t* best, hipStream_t s
 // gemv.hip (vector-ALU GEMV, M <= 2), skinny.hip (matrix-core decode kernels: LDS-ring kernel for M <= 16, register-staged up to
 // 64 where it beats the GEMM), gemm.hip / gemm_pipe.hip (matrix-core GEMM)
 bool gemv_dot2_supported(int64_t M, int64_t K);
+// The input side of the per-channel scaling: inv_s = 1 / s; xs = fp16(x * inv_s);
+// the M <= 2 GEMV with that scaling applied to x as it is loaded.
+hipError_t launch_inverse_scale(const float* s, int64_t K, float* inv_s, hipStream_t st);
+hipError_t launch_scale_input(const void* x, const float* inv_s, int64_t M, int64_t K, void* xs, hipStream_t st);
+hipError_t launch_gemv_dot2_scaled(const void* x, const float* inv_s, const void* packed, const void* scales,
+                                   const void* zeros, void* y, int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st);
 bool ring3_supported(int64_t M, int64_t N, int64_t K);

@@ -42,6 +42,12 @@ __device__ inline float dot2_acc(f16x2 a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, a), __builtin_bit_cast(h16x2, b), c, false);
 }
 
+// The fp16 pair xw scaled channel-wise by (a, b) in fp32, each rounded once to fp16.
+__device__ inline uint32_t scale_pair(uint32_t xw, float a, float b) {
+  const f16x2 v = as_f16x2(xw);
+  return as_u32(f16x2{(f16)((float)v.x * a), (f16)((float)v.y * b)});
+}
+
 // DPP add: v + v[permuted lane]; lanes whose source row is masked off add 0.
 template <int CTRL, int ROW_MASK>
 __device__ inline float dpp_add(float v) {
@@ -70,10 +76,17 @@ __host__ __device__ inline int gemv_waves(int64_t K) {
 }
 
 // K <= 32768 (at most 1024 chunks) keeps a block within 16 waves.
-template <int MB, int R>
+//
+// With SC, x is first divided by the per-channel scale s of the method
+// ([summary] paragraph 3: a channel whose weights were scaled up by s has its
+// input divided by s): each lane also loads inv_s (fp32 1/s, 128 B for its 32
+// channels) with its other loads, and every x value becomes
+// fp16(fp32(x) * inv_s), rounded once, before the products -- the values
+// awq_scale_input writes, so the result equals this kernel on those values.
+template <int MB, int R, bool SC = false>
 __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                     const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                                                    f16* __restrict__ y, int N, int K) {
+                                                    f16* __restrict__ y, int N, int K, const float* __restrict__ inv_s) {
   __shared__ float red[kMaxWaves][R * MB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = gemv_waves(K);  // == blockDim.x / 64, from the arguments (all preloaded)
@@ -105,6 +118,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
   uint32_t sr[R], zr[R];
   uint4 xv[MB][4];
   u32x4 wv[R];
+  float4 iv[SC ? 8 : 1];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     sr[r] = srow[r][g];
@@ -114,9 +128,25 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int u = 0; u < 4; ++u) xv[m][u] = reinterpret_cast<const uint4*>(x + (int64_t)m * K)[c * 4 + u];
+  if constexpr (SC) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) iv[u] = reinterpret_cast<const float4*>(inv_s)[c * 8 + u];
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r) wv[r] = __builtin_nontemporal_load(wrow[r] + c);
   __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (SC) {  // x word u.{x,y,z,w} holds channels 8u + {0,1}, {2,3}, {4,5}, {6,7} of the chunk
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        xv[m][u].x = scale_pair(xv[m][u].x, iv[2 * u].x, iv[2 * u].y);
+        xv[m][u].y = scale_pair(xv[m][u].y, iv[2 * u].z, iv[2 * u].w);
+        xv[m][u].z = scale_pair(xv[m][u].z, iv[2 * u + 1].x, iv[2 * u + 1].y);
+        xv[m][u].w = scale_pair(xv[m][u].w, iv[2 * u + 1].z, iv[2 * u + 1].w);
+      }
+  }
 
   // 2^-24 * (sum of the lane's 32 x values), per activation row
   float xs[MB];
@@ -188,15 +218,15 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
   }
 }
 
-template <int MB, int R>
+template <int MB, int R, bool SC>
 static hipError_t gemv_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                              int64_t N, int64_t K, hipStream_t st) {
+                              int64_t N, int64_t K, const float* inv_s, hipStream_t st) {
   const int waves = gemv_waves(K);
   if (waves > kMaxWaves) return hipErrorInvalidValue;
   dim3 grid((unsigned)((N + R - 1) / R));
-  gemv_kernel<MB, R><<<grid, dim3(waves * kWave), 0, st>>>(
+  gemv_kernel<MB, R, SC><<<grid, dim3(waves * kWave), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
-      reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)N, (int)K);
+      reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)N, (int)K, inv_s);
   return hipGetLastError();
 }
 
@@ -217,11 +247,12 @@ bool gemv_dot2_supported(int64_t M, int64_t K) {
 // layer; 4 elsewhere, which keeps more blocks in flight (4096 x 11008 at
 // 6.1 us and 11008 x 4096 at 6.8 us, against 6.8 and 7.2 us with 8).  More
 // chunks per lane (fewer waves) measured slower on every shape.
-template <int MB>
+template <int MB, bool SC = false>
 static hipError_t gemv_rows_launch(const void* x, const void* packed, const void* scales, const void* zeros,
-                                   void* y, int64_t N, int64_t K, hipStream_t st) {
-  if ((K >= 8192 && N >= 8192) || (MB == 2 && N >= 16384)) return gemv_launch<MB, 8>(x, packed, scales, zeros, y, N, K, st);
-  return gemv_launch<MB, 4>(x, packed, scales, zeros, y, N, K, st);
+                                   void* y, int64_t N, int64_t K, hipStream_t st, const float* inv_s = nullptr) {
+  if ((K >= 8192 && N >= 8192) || (MB == 2 && N >= 16384))
+    return gemv_launch<MB, 8, SC>(x, packed, scales, zeros, y, N, K, inv_s, st);
+  return gemv_launch<MB, 4, SC>(x, packed, scales, zeros, y, N, K, inv_s, st);
 }
 
 // 3-bit format (three words per 32 channels of a row; see the packer).  The
@@ -382,6 +413,44 @@ hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scale
   if (M == 1) return gemv_rows_launch<1>(x, packed, scales, zeros, y, N, K, st);
   if (M == 2) return gemv_rows_launch<2>(x, packed, scales, zeros, y, N, K, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_dot2_scaled(const void* x, const float* inv_s, const void* packed, const void* scales,
+                                   const void* zeros, void* y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  if (M == 1) return gemv_rows_launch<1, true>(x, packed, scales, zeros, y, N, K, st, inv_s);
+  if (M == 2) return gemv_rows_launch<2, true>(x, packed, scales, zeros, y, N, K, st, inv_s);
+  return hipErrorInvalidValue;
+}
+
+// inv_s[k] = 1 / s[k], IEEE fp32 division (correctly rounded).
+__global__ void inverse_scale_kernel(const float* __restrict__ s, int64_t K, float* __restrict__ inv_s) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < K) inv_s[k] = 1.0f / s[k];
+}
+
+hipError_t launch_inverse_scale(const float* s, int64_t K, float* inv_s, hipStream_t st) {
+  inverse_scale_kernel<<<dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st>>>(s, K, inv_s);
+  return hipGetLastError();
+}
+
+// xs[m][k] = fp16(fp32(x[m][k]) * inv_s[k]); 8 channels per thread (K % 8 == 0).
+__global__ void scale_input_kernel(const f16* __restrict__ x, const float* __restrict__ inv_s, int64_t M, int64_t K,
+                                   f16* __restrict__ xs) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // chunk of 8 channels
+  if (i >= M * (K / 8)) return;
+  const int64_t k0 = (i % (K / 8)) * 8;
+  const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+  const float4 a = *reinterpret_cast<const float4*>(inv_s + k0), b = *reinterpret_cast<const float4*>(inv_s + k0 + 4);
+  const uint4 r{scale_pair(v.x, a.x, a.y), scale_pair(v.y, a.z, a.w), scale_pair(v.z, b.x, b.y),
+                scale_pair(v.w, b.z, b.w)};
+  reinterpret_cast<uint4*>(xs)[i] = r;
+}
+
+hipError_t launch_scale_input(const void* x, const float* inv_s, int64_t M, int64_t K, void* xs, hipStream_t st) {
+  const int64_t chunks = M * (K / 8);
+  scale_input_kernel<<<dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st>>>(
+      reinterpret_cast<const f16*>(x), inv_s, M, K, reinterpret_cast<f16*>(xs));
+  return hipGetLastError();
 }
 
 }  // namespace awq
