@@ -11,12 +11,16 @@ from .api import (  # noqa: F401
     awq_ablation_workspace_bytes,
     awq_channel_mean_abs,
     awq_gemm,
+    awq_gemm_scaled,
+    awq_gemm_scaled_workspace_bytes,
+    awq_inverse_scale,
     awq_keep_fp16_ablation,
     awq_last_error,
     awq_pack,
     awq_packed_bytes,
     awq_quantize,
     awq_quantize_workspace_bytes,
+    awq_scale_input,
     awq_scales_bytes,
     awq_status_string,
     awq_unpack,
