@@ -234,9 +234,10 @@ def run_decode_3bit(args, torch, awq, dev):
 
 
 def run_decode_scaled(args, torch, awq, dev):
-    """The 7-launch decode step of run_decode with x not yet divided by s: awq_gemm_scaled
-    divides it (as x * inv_s, inv_s = 1/s from awq_inverse_scale) inside the GEMV's x load.
-    Bytes per step add inv_s (4 K per layer).  s is a^0.5 of a lognormal channel profile."""
+    """The decode step of run_decode with x not yet divided by s: awq_gemm_scaled divides it
+    (as x * inv_s, inv_s = 1/s from awq_inverse_scale) inside the GEMV's x load on the
+    4096 x 4096 layers and with a separate scaling launch on the larger ones.  Bytes per
+    step add inv_s (4 K per layer).  s is a^0.5 of a lognormal channel profile."""
     from gen import activations_fp16
     step_bytes = sum(gemv_bytes(1, K, N) + 4 * K for _, K, N in LAYERS_7B)
     copies = max(2, int(np.ceil((1 << 30) / step_bytes)) + 1)
@@ -245,18 +246,20 @@ def run_decode_scaled(args, torch, awq, dev):
         g = np.random.default_rng(2200 + L.K)
         sv = np.sqrt(np.exp(g.normal(0.0, 0.8, L.K))).astype(np.float32)
         L.inv = awq.awq_inverse_scale(torch.from_numpy(sv).to(dev))
+        L.ws = torch.empty(max(awq.awq_gemm_scaled_workspace_bytes(1, L.N, L.K), 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(c):
         for L in layers:
             p, s, z = L.copies[c]
-            awq.awq_gemm_scaled(L.x, L.inv, p, s, z, out=L.y)
+            awq.awq_gemm_scaled(L.x, L.inv, p, s, z, out=L.y, workspace=L.ws)
 
     ms = time_steps(torch, step, copies, args.steps, args.warmup)
     del layers
+    fused = [n for n, K, N in LAYERS_7B if awq.awq_gemm_scaled_workspace_bytes(1, N, K) == 0]
     return dict(us_per_step=round(ms * 1e3, 3), GBs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
                 hbm_frac=round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_per_step=step_bytes,
-                launches=len(LAYERS_7B))
+                launches=len(LAYERS_7B) + len(LAYERS_7B) - len(fused), fused_layers=fused)
 
 
 def run_sweep(args, torch, awq, dev):

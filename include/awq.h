@@ -255,17 +255,18 @@ int awq_scale_input(const void* x, const float* inv_s, int64_t M, int64_t K, voi
 /*
  * awq_gemm_scaled -- y = awq_scale_input(x, inv_s) times w_hat^T: the product
  * of awq_gemm_bits on the scaled input, bit for bit.  At 4 bits with M = 1, and
- * M = 2 with K < 16384 (the vector-ALU GEMV), the scaling happens in the
- * GEMV's own x load: one launch, no intermediate, and
+ * M = 2 with K < 16384 (the vector-ALU GEMV), on layers with N * K <= 2^24, the
+ * scaling happens in the GEMV's own x load: one launch, no intermediate, and
  * awq_gemm_scaled_workspace_bytes is 0 (workspace may be NULL).  Otherwise
  * the scaled input goes through `workspace` (device, M * K * 2 bytes rounded up
- * to 256) and awq_gemm_bits runs on it.
+ * to 256) and awq_gemm_bits runs on it: on larger layers the fused form's
+ * per-block re-read of inv_s costs more than the second launch.
  *   x      device fp16 [M][K]   activations, not divided by s
  *   inv_s  device fp32 [K]      from awq_inverse_scale
  *   other arguments as awq_gemm_bits
  * Requires what awq_gemm_bits requires.
  */
-size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t K, int32_t bits);
+size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits);
 int awq_gemm_scaled(const void* x, const float* inv_s, const void* packed, const void* scales, const void* zeros,
                     void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* workspace,
                     size_t workspace_bytes, void* stream);

@@ -112,11 +112,12 @@ def test_gemm_argument_errors_before_launch():
 def test_input_scaling_queries_and_errors_before_launch():
     lib = _lib_()
     ws = lib.awq_gemm_scaled_workspace_bytes
-    assert ws(1, 4096, 4) == 0 and ws(2, 4096, 4) == 0          # fused into the GEMV's x load
-    assert ws(2, 16384, 4) == 2 * 16384 * 2                      # M = 2 on long rows: another kernel
-    assert ws(3, 4096, 4) == 3 * 4096 * 2 and ws(1, 4096, 3) == 4096 * 2
-    assert ws(5, 136, 4) == (5 * 136 * 2 + 255) // 256 * 256
-    assert ws(0, 4096, 4) == 0 and ws(1, 4096, 5) == 0
+    assert ws(1, 4096, 4096, 4) == 0 and ws(2, 4096, 4096, 4) == 0  # fused into the GEMV's x load
+    assert ws(1, 11008, 4096, 4) == 4096 * 2                           # larger layer: scale, then GEMV
+    assert ws(2, 300, 16384, 4) == 2 * 16384 * 2                        # M = 2 on long rows: another kernel
+    assert ws(3, 64, 4096, 4) == 3 * 4096 * 2 and ws(1, 64, 4096, 3) == 4096 * 2
+    assert ws(5, 64, 136, 4) == (5 * 136 * 2 + 255) // 256 * 256
+    assert ws(0, 64, 4096, 4) == 0 and ws(1, 64, 4096, 5) == 0
     assert lib.awq_inverse_scale(None, 128, FAKE, None) == INVALID
     assert lib.awq_inverse_scale(FAKE, 0, FAKE, None) == INVALID
     assert lib.awq_inverse_scale(FAKE_MISALIGNED, 128, FAKE, None) == MISALIGNED

@@ -4,7 +4,7 @@ awq_inverse_scale is IEEE fp32 division, checked bit for bit against numpy's; aw
 is one fp32 product rounded once to fp16, checked bit for bit against the same two numpy
 operations, and against the oracle's x / s (one fp32 division rounded once), from which it
 may differ only by one fp16 ulp on a few values.  awq_gemm_scaled must equal awq_gemm_bits
-on awq_scale_input's output bit for bit (fused into the GEMV's x load at 4 bits and M <= 2,
+on awq_scale_input's output bit for bit (fused into the GEMV's x load at 4 bits, M <= 2 and N K <= 2^24,
 through the workspace otherwise), and the oracle's product on x / s to the usual bars
 (relative Frobenius error <= 1e-3, max |dy| <= 1e-2 max |y_ref|)."""
 import numpy as np
@@ -55,6 +55,7 @@ def test_scale_input_bits(M, K):
 
 @pytest.mark.parametrize("M,N,K,bits", [
     (1, 4096, 4096, 4), (2, 4096, 4096, 4), (1, 1000, 11008, 4), (2, 515, 2176, 4),  # fused GEMV
+    (1, 11008, 4096, 4), (2, 4100, 4096, 4),                                           # larger: two launches
     (2, 300, 16384, 4),                                                                # M = 2, long rows
     (3, 700, 1024, 4), (16, 257, 2048, 4), (100, 300, 1024, 4),                        # workspace path
     (1, 600, 4096, 3), (7, 300, 1024, 3),                                              # 3-bit
@@ -66,7 +67,8 @@ def test_gemm_scaled_parity(M, N, K, bits):
     s = _scales(K, seed + 1)
     x = activations_fp16(M, K, seed=seed + 2)
     inv = awq.awq_inverse_scale(dev(s))
-    assert (awq.awq_gemm_scaled_workspace_bytes(M, K, bits) == 0) == (bits == 4 and (M == 1 or (M == 2 and K < 16384)))
+    fused = bits == 4 and (M == 1 or (M == 2 and K < 16384)) and N * K <= 1 << 24
+    assert (awq.awq_gemm_scaled_workspace_bytes(M, N, K, bits) == 0) == fused
     y = host(awq.awq_gemm_scaled(dev(x), inv, p, scd, zd, bits=bits))
     xs = awq.awq_scale_input(dev(x), inv)
     y2 = host(awq.awq_gemm(xs, p, scd, zd, bits=bits))

@@ -36,7 +36,7 @@ SIGNATURES = {
                                               c_vp, c_vp, c_vp, c_size, c_vp]),
     "awq_inverse_scale": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp]),
     "awq_scale_input": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
-    "awq_gemm_scaled_workspace_bytes": (c_size, [c_i64, c_i64, c_i32]),
+    "awq_gemm_scaled_workspace_bytes": (c_size, [c_i64, c_i64, c_i64, c_i32]),
     "awq_gemm_scaled": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32,
                                        c_vp, c_size, c_vp]),
     "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),

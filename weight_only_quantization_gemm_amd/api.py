@@ -222,16 +222,17 @@ def awq_scale_input(x: torch.Tensor, inv_s: torch.Tensor, out: Optional[torch.Te
     return out
 
 
-def awq_gemm_scaled_workspace_bytes(M: int, K: int, bits: int = 4) -> int:
-    return int(load().awq_gemm_scaled_workspace_bytes(M, K, bits))
+def awq_gemm_scaled_workspace_bytes(M: int, N: int, K: int, bits: int = 4) -> int:
+    return int(load().awq_gemm_scaled_workspace_bytes(M, N, K, bits))
 
 
 def awq_gemm_scaled(x: torch.Tensor, inv_s: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
                     zeros: torch.Tensor, out: Optional[torch.Tensor] = None, group: int = GROUP,
                     bits: Optional[int] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y = awq_scale_input(x, inv_s) @ w_hat^T; x fp16 [M][K] not divided by s.  At 4 bits
-    and M <= 2 the division happens inside the GEMV's x load (no workspace); otherwise a
-    workspace of awq_gemm_scaled_workspace_bytes bytes is taken from `workspace` or allocated."""
+    """y = awq_scale_input(x, inv_s) @ w_hat^T; x fp16 [M][K] not divided by s.  At 4 bits,
+    M <= 2 and N * K <= 2^24 the division happens inside the GEMV's x load (no workspace);
+    otherwise a workspace of awq_gemm_scaled_workspace_bytes bytes is taken from `workspace`
+    or allocated."""
     _need(x, "x", torch.float16, 2)
     _need(inv_s, "inv_s", torch.float32, 1)
     _need(packed, "packed", torch.int32, 2)
@@ -251,7 +252,7 @@ def awq_gemm_scaled(x: torch.Tensor, inv_s: torch.Tensor, packed: torch.Tensor, 
         _need(out, "out", torch.float16, 2)
         if tuple(out.shape) != (M, N):
             raise ValueError("out must be fp16 [M][N]")
-    need = awq_gemm_scaled_workspace_bytes(M, K, bits)
+    need = awq_gemm_scaled_workspace_bytes(M, N, K, bits)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     with torch.cuda.device(x.device):

@@ -362,9 +362,19 @@ int awq_scale_input(const void* x, const float* inv_s, int64_t M, int64_t K, voi
   AWQ_GUARD_END
 }
 
-size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t K, int32_t bits) {
-  if (M < 1 || K < 1 || (bits != 4 && bits != 3)) return 0;
-  if (bits == 4 && awq::gemv_dot2_supported(M, K)) return 0;  // fused: no intermediate
+// The division fused into the M <= 2 GEMV's x load costs every block another read
+// of inv_s (4 bytes per channel, twice what x takes): on layers up to 4096 x 4096
+// that is cheaper than a second launch (measured on 4096 x 4096: 5.1 us fused,
+// 5.6 us as scale-then-GEMV, 3.8 us unscaled); on larger ones the extra L2 traffic
+// costs more than the launch (4096 x 11008: 10.1 against 7.9 us; 8192 x 28672:
+// 31.2 against 23.2 us), so those take the two-launch path.
+static bool scaled_fused(int64_t M, int64_t N, int64_t K, int32_t bits) {
+  return bits == 4 && awq::gemv_dot2_supported(M, K) && N * K <= (int64_t(1) << 24);
+}
+
+size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits) {
+  if (M < 1 || N < 1 || K < 1 || (bits != 4 && bits != 3)) return 0;
+  if (scaled_fused(M, N, K, bits)) return 0;  // no intermediate
   return (size_t)((M * K * 2 + 255) / 256 * 256);
 }
 
@@ -380,7 +390,7 @@ int awq_gemm_scaled(const void* x, const float* inv_s, const void* packed, const
   AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
   AWQ_REQUIRE(aligned16(x) && aligned16(inv_s) && aligned16(packed), AWQ_ERROR_MISALIGNED,
               "x, inv_s and packed must be 16-byte aligned");
-  const size_t need = awq_gemm_scaled_workspace_bytes(M, K, bits);
+  const size_t need = awq_gemm_scaled_workspace_bytes(M, N, K, bits);
   const hipStream_t hs = as_stream(stream);
   if (need == 0)
     return device_status(awq::launch_gemv_dot2_scaled(x, inv_s, packed, scales, zeros, y, M, N, K, hs),
