@@ -385,6 +385,23 @@ def run_ablation(torch, awq, dev, W, X, search_loss):
                 awq_search_ratio_vs_rtn=float(search_loss.min() / search_loss[0]))
 
 
+def search_roofline_ms(M, K, N, n_alpha=20, statistics=True):
+    """Composite roofline of one awq_quantize call, sum over its phases of
+    max(bytes / 8 TB/s, flops / 2.5 PFLOP/s), algorithmic amounts: statistics read X
+    once (2 M K bytes); the Gram is a symmetric product (M K (K + 1) flops); each alpha
+    reads W and writes its error as an fp16 hi/lo pair (6 N K bytes) and forms the
+    quadratic form as the three-term fp16 split (3 x 2 N K^2 flops); the pack reads W
+    and writes the packed layer."""
+    bw, pk = HBM_PEAK_GBS * 1e9, 2.5e15
+    t = 0.0
+    if statistics:  # without: taken from an earlier call on the same input
+        t += 2.0 * M * K / bw
+        t += M * K * (K + 1) / pk
+    t += n_alpha * max(6.0 * N * K / bw, 6.0 * N * K * K / pk)
+    t += (2.0 * N * K + gemv_bytes(1, K, N)) / bw
+    return t * 1e3
+
+
 def run_search(args, torch, awq, dev):
     """awq_quantize on the 7 linears of a 7B block, 65,536 calibration rows per input."""
     from gen import activations_fp16, normal_fp16, seed_for
@@ -418,8 +435,44 @@ def run_search(args, torch, awq, dev):
             res[lname]["keep_fp16_ablation"] = run_ablation(torch, awq, dev, W, inputs[src], loss)
         del W, ws, r
         torch.cuda.empty_cache()
+    # The same 7 searches with the statistics of each input computed once: layers that read
+    # one input run on one workspace, and the later ones reuse its statistics
+    # (awq_quantize_shared; q/k/v share the attention input, gate/up the MLP input).
+    shared_ms, by_src = 0.0, {}
+    for li, (lname, src) in enumerate(layer_inputs_7b_block()):
+        by_src.setdefault(src, []).append((li, lname))
+    for src, group in by_src.items():
+        K = Ks[group[0][1]][0]
+        nmax = max(Ks[l][1] for _, l in group)
+        ws = torch.empty((awq.awq_quantize_workspace_bytes(nmax, K, M, 128, 20),), dtype=torch.uint8, device=dev)
+        Ws = {l: torch.from_numpy(normal_fp16((Ks[l][1], K), 0.02, seed=seed_for(5, 100 + li))).to(dev)
+              for li, l in group}
+        awq.awq_quantize(Ws[group[0][1]], inputs[src], None, workspace=ws)  # warm-up
+        torch.cuda.synchronize()
+        for j, (li, l) in enumerate(group):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            r = awq.awq_quantize(Ws[l], inputs[src], None, workspace=ws, reuse_statistics=j > 0)
+            b.record()
+            torch.cuda.synchronize()
+            res[l]["ms_shared_statistics"] = round(a.elapsed_time(b), 2)
+            shared_ms += a.elapsed_time(b)
+            assert int(r["best_alpha"].item()) == res[l]["alpha_index"]
+            del r
+        del ws, Ws
+        torch.cuda.empty_cache()
+    roof = sum(search_roofline_ms(M, K, N) for _, K, N in LAYERS_7B)
+    roof_shared = sum(search_roofline_ms(M, Ks[l][0], Ks[l][1], statistics=j == 0)
+                      for group in by_src.values() for j, (_, l) in enumerate(group))
+    for lname, r_ in res.items():
+        r_["roofline_ms"] = round(search_roofline_ms(M, r_["K"], r_["N"]), 3)
     return dict(layers=res, s_per_layer=round(total_ms / 7 / 1e3, 4), total_s=round(total_ms / 1e3, 3),
-                calib_rows=M, n_alpha=20)
+                calib_rows=M, n_alpha=20, composite_roofline_s=round(roof / 1e3, 4),
+                composite_roofline_frac=round(roof / total_ms, 4),
+                total_s_shared_statistics=round(shared_ms / 1e3, 3),
+                s_per_layer_shared_statistics=round(shared_ms / 7 / 1e3, 4),
+                composite_roofline_s_shared_statistics=round(roof_shared / 1e3, 4),
+                composite_roofline_frac_shared_statistics=round(roof_shared / shared_ms, 4))
 
 
 def run_search_joint(args, torch, awq, dev):

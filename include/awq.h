@@ -190,6 +190,25 @@ int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * awq_quantize_shared -- awq_quantize_bits for layers that read the same input
+ * (q/k/v, gate/up): with reuse_statistics = 1 the statistics of X (the channel
+ * means a and, for M >= K, the scaled fp16 split of G = X^T X) are taken from
+ * `workspace`, where the previous awq_quantize* call on this workspace left
+ * them, instead of being recomputed; everything after them (s(alpha), the
+ * errors, the losses, the pack) runs as in awq_quantize_bits, so the outputs
+ * are identical.  The caller guarantees that the previous call on this
+ * workspace had the same X contents, M and K (N, bits, the alpha grid and W
+ * may differ) and that the workspace was not written in between; otherwise the
+ * outputs are unspecified.  reuse_statistics = 0 is awq_quantize_bits.  The
+ * workspace must cover awq_quantize_workspace_bytes of this call.
+ */
+int awq_quantize_shared(const void* W, const void* X, int64_t N, int64_t K, int64_t M, int32_t group, int32_t bits,
+                        const float* alphas, int32_t n_alpha, int32_t reuse_statistics,
+                        void* packed, void* scales, void* zeros, float* s,
+                        int32_t* best_alpha, double* loss,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * awq_gemm -- the W4A16 product that 4-bit decoding runs on ([summary]
  * paragraphs 1 and 6: decoding is memory-bound, 4-bit weights cut its
  * traffic about 4x; [profile]: W4A16 GEMM kernels).  The int4 weights are

@@ -134,6 +134,17 @@ def test_input_scaling_queries_and_errors_before_launch():
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE_MISALIGNED, 768, None) == MISALIGNED
 
 
+def test_quantize_shared_argument_errors_before_launch():
+    lib = _lib_()
+    al = (ctypes.c_float * 2)(0.0, 0.5)
+    f = lib.awq_quantize_shared
+    args = lambda reuse, ws=FAKE, wsb=1 << 40: (FAKE, FAKE, 64, 512, 600, 128, 4, ctypes.cast(al, ctypes.c_void_p), 2,
+                                                reuse, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, wsb, None)
+    assert f(*args(2)) == INVALID
+    assert f(*args(-1)) == INVALID
+    assert f(*args(1, wsb=16)) == WS_SMALL
+
+
 def test_pack_and_unpack_argument_errors_before_launch():
     lib = _lib_()
     assert lib.awq_pack(None, None, 4, 128, 128, FAKE, FAKE, FAKE, None) == INVALID

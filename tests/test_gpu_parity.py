@@ -192,6 +192,28 @@ def test_search_determinism():
         assert np.array_equal(host(r1[k]).view(np.uint8), host(r2[k]).view(np.uint8)), k
 
 
+@pytest.mark.parametrize("K,M", [(512, 700), (512, 300)])  # Gram form (M >= K), direct form (M < K)
+def test_search_reused_statistics(K, M):
+    """Layers on one input searched one after another on one workspace, the later ones taking
+    the statistics of X from it (awq_quantize_shared): every output equals a search that
+    recomputes them, bit for bit, whatever N, bits and alpha grid the earlier layer had; the
+    first layer is checked against the oracle."""
+    note(f"search reused statistics K={K} M={M}")
+    X = dev(activations_fp16(M, K, seed=88, lognormal=True))
+    layers = [(384, 4, ALPHAS), (128, 4, ALPHAS[:7]), (256, 3, ALPHAS)]
+    Ws = [dev(normal_fp16((n, K), 0.02, seed=89 + i)) for i, (n, _, _) in enumerate(layers)]
+    need = max(awq.awq_quantize_workspace_bytes(n, K, M, 128, len(al)) for n, _, al in layers)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    for i, ((n, bits, al), W) in enumerate(zip(layers, Ws)):
+        shared = awq.awq_quantize(W, X, al, workspace=ws, bits=bits, reuse_statistics=i > 0)
+        fresh = awq.awq_quantize(W, X, al, bits=bits)
+        for k in ("packed", "scales", "zeros", "s", "best_alpha", "loss"):
+            assert np.array_equal(host(shared[k]).view(np.uint8), host(fresh[k]).view(np.uint8)), (i, k)
+        if i == 0:
+            Wh = host(W)
+            _check_search(Wh, host(X), shared, oracle.search(Wh, host(X), alphas=al, bits=bits))
+
+
 # ------------------------------------------------------------------ W4A16 product
 def _random_packed(N, K, seed, sigma=0.02):
     g = np.random.default_rng(seed)

@@ -131,9 +131,12 @@ def awq_pack(W: torch.Tensor, s: Optional[torch.Tensor] = None, group: int = GRO
 
 
 def awq_quantize(W: torch.Tensor, X: torch.Tensor, alphas: Optional[Sequence[float]] = None,
-                 group: int = GROUP, workspace: Optional[torch.Tensor] = None, bits: int = 4) -> dict:
+                 group: int = GROUP, workspace: Optional[torch.Tensor] = None, bits: int = 4,
+                 reuse_statistics: bool = False) -> dict:
     """AWQ scale search for one linear layer; returns packed, scales, zeros, s,
-    best_alpha (int32 [1] on device), loss (fp64 [n_alpha] on device)."""
+    best_alpha (int32 [1] on device), loss (fp64 [n_alpha] on device).  With
+    reuse_statistics the statistics of X are taken from `workspace`, which the previous
+    call must have filled from the same X (awq_quantize_shared)."""
     _need(W, "W", torch.float16, 2)
     _check_bits(bits)
     _need(X, "X", torch.float16, 2)
@@ -152,6 +155,8 @@ def awq_quantize(W: torch.Tensor, X: torch.Tensor, alphas: Optional[Sequence[flo
     if ws_bytes == 0:
         raise ValueError("unsupported sizes for awq_quantize")
     if workspace is None:
+        if reuse_statistics:
+            raise ValueError("reuse_statistics needs the workspace of the previous call on the same X")
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
     elif workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_cuda:
         raise ValueError(f"workspace must be a GPU buffer of at least {ws_bytes} bytes")
@@ -160,10 +165,11 @@ def awq_quantize(W: torch.Tensor, X: torch.Tensor, alphas: Optional[Sequence[flo
     best = torch.empty((1,), dtype=torch.int32, device=W.device)
     loss = torch.empty((n_alpha,), dtype=torch.float64, device=W.device)
     with torch.cuda.device(W.device):
-        check(lib.awq_quantize_bits(W.data_ptr(), X.data_ptr(), N, K, M, group, bits, al.ctypes.data, n_alpha,
-                                    packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), s.data_ptr(),
-                                    best.data_ptr(), loss.data_ptr(), workspace.data_ptr(),
-                                    workspace.numel() * workspace.element_size(), _stream(W.device)))
+        check(lib.awq_quantize_shared(W.data_ptr(), X.data_ptr(), N, K, M, group, bits, al.ctypes.data, n_alpha,
+                                      int(bool(reuse_statistics)), packed.data_ptr(), scales.data_ptr(),
+                                      zeros.data_ptr(), s.data_ptr(), best.data_ptr(), loss.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                      _stream(W.device)))
     return dict(packed=packed, scales=scales, zeros=zeros, s=s, best_alpha=best, loss=loss, alphas=al, bits=bits)
 
 
@@ -294,6 +300,8 @@ def awq_keep_fp16_ablation(W: torch.Tensor, X: torch.Tensor, n_keep: int, random
     if ws_bytes == 0:
         raise ValueError("unsupported sizes for awq_keep_fp16_ablation")
     if workspace is None:
+        if reuse_statistics:
+            raise ValueError("reuse_statistics needs the workspace of the previous call on the same X")
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
     elif workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_cuda:
         raise ValueError(f"workspace must be a GPU buffer of at least {ws_bytes} bytes")

@@ -68,7 +68,8 @@ int check_layer(int64_t N, int64_t K, int32_t group) {
 
 // Workspace of awq_quantize, carved in this order (each piece 256-byte aligned).
 // M < K uses the direct form of the loss (E in fp32); M >= K the Gram form
-// (X^T, G in fp32 and as scaled fp16 hi/lo, channel exponents, E' hi/lo).
+// (channel exponents, G as scaled fp16 hi/lo, X^T and G in fp32, E' hi/lo).
+// The statistics of X come first, at offsets that depend on K and M only.
 struct QuantizeWorkspace {
   bool direct;
   size_t a, s_all, xt, g, gh, gl, ex, eh, el, e32, partial, loss, b, mask, total;
@@ -87,16 +88,19 @@ QuantizeWorkspace quantize_workspace(int64_t N, int64_t K, int64_t M, int32_t n_
     off = round_up(off + bytes, 256);
     return at;
   };
+  // statistics of X first (they depend on K and M only), then what depends on N and n_alpha
   w.a = take(sizeof(double) * (size_t)K);
+  if (!w.direct) {
+    w.ex = take(sizeof(int32_t) * (size_t)K);
+    w.gh = take(2 * (size_t)K * (size_t)K);
+    w.gl = take(2 * (size_t)K * (size_t)K);
+    w.xt = take(2 * (size_t)K * (size_t)w.mp);
+    w.g = take(sizeof(float) * (size_t)K * (size_t)K);
+  }
   w.s_all = take(sizeof(float) * (size_t)n_alpha * (size_t)K);
   if (w.direct) {
     w.e32 = take(sizeof(float) * (size_t)N * (size_t)K);
   } else {
-    w.xt = take(2 * (size_t)K * (size_t)w.mp);
-    w.g = take(sizeof(float) * (size_t)K * (size_t)K);
-    w.gh = take(2 * (size_t)K * (size_t)K);
-    w.gl = take(2 * (size_t)K * (size_t)K);
-    w.ex = take(sizeof(int32_t) * (size_t)K);
     w.eh = take(2 * (size_t)N * (size_t)K);
     w.el = take(2 * (size_t)N * (size_t)K);
   }
@@ -194,7 +198,17 @@ int awq_quantize(const void* W, const void* X, int64_t N, int64_t K, int64_t M, 
 int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_t M, int32_t group, int32_t bits,
                       const float* alphas, int32_t n_alpha, void* packed, void* scales, void* zeros, float* s,
                       int32_t* best_alpha, double* loss, void* workspace, size_t workspace_bytes, void* stream) {
+  return awq_quantize_shared(W, X, N, K, M, group, bits, alphas, n_alpha, 0, packed, scales, zeros, s, best_alpha,
+                             loss, workspace, workspace_bytes, stream);
+}
+
+int awq_quantize_shared(const void* W, const void* X, int64_t N, int64_t K, int64_t M, int32_t group, int32_t bits,
+                        const float* alphas, int32_t n_alpha, int32_t reuse_statistics, void* packed, void* scales,
+                        void* zeros, float* s, int32_t* best_alpha, double* loss, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(reuse_statistics == 0 || reuse_statistics == 1, AWQ_ERROR_INVALID_VALUE,
+              "reuse_statistics=%d must be 0 or 1", reuse_statistics);
   AWQ_REQUIRE(W && X && alphas && packed && scales && zeros && s && best_alpha && workspace, AWQ_ERROR_INVALID_VALUE,
               "W, X, alphas, packed, scales, zeros, s, best_alpha and workspace must not be NULL");
   int st = check_layer(N, K, group);
@@ -224,7 +238,10 @@ int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_
   hipStream_t hs = as_stream(stream);
   const double mn = (double)M * (double)N;
 
-  hipError_t e = awq::launch_channel_mean_abs(X, M, K, a, hs);
+  // The statistics of X (a, and in the Gram form the exponents and the scaled
+  // hi/lo split of G) sit in the workspace ahead of everything that depends on N,
+  // so a call with the same X, M and K may take them from the previous call.
+  hipError_t e = reuse_statistics ? hipSuccess : awq::launch_channel_mean_abs(X, M, K, a, hs);
   if (e == hipSuccess) e = awq::launch_scales(a, grid, n_alpha, K, s_all, hs);
   if (w.direct) {
     float* E = reinterpret_cast<float*>(base + w.e32);
@@ -241,9 +258,11 @@ int awq_quantize_bits(const void* W, const void* X, int64_t N, int64_t K, int64_
     int32_t* ex = reinterpret_cast<int32_t*>(base + w.ex);
     void* Ehi = base + w.eh;
     void* Elo = base + w.el;
-    if (e == hipSuccess) e = awq::launch_transpose(X, M, K, w.mp, xt, hs);
-    if (e == hipSuccess) e = awq::launch_gram(xt, w.mp, K, G, hs);
-    if (e == hipSuccess) e = awq::launch_gram_split(G, K, ex, Ghi, Glo, hs);
+    if (!reuse_statistics) {
+      if (e == hipSuccess) e = awq::launch_transpose(X, M, K, w.mp, xt, hs);
+      if (e == hipSuccess) e = awq::launch_gram(xt, w.mp, K, G, hs);
+      if (e == hipSuccess) e = awq::launch_gram_split(G, K, ex, Ghi, Glo, hs);
+    }
     for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
       e = awq::launch_quant_error(W, s_all + (size_t)i * (size_t)K, ex, nullptr, N, K, bits, Ehi, Elo, hs);
       if (e == hipSuccess) e = awq::launch_loss_partials(Ehi, Elo, Ghi, Glo, N, K, partial, hs);
