@@ -300,8 +300,6 @@ def awq_keep_fp16_ablation(W: torch.Tensor, X: torch.Tensor, n_keep: int, random
     if ws_bytes == 0:
         raise ValueError("unsupported sizes for awq_keep_fp16_ablation")
     if workspace is None:
-        if reuse_statistics:
-            raise ValueError("reuse_statistics needs the workspace of the previous call on the same X")
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=W.device)
     elif workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_cuda:
         raise ValueError(f"workspace must be a GPU buffer of at least {ws_bytes} bytes")
