@@ -34,7 +34,7 @@ namespace awq {
 
 constexpr int kFT = 256;     // tile of T: 256 rows n x 256 columns j
 // Stage width, measured on the 7B shapes: two 32-channel stages beat four
-// 16-channel stages by 10-15 % (half the barriers).
+// 16-channel stages by 5-9 % (half the barriers).
 #ifndef AWQ_LOSS_KS
 #define AWQ_LOSS_KS 32
 #endif
@@ -101,8 +101,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void loss_full_kernel(const f16* __restrict__ Ehi, const f16* __restrict__ Elo, const f16* __restrict__ Ghi,
                       const f16* __restrict__ Glo, int64_t N, int64_t K, int nt, int jt, double* __restrict__ partial) {
   constexpr int D = kFStages - 1;  // stages in flight ahead of the one computed
+  // The only LDS variable of the kernel: with a second one the compiler tags every LDS
+  // access with alias scopes, and then waits for all outstanding direct loads before
+  // each fragment read (it cannot tell the stage being filled from the one being read),
+  // which would serialize the pipeline.  The final reduction reuses the stage buffers.
   __shared__ __attribute__((aligned(16))) f16 lds[kFStages][4][kFT * kFKS];  // 131,072 B
-  __shared__ double red[8];
   const FullTile ft = full_tile((int)blockIdx.x, nt, jt);
   if (ft.t < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -190,6 +193,8 @@ void loss_full_kernel(const f16* __restrict__ Ehi, const f16* __restrict__ Elo, 
       }
   }
   sum = wave_sum(sum);
+  double* red = reinterpret_cast<double*>(&lds[0][0][0]);
+  __syncthreads();  // every wave is past its last fragment read
   if (lane == 0) red[wave] = sum;
   __syncthreads();
   if (tid == 0) {
