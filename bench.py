@@ -24,7 +24,7 @@ Also reported in the same JSON line:
                  with one shared s per input (q/k/v and gate/up jointly).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--no-search] [--no-sweep] [--profile-mode gemv|copy]
+       [--no-search] [--no-sweep] [--no-decode-legs] [--profile-mode gemv|copy|gemm|ring]
 """
 from __future__ import annotations
 
@@ -577,6 +577,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-search", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-decode-legs", action="store_true",
+                    help="skip the fused, scaled-input and 3-bit decode legs (the headline step only)")
     ap.add_argument("--profile-mode", choices=["gemv", "copy", "gemm", "ring"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -602,15 +604,16 @@ def main():
     torch.cuda.empty_cache()
 
     legs = {}
-    log("decode, q/k/v and gate/up fused by concatenated rows (4 launches)")
-    legs["decode_fused_qkv_gateup"] = run_decode_fused(args, torch, awq, dev)
-    torch.cuda.empty_cache()
-    log("decode, x divided by s on the device (fused into the GEMV on 4096 x 4096 layers)")
-    legs["decode_llama2_7b_scaled_input"] = run_decode_scaled(args, torch, awq, dev)
-    torch.cuda.empty_cache()
-    log("decode, 3-bit weights (7 launches)")
-    legs["decode_llama2_7b_3bit"] = run_decode_3bit(args, torch, awq, dev)
-    torch.cuda.empty_cache()
+    if not args.no_decode_legs:
+        log("decode, q/k/v and gate/up fused by concatenated rows (4 launches)")
+        legs["decode_fused_qkv_gateup"] = run_decode_fused(args, torch, awq, dev)
+        torch.cuda.empty_cache()
+        log("decode, x divided by s on the device (fused into the GEMV on 4096 x 4096 layers)")
+        legs["decode_llama2_7b_scaled_input"] = run_decode_scaled(args, torch, awq, dev)
+        torch.cuda.empty_cache()
+        log("decode, 3-bit weights (7 launches)")
+        legs["decode_llama2_7b_3bit"] = run_decode_3bit(args, torch, awq, dev)
+        torch.cuda.empty_cache()
     if not args.no_sweep:
         log("sweep: (4096, 11008) at M = 1..1024")
         legs["batch_sweep_4096x11008"] = run_sweep(args, torch, awq, dev)
