@@ -171,21 +171,37 @@ void loss_full_kernel(const f16* __restrict__ Ehi, const f16* __restrict__ Elo, 
   }
   wait_vmcnt<0>();  // the tail's redundant loads land before the block can exit
 
-  // partial = sum over the tile of E'[n][j] * T[n][j], E' = hi + lo in fp32
+  // partial = sum over the tile of E'[n][j] * T[n][j], E' = hi + lo in fp32.  The lane's
+  // 32 E' pairs are all loaded before any is used (one round trip to memory); rows past N
+  // and channels past K (all 4 of a quad or none, K % 128 == 0) read a valid element and
+  // are dropped from the sum.
+  u32x2 hv[2][4][4], lv[2][4][4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    int64_t n = n0 + wn * 64 + b * 32 + l32;
+    n = n < N ? n : N - 1;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int64_t j = j0 + wj * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
+        j = j < K ? j : K - 4;
+        hv[b][a][q] = *reinterpret_cast<const u32x2*>(Ehi + n * K + j);
+        lv[b][a][q] = *reinterpret_cast<const u32x2*>(Elo + n * K + j);
+      }
+  }
   double sum = 0.0;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int64_t n = n0 + wn * 64 + b * 32 + l32;
-    if (n >= N) continue;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t j = j0 + wj * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
-        if (j >= K) continue;  // K % 128 == 0: the 4 channels j .. j + 3 are all in range or all out
-        const uint2 hv = *reinterpret_cast<const uint2*>(Ehi + n * K + j);
-        const uint2 lv = *reinterpret_cast<const uint2*>(Elo + n * K + j);
-        const f16x2 h01 = as_f16x2(hv.x), h23 = as_f16x2(hv.y), l01 = as_f16x2(lv.x), l23 = as_f16x2(lv.y);
+        if (n >= N || j >= K) continue;
+        const f16x2 h01 = as_f16x2(hv[b][a][q].x), h23 = as_f16x2(hv[b][a][q].y);
+        const f16x2 l01 = as_f16x2(lv[b][a][q].x), l23 = as_f16x2(lv[b][a][q].y);
         const float e[4] = {(float)h01.x + (float)l01.x, (float)h01.y + (float)l01.y, (float)h23.x + (float)l23.x,
                             (float)h23.y + (float)l23.y};
 #pragma unroll
