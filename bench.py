@@ -583,7 +583,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the W4A16 kernels are measured on one MI355X; "
-              f"--gpus {args.gpus} is not supported (see the sharding notes in DESIGN.md)", file=sys.stderr)
+              f"--gpus {args.gpus} is not supported: column-parallel layers would shard N and row-parallel ones K, "
+              f"with one all-reduce of y, and that path is not built", file=sys.stderr)
         sys.exit(2)
 
     import torch
