@@ -111,6 +111,58 @@ def test_quantizer_hand_worked_positive_group_fp16_step():
     assert list(q[0, :4]) == [5, 10, 15, 15]
 
 
+def _fp16_rne_bits(u32):
+    """fp32 bit patterns -> fp16 bit patterns, round to nearest even, by integer arithmetic
+    alone (finite inputs; overflow to inf).  Independent of numpy's cast, which the oracle
+    uses for the fp16 group step."""
+    u = np.asarray(u32, dtype=np.uint64)
+    sign = (u >> np.uint64(31)) << np.uint64(15)
+    exp = ((u >> np.uint64(23)) & np.uint64(0xFF)).astype(np.int64)
+    man = (u & np.uint64(0x7FFFFF)) | np.uint64(0x800000)      # 24-bit significand with the hidden bit
+    out = np.zeros(u.shape, dtype=np.uint64)
+    e16 = exp - 127 + 15                                         # fp16 biased exponent if normal
+    # number of significand bits to drop: 13 for normals, more for subnormals (value = m * 2^(e-24) ...)
+    shift = np.where(e16 >= 1, 13, 13 + 1 - e16).astype(np.int64)
+    shift = np.minimum(shift, 40)
+    sh = shift.astype(np.uint64)
+    q = man >> sh
+    rem = man - (q << sh)
+    half = np.uint64(1) << (sh - np.uint64(1))
+    up = (rem > half) | ((rem == half) & ((q & np.uint64(1)) == np.uint64(1)))
+    q = q + up.astype(np.uint64)
+    # q is the fp16 significand (with hidden bit for normals); re-assemble (a carry bumps the exponent)
+    normal = e16 >= 1
+    eo = np.where(normal, e16, 0).astype(np.int64)
+    carry = normal & (q >= np.uint64(0x800))
+    q = np.where(carry, q >> np.uint64(1), q)
+    eo = np.where(carry, eo + 1, eo)
+    bits = np.where(normal, (eo.astype(np.uint64) << np.uint64(10)) | (q & np.uint64(0x3FF)), q)
+    bits = np.where(normal & (eo >= 31), np.uint64(0x7C00), bits)  # overflow -> inf
+    zero = exp == 0                                              # fp32 zero or subnormal -> +-0 in fp16
+    bits = np.where(zero, np.uint64(0), bits)
+    return (sign | bits).astype(np.uint16)
+
+
+def test_fp16_rounding_is_round_to_nearest_even():
+    # The oracle rounds the group step to fp16 with numpy's cast: pin that cast against an
+    # integer-only round-to-nearest-even on 2^20 random patterns spanning normals, fp16
+    # subnormals, overflow and exact ties.
+    g = np.random.default_rng(55)
+    u = g.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    e = g.integers(127 - 30, 127 + 17, size=u.shape[0]).astype(np.uint32)   # exponents around the fp16 range
+    u = (u & np.uint32(0x807FFFFF)) | (e << np.uint32(23))
+    ties = (u[: 1 << 16] & np.uint32(0xFFFFE000)) | np.uint32(0x1000)        # exactly half an fp16 ulp
+    u = np.concatenate([u, ties])
+    want = _fp16_rne_bits(u)
+    with np.errstate(over="ignore"):
+        got = u.view(np.float32).astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+    # hand cases: 1 + 2^-11 ties down to 1; 1 + 3 * 2^-11 ties up to 1 + 2^-9; 65520 overflows
+    with np.errstate(over="ignore"):
+        for v, r in [(1 + 2.0 ** -11, 1.0), (1 + 3 * 2.0 ** -11, 1 + 2.0 ** -9), (65520.0, np.inf), (2.0 ** -25, 0.0)]:
+            assert float(np.float32(v).astype(np.float16)) == r
+
+
 def test_quantizer_hand_worked_negative_and_zero_groups():
     # all-negative: lo = -3, hi = 0, same step 0.19995...; z = rint(15.0037) = 15;
     # -3 -> rint(-15.0037) + 15 = 0, -1.5 -> rint(-7.5018) + 15 = -8 + 15 = 7.
