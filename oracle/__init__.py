@@ -7,7 +7,8 @@ Parity status per function (what pins it is in the tests named here):
   channel_mean_abs   pinned: exact sums vs math.fsum, constant columns, sign flips
   scales_for_alpha   pinned: alpha = 0, a = 0, powers of two, monotonicity
   quantize_groups    pinned: brute-force nearest code, error bound, hand-worked groups,
-                     power-of-two scale covariance, code ranges
+                     power-of-two scale covariance, code ranges; the fp16 cast of the step
+                     against an integer-only round-to-nearest-even
   dequantize / effective_weight / weight_error
                      pinned: lossless on-grid construction, scaling invariance
   output_mse / output_mse_gram
