@@ -125,12 +125,13 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
   TilePlan<kPBN, S::NW, 32> wplan;
   xplan.init(x, K, m0, M, wave, lane);
   wplan.init(packed_h, K / 4, n0, N, wave, lane);
-  auto issue = [&](int64_t t) {
-    f16* st = lds + (t % STAGES) * S::STAGE;
-    const int64_t g = t < G ? t : G - 1;
-    xplan.issue(st, g * kGroup);
-    xplan.issue(st + S::A_HALF, g * kGroup + 64);
-    wplan.issue(st + 2 * S::A_HALF, g * 32);
+  const int G32 = (int)G;
+  auto issue = [&](int t, int slot) {
+    f16* st = lds + slot * S::STAGE;
+    const int g = t < G32 ? t : G32 - 1;
+    xplan.issue(st, (int64_t)g * kGroup);
+    xplan.issue(st + S::A_HALF, (int64_t)g * kGroup + 64);
+    wplan.issue(st + 2 * S::A_HALF, (int64_t)g * 32);
   };
 
   // The block's scales and zeros are two contiguous byte ranges (rows
@@ -144,7 +145,7 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
   const uint16_t* msc = reinterpret_cast<const uint16_t*>(meta);
   const uint8_t* mz = meta + soff;
 
-  for (int t = 0; t < D; ++t) issue(t);
+  for (int t = 0; t < D; ++t) issue(t, t);
 
   int mrow[S::JB];  // LDS meta row of the lane's weight rows (clamped to the block's rows)
 #pragma unroll
@@ -168,12 +169,15 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][j][r] = 0.f;
 
-  for (int64_t g = 0; g < G; ++g) {
+  int cur = 0, nxt = D;  // ring slots of stage g and of stage g + D
+  for (int g = 0; g < G32; ++g) {
     wait_vmcnt<(D - 1) * S::LOADS>();  // stage g has landed; stages g+1 .. g+D-1 may be pending
     lds_barrier();  // stage g is in LDS for every wave; stage g - 1 is no longer read
-    issue(g + D);
+    issue(g + D, nxt);
+    nxt = nxt + 1 == STAGES ? 0 : nxt + 1;
 
-    const f16* st = lds + (g % STAGES) * S::STAGE;
+    const f16* st = lds + cur * S::STAGE;
+    cur = cur + 1 == STAGES ? 0 : cur + 1;
     const f16* Ah = st + ahalf * S::A_HALF;
     const f16* Bt = st + 2 * S::A_HALF;
     u32x4 wv[S::JB][S::STEPS / 4];
