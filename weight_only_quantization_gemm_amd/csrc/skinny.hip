@@ -566,10 +566,12 @@ hipError_t launch_ring3(const void* x, const void* packed, const void* scales, c
 // 8192 at 27-46 us against 53 us, 28672 x 8192 at 81-139 us against 239 us)
 // and, with four tiles per wave in batches of two groups, on wider K = 4096
 // layers up to M = 32 (4096 x 11008 at 22-24 us against 25 us; at M = 48 the
-// GEMM takes 25.5 us against 29); elsewhere the GEMM is faster.
+// GEMM takes 25.5 us against 29) and on layers up to 12288 wide to M = 32
+// (8192 x 10240 at M = 24: 43 us against 54); elsewhere the GEMM is faster
+// (8192 x 28672 at M = 24: 84 us against 67).
 bool gemv_wide_preferred(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 || M > 64) return false;
-  return N <= 8192 || (M <= 32 && K <= 4096);
+  return N <= 8192 || (M <= 32 && (K <= 4096 || N <= 12288));
 }
 
 template <int RW, int P>
