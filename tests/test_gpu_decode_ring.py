@@ -75,6 +75,7 @@ def test_ring_determinism():
 @pytest.mark.parametrize("N,K,M", [(10240, 8192, 24), (12288, 6144, 32), (12300, 4224, 17)])
 def test_multi_row_kernel_wide_layers(N, K, M):
     """17 <= M <= 32 on layers up to 12288 wide with K above 4096 (the 70B q/k/v shape) run
-    on the register-staged multi-row kernel; checked on sampled rows and the last block."""
+    on the register-staged multi-row kernel; 12300 rows is just past that bound and takes the
+    pipelined GEMM.  Checked on sampled rows and the last block."""
     note(f"multi-row N={N} K={K} M={M}")
     _check(N, K, M, seed=N + K + M, sample=256)
