@@ -48,6 +48,7 @@ def test_ring_small_layers(N, K, M):
     (9000, 4352, 6),                    # 8192 < N < 16384: one tile, four waves
     (16400, 4480, 9),                   # N >= 16384: two tiles, four waves; 16400 = 512 * 32 + 16
     (16400, 4480, 4),                   # M <= 4: one tile, eight waves
+    (10240, 8192, 16), (12300, 8320, 9),  # K >= 8192, 8192 < N < 16384, M > 8: four tiles; 12300 = 192 * 64 + 12
 ])
 def test_ring_wide_layers_sampled_rows(N, K, M):
     note(f"ring N={N} K={K} M={M}")

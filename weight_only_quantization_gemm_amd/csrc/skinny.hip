@@ -501,7 +501,11 @@ static hipError_t ring_launch(const void* x, const void* packed, const void* sca
 // K <= 4096 (4096 x 11008 at M = 16: 11.6 us against 14.8) and on layers up
 // to 16384 wide; two tiles and four waves on wider ones (8192 x 28672 at
 // M = 16: 44 us against 58 with eight waves); two tiles and eight waves on
-// the rest (8192 x 8192, 28672 x 8192).
+// the rest (8192 x 8192, 28672 x 8192).  For M > 8 on layers 8192 < N < 16384
+// wide with K >= 8192 (the 70B q/k/v), four tiles and eight waves: x, which
+// every block reads whole, is then shared by 64 weight rows instead of 16
+// (8192 x 10240 at M = 16: 20.9 us against 22.6; at M = 8 it is slower, 18.7
+// against 17.4, with only 160 blocks).
 constexpr int kRingP = 1, kRingStages = 2;
 
 struct RingShape {
@@ -509,6 +513,7 @@ struct RingShape {
 };
 
 static RingShape ring_shape(int64_t M, int64_t N, int64_t K) {
+  if (M > 8 && K >= 8192 && N > 8192 && N < 16384) return {4, 8};
   if (M <= 4 || N <= 4096) return {1, 8};
   if (K <= 4096 || (N > 8192 && N < 16384)) return {1, 4};
   if (N >= 16384) return {2, 4};
@@ -519,6 +524,7 @@ template <int BITS, int MX>
 static bool ring_fits(const RingShape& r, int64_t K) {
   const int W = ring_waves<kRingP>(r.waves, K);
   if (r.rw == 1) return ring_lds_bytes<BITS, 1, kRingP, kRingStages, MX>(W, K) <= kLdsBytes;
+  if (r.rw == 4) return ring_lds_bytes<BITS, 4, kRingP, kRingStages, MX>(W, K) <= kLdsBytes;
   return ring_lds_bytes<BITS, 2, kRingP, kRingStages, MX>(W, K) <= kLdsBytes;
 }
 
@@ -526,6 +532,7 @@ template <int BITS, int MX>
 static hipError_t ring_dispatch(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
                                 int64_t N, int64_t K, const RingShape& r, hipStream_t st) {
   if (r.rw == 1) return ring_launch<BITS, 1, kRingP, kRingStages, MX>(x, packed, scales, zeros, y, M, N, K, r.waves, st);
+  if (r.rw == 4) return ring_launch<BITS, 4, kRingP, kRingStages, MX>(x, packed, scales, zeros, y, M, N, K, r.waves, st);
   return ring_launch<BITS, 2, kRingP, kRingStages, MX>(x, packed, scales, zeros, y, M, N, K, r.waves, st);
 }
 
