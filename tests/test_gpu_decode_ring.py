@@ -49,6 +49,8 @@ def test_ring_small_layers(N, K, M):
     (16400, 4480, 9),                   # N >= 16384: two tiles, four waves; 16400 = 512 * 32 + 16
     (16400, 4480, 4),                   # M <= 4: one tile, eight waves
     (10240, 8192, 16), (12300, 8320, 9),  # K >= 8192, 8192 < N < 16384, M > 8: four tiles; 12300 = 192 * 64 + 12
+    (16400, 8320, 13),                    # N >= 16384, K >= 8192, M > 8: four tiles, four waves
+    (22016, 4096, 16),                    # N >= 16384, K < 8192, M > 8: two tiles, four waves
 ])
 def test_ring_wide_layers_sampled_rows(N, K, M):
     note(f"ring N={N} K={K} M={M}")

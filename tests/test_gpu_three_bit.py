@@ -167,7 +167,8 @@ def test_gemm3_decode_ring(N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(8190, 4224, 8), (9000, 4352, 6), (16400, 4480, 9), (16400, 4480, 4),
-                                   (10240, 8192, 16), (12300, 8320, 11)])  # four 16-row tiles per block
+                                   (10240, 8192, 16), (12300, 8320, 11),   # four 16-row tiles per block
+                                   (16400, 8320, 12)])
 def test_gemm3_decode_ring_wide_sampled_rows(N, K, M):
     """Two tiles per wave with eight or four waves, and one tile with four, on wide layers
     with a partial last block (sampled rows, always including the last block's)."""
