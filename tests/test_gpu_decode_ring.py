@@ -51,6 +51,7 @@ def test_ring_small_layers(N, K, M):
     (10240, 8192, 16), (12300, 8320, 9),  # K >= 8192, 8192 < N < 16384, M > 8: four tiles; 12300 = 192 * 64 + 12
     (16400, 8320, 13),                    # N >= 16384, K >= 8192, M > 8: four tiles, four waves
     (22016, 4096, 16),                    # N >= 16384, K < 8192, M > 8: two tiles, four waves
+    (16400, 8320, 6), (22016, 4096, 7),   # the same for 4 < M <= 8
 ])
 def test_ring_wide_layers_sampled_rows(N, K, M):
     note(f"ring N={N} K={K} M={M}")

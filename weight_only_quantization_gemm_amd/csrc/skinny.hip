@@ -501,11 +501,12 @@ static hipError_t ring_launch(const void* x, const void* packed, const void* sca
 // K <= 4096 (4096 x 11008 at M = 16: 11.6 us against 14.8) and on layers up
 // to 16384 wide; two tiles and four waves on wider ones (8192 x 28672 at
 // M = 16: 44 us against 58 with eight waves); two tiles and eight waves on
-// the rest (8192 x 8192, 28672 x 8192).  For M > 8 every block reads all of x
-// (M rows x K), so wider blocks share it among more weight rows: on layers at
+// the rest (8192 x 8192, 28672 x 8192).  Every block reads all of x (M rows x
+// K), so for M > 4 wider blocks share it among more weight rows: on layers at
 // least 16384 wide two tiles and four waves for K < 8192 (4096 x 22016 at
-// M = 16: 18.7 us against 22.7 with one tile) and four tiles and four waves for
-// K >= 8192 (8192 x 28672: 38.0 us against 43.4); on the 70B q/k/v (8192 <
+// M = 16: 18.7 us against 22.7 with one tile; at M = 8: 15.6 against 16.9) and
+// four tiles and four waves for K >= 8192 (8192 x 28672: 38.0 us against 43.4
+// at M = 16, 35.6 against 36.2 at M = 8); for M > 8 on the 70B q/k/v (8192 <
 // N < 16384, K >= 8192) four tiles and eight waves (8192 x 10240: 20.9 us
 // against 22.6; at M = 8 that shape is slower, 18.7 against 17.4, with only
 // 160 blocks).
@@ -516,7 +517,7 @@ struct RingShape {
 };
 
 static RingShape ring_shape(int64_t M, int64_t N, int64_t K) {
-  if (M > 8 && N >= 16384) return {K >= 8192 ? 4 : 2, 4};
+  if (M > 4 && N >= 16384) return {K >= 8192 ? 4 : 2, 4};
   if (M > 8 && K >= 8192 && N > 8192) return {4, 8};
   if (M <= 4 || N <= 4096) return {1, 8};
   if (K <= 4096 || (N > 8192 && N < 16384)) return {1, 4};
