@@ -83,3 +83,16 @@ def test_multi_row_kernel_wide_layers(N, K, M):
     pipelined GEMM.  Checked on sampled rows and the last block."""
     note(f"multi-row N={N} K={K} M={M}")
     _check(N, K, M, seed=N + K + M, sample=256)
+
+
+@pytest.mark.parametrize("N,K,M", [
+    (4100, 4096, 20), (300, 640, 64),     # N <= 8192: one tile and two (M <= 32) or four x tiles; ragged blocks
+    (1000, 16640, 24), (70, 28672, 32),   # K >= 16384, M <= 32: two tiles per block
+    (11008, 4096, 32),                    # wider layer, K <= 4096, M <= 32
+    (9000, 4096, 48),                     # wider layer above M = 32: the pipelined GEMM
+])
+def test_ring_mid_m(N, K, M):
+    """17 <= M <= 64 on the ring kernel with two or four 16-row x tiles per stage (each weight
+    operand feeding that many MFMAs), on the layers where it is chosen; sampled rows on wide layers."""
+    note(f"ring mid N={N} K={K} M={M}")
+    _check(N, K, M, seed=N * 5 + K + M, sample=256 if N > 2000 else None)

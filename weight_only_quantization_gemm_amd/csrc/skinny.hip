@@ -265,7 +265,9 @@ template <int BITS, int RW, int P, int S, int MX>
 __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                    const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
                                                    f16* __restrict__ y, int M, int N32, int K32, int W) {
-  static_assert((P == 1 || P == 2) && S >= 2 && S <= 4 && MX % 4 == 0 && MX <= 16, "ring shape");
+  static_assert((P == 1 || P == 2) && S >= 2 && S <= 4 && MX % 4 == 0 && (MX <= 16 || MX % 16 == 0) && MX <= 64,
+                "ring shape");
+  constexpr int MT = MX > 16 ? MX / 16 : 1;  // 16-row x tiles; each weight operand feeds MT MFMAs
   static_assert(BITS == 4 || (BITS == 3 && P == 1), "4-bit, or 3-bit in one-group chunks");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int ROWB = 64 * P, RPI = 1024 / ROWB, SLOTS = 4 * P;
@@ -320,9 +322,11 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
     xsrc[q] = (int64_t)(r < M ? r : M - 1) * K + (piece & 15) * 8;
   }
 
-  f32x4 acc[RW];
+  f32x4 acc[RW][MT];
 #pragma unroll
-  for (int t = 0; t < RW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < RW; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto issue = [&](int j) {
     int64_t c = (int64_t)j * W + wave;
@@ -374,7 +378,9 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
   // the staged scales and zeros are read by every wave: all of this wave's loads land, then the barrier
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  const int xr = nl < MX ? nl : MX - 1;
+  int xr[MT];  // LDS x row of the lane's A operand in x tile mt (rows past MX repeat the last)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) xr[mt] = 16 * mt + nl < MX ? 16 * mt + nl : MX - 1;
   const uint32_t bias = bias_in_vgpr();
   for (int j = 0; j < T; ++j) {
     // the slot refilled here was read by the previous stage, whose LDS reads are done
@@ -400,15 +406,20 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
       const int64_t g = c * P + i;
       const bool live = g < G;
       const int gc = (int)(live ? g : G - 1);
-      f16x8 a[4];
+      f16x8 a[MT][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        a[s] = *reinterpret_cast<const f16x8*>(src + WBYTES + xr * XROWB + ((i * 16 + kq * 4 + s) ^ xr) * 16);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          a[mt][s] = *reinterpret_cast<const f16x8*>(src + WBYTES + xr[mt] * XROWB +
+                                                     ((i * 16 + kq * 4 + s) ^ (xr[mt] & 15)) * 16);
 #pragma unroll
       for (int t = 0; t < RW; ++t) {
         const int r = 16 * t + nl;
         const f16x2 zb = zero_biased((zl[r * P2 + (gc >> 1)] >> (4 * (gc & 1))) & 0xFu);
-        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 d[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) d[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (BITS == 4) {
           const u32x4 w =
               *reinterpret_cast<const u32x4*>(src + t * TILE + nl * ROWB + ((i * 4 + kq) ^ ring_swizzle<P>(nl)) * 16);
@@ -417,7 +428,8 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
             const f16x2 q0 = pair_biased(w[s], 0, bias) - zb, q1 = pair_biased(w[s], 1, bias) - zb;
             const f16x2 q2 = pair_biased(w[s], 2, bias) - zb, q3 = pair_biased(w[s], 3, bias) - zb;
             const f16x8 b = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], b, d, 0, 0, 0);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][s], b, d[mt], 0, 0, 0);
           }
         } else {
           // the three words of the lane's 32 channels (rows of 48 bytes: 16 rows on
@@ -434,33 +446,40 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
           for (int s = 0; s < 4; ++s) {
             const f16x8 b = f16x8{q[4 * s].x,     q[4 * s].y,     q[4 * s + 1].x, q[4 * s + 1].y,
                                   q[4 * s + 2].x, q[4 * s + 2].y, q[4 * s + 3].x, q[4 * s + 3].y};
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[s], b, d, 0, 0, 0);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][s], b, d[mt], 0, 0, 0);
           }
         }
         const float scf = live ? (float)sl[r * G + gc] : 0.0f;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc[t][rr] = fmaf(scf, d[rr], acc[t][rr]);
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) acc[t][mt][rr] = fmaf(scf, d[mt][rr], acc[t][mt][rr]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
   // every wave's DMA has landed (the last stage waited for all); the rings become the
-  // reduction buffer: lane holds y[m = 4*kq + r][n0 + 16t + nl]
+  // reduction buffer (W x RW x 16 MT x 16 fp32, within the rings): lane holds
+  // y[m = 16 mt + 4 kq + r][n0 + 16 t + nl]
+  constexpr int MR = 16 * MT;
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int t = 0; t < RW; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * kq + r;
-      if (m < M) red[((wave * RW + t) * 16 + m) * 16 + nl] = acc[t][r];
-    }
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * mt + 4 * kq + r;
+        if (m < M) red[((wave * RW + t) * MR + m) * 16 + nl] = acc[t][mt][r];
+      }
   __syncthreads();
   for (int i = threadIdx.x; i < RW * 16 * M; i += W * kWave) {
     const int t = i / (16 * M), rem = i - t * 16 * M, m = rem >> 4, nn = rem & 15;
     float v = 0.f;
-    for (int w = 0; w < W; ++w) v += red[((w * RW + t) * 16 + m) * 16 + nn];
+    for (int w = 0; w < W; ++w) v += red[((w * RW + t) * MR + m) * 16 + nn];
     const int64_t n = n0 + 16 * t + nn;
     if (n < N) y[(int64_t)m * N + n] = (f16)v;
   }
@@ -553,7 +572,44 @@ static hipError_t ring_run(const void* x, const void* packed, const void* scales
                            int64_t N, int64_t K, const RingShape& r, int mx, hipStream_t st) {
   if (mx == 4) return ring_dispatch<BITS, 4>(x, packed, scales, zeros, y, M, N, K, r, st);
   if (mx == 8) return ring_dispatch<BITS, 8>(x, packed, scales, zeros, y, M, N, K, r, st);
+  if (mx == 32) return ring_dispatch<BITS, 32>(x, packed, scales, zeros, y, M, N, K, r, st);
+  if (mx == 64) return ring_dispatch<BITS, 64>(x, packed, scales, zeros, y, M, N, K, r, st);
   return ring_dispatch<BITS, 16>(x, packed, scales, zeros, y, M, N, K, r, st);
+}
+
+// 17 <= M <= 64: two or four 16-row x tiles per stage, each weight operand
+// feeding that many MFMAs.  Measured against the register-staged multi-row
+// kernel and the pipelined GEMM at M = 24, 32, 48, 64 (us, ring / previous):
+// 4096 x 4096 10.4-15.6 / 16.2-26.7; 11008 x 4096 18.2-29.6 / 32.3-56.6;
+// 28672 x 8192 54-56 with two tiles per block at M <= 32 / 84-94, 109-123
+// with one above / 118-143; 4096 x 11008 19.5-20.0 / 24.7-26.3 at M <= 32,
+// but 33-38 / 28 above; 8192 x 28672 no better than the GEMM (66-135 / 67-71).
+// Waves per block: four.  {0, 0}: the layer goes to the other kernels.
+static RingShape ring_mid_shape(int64_t M, int64_t N, int64_t K) {
+  if (N <= 8192) return {K >= 16384 && M <= 32 ? 2 : 1, 4};
+  if (M <= 32 && K <= 4096) return {1, 4};
+  return {0, 0};
+}
+
+template <int BITS>
+static bool ring_mid_select(int64_t M, int64_t K, const RingShape& r, int* mx) {
+  if (M <= 16 || M > 64) return false;
+  *mx = M <= 32 ? 32 : 64;
+  return *mx == 32 ? ring_fits<BITS, 32>(r, K) : ring_fits<BITS, 64>(r, K);
+}
+
+bool ring_mid_supported(int64_t M, int64_t N, int64_t K) {
+  const RingShape r = ring_mid_shape(M, N, K);
+  int mx;
+  return r.rw != 0 && ring_mid_select<4>(M, K, r, &mx);
+}
+
+hipError_t launch_ring_mid(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                           int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const RingShape r = ring_mid_shape(M, N, K);
+  int mx;
+  if (r.rw == 0 || !ring_mid_select<4>(M, K, r, &mx)) return hipErrorInvalidValue;
+  return ring_run<4>(x, packed, scales, zeros, y, M, N, K, r, mx, st);
 }
 
 // 3-bit codes, 2 <= M <= 16: the ring kernel with rows of 48 bytes, tile and
