@@ -238,7 +238,7 @@ int awq_gemm(const void* x, const void* packed, const void* scales, const void* 
 /* awq_gemm on the format written at `bits` = 4 (awq_gemm itself) or 3.  At 3
  * bits: M = 1, and M = 2 with K < 16384, run the vector-ALU GEMV with the
  * arithmetic stated above (every product exact in fp32, zero point as
- * zero * sum(x)); other M <= 16 the matrix-core decode kernel and M > 16 the
+ * zero * sum(x)); other M <= 64 the matrix-core decode kernel and M > 64 the
  * general-shape matrix-core kernel, both on exact (code - zero) with the group
  * scale applied in fp32.  Requires bits == 4 or 3 and M <= 65535 * 64 at 3
  * bits. */

@@ -179,3 +179,18 @@ def test_gemm3_decode_ring_wide_sampled_rows(N, K, M):
     g = np.random.default_rng(N + M)
     rows = np.union1d(g.choice(N, size=256, replace=False), np.arange(N - 40, N))
     assert_y_close(y[:, rows], oracle.gemm(x, q[rows], z[rows], sc[rows]), f"N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(300, 640, 40), (1000, 16640, 24), (4100, 4096, 64), (11008, 4096, 20),
+                                   (9000, 4224, 50)])
+def test_gemm3_ring_mid_m(N, K, M):
+    """17 <= M <= 64 at 3 bits on the ring kernel with two or four x tiles per stage."""
+    note(f"gemm3 ring mid N={N} K={K} M={M}")
+    q, z, sc, p, scd, zd = _random_packed3(N, K, seed=N + K + M)
+    x = activations_fp16(M, K, seed=N + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd, bits=3))
+    if N > 2000:
+        rows = np.union1d(np.random.default_rng(M).choice(N, size=256, replace=False), np.arange(N - 40, N))
+        assert_y_close(y[:, rows], oracle.gemm(x, q[rows], z[rows], sc[rows]), f"N={N} K={K} M={M}")
+    else:
+        assert_y_close(y, oracle.gemm(x, q, z, sc), f"N={N} K={K} M={M}")

@@ -62,9 +62,9 @@ hipError_t launch_gemv_dot2_scaled(const void* x, const float* inv_s, const void
 hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st);
 bool ring3_supported(int64_t M, int64_t N, int64_t K);
-bool ring_mid_supported(int64_t M, int64_t N, int64_t K);  // 17 <= M <= 64 on the ring kernel
+bool ring_mid_supported(int64_t M, int64_t N, int64_t K, int bits);  // 17 <= M <= 64 on the ring kernel
 hipError_t launch_ring_mid(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                           int64_t M, int64_t N, int64_t K, hipStream_t st);
+                           int64_t M, int64_t N, int64_t K, int bits, hipStream_t st);
 hipError_t launch_ring3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                         int64_t M, int64_t N, int64_t K, hipStream_t st);
 bool gemv_wide_preferred(int64_t M, int64_t N, int64_t K);

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const f16* __restrict__ x, co
 
 hipError_t launch_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
                        int64_t N, int64_t K, hipStream_t st) {
-  if (ring_mid_supported(M, N, K)) return launch_ring_mid(x, packed, scales, zeros, y, M, N, K, st);
+  if (ring_mid_supported(M, N, K, 4)) return launch_ring_mid(x, packed, scales, zeros, y, M, N, K, 4, st);
   if (gemv_wide_preferred(M, N, K)) return launch_gemv_wide(x, packed, scales, zeros, y, M, N, K, st);
   if (gemm_pipe_supported(M, N, K)) return launch_gemm_pipe(x, packed, scales, zeros, y, M, N, K, st);
   if ((M + kBM - 1) / kBM > 65535) return hipErrorInvalidValue;  // grid.y limit
@@ -145,6 +145,7 @@ hipError_t launch_gemm3(const void* x, const void* packed, const void* scales, c
                         int64_t N, int64_t K, hipStream_t st) {
   if (gemv3_supported(M, K)) return launch_gemv3(x, packed, scales, zeros, y, M, N, K, st);
   if (ring3_supported(M, N, K)) return launch_ring3(x, packed, scales, zeros, y, M, N, K, st);
+  if (ring_mid_supported(M, N, K, 3)) return launch_ring_mid(x, packed, scales, zeros, y, M, N, K, 3, st);
   if ((M + kBM - 1) / kBM > 65535) return hipErrorInvalidValue;  // grid.y limit
   dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
   gemm_kernel<3><<<grid, dim3(256), 0, st>>>(reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),

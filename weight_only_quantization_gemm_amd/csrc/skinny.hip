@@ -598,17 +598,32 @@ static bool ring_mid_select(int64_t M, int64_t K, const RingShape& r, int* mx) {
   return *mx == 32 ? ring_fits<BITS, 32>(r, K) : ring_fits<BITS, 64>(r, K);
 }
 
-bool ring_mid_supported(int64_t M, int64_t N, int64_t K) {
+// At 3 bits the alternative for M > 16 is the general-shape kernel (2-6x
+// slower than the ring where both run: 28672 x 8192 at M = 24, 53 against
+// 286 us), so the ring takes every layer there.
+static RingShape ring_mid_shape_bits(int64_t M, int64_t N, int64_t K, int bits) {
   const RingShape r = ring_mid_shape(M, N, K);
+  if (r.rw == 0 && bits == 3) return {1, 4};
+  return r;
+}
+
+bool ring_mid_supported(int64_t M, int64_t N, int64_t K, int bits) {
+  const RingShape r = ring_mid_shape_bits(M, N, K, bits);
   int mx;
-  return r.rw != 0 && ring_mid_select<4>(M, K, r, &mx);
+  if (r.rw == 0) return false;
+  return bits == 3 ? ring_mid_select<3>(M, K, r, &mx) : ring_mid_select<4>(M, K, r, &mx);
 }
 
 hipError_t launch_ring_mid(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                           int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const RingShape r = ring_mid_shape(M, N, K);
+                           int64_t M, int64_t N, int64_t K, int bits, hipStream_t st) {
+  const RingShape r = ring_mid_shape_bits(M, N, K, bits);
   int mx;
-  if (r.rw == 0 || !ring_mid_select<4>(M, K, r, &mx)) return hipErrorInvalidValue;
+  if (r.rw == 0) return hipErrorInvalidValue;
+  if (bits == 3) {
+    if (!ring_mid_select<3>(M, K, r, &mx)) return hipErrorInvalidValue;
+    return ring_run<3>(x, packed, scales, zeros, y, M, N, K, r, mx, st);
+  }
+  if (!ring_mid_select<4>(M, K, r, &mx)) return hipErrorInvalidValue;
   return ring_run<4>(x, packed, scales, zeros, y, M, N, K, r, mx, st);
 }
 
