@@ -90,6 +90,7 @@ def test_multi_row_kernel_wide_layers(N, K, M):
     (1000, 16640, 24), (70, 28672, 32),   # K >= 16384, M <= 32: two tiles per block
     (11008, 4096, 32),                    # wider layer, K <= 4096, M <= 32
     (9000, 4096, 48),                     # wider layer above M = 32: the pipelined GEMM
+    (100, 139264, 40),                    # K so long the block's scales leave the ring no LDS: fallback kernel
 ])
 def test_ring_mid_m(N, K, M):
     """17 <= M <= 64 on the ring kernel with two or four 16-row x tiles per stage (each weight
