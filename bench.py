@@ -293,8 +293,9 @@ def run_sweep(args, torch, awq, dev):
 
 
 def run_sweep3(args, torch, awq, dev):
-    """The same (K=4096, N=11008) layer with 3-bit codes at M = 1..64 (decode batch sizes, and
-    M = 64 on the matrix-core ring kernel with four x tiles per stage)."""
+    """The same (K=4096, N=11008) layer with 3-bit codes at M = 1..1024 (decode batch sizes, and
+    M = 64 on the matrix-core ring kernel with four x tiles per stage) and prefill sizes 256 and 1024
+    on the pipelined matrix-core GEMM."""
     from gen import activations_fp16, normal_fp16
     K, N = 4096, 11008
     W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=3001)).to(dev)
@@ -303,7 +304,7 @@ def run_sweep3(args, torch, awq, dev):
     copies = 64  # 64 x 17.6 MB > 1 GiB
     packs = [base] + [tuple(t.clone() for t in base) for _ in range(copies - 1)]
     out = {}
-    for M in (1, 2, 4, 8, 16, 64):
+    for M in (1, 2, 4, 8, 16, 64, 256, 1024):
         x = torch.from_numpy(activations_fp16(M, K, seed=3100 + M)).to(dev)
         y = torch.empty((M, N), dtype=torch.float16, device=dev)
 
@@ -317,7 +318,7 @@ def run_sweep3(args, torch, awq, dev):
         out[str(M)] = dict(us=round(us, 3), GBs=round(nbytes / us / 1e3, 1),
                            hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                            TFLOPs=round(2.0 * M * N * K / us / 1e6, 2),
-                           kernel="gemv3_dot2" if M <= 2 else "ring_mfma")
+                           kernel="gemv3_dot2" if M <= 2 else "ring_mfma" if M <= 64 else "gemm_pipe_mfma")
     del packs
     return out
 
@@ -623,7 +624,7 @@ def main():
         m256 = legs["batch_sweep_4096x11008"]["256"]
         legs["gemm_m256_4096x11008"] = dict(TFLOPs=m256["TFLOPs"], mfma_frac=m256["mfma_frac"], us=m256["us"])
         torch.cuda.empty_cache()
-        log("sweep: (4096, 11008) with 3-bit codes at M = 1..64")
+        log("sweep: (4096, 11008) with 3-bit codes at M = 1..1024")
         legs["batch_sweep_4096x11008_3bit"] = run_sweep3(args, torch, awq, dev)
         torch.cuda.empty_cache()
         log("70B layers: q/k/v, o, gate, up, down at M = 1, 8, 16")

@@ -238,10 +238,12 @@ int awq_gemm(const void* x, const void* packed, const void* scales, const void* 
 /* awq_gemm on the format written at `bits` = 4 (awq_gemm itself) or 3.  At 3
  * bits: M = 1, and M = 2 with K < 16384, run the vector-ALU GEMV with the
  * arithmetic stated above (every product exact in fp32, zero point as
- * zero * sum(x)); other M <= 64 the matrix-core decode kernel and M > 64 the
- * general-shape matrix-core kernel, both on exact (code - zero) with the group
- * scale applied in fp32.  Requires bits == 4 or 3 and M <= 65535 * 64 at 3
- * bits. */
+ * zero * sum(x)); other M <= 64 the matrix-core decode kernel on exact
+ * (code - zero) with the group scale applied in fp32; M > 64 the pipelined
+ * matrix-core GEMM with the 4-bit arithmetic above (the dequantized weight
+ * rounded once to fp16), or, where the block's scales do not fit its LDS, the
+ * general-shape kernel on exact (code - zero).  Requires bits == 4 or 3 and
+ * M <= 65535 * 64 at 3 bits. */
 int awq_gemm_bits(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                   int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* stream);
 

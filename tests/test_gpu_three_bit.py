@@ -194,3 +194,20 @@ def test_gemm3_ring_mid_m(N, K, M):
         assert_y_close(y[:, rows], oracle.gemm(x, q[rows], z[rows], sc[rows]), f"N={N} K={K} M={M}")
     else:
         assert_y_close(y, oracle.gemm(x, q, z, sc), f"N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(11008, 4096, 256), (4096, 11008, 100), (1000, 4224, 130), (300, 1024, 1000),
+                                   (64, 139264, 70)])
+def test_gemm3_pipelined_large_m(N, K, M):
+    """M > 64 at 3 bits on the pipelined matrix-core GEMM (64- and 128-row tiles, ragged row and
+    column blocks, 33 groups); on K = 139264 the block's scales no longer fit beside the
+    pipeline and the general-shape kernel runs.  Sampled rows on wide layers."""
+    note(f"gemm3 pipe N={N} K={K} M={M}")
+    q, z, sc, p, scd, zd = _random_packed3(N, K, seed=N + K + M)
+    x = activations_fp16(M, K, seed=N + 2 * M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd, bits=3))
+    if N > 2000:
+        rows = np.union1d(np.random.default_rng(M).choice(N, size=256, replace=False), np.arange(N - 40, N))
+        assert_y_close(y[:, rows], oracle.gemm(x, q[rows], z[rows], sc[rows]), f"N={N} K={K} M={M}")
+    else:
+        assert_y_close(y, oracle.gemm(x, q, z, sc), f"N={N} K={K} M={M}")

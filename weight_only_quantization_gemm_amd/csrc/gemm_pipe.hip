@@ -94,7 +94,12 @@ __device__ __forceinline__ void dma_blob(unsigned char* dst, const unsigned char
 // 64i .. 64i + 63 of every group (lane half h: channels 64i + 32h + 8s,
 // s = 0..3); the two sets' fp32 partials are summed through LDS at the end,
 // in a fixed order.  WN: waves of a set along N (2: 2 x 2, 4: 1 x 4).
-template <int BM, int STAGES, int LDS_BYTES, int KS, int WN>
+// BITS = 3: the packed tile holds each row's 48 bytes of the group (three words
+// per 32 channels) back to back, 6 KB of the 8 KB tile, moved as 16-byte pieces
+// (the spare lanes of the last instructions copy the last piece into the
+// padding, so every wave issues as many loads as at 4 bits); a lane reads the
+// three words of its 32-channel chunk and unpacks all 16 channel pairs at once.
+template <int BM, int STAGES, int LDS_BYTES, int KS, int WN, int BITS = 4>
 __global__ __launch_bounds__(256 * KS)
 __attribute__((amdgpu_waves_per_eu(KS * 163840 / LDS_BYTES, KS * 163840 / LDS_BYTES)))
 void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed, const f16* __restrict__ scales,
@@ -124,14 +129,36 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
   TilePlan<BM, S::NW, 64> xplan;
   TilePlan<kPBN, S::NW, 32> wplan;
   xplan.init(x, K, m0, M, wave, lane);
-  wplan.init(packed_h, K / 4, n0, N, wave, lane);
+  constexpr int WPER = kPBN / 16 / S::NW;  // packed-tile loads per wave per stage
+  const unsigned char* w3src[WPER];
+  if constexpr (BITS == 4) {
+    wplan.init(packed_h, K / 4, n0, N, wave, lane);
+  } else {
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int jj = 0; jj < WPER; ++jj) {
+      int c = (wu * WPER + jj) * 64 + lane;  // 16-byte piece of the tile
+      c = c < kPBN * 3 ? c : kPBN * 3 - 1;
+      int64_t n = n0 + c / 3;
+      n = n < N ? n : N - 1;
+      w3src[jj] = reinterpret_cast<const unsigned char*>(packed) + n * (K / 32 * 12) + (c % 3) * 16;
+    }
+  }
   const int G32 = (int)G;
   auto issue = [&](int t, int slot) {
     f16* st = lds + slot * S::STAGE;
     const int g = t < G32 ? t : G32 - 1;
     xplan.issue(st, (int64_t)g * kGroup);
     xplan.issue(st + S::A_HALF, (int64_t)g * kGroup + 64);
-    wplan.issue(st + 2 * S::A_HALF, (int64_t)g * 32);
+    if constexpr (BITS == 4) {
+      wplan.issue(st + 2 * S::A_HALF, (int64_t)g * 32);
+    } else {
+      const int wu = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+      for (int jj = 0; jj < WPER; ++jj)
+        __builtin_amdgcn_global_load_lds((global_ptr_t)(w3src[jj] + (int64_t)g * 48),
+                                         (lds_ptr_t)(st + 2 * S::A_HALF + (wu * WPER + jj) * 512), 16, 0, 0);
+    }
   };
 
   // The block's scales and zeros are two contiguous byte ranges (rows
@@ -185,10 +212,16 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
 #pragma unroll
     for (int j = 0; j < S::JB; ++j) {
       const int row = wn * S::TN + j * 32 + l32;
-      const int sw = (row >> 2) & 3;  // the tile's chunk swizzle (as frag32)
 #pragma unroll
-      for (int q = 0; q < S::STEPS / 4; ++q)
-        wv[j][q] = *reinterpret_cast<const u32x4*>(Bt + row * 32 + (((bchunk + q) ^ sw) << 3));
+      for (int q = 0; q < S::STEPS / 4; ++q) {
+        if constexpr (BITS == 4) {
+          const int sw = (row >> 2) & 3;  // the tile's chunk swizzle (as frag32)
+          wv[j][q] = *reinterpret_cast<const u32x4*>(Bt + row * 32 + (((bchunk + q) ^ sw) << 3));
+        } else {  // the chunk's three words (row stride 48 bytes)
+          const uint32_t* wp = reinterpret_cast<const uint32_t*>(Bt) + row * 12 + (bchunk + q) * 3;
+          wv[j][q] = u32x4{wp[0], wp[1], wp[2], 0u};
+        }
+      }
       zb[j] = zero_biased((mz[mrow[j] * P2 + (g >> 1)] >> (4 * (g & 1))) & 0xFu);
       const uint32_t sbits = msc[mrow[j] * G + g];
       sc2[j] = as_f16x2(sbits | (sbits << 16));
@@ -199,6 +232,20 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     auto unpack = [&](int st_, f16x8(&bq)[S::JB]) {
 #pragma unroll
       for (int j = 0; j < S::JB; ++j) {
+        if constexpr (BITS == 3) {  // pairs 4 (st_ % 4) .. + 3 of chunk st_ / 4
+          const u32x4 w = wv[j][st_ >> 2];
+          f16x2 q[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int pp = 4 * (st_ & 3) + u;
+            const uint32_t bits =
+                pp < 15 ? ((w[pp / 5] >> (3 * (pp % 5))) & 0x00070007u)
+                        : (((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) | ((w[2] >> 13) & 0x00040004u));
+            q[u] = (as_f16x2(bits | magic) - zb[j]) * sc2[j];
+          }
+          bq[j] = f16x8{q[0].x, q[0].y, q[1].x, q[1].y, q[2].x, q[2].y, q[3].x, q[3].y};
+          continue;
+        }
         const uint32_t word = wv[j][st_ >> 2][st_ & 3];
         const f16x2 q0 = (as_f16x2((word & 0x000F000Fu) | magic) - zb[j]) * sc2[j];
         const f16x2 q1 = (as_f16x2(((word >> 4) & 0x000F000Fu) | magic) - zb[j]) * sc2[j];
@@ -266,12 +313,12 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     }
 }
 
-template <int BM, int STAGES, int LDS_BYTES, int KS, int WN>
+template <int BM, int STAGES, int LDS_BYTES, int KS, int WN, int BITS = 4>
 static hipError_t pipe_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                               int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int mt = (int)((M + BM - 1) / BM), nt = (int)((N + kPBN - 1) / kPBN);
   const int64_t blocks = (int64_t)((nt + kXcds - 1) / kXcds) * kXcds * mt;
-  gemm_pipe_kernel<BM, STAGES, LDS_BYTES, KS, WN><<<dim3((unsigned)blocks), dim3(256 * KS), 0, st>>>(
+  gemm_pipe_kernel<BM, STAGES, LDS_BYTES, KS, WN, BITS><<<dim3((unsigned)blocks), dim3(256 * KS), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),
       reinterpret_cast<const f16*>(scales), reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), M, N,
       K, mt, nt);
@@ -337,6 +384,26 @@ hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scale
     return pipe_launch<64, 2, kLdsBytes / 2, 1, 2>(x, packed, scales, zeros, y, M, N, K, st);
   if (pipe_fits<64, 3, kLdsBytes>(G)) return pipe_launch<64, 3, kLdsBytes, 1, 2>(x, packed, scales, zeros, y, M, N, K, st);
   return hipErrorInvalidValue;
+}
+
+// 3-bit codes, M > 64: the same tiles and rules with the 3-bit packed tile.
+bool gemm_pipe3_supported(int64_t M, int64_t N, int64_t K) {
+  const int64_t G = K / kGroup;
+  if (M <= 64) return false;
+  if (!pipe_rows64(M, N, G)) return pipe_fits<128, 3, kLdsBytes>(G);
+  return pipe_fits<64, 4, kLdsBytes>(G);
+}
+
+hipError_t launch_gemm_pipe3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                             int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t G = K / kGroup;
+  if (M <= 64) return hipErrorInvalidValue;
+  if (!pipe_rows64(M, N, G)) {
+    if (!pipe_fits<128, 3, kLdsBytes>(G)) return hipErrorInvalidValue;
+    return pipe_launch<128, 3, kLdsBytes, AWQ_PIPE_KS, AWQ_PIPE_WN, 3>(x, packed, scales, zeros, y, M, N, K, st);
+  }
+  if (!pipe_fits<64, 4, kLdsBytes>(G)) return hipErrorInvalidValue;
+  return pipe_launch<64, 4, kLdsBytes, 2, 4, 3>(x, packed, scales, zeros, y, M, N, K, st);
 }
 
 }  // namespace awq
