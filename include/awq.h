@@ -239,7 +239,8 @@ int awq_gemm(const void* x, const void* packed, const void* scales, const void* 
  * bits: M = 1, and M = 2 with K < 16384, run the vector-ALU GEMV with the
  * arithmetic stated above (every product exact in fp32, zero point as
  * zero * sum(x)); other M <= 64 the matrix-core decode kernel on exact
- * (code - zero) with the group scale applied in fp32; M > 64 the pipelined
+ * (code - zero) with the group scale applied in fp32; M > 64, and M > 32 on
+ * layers wider than 12288 rows or with K <= 4096 (N > 8192), the pipelined
  * matrix-core GEMM with the 4-bit arithmetic above (the dequantized weight
  * rounded once to fp16), or, where the block's scales do not fit its LDS, the
  * general-shape kernel on exact (code - zero).  Requires bits == 4 or 3 and

@@ -182,9 +182,10 @@ def test_gemm3_decode_ring_wide_sampled_rows(N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(300, 640, 40), (1000, 16640, 24), (4100, 4096, 64), (11008, 4096, 20),
-                                   (9000, 4224, 50)])
+                                   (10240, 8192, 24), (10240, 8192, 48), (9000, 4224, 50)])
 def test_gemm3_ring_mid_m(N, K, M):
-    """17 <= M <= 64 at 3 bits on the ring kernel with two or four x tiles per stage."""
+    """17 <= M <= 64 at 3 bits on the ring kernel with two or four x tiles per stage (10240 x
+    8192 and 9000 x 4224 take its fallback layout, where the 4-bit product takes other kernels)."""
     note(f"gemm3 ring mid N={N} K={K} M={M}")
     q, z, sc, p, scd, zd = _random_packed3(N, K, seed=N + K + M)
     x = activations_fp16(M, K, seed=N + M)
@@ -197,11 +198,12 @@ def test_gemm3_ring_mid_m(N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(11008, 4096, 256), (4096, 11008, 100), (1000, 4224, 130), (300, 1024, 1000),
-                                   (64, 139264, 70)])
+                                   (64, 139264, 70), (11008, 4096, 64), (28672, 8192, 48), (12300, 4224, 50)])
 def test_gemm3_pipelined_large_m(N, K, M):
     """M > 64 at 3 bits on the pipelined matrix-core GEMM (64- and 128-row tiles, ragged row and
-    column blocks, 33 groups); on K = 139264 the block's scales no longer fit beside the
-    pipeline and the general-shape kernel runs.  Sampled rows on wide layers."""
+    column blocks, 33 groups), and 32 < M <= 64 on the widest layers or short K, where the
+    ring has no layout of its own; on K = 139264 the block's scales no longer fit beside the pipeline and the
+    general-shape kernel runs.  Sampled rows on wide layers."""
     note(f"gemm3 pipe N={N} K={K} M={M}")
     q, z, sc, p, scd, zd = _random_packed3(N, K, seed=N + K + M)
     x = activations_fp16(M, K, seed=N + 2 * M)

@@ -73,7 +73,8 @@ hipError_t launch_gemv_wide(const void* x, const void* packed, const void* scale
 hipError_t launch_gemv(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                        int64_t M, int64_t N, int64_t K, hipStream_t st);
 bool gemm_pipe_supported(int64_t M, int64_t N, int64_t K);
-bool gemm_pipe3_supported(int64_t M, int64_t N, int64_t K);  // 3-bit codes, M > 64
+bool gemm_pipe3_supported(int64_t M, int64_t N, int64_t K);  // 3-bit codes, M > 16
+bool ring_mid_pipe_preferred(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_pipe3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                              int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scales, const void* zeros, void* y,

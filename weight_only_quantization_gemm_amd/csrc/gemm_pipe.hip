@@ -386,10 +386,10 @@ hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scale
   return hipErrorInvalidValue;
 }
 
-// 3-bit codes, M > 64: the same tiles and rules with the 3-bit packed tile.
+// 3-bit codes, M > 16: the same tiles and rules with the 3-bit packed tile.
 bool gemm_pipe3_supported(int64_t M, int64_t N, int64_t K) {
   const int64_t G = K / kGroup;
-  if (M <= 64) return false;
+  if (M <= 16) return false;
   if (!pipe_rows64(M, N, G)) return pipe_fits<128, 3, kLdsBytes>(G);
   return pipe_fits<64, 4, kLdsBytes>(G);
 }
@@ -397,7 +397,7 @@ bool gemm_pipe3_supported(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_pipe3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                              int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t G = K / kGroup;
-  if (M <= 64) return hipErrorInvalidValue;
+  if (M <= 16) return hipErrorInvalidValue;
   if (!pipe_rows64(M, N, G)) {
     if (!pipe_fits<128, 3, kLdsBytes>(G)) return hipErrorInvalidValue;
     return pipe_launch<128, 3, kLdsBytes, AWQ_PIPE_KS, AWQ_PIPE_WN, 3>(x, packed, scales, zeros, y, M, N, K, st);

@@ -607,6 +607,15 @@ static RingShape ring_mid_shape_bits(int64_t M, int64_t N, int64_t K, int bits) 
   return r;
 }
 
+// 3-bit codes, 32 < M <= 64 on a layer with no ring layout of its own: the
+// pipelined GEMM where the layer is very wide or K is short (8192 x 28672 at
+// M = 64: 71 against 135 us on the fallback ring layout; 4096 x 11008: 31
+// against 38), the ring elsewhere (8192 x 10240 at M = 48: 55 against 60 us on
+// the pipelined GEMM, and about even at M <= 32).
+bool ring_mid_pipe_preferred(int64_t M, int64_t N, int64_t K) {
+  return M > 32 && M <= 64 && ring_mid_shape(M, N, K).rw == 0 && (N > 12288 || K <= 4096);
+}
+
 bool ring_mid_supported(int64_t M, int64_t N, int64_t K, int bits) {
   const RingShape r = ring_mid_shape_bits(M, N, K, bits);
   int mx;
