@@ -58,7 +58,7 @@ def test_scale_input_bits(M, K):
     (1, 11008, 4096, 4), (2, 4100, 4096, 4),                                           # larger: two launches
     (2, 300, 16384, 4),                                                                # M = 2, long rows
     (3, 700, 1024, 4), (16, 257, 2048, 4), (100, 300, 1024, 4),                        # workspace path
-    (1, 600, 4096, 3), (7, 300, 1024, 3),                                              # 3-bit
+    (1, 600, 4096, 3), (7, 300, 1024, 3), (100, 300, 1024, 3),                         # 3-bit
 ])
 def test_gemm_scaled_parity(M, N, K, bits):
     note(f"gemm scaled M={M} N={N} K={K} bits={bits}")
