@@ -185,7 +185,8 @@ def test_gemm3_decode_ring_wide_sampled_rows(N, K, M):
                                    (10240, 8192, 24), (10240, 8192, 48), (9000, 4224, 50)])
 def test_gemm3_ring_mid_m(N, K, M):
     """17 <= M <= 64 at 3 bits on the ring kernel with two or four x tiles per stage (10240 x
-    8192 and 9000 x 4224 take its fallback layout, where the 4-bit product takes other kernels)."""
+    8192 and 9000 x 4224 take its fallback layout, where the 4-bit product takes other kernels:
+    one weight tile per block at M <= 32, two above)."""
     note(f"gemm3 ring mid N={N} K={K} M={M}")
     q, z, sc, p, scd, zd = _random_packed3(N, K, seed=N + K + M)
     x = activations_fp16(M, K, seed=N + M)

@@ -600,10 +600,14 @@ static bool ring_mid_select(int64_t M, int64_t K, const RingShape& r, int* mx) {
 
 // At 3 bits the alternative for M > 16 is the general-shape kernel (2-6x
 // slower than the ring where both run: 28672 x 8192 at M = 24, 53 against
-// 286 us), so the ring takes every layer there.
+// 286 us), so the ring takes every layer there that the 3-bit pipelined GEMM
+// does not.
 static RingShape ring_mid_shape_bits(int64_t M, int64_t N, int64_t K, int bits) {
   const RingShape r = ring_mid_shape(M, N, K);
-  if (r.rw == 0 && bits == 3) return {1, 4};
+  if (r.rw == 0 && bits == 3) {  // two weight tiles per block above M = 32 (8192 x 10240 at M = 64: 51 against 58 us)
+    const RingShape r2{2, 4};
+    return M > 32 && ring_fits<3, 64>(r2, K) ? r2 : RingShape{1, 4};
+  }
   return r;
 }
 
