@@ -76,11 +76,13 @@ def test_ring_determinism():
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), M
 
 
-@pytest.mark.parametrize("N,K,M", [(10240, 8192, 24), (12288, 6144, 32), (12300, 4224, 17)])
-def test_multi_row_kernel_wide_layers(N, K, M):
-    """17 <= M <= 32 on layers up to 12288 wide with K above 4096 (the 70B q/k/v shape) run
-    on the register-staged multi-row kernel; 12300 rows is just past that bound and takes the
-    pipelined GEMM.  Checked on sampled rows and the last block."""
+@pytest.mark.parametrize("N,K,M", [(10240, 8192, 24), (12288, 6144, 32), (10240, 8192, 48), (12300, 4224, 17),
+                                   (12288, 6144, 48)])
+def test_ring_wide_layers_long_k(N, K, M):
+    """17 <= M <= 64 on layers up to 12288 wide with K above 4096 (the 70B q/k/v shape) run
+    on the ring with one weight tile per block up to M = 32 and two above; 12300 rows is just
+    past that bound and takes the pipelined GEMM, as does K = 6144 above M = 32.  Checked on
+    sampled rows and the last block."""
     note(f"multi-row N={N} K={K} M={M}")
     _check(N, K, M, seed=N + K + M, sample=256)
 

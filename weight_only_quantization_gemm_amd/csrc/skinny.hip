@@ -583,11 +583,15 @@ static hipError_t ring_run(const void* x, const void* packed, const void* scales
 // 4096 x 4096 10.4-15.6 / 16.2-26.7; 11008 x 4096 18.2-29.6 / 32.3-56.6;
 // 28672 x 8192 54-56 with two tiles per block at M <= 32 / 84-94, 109-123
 // with one above / 118-143; 4096 x 11008 19.5-20.0 / 24.7-26.3 at M <= 32,
-// but 33-38 / 28 above; 8192 x 28672 no better than the GEMM (66-135 / 67-71).
+// but 33-38 / 28 above; 8192 x 28672 no better than the GEMM (66-135 / 67-71);
+// 8192 x 10240 and 8192 x 12288 29.8-33.3 / 41.9-47.5 at M = 20-32 with one
+// tile per block, 50.2-53.7 / 56.7-57.9 above with two; 6144 x 12288 26.2-27.2
+// / 31.9-35.6 at M = 24-32, but 42.6-44.7 / 36.1-36.6 above.
 // Waves per block: four.  {0, 0}: the layer goes to the other kernels.
 static RingShape ring_mid_shape(int64_t M, int64_t N, int64_t K) {
   if (N <= 8192) return {K >= 16384 && M <= 32 ? 2 : 1, 4};
   if (M <= 32 && K <= 4096) return {1, 4};
+  if (N <= 12288 && (M <= 32 ? K > 4096 : K >= 8192)) return {M > 32 ? 2 : 1, 4};
   return {0, 0};
 }
 
@@ -604,7 +608,7 @@ static bool ring_mid_select(int64_t M, int64_t K, const RingShape& r, int* mx) {
 // does not.
 static RingShape ring_mid_shape_bits(int64_t M, int64_t N, int64_t K, int bits) {
   const RingShape r = ring_mid_shape(M, N, K);
-  if (r.rw == 0 && bits == 3) {  // two weight tiles per block above M = 32 (8192 x 10240 at M = 64: 51 against 58 us)
+  if (r.rw == 0 && bits == 3) {  // two weight tiles per block above M = 32, as on 8192 x 10240
     const RingShape r2{2, 4};
     return M > 32 && ring_fits<3, 64>(r2, K) ? r2 : RingShape{1, 4};
   }
