@@ -223,8 +223,8 @@ int awq_quantize_shared(const void* W, const void* X, int64_t N, int64_t K, int6
  * zero point enters once per 32 codes as zero * sum(x) (so y is 0 only up to
  * fp32 rounding when every code equals its zero).  Other M <= 16, and
  * 17 <= M <= 64 on the layer shapes the matrix-core decode kernels serve
- * (N <= 8192; N <= 12288 with K > 4096, K >= 8192 above M = 32; K <= 4096 up
- * to M = 32): matrix-core kernels on (code - zero), exact in fp16, with fp32 sums per
+ * (N <= 8192; N <= 12288 with K > 4096, K >= 8192 above M = 32; K <= 4096 or
+ * K >= 8192 up to M = 32): matrix-core kernels on (code - zero), exact in fp16, with fp32 sums per
  * 128-channel group and the group scale applied in fp32, so no dequantized
  * weight is rounded.  Other
  * M >= 17: the pipelined matrix-core GEMM multiplies the dequantized weight

@@ -77,11 +77,12 @@ def test_ring_determinism():
 
 
 @pytest.mark.parametrize("N,K,M", [(10240, 8192, 24), (12288, 6144, 32), (10240, 8192, 48), (12300, 4224, 17),
-                                   (12288, 6144, 48)])
+                                   (12288, 6144, 48), (16400, 8320, 24), (28672, 8192, 32)])
 def test_ring_wide_layers_long_k(N, K, M):
     """17 <= M <= 64 on layers up to 12288 wide with K above 4096 (the 70B q/k/v shape) run
     on the ring with one weight tile per block up to M = 32 and two above; 12300 rows is just
-    past that bound and takes the pipelined GEMM, as does K = 6144 above M = 32.  Checked on
+    past that bound and takes the pipelined GEMM, as does K = 6144 above M = 32.  Wider layers
+    with K >= 8192 (the 70B gate/up) take four tiles per block up to M = 32.  Checked on
     sampled rows and the last block."""
     note(f"multi-row N={N} K={K} M={M}")
     _check(N, K, M, seed=N + K + M, sample=256)

@@ -182,7 +182,7 @@ def test_gemm3_decode_ring_wide_sampled_rows(N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(300, 640, 40), (1000, 16640, 24), (4100, 4096, 64), (11008, 4096, 20),
-                                   (10240, 8192, 24), (10240, 8192, 48), (9000, 4224, 50)])
+                                   (10240, 8192, 24), (10240, 8192, 48), (9000, 4224, 50), (16400, 8320, 24)])
 def test_gemm3_ring_mid_m(N, K, M):
     """17 <= M <= 64 at 3 bits on the ring kernel with two or four x tiles per stage (10240 x
     8192 and 9000 x 4224 take its fallback layout, where the 4-bit product takes other kernels:

@@ -586,12 +586,15 @@ static hipError_t ring_run(const void* x, const void* packed, const void* scales
 // but 33-38 / 28 above; 8192 x 28672 no better than the GEMM (66-135 / 67-71);
 // 8192 x 10240 and 8192 x 12288 29.8-33.3 / 41.9-47.5 at M = 20-32 with one
 // tile per block, 50.2-53.7 / 56.7-57.9 above with two; 6144 x 12288 26.2-27.2
-// / 31.9-35.6 at M = 24-32, but 42.6-44.7 / 36.1-36.6 above.
+// / 31.9-35.6 at M = 24-32, but 42.6-44.7 / 36.1-36.6 above; wider layers
+// with K >= 8192 at M <= 32 with four tiles per block: 8192 x 28672 55.3-57.8
+// / 66.4-68.1, 8192 x 16384 30.5-31.7 / 58.0-58.9 (two tiles: 65-67, 35-37).
 // Waves per block: four.  {0, 0}: the layer goes to the other kernels.
 static RingShape ring_mid_shape(int64_t M, int64_t N, int64_t K) {
   if (N <= 8192) return {K >= 16384 && M <= 32 ? 2 : 1, 4};
   if (M <= 32 && K <= 4096) return {1, 4};
   if (N <= 12288 && (M <= 32 ? K > 4096 : K >= 8192)) return {M > 32 ? 2 : 1, 4};
+  if (M <= 32 && K >= 8192) return {4, 4};
   return {0, 0};
 }
 
