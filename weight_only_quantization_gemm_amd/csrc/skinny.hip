@@ -588,7 +588,9 @@ static hipError_t ring_run(const void* x, const void* packed, const void* scales
 // tile per block, 50.2-53.7 / 56.7-57.9 above with two; 6144 x 12288 26.2-27.2
 // / 31.9-35.6 at M = 24-32, but 42.6-44.7 / 36.1-36.6 above; wider layers
 // with K >= 8192 at M <= 32 with four tiles per block: 8192 x 28672 55.3-57.8
-// / 66.4-68.1, 8192 x 16384 30.5-31.7 / 58.0-58.9 (two tiles: 65-67, 35-37).
+// / 66.4-68.1, 8192 x 16384 30.5-31.7 / 58.0-58.9 (two tiles: 65-67, 35-37);
+// above M = 32 they stay on the GEMM (the best ring layout gains at most 4%
+// there, and the layout that wins on one shape loses up to 40% on the other).
 // Waves per block: four.  {0, 0}: the layer goes to the other kernels.
 static RingShape ring_mid_shape(int64_t M, int64_t N, int64_t K) {
   if (N <= 8192) return {K >= 16384 && M <= 32 ? 2 : 1, 4};
