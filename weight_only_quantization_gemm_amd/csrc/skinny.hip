@@ -591,6 +591,8 @@ static hipError_t ring_run(const void* x, const void* packed, const void* scales
 // / 66.4-68.1, 8192 x 16384 30.5-31.7 / 58.0-58.9 (two tiles: 65-67, 35-37);
 // above M = 32 they stay on the GEMM (the best ring layout gains at most 4%
 // there, and the layout that wins on one shape loses up to 40% on the other).
+// On K <= 4096 layers up to M = 32, two or four tiles per block come within 3%
+// of one (4096 x 11008, 4096 x 22016 at M = 20-32), so one it is.
 // Waves per block: four.  {0, 0}: the layer goes to the other kernels.
 static RingShape ring_mid_shape(int64_t M, int64_t N, int64_t K) {
   if (N <= 8192) return {K >= 16384 && M <= 32 ? 2 : 1, 4};
