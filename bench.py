@@ -235,24 +235,25 @@ def run_decode_3bit(args, torch, awq, dev):
 
 def run_decode_scaled(args, torch, awq, dev):
     """The decode step of run_decode with x not yet divided by s: awq_gemm_scaled divides it
-    (as x * inv_s, inv_s = 1/s from awq_inverse_scale) inside the GEMV's x load on the
+    (exactly, from s and inv_s = 1/s of awq_inverse_scale) inside the GEMV's x load on the
     4096 x 4096 layers and with a separate scaling launch on the larger ones.  Bytes per
-    step add inv_s (4 K per layer).  s is a^0.5 of a lognormal channel profile."""
+    step add s and inv_s (8 K per layer).  s is a^0.5 of a lognormal channel profile."""
     from gen import activations_fp16
-    step_bytes = sum(gemv_bytes(1, K, N) + 4 * K for _, K, N in LAYERS_7B)
+    step_bytes = sum(gemv_bytes(1, K, N) + 8 * K for _, K, N in LAYERS_7B)
     copies = max(2, int(np.ceil((1 << 30) / step_bytes)) + 1)
     layers = [Layer(n, K, N, torch, awq, copies, dev) for n, K, N in LAYERS_7B]
     for L in layers:
         g = np.random.default_rng(2200 + L.K)
         sv = np.sqrt(np.exp(g.normal(0.0, 0.8, L.K))).astype(np.float32)
-        L.inv = awq.awq_inverse_scale(torch.from_numpy(sv).to(dev))
+        L.s = torch.from_numpy(sv).to(dev)
+        L.inv = awq.awq_inverse_scale(L.s)
         L.ws = torch.empty(max(awq.awq_gemm_scaled_workspace_bytes(1, L.N, L.K), 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(c):
         for L in layers:
             p, s, z = L.copies[c]
-            awq.awq_gemm_scaled(L.x, L.inv, p, s, z, out=L.y, workspace=L.ws)
+            awq.awq_gemm_scaled(L.x, L.s, p, s, z, out=L.y, workspace=L.ws, inv_s=L.inv)
 
     ms = time_steps(torch, step, copies, args.steps, args.warmup)
     del layers

@@ -22,7 +22,10 @@
  * Memory.  Every pointer argument documented "device" is device memory of the
  * current HIP device; "host" pointers are ordinary host memory.  The caller
  * owns all buffers; the library allocates nothing and keeps no pointer after a
- * call returns.  Device pointers must be 16-byte aligned.
+ * call returns.  Every device pointer must be 16-byte aligned: each entry
+ * point checks all of its device pointers (optional ones only when given)
+ * and returns AWQ_ERROR_MISALIGNED, naming the first misaligned one in
+ * awq_last_error(), before anything is enqueued.
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  All device work is enqueued on it in order and the calls return
@@ -219,9 +222,10 @@ int awq_quantize_shared(const void* W, const void* X, int64_t N, int64_t K, int6
  *   y       device fp16 [M][N]  out: y[m][n] = sum_k x[m][k] * w_hat[n][k]
  *
  * Accumulation is fp32 and y is rounded to fp16 once.  M = 1, and M = 2 with
- * K < 16384: vector-ALU GEMV; every product x * code is exact in fp32 and the
- * zero point enters once per 32 codes as zero * sum(x) (so y is 0 only up to
- * fp32 rounding when every code equals its zero).  Other M <= 16, and
+ * K < 16384: vector-ALU GEMV on (code - zero), exact in fp16, every product
+ * with x exact in fp32, the group scale applied to each 32-code partial sum in
+ * fp32 (so a row whose codes all equal their zero points gives y = 0 exactly).
+ * Other M <= 16, and
  * 17 <= M <= 64 on the layer shapes the matrix-core decode kernels serve
  * (N <= 8192; N <= 12288 with K > 4096, K >= 8192 above M = 32; K <= 4096 or
  * K >= 8192 up to M = 32): matrix-core kernels on (code - zero), exact in fp16, with fp32 sums per
@@ -238,8 +242,8 @@ int awq_gemm(const void* x, const void* packed, const void* scales, const void* 
              int64_t M, int64_t N, int64_t K, int32_t group, void* stream);
 /* awq_gemm on the format written at `bits` = 4 (awq_gemm itself) or 3.  At 3
  * bits: M = 1, and M = 2 with K < 16384, run the vector-ALU GEMV with the
- * arithmetic stated above (every product exact in fp32, zero point as
- * zero * sum(x)); other M <= 64 the matrix-core decode kernel on exact
+ * arithmetic stated above (exact code - zero, every product exact in
+ * fp32); other M <= 64 the matrix-core decode kernel on exact
  * (code - zero) with the group scale applied in fp32; M > 64, and M > 32 on
  * layers wider than 12288 rows or with K <= 4096 (N > 8192), the pipelined
  * matrix-core GEMM with the 4-bit arithmetic above (the dequantized weight
@@ -253,10 +257,12 @@ int awq_gemm_bits(const void* x, const void* packed, const void* scales, const v
  * The input side of the per-channel scaling ([summary] paragraph 3: a weight
  * channel scaled up by s has its input divided by s, so the product keeps its
  * value).  awq_gemm takes x already divided; these calls do the division on
- * the device, fused into the decode GEMV where that kernel serves M.
+ * the device, fused into the decode GEMV where that kernel serves M.  The
+ * scaled input is fp16(x / s): one IEEE fp32 division of fp32(x) by s
+ * (correctly rounded), rounded once more to fp16 (round to nearest even).
  *
  * awq_inverse_scale -- inv_s[k] = 1 / s[k], IEEE fp32 division (correctly
- * rounded), once per layer.
+ * rounded), once per layer; awq_gemm_scaled's fused path needs it.
  *   s      device fp32 [K]   the s written by awq_quantize
  *   inv_s  device fp32 [K]   out
  * Requires 1 <= K <= 2^20.
@@ -264,35 +270,40 @@ int awq_gemm_bits(const void* x, const void* packed, const void* scales, const v
 int awq_inverse_scale(const float* s, int64_t K, float* inv_s, void* stream);
 
 /*
- * awq_scale_input -- xs[m][k] = fp16(fp32(x[m][k]) * inv_s[k]): one fp32
- * product, rounded once to fp16 (round to nearest even).  It equals the
- * correctly rounded x / s except where x * fl(1/s) and x / s (at most 1.5 fp32
- * ulp apart) round to neighbouring fp16 values.
+ * awq_scale_input -- xs[m][k] = fp16(fp32(x[m][k]) / s[k]), the division
+ * correctly rounded in fp32, then rounded to fp16.
  *   x      device fp16 [M][K]
- *   inv_s  device fp32 [K]   from awq_inverse_scale
+ *   s      device fp32 [K]   per-channel scale (awq_quantize's s)
  *   xs     device fp16 [M][K]   out (may not overlap x)
  * Requires 1 <= M <= 2^22, K % 8 == 0, 8 <= K <= 2^20.
  */
-int awq_scale_input(const void* x, const float* inv_s, int64_t M, int64_t K, void* xs, void* stream);
+int awq_scale_input(const void* x, const float* s, int64_t M, int64_t K, void* xs, void* stream);
 
 /*
- * awq_gemm_scaled -- y = awq_scale_input(x, inv_s) times w_hat^T: the product
+ * awq_gemm_scaled -- y = awq_scale_input(x, s) times w_hat^T: the product
  * of awq_gemm_bits on the scaled input, bit for bit.  At 4 bits with M = 1, and
  * M = 2 with K < 16384 (the vector-ALU GEMV), on layers with N * K <= 2^24, the
- * scaling happens in the GEMV's own x load: one launch, no intermediate, and
- * awq_gemm_scaled_workspace_bytes is 0 (workspace may be NULL).  Otherwise
- * the scaled input goes through `workspace` (device, M * K * 2 bytes rounded up
- * to 256) and awq_gemm_bits runs on it: on larger layers the fused form's
- * per-block re-read of inv_s costs more than the second launch.
+ * division happens in the GEMV's own x load: one launch, no intermediate, and
+ * awq_gemm_scaled_workspace_bytes is 0 (workspace may be NULL).  There the
+ * quotient comes from inv_s and one exact residual step (q0 = x inv_s,
+ * r = x - s q0 in one fma, q = q0 + r inv_s in one fma), which equals the
+ * correctly rounded x / s when inv_s is the correctly rounded 1/s and the
+ * quotient is a normal fp32 number: s must be awq_inverse_scale's input and
+ * inv_s its output, and every s must lie in [2^-64, 2^64] (awq_quantize's s
+ * always does).  Otherwise the scaled input goes through `workspace` (device,
+ * M * K * 2 bytes rounded up to 256) and awq_gemm_bits runs on it: on larger
+ * layers the fused form's per-block re-read of s and inv_s costs more than the
+ * second launch.
  *   x      device fp16 [M][K]   activations, not divided by s
- *   inv_s  device fp32 [K]      from awq_inverse_scale
+ *   s      device fp32 [K]      per-channel scale
+ *   inv_s  device fp32 [K]      awq_inverse_scale(s)
  *   other arguments as awq_gemm_bits
  * Requires what awq_gemm_bits requires.
  */
 size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits);
-int awq_gemm_scaled(const void* x, const float* inv_s, const void* packed, const void* scales, const void* zeros,
-                    void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* workspace,
-                    size_t workspace_bytes, void* stream);
+int awq_gemm_scaled(const void* x, const float* s, const float* inv_s, const void* packed, const void* scales,
+                    const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * awq_unpack -- logical view of the packed format, for checking it.

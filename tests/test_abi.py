@@ -120,18 +120,71 @@ def test_input_scaling_queries_and_errors_before_launch():
     assert ws(0, 64, 4096, 4) == 0 and ws(1, 64, 4096, 5) == 0
     assert lib.awq_inverse_scale(None, 128, FAKE, None) == INVALID
     assert lib.awq_inverse_scale(FAKE, 0, FAKE, None) == INVALID
-    assert lib.awq_inverse_scale(FAKE_MISALIGNED, 128, FAKE, None) == MISALIGNED
     assert lib.awq_scale_input(FAKE, FAKE, 1, 12, FAKE, None) == INVALID       # K % 8
     assert lib.awq_scale_input(FAKE, FAKE, 0, 128, FAKE, None) == INVALID
-    assert lib.awq_scale_input(FAKE, FAKE_MISALIGNED, 1, 128, FAKE, None) == MISALIGNED
     f = lib.awq_gemm_scaled
-    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 4, None, 0, None) == INVALID
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 128, 4, None, 0, None) == INVALID   # K % group
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 5, None, 0, None) == INVALID   # bits
-    assert f(FAKE, FAKE_MISALIGNED, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 4, None, 0, None) == MISALIGNED
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, None, 0, None) == WS_SMALL
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE, 767, None) == WS_SMALL
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE_MISALIGNED, 768, None) == MISALIGNED
+    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 4, None, 0, None) == INVALID
+    assert f(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 4, None, 0, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 128, 4, None, 0, None) == INVALID   # K % group
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 5, None, 0, None) == INVALID   # bits
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, None, 0, None) == WS_SMALL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE, 767, None) == WS_SMALL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE_MISALIGNED, 768, None) == MISALIGNED
+    assert "workspace" in awq.awq_last_error()
+
+
+# Every device pointer of every entry point, by argument position: a call that is valid
+# except for that one pointer being 8 bytes off a 16-byte boundary must return
+# AWQ_ERROR_MISALIGNED and name the pointer (so no kernel ever sees it).
+_AL = np.arange(20, dtype=np.float32) / np.float32(20)
+_WS_Q = 1 << 40
+MISALIGNED_CASES = {
+    "awq_channel_mean_abs": ((FAKE, 64, 256, FAKE, None), {0: "X", 3: "a"}),
+    "awq_pack_bits": ((FAKE, FAKE, 64, 256, 128, 4, FAKE, FAKE, FAKE, None),
+                      {0: "W", 1: "s", 6: "packed", 7: "scales", 8: "zeros"}),
+    "awq_quantize_shared": ((FAKE, FAKE, 64, 256, 32, 128, 4, _AL.ctypes.data, 20, 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, FAKE, _WS_Q, None),
+                            {0: "W", 1: "X", 10: "packed", 11: "scales", 12: "zeros", 13: "s", 14: "best_alpha",
+                             15: "loss", 16: "workspace"}),
+    "awq_keep_fp16_ablation": ((FAKE, FAKE, 64, 256, 32, 128, 4, 3, FAKE, FAKE, FAKE, FAKE, FAKE, _WS_Q, None),
+                               {0: "W", 1: "X", 8: "random_keep", 9: "keep_act", 10: "keep_wt", 11: "loss",
+                                12: "workspace"}),
+    "awq_gemm_bits": ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 256, 128, 4, None),
+                      {0: "x", 1: "packed", 2: "scales", 3: "zeros", 4: "y"}),
+    "awq_inverse_scale": ((FAKE, 256, FAKE, None), {0: "s", 2: "inv_s"}),
+    "awq_scale_input": ((FAKE, FAKE, 1, 256, FAKE, None), {0: "x", 1: "s", 4: "xs"}),
+    "awq_gemm_scaled": ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 256, 128, 4, FAKE, 1 << 20, None),
+                        {0: "x", 1: "s", 2: "inv_s", 3: "packed", 4: "scales", 5: "zeros", 6: "y",
+                         12: "workspace"}),
+    "awq_unpack_bits": ((FAKE, FAKE, 64, 256, 128, 4, FAKE, FAKE, None),
+                        {0: "packed", 1: "zeros", 6: "codes", 7: "zeros_u8"}),
+}
+
+
+@pytest.mark.parametrize("entry", sorted(MISALIGNED_CASES))
+def test_every_device_pointer_is_alignment_checked(entry):
+    lib = _lib_()
+    fn = getattr(lib, entry)
+    args, pointers = MISALIGNED_CASES[entry]
+    for pos, name in pointers.items():
+        bad = list(args)
+        bad[pos] = FAKE_MISALIGNED
+        assert fn(*bad) == MISALIGNED, f"{entry}: {name} at argument {pos}"
+        assert awq.awq_last_error() == f"{name} must be 16-byte aligned", (entry, awq.awq_last_error())
+
+
+def test_misaligned_case_table_covers_every_pointer_argument():
+    """The table above names every pointer parameter the header declares for these entry
+    points (host pointers excepted: the alpha grid and the stream)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for entry, (args, pointers) in MISALIGNED_CASES.items():
+        decl = re.search(entry + r"\s*\(([^;]*)\)\s*;", text).group(1)
+        params = [p.strip() for p in decl.split(",")]
+        assert len(params) == len(args), entry
+        ptr_params = {i for i, p in enumerate(params) if "*" in p and not p.endswith(("alphas", "stream"))}
+        assert ptr_params == set(pointers), (entry, sorted(ptr_params), sorted(pointers))
+        for i, name in pointers.items():
+            assert re.search(r"\b" + name + r"$", params[i]), (entry, i, params[i])
 
 
 def test_quantize_shared_argument_errors_before_launch():

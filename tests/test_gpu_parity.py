@@ -268,10 +268,13 @@ def test_gemm_one_hot_reproduces_dequantized_column(M):
         assert np.array_equal(y[m], col.astype(np.float16)), (m, k)
 
 
-@pytest.mark.parametrize("M", [1, 5, 8, 9, 64])
-def test_gemm_codes_equal_zeros_gives_zero(M):
-    note(f"gemm zero codes M={M}")
-    N, K = 64, 256
+@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (2, 64, 256), (5, 64, 256), (8, 64, 256), (9, 64, 256),
+                                   (64, 64, 256), (1, 4096, 4096), (2, 11008, 4096), (1, 4096, 11008),
+                                   (1, 8192, 28672), (16, 300, 4096), (256, 300, 4096)])
+def test_gemm_codes_equal_zeros_gives_zero(M, N, K):
+    """Every code equal to its zero point: w_hat = 0, so y = 0 exactly on every kernel (each
+    subtracts the zero point per code before any product)."""
+    note(f"gemm zero codes M={M} N={N} K={K}")
     g = np.random.default_rng(5)
     z = g.integers(0, 16, size=(N, K // 128)).astype(np.uint8)
     q = np.repeat(z, 128, axis=1)
@@ -279,13 +282,7 @@ def test_gemm_codes_equal_zeros_gives_zero(M):
     p, zb = encode(q, z)
     x = activations_fp16(M, K, seed=6)
     y = host(awq.awq_gemm(dev(x), dev(p), dev(sc), dev(zb))).astype(np.float64)
-    if M > 2:
-        assert np.all(y == 0)  # the matrix-core kernels subtract the zero point per code, exactly
-    else:
-        # the decode GEMV (M <= 2) folds the zero point as z * sum(x): y is 0 up to fp32 rounding of
-        # sums of at most 32 * 15 * |x| (2^-24 relative per addition)
-        bound = 1e-6 * np.abs(x.astype(np.float64)).sum(axis=1, keepdims=True) * 15 * 0.01
-        assert np.all(np.abs(y) <= bound)
+    assert np.all(y == 0), f"M={M} N={N} K={K}: max |y| {np.abs(y).max()}"
 
 
 def test_gemm_quantized_layer_end_to_end():

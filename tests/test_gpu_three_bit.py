@@ -121,21 +121,19 @@ def test_gemm3_one_hot_reproduces_dequantized_column(M):
         assert np.array_equal(y[m], col.astype(np.float16)), (m, k)
 
 
-@pytest.mark.parametrize("M", [1, 2, 5, 64])
-def test_gemm3_codes_equal_zeros_gives_zero(M):
-    note(f"gemm3 zero codes M={M}")
-    N, K = 64, 256
+@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (2, 64, 256), (5, 64, 256), (64, 64, 256), (1, 4096, 4096),
+                                   (2, 1000, 11008), (16, 300, 4096), (100, 300, 1024)])
+def test_gemm3_codes_equal_zeros_gives_zero(M, N, K):
+    """Every code equal to its zero point: w_hat = 0, so y = 0 exactly on every kernel (each
+    subtracts the zero point per code before any product)."""
+    note(f"gemm3 zero codes M={M} N={N} K={K}")
     z = np.random.default_rng(6).integers(0, 8, size=(N, K // 128)).astype(np.uint8)
     q = np.repeat(z, 128, axis=1)
     sc = np.full((N, K // 128), 0.01, np.float16)
     p, zb = encode3(q, z)
     x = activations_fp16(M, K, seed=7)
     y = host(awq.awq_gemm(dev(x), dev(p), dev(sc), dev(zb))).astype(np.float64)
-    if M > 2:
-        assert np.all(y == 0)  # the matrix-core kernel subtracts the zero point per code, exactly
-    else:
-        bound = 1e-6 * np.abs(x.astype(np.float64)).sum(axis=1, keepdims=True) * 7 * 0.01
-        assert np.all(np.abs(y) <= bound)
+    assert np.all(y == 0), f"M={M} N={N} K={K}: max |y| {np.abs(y).max()}"
 
 
 def test_gemm3_after_search_end_to_end():

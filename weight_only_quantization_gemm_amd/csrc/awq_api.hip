@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 
 #include "awq.h"
@@ -34,6 +35,20 @@ int device_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Every device pointer an entry point takes must be 16-byte aligned (the
+// kernels move 16-byte pieces, several of them straight into LDS); the first
+// misaligned one is named in the error.  NULL entries (optional arguments
+// left out) are skipped.
+struct DevPtr {
+  const void* p;
+  const char* name;
+};
+int check_aligned(std::initializer_list<DevPtr> ptrs) {
+  for (const DevPtr& d : ptrs)
+    if (d.p != nullptr && !aligned16(d.p)) return fail(AWQ_ERROR_MISALIGNED, "%s must be 16-byte aligned", d.name);
+  return AWQ_OK;
+}
 
 #define AWQ_REQUIRE(cond, status, ...) \
   do {                                 \
@@ -165,7 +180,7 @@ int awq_channel_mean_abs(const void* X, int64_t M, int64_t K, double* a, void* s
   AWQ_REQUIRE(M >= 1 && M <= AWQ_MAX_CALIB_ROWS, AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^23]", (long long)M);
   AWQ_REQUIRE(K >= 8 && K % 8 == 0 && K <= (int64_t(1) << 20), AWQ_ERROR_INVALID_VALUE,
               "K=%lld must be a positive multiple of 8", (long long)K);
-  AWQ_REQUIRE(aligned16(X) && aligned16(a), AWQ_ERROR_MISALIGNED, "X and a must be 16-byte aligned");
+  if (int st = check_aligned({{X, "X"}, {a, "a"}})) return st;
   return device_status(awq::launch_channel_mean_abs(X, M, K, a, as_stream(stream)), "awq_channel_mean_abs");
   AWQ_GUARD_END
 }
@@ -182,8 +197,8 @@ int awq_pack_bits(const void* W, const float* s, int64_t N, int64_t K, int32_t g
   int st = check_layer(N, K, group);
   if (st == AWQ_OK) st = check_bits(bits);
   if (st != AWQ_OK) return st;
-  AWQ_REQUIRE(aligned16(W) && aligned16(packed) && (s == nullptr || aligned16(s)), AWQ_ERROR_MISALIGNED,
-              "W, s and packed must be 16-byte aligned");
+  if (int st2 = check_aligned({{W, "W"}, {s, "s"}, {packed, "packed"}, {scales, "scales"}, {zeros, "zeros"}}))
+    return st2;
   return device_status(awq::launch_pack(W, s, N, K, bits, packed, scales, zeros, as_stream(stream)), "awq_pack");
   AWQ_GUARD_END
 }
@@ -223,9 +238,9 @@ int awq_quantize_shared(const void* W, const void* X, int64_t N, int64_t K, int6
                 "alphas[%d]=%g must be finite and >= 0", i, (double)alphas[i]);
     grid.v[i] = alphas[i];
   }
-  AWQ_REQUIRE(aligned16(W) && aligned16(X) && aligned16(packed) && aligned16(s) && aligned16(workspace) &&
-                  (loss == nullptr || aligned16(loss)),
-              AWQ_ERROR_MISALIGNED, "device pointers must be 16-byte aligned");
+  if (int st2 = check_aligned({{W, "W"}, {X, "X"}, {packed, "packed"}, {scales, "scales"}, {zeros, "zeros"},
+                                {s, "s"}, {best_alpha, "best_alpha"}, {loss, "loss"}, {workspace, "workspace"}}))
+    return st2;
   const QuantizeWorkspace w = quantize_workspace(N, K, M, n_alpha);
   AWQ_REQUIRE(workspace_bytes >= w.total, AWQ_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu",
               workspace_bytes, w.total);
@@ -293,8 +308,9 @@ int awq_keep_fp16_ablation(const void* W, const void* X, int64_t N, int64_t K, i
   AWQ_REQUIRE(M >= 1 && M <= AWQ_MAX_CALIB_ROWS && N <= AWQ_MAX_CALIB_ROWS, AWQ_ERROR_INVALID_VALUE,
               "M=%lld and N=%lld must be in [1, 2^23]", (long long)M, (long long)N);
   AWQ_REQUIRE(n_keep >= 0 && n_keep <= K, AWQ_ERROR_INVALID_VALUE, "n_keep=%d outside [0, K]", n_keep);
-  AWQ_REQUIRE(aligned16(W) && aligned16(X) && aligned16(workspace), AWQ_ERROR_MISALIGNED,
-              "W, X and workspace must be 16-byte aligned");
+  if (int st2 = check_aligned({{W, "W"}, {X, "X"}, {random_keep, "random_keep"}, {keep_act, "keep_act"},
+                                {keep_wt, "keep_wt"}, {loss, "loss"}, {workspace, "workspace"}}))
+    return st2;
   const QuantizeWorkspace w = quantize_workspace(N, K, M, 1, true);
   AWQ_REQUIRE(workspace_bytes >= w.total, AWQ_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu",
               workspace_bytes, w.total);
@@ -351,7 +367,8 @@ int awq_gemm_bits(const void* x, const void* packed, const void* scales, const v
   if (st == AWQ_OK) st = check_bits(bits);
   if (st != AWQ_OK) return st;
   AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
-  AWQ_REQUIRE(aligned16(x) && aligned16(packed), AWQ_ERROR_MISALIGNED, "x and packed must be 16-byte aligned");
+  if (int st2 = check_aligned({{x, "x"}, {packed, "packed"}, {scales, "scales"}, {zeros, "zeros"}, {y, "y"}}))
+    return st2;
   hipError_t e;
   if (bits == 3) e = awq::launch_gemm3(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
   else if (M <= 16) e = awq::launch_gemv(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
@@ -364,20 +381,19 @@ int awq_inverse_scale(const float* s, int64_t K, float* inv_s, void* stream) {
   AWQ_GUARD_BEGIN
   AWQ_REQUIRE(s && inv_s, AWQ_ERROR_INVALID_VALUE, "s and inv_s must not be NULL");
   AWQ_REQUIRE(K >= 1 && K <= (int64_t(1) << 20), AWQ_ERROR_INVALID_VALUE, "K=%lld outside [1, 2^20]", (long long)K);
-  AWQ_REQUIRE(aligned16(s) && aligned16(inv_s), AWQ_ERROR_MISALIGNED, "s and inv_s must be 16-byte aligned");
+  if (int st = check_aligned({{s, "s"}, {inv_s, "inv_s"}})) return st;
   return device_status(awq::launch_inverse_scale(s, K, inv_s, as_stream(stream)), "awq_inverse_scale");
   AWQ_GUARD_END
 }
 
-int awq_scale_input(const void* x, const float* inv_s, int64_t M, int64_t K, void* xs, void* stream) {
+int awq_scale_input(const void* x, const float* s, int64_t M, int64_t K, void* xs, void* stream) {
   AWQ_GUARD_BEGIN
-  AWQ_REQUIRE(x && inv_s && xs, AWQ_ERROR_INVALID_VALUE, "x, inv_s and xs must not be NULL");
+  AWQ_REQUIRE(x && s && xs, AWQ_ERROR_INVALID_VALUE, "x, s and xs must not be NULL");
   AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
   AWQ_REQUIRE(K >= 8 && K % 8 == 0 && K <= (int64_t(1) << 20), AWQ_ERROR_INVALID_VALUE,
               "K=%lld must be a positive multiple of 8, at most 2^20", (long long)K);
-  AWQ_REQUIRE(aligned16(x) && aligned16(inv_s) && aligned16(xs), AWQ_ERROR_MISALIGNED,
-              "x, inv_s and xs must be 16-byte aligned");
-  return device_status(awq::launch_scale_input(x, inv_s, M, K, xs, as_stream(stream)), "awq_scale_input");
+  if (int st = check_aligned({{x, "x"}, {s, "s"}, {xs, "xs"}})) return st;
+  return device_status(awq::launch_scale_input(x, s, M, K, xs, as_stream(stream)), "awq_scale_input");
   AWQ_GUARD_END
 }
 
@@ -391,39 +407,47 @@ static bool scaled_fused(int64_t M, int64_t N, int64_t K, int32_t bits) {
   return bits == 4 && awq::gemv_dot2_supported(M, K) && N * K <= (int64_t(1) << 24);
 }
 
+// The scaled input through a buffer of M * K halfs: awq_scale_input, then the
+// product awq_gemm_bits would run on it.
+static hipError_t gemm_scaled_via(const void* x, const float* s, const void* packed, const void* scales,
+                                  const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int32_t bits,
+                                  void* xs, hipStream_t hs) {
+  hipError_t e = awq::launch_scale_input(x, s, M, K, xs, hs);
+  if (e != hipSuccess) return e;
+  if (bits == 3) return awq::launch_gemm3(xs, packed, scales, zeros, y, M, N, K, hs);
+  if (M <= 16) return awq::launch_gemv(xs, packed, scales, zeros, y, M, N, K, hs);
+  return awq::launch_gemm(xs, packed, scales, zeros, y, M, N, K, hs);
+}
+
 size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits) {
   if (M < 1 || N < 1 || K < 1 || (bits != 4 && bits != 3)) return 0;
   if (scaled_fused(M, N, K, bits)) return 0;  // no intermediate
   return (size_t)((M * K * 2 + 255) / 256 * 256);
 }
 
-int awq_gemm_scaled(const void* x, const float* inv_s, const void* packed, const void* scales, const void* zeros,
-                    void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int awq_gemm_scaled(const void* x, const float* s, const float* inv_s, const void* packed, const void* scales,
+                    const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   AWQ_GUARD_BEGIN
-  AWQ_REQUIRE(x && inv_s && packed && scales && zeros && y, AWQ_ERROR_INVALID_VALUE,
-              "x, inv_s, packed, scales, zeros and y must not be NULL");
+  AWQ_REQUIRE(x && s && inv_s && packed && scales && zeros && y, AWQ_ERROR_INVALID_VALUE,
+              "x, s, inv_s, packed, scales, zeros and y must not be NULL");
   int st = check_layer(N, K, group);
   if (st == AWQ_OK) st = check_bits(bits);
   if (st != AWQ_OK) return st;
   AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
-  AWQ_REQUIRE(aligned16(x) && aligned16(inv_s) && aligned16(packed), AWQ_ERROR_MISALIGNED,
-              "x, inv_s and packed must be 16-byte aligned");
+  if (int st2 = check_aligned({{x, "x"}, {s, "s"}, {inv_s, "inv_s"}, {packed, "packed"}, {scales, "scales"},
+                                {zeros, "zeros"}, {y, "y"}}))
+    return st2;
   const size_t need = awq_gemm_scaled_workspace_bytes(M, N, K, bits);
   const hipStream_t hs = as_stream(stream);
   if (need == 0)
-    return device_status(awq::launch_gemv_dot2_scaled(x, inv_s, packed, scales, zeros, y, M, N, K, hs),
+    return device_status(awq::launch_gemv_dot2_scaled(x, s, inv_s, packed, scales, zeros, y, M, N, K, hs),
                          "awq_gemm_scaled");
   AWQ_REQUIRE(workspace && workspace_bytes >= need, AWQ_ERROR_WORKSPACE_TOO_SMALL,
               "workspace_bytes=%zu below awq_gemm_scaled_workspace_bytes=%zu", workspace_bytes, need);
-  AWQ_REQUIRE(aligned16(workspace), AWQ_ERROR_MISALIGNED, "workspace must be 16-byte aligned");
-  hipError_t e = awq::launch_scale_input(x, inv_s, M, K, workspace, hs);
-  if (e == hipSuccess) {
-    if (bits == 3) e = awq::launch_gemm3(workspace, packed, scales, zeros, y, M, N, K, hs);
-    else if (M <= 16) e = awq::launch_gemv(workspace, packed, scales, zeros, y, M, N, K, hs);
-    else e = awq::launch_gemm(workspace, packed, scales, zeros, y, M, N, K, hs);
-  }
-  return device_status(e, "awq_gemm_scaled");
+  if (int st2 = check_aligned({{workspace, "workspace"}})) return st2;
+  return device_status(gemm_scaled_via(x, s, packed, scales, zeros, y, M, N, K, bits, workspace, hs),
+                       "awq_gemm_scaled");
   AWQ_GUARD_END
 }
 
@@ -439,7 +463,8 @@ int awq_unpack_bits(const void* packed, const void* zeros, int64_t N, int64_t K,
   int st = check_layer(N, K, group);
   if (st == AWQ_OK) st = check_bits(bits);
   if (st != AWQ_OK) return st;
-  AWQ_REQUIRE(aligned16(packed), AWQ_ERROR_MISALIGNED, "packed must be 16-byte aligned");
+  if (int st2 = check_aligned({{packed, "packed"}, {zeros, "zeros"}, {codes, "codes"}, {zeros_u8, "zeros_u8"}}))
+    return st2;
   return device_status(awq::launch_unpack(packed, zeros, N, K, bits, codes, zeros_u8, as_stream(stream)),
                        "awq_unpack");
   AWQ_GUARD_END

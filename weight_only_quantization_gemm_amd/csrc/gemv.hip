@@ -8,18 +8,20 @@
 // and 6).  Codes are dequantized on the fly in registers (OpenAlex record of
 // the GetMobile AWQ article, abstract).
 //
-// Arithmetic, designed for few vector instructions per code: a code q in the
-// low mantissa bits of an fp16 with a zero exponent field is the subnormal
-// q * 2^-24, exactly.  The packed nibble order puts channels 2j and 2j + 1 of
-// a word in bits 4j and 16 + 4j, so with one shift (w8 = w >> 8) the four
-// channel pairs of a word are w & 0x000F000F (q units), w & 0x00F000F0 (16 q
-// units), and the same two masks of w8: four and-operations, no bias to add
-// or subtract.  v_dot2_f32_f16 multiplies each pair with x exactly (an fp16
-// times a 4-bit integer times 2^-24 fits fp32) into two fp32 sums (q units and
-// 16 q units).  The zero point enters once per 32 codes as z * sum(x), with
-// sum(x) over the lane's 32 channels computed once per lane; the group scale
-// then multiplies the 32-code partial sum in fp32, and the final 2^24 is an
-// exact rescale.
+// Arithmetic: every product is exact and the zero point is subtracted per
+// code.  OR-ing a 4-bit field into the mantissa of fp16 1024.0 (0x6400) gives
+// 1024 + code; a field that sits 4 bits higher gives 1024 + 16 code (still
+// below 2048, where the fp16 spacing is 1).  The packed nibble order puts
+// channels 2j and 2j + 1 of a word in bits 4j and 16 + 4j, so with one shift
+// (w8 = w >> 8) the four channel pairs of a word are w & 0x000F000F (code
+// units), w & 0x00F000F0 (16 code units) and the same two masks of w8, each
+// OR-ed with the bias in one and-or.  One packed fp16 subtraction of
+// (1024 + zero) or (1024 + 16 zero) leaves (code - zero) or 16 (code - zero),
+// exact, and v_dot2_f32_f16 multiplies each pair with x exactly in fp32 (an
+// fp16 times an integer below 2^8).  Two fp32 sums (code and 16 code units)
+// are combined with the exact factor 1/16, and the group scale multiplies the
+// 32-code partial sum in fp32.  A row whose codes all equal their zero points
+// therefore gives exactly 0.
 //
 // Mapping: a block owns R output rows and spans all of K; lane l of wave w
 // owns the 16-byte chunk c = 64 w + l (32 codes) of each of the R rows, so
@@ -42,10 +44,26 @@ __device__ inline float dot2_acc(f16x2 a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, a), __builtin_bit_cast(h16x2, b), c, false);
 }
 
-// The fp16 pair xw scaled channel-wise by (a, b) in fp32, each rounded once to fp16.
-__device__ inline uint32_t scale_pair(uint32_t xw, float a, float b) {
+// The correctly rounded quotient x / s in fp32 from inv = RN(1/s), with no
+// division instruction.  q0 = RN(x inv) can be off by a little more than one
+// ulp, so one residual step q1 = RN(q0 + RN(x - s q0) inv) first makes it
+// faithful (within one ulp); then the residual r = x - s q1 is exact in one
+// fma, and RN(q1 + r inv) is the correctly rounded quotient (Markstein's
+// theorem on division with a correctly rounded reciprocal; it holds while
+// x / s is a normal fp32 number).  q0 is kept when it is 0, so a zero x keeps
+// its sign.
+__device__ inline float div_by_scale(float x, float s, float inv) {
+  const float q0 = x * inv;
+  const float q1 = fmaf(fmaf(-q0, s, x), inv, q0);
+  const float q2 = fmaf(fmaf(-q1, s, x), inv, q1);
+  return q0 == 0.0f ? q0 : q2;
+}
+
+// The fp16 pair xw divided channel-wise by (sa, sb): fp16(RN32(x / s)) per
+// value, the fp32 quotient rounded once more to fp16.
+__device__ inline uint32_t scale_pair(uint32_t xw, float sa, float sb, float ia, float ib) {
   const f16x2 v = as_f16x2(xw);
-  return as_u32(f16x2{(f16)((float)v.x * a), (f16)((float)v.y * b)});
+  return as_u32(f16x2{(f16)div_by_scale((float)v.x, sa, ia), (f16)div_by_scale((float)v.y, sb, ib)});
 }
 
 // DPP add: v + v[permuted lane]; lanes whose source row is masked off add 0.
@@ -79,14 +97,15 @@ __host__ __device__ inline int gemv_waves(int64_t K) {
 //
 // With SC, x is first divided by the per-channel scale s of the method
 // ([summary] paragraph 3: a channel whose weights were scaled up by s has its
-// input divided by s): each lane also loads inv_s (fp32 1/s, 128 B for its 32
-// channels) with its other loads, and every x value becomes
-// fp16(fp32(x) * inv_s), rounded once, before the products -- the values
+// input divided by s): each lane also loads s and inv_s = RN(1/s) (fp32, 256 B
+// for its 32 channels) with its other loads, and every x value becomes
+// fp16(RN32(x / s)) (div_by_scale) before the products -- the values
 // awq_scale_input writes, so the result equals this kernel on those values.
 template <int MB, int R, bool SC = false>
 __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                     const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                                                    f16* __restrict__ y, int N, int K, const float* __restrict__ inv_s) {
+                                                    f16* __restrict__ y, int N, int K, const float* __restrict__ s_in,
+                                                    const float* __restrict__ inv_s) {
   __shared__ float red[kMaxWaves][R * MB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = gemv_waves(K);  // == blockDim.x / 64, from the arguments (all preloaded)
@@ -118,7 +137,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
   uint32_t sr[R], zr[R];
   uint4 xv[MB][4];
   u32x4 wv[R];
-  float4 iv[SC ? 8 : 1];
+  float4 sv[SC ? 8 : 1], iv[SC ? 8 : 1];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     sr[r] = srow[r][g];
@@ -130,7 +149,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
     for (int u = 0; u < 4; ++u) xv[m][u] = reinterpret_cast<const uint4*>(x + (int64_t)m * K)[c * 4 + u];
   if constexpr (SC) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) iv[u] = reinterpret_cast<const float4*>(inv_s)[c * 8 + u];
+    for (int u = 0; u < 8; ++u) {
+      sv[u] = reinterpret_cast<const float4*>(s_in)[c * 8 + u];
+      iv[u] = reinterpret_cast<const float4*>(inv_s)[c * 8 + u];
+    }
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) wv[r] = __builtin_nontemporal_load(wrow[r] + c);
@@ -141,30 +163,21 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        xv[m][u].x = scale_pair(xv[m][u].x, iv[2 * u].x, iv[2 * u].y);
-        xv[m][u].y = scale_pair(xv[m][u].y, iv[2 * u].z, iv[2 * u].w);
-        xv[m][u].z = scale_pair(xv[m][u].z, iv[2 * u + 1].x, iv[2 * u + 1].y);
-        xv[m][u].w = scale_pair(xv[m][u].w, iv[2 * u + 1].z, iv[2 * u + 1].w);
+        const float4 sa = sv[2 * u], sb = sv[2 * u + 1], ia = iv[2 * u], ib = iv[2 * u + 1];
+        xv[m][u].x = scale_pair(xv[m][u].x, sa.x, sa.y, ia.x, ia.y);
+        xv[m][u].y = scale_pair(xv[m][u].y, sa.z, sa.w, ia.z, ia.w);
+        xv[m][u].z = scale_pair(xv[m][u].z, sb.x, sb.y, ib.x, ib.y);
+        xv[m][u].w = scale_pair(xv[m][u].w, sb.z, sb.w, ib.z, ib.w);
       }
   }
 
-  // 2^-24 * (sum of the lane's 32 x values), per activation row
-  float xs[MB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    float t = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t xw[4] = {xv[m][u].x, xv[m][u].y, xv[m][u].z, xv[m][u].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) t = dot2_acc(as_f16x2(0x3C003C00u), xw[q], t);  // (1, 1) . x pair
-    }
-    xs[m] = t * 0x1p-24f;
-  }
-
+  const uint32_t bias = bias_in_vgpr();
   float acc[R][MB];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    const uint32_t z = (zr[r] >> (4 * (g & 1))) & 0xFu;
+    const f16x2 zb1 = as_f16x2(0x64006400u | z | (z << 16));           // (1024 + z) pair
+    const f16x2 zb16 = as_f16x2(0x64006400u | (z << 4) | (z << 20));  // (1024 + 16 z) pair
     const uint32_t words[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
     float lo[MB], hi[MB];
 #pragma unroll
@@ -172,8 +185,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
 #pragma unroll
     for (int wi = 0; wi < 4; ++wi) {
       const uint32_t w = words[wi], w8 = w >> 8;
-      const f16x2 p0 = as_f16x2(w & 0x000F000Fu), p1 = as_f16x2(w & 0x00F000F0u);
-      const f16x2 p2 = as_f16x2(w8 & 0x000F000Fu), p3 = as_f16x2(w8 & 0x00F000F0u);
+      const f16x2 p0 = as_f16x2((w & 0x000F000Fu) | bias) - zb1;    // channels 0, 1: code - zero
+      const f16x2 p1 = as_f16x2((w & 0x00F000F0u) | bias) - zb16;   // channels 2, 3: 16 (code - zero)
+      const f16x2 p2 = as_f16x2((w8 & 0x000F000Fu) | bias) - zb1;   // channels 4, 5
+      const f16x2 p3 = as_f16x2((w8 & 0x00F000F0u) | bias) - zb16;  // channels 6, 7
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         lo[m] = dot2_acc(p0, xv[m][wi].x, lo[m]);
@@ -182,14 +197,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
         hi[m] = dot2_acc(p3, xv[m][wi].w, hi[m]);
       }
     }
-    const float z = (float)((zr[r] >> (4 * (g & 1))) & 0xFu);
     const float sc = (float)as_f16x2(sr[r]).x;
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      float t = fmaf(hi[m], 0.0625f, lo[m]);  // 2^-24 * sum x q
-      t = fmaf(-z, xs[m], t);                  // 2^-24 * sum x (q - z)
-      acc[r][m] = live ? sc * t : 0.0f;
-    }
+    for (int m = 0; m < MB; ++m) acc[r][m] = live ? sc * fmaf(hi[m], 0.0625f, lo[m]) : 0.0f;
   }
 
   if (nwaves == 1) {  // the whole row is in this wave: no cross-wave step
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         const float v = wave_sum_to_lane63(acc[r][m]);
-        if (lane == 63 && row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)(v * 0x1p24f);
+        if (lane == 63 && row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)v;
       }
     return;
   }
@@ -214,19 +224,19 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
     const int r = threadIdx.x / MB, m = threadIdx.x % MB;
     float v = 0.0f;
     for (int w = 0; w < nwaves; ++w) v += red[w][threadIdx.x];
-    if (row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)(v * 0x1p24f);
+    if (row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)v;
   }
 }
 
 template <int MB, int R, bool SC>
 static hipError_t gemv_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                              int64_t N, int64_t K, const float* inv_s, hipStream_t st) {
+                              int64_t N, int64_t K, const float* s, const float* inv_s, hipStream_t st) {
   const int waves = gemv_waves(K);
   if (waves > kMaxWaves) return hipErrorInvalidValue;
   dim3 grid((unsigned)((N + R - 1) / R));
   gemv_kernel<MB, R, SC><<<grid, dim3(waves * kWave), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
-      reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)N, (int)K, inv_s);
+      reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)N, (int)K, s, inv_s);
   return hipGetLastError();
 }
 
@@ -249,20 +259,22 @@ bool gemv_dot2_supported(int64_t M, int64_t K) {
 // chunks per lane (fewer waves) measured slower on every shape.
 template <int MB, bool SC = false>
 static hipError_t gemv_rows_launch(const void* x, const void* packed, const void* scales, const void* zeros,
-                                   void* y, int64_t N, int64_t K, hipStream_t st, const float* inv_s = nullptr) {
+                                   void* y, int64_t N, int64_t K, hipStream_t st, const float* s = nullptr,
+                                   const float* inv_s = nullptr) {
   if ((K >= 8192 && N >= 8192) || (MB == 2 && N >= 16384))
-    return gemv_launch<MB, 8, SC>(x, packed, scales, zeros, y, N, K, inv_s, st);
-  return gemv_launch<MB, 4, SC>(x, packed, scales, zeros, y, N, K, inv_s, st);
+    return gemv_launch<MB, 8, SC>(x, packed, scales, zeros, y, N, K, s, inv_s, st);
+  return gemv_launch<MB, 4, SC>(x, packed, scales, zeros, y, N, K, s, inv_s, st);
 }
 
 // 3-bit format (three words per 32 channels of a row; see the packer).  The
 // same mapping as above: lane l of wave w owns the chunk c = 64 w + l of each
 // of R rows, now 12 bytes.  In a 16-bit half, fields 0, 1, 2 (bits 0-2, 3-5,
-// 6-8) come out with one AND each as q, 8 q and 64 q units of 2^-24 -- all
-// below 2^10, so still exact fp16 subnormals -- and fields 3, 4 the same way
-// after one shift by 9; the pair in the spare bits takes three shifts and
-// ANDs.  Three fp32 sums (1, 8 and 64 q units) are combined with exact
-// power-of-two factors.  Pair p of the chunk multiplies x word p.
+// 6-8) OR-ed into fp16 1024.0 give 1024 + q, 1024 + 8 q and 1024 + 64 q (all
+// below 2048, so exact), and fields 3, 4 the same way after one shift by 9;
+// the pair in the spare bits takes three shifts and ANDs.  Subtracting
+// (1024 + z), (1024 + 8 z) or (1024 + 64 z) leaves the exact (q - z) times 1,
+// 8 or 64, and three fp32 sums are combined with exact power-of-two factors,
+// as in the 4-bit kernel.  Pair p of the chunk multiplies x word p.
 template <int MB, int R>
 __global__ __launch_bounds__(1024) void gemv3_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                      const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
@@ -303,22 +315,14 @@ __global__ __launch_bounds__(1024) void gemv3_kernel(const f16* __restrict__ x, 
     for (int t = 0; t < 3; ++t) wv[r][t] = __builtin_nontemporal_load(wrow[r] + 3 * c + t);
   __builtin_amdgcn_sched_barrier(0);  // every load before the first wait, as in the 4-bit kernel
 
-  float xs[MB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    float t = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t xw[4] = {xv[m][u].x, xv[m][u].y, xv[m][u].z, xv[m][u].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) t = dot2_acc(as_f16x2(0x3C003C00u), xw[q], t);
-    }
-    xs[m] = t * 0x1p-24f;
-  }
-
+  const uint32_t bias = bias_in_vgpr();
   float acc[R][MB];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    const uint32_t z = (zr[r] >> (4 * (g & 1))) & 0xFu;
+    const f16x2 zb1 = as_f16x2(0x64006400u | z | (z << 16));           // (1024 + z) pair
+    const f16x2 zb8 = as_f16x2(0x64006400u | (z << 3) | (z << 19));    // (1024 + 8 z) pair
+    const f16x2 zb64 = as_f16x2(0x64006400u | (z << 6) | (z << 22));  // (1024 + 64 z) pair
     float a1[MB], a8[MB], a64[MB];
 #pragma unroll
     for (int m = 0; m < MB; ++m) a1[m] = a8[m] = a64[m] = 0.0f;
@@ -329,9 +333,9 @@ __global__ __launch_bounds__(1024) void gemv3_kernel(const f16* __restrict__ x, 
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       const uint32_t w = wv[r][t], w9 = w >> 9;
-      const f16x2 p0 = as_f16x2(w & 0x00070007u), p1 = as_f16x2(w & 0x00380038u);
-      const f16x2 p2 = as_f16x2(w & 0x01C001C0u), p3 = as_f16x2(w9 & 0x00070007u);
-      const f16x2 p4 = as_f16x2(w9 & 0x00380038u);
+      const f16x2 p0 = as_f16x2((w & 0x00070007u) | bias) - zb1, p1 = as_f16x2((w & 0x00380038u) | bias) - zb8;
+      const f16x2 p2 = as_f16x2((w & 0x01C001C0u) | bias) - zb64, p3 = as_f16x2((w9 & 0x00070007u) | bias) - zb1;
+      const f16x2 p4 = as_f16x2((w9 & 0x00380038u) | bias) - zb8;
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         a1[m] = dot2_acc(p0, xword(m, 5 * t), a1[m]);
@@ -342,14 +346,12 @@ __global__ __launch_bounds__(1024) void gemv3_kernel(const f16* __restrict__ x, 
       }
     }
     const f16x2 p15 = as_f16x2(((wv[r][0] >> 15) & 0x00010001u) | ((wv[r][1] >> 14) & 0x00020002u) |
-                               ((wv[r][2] >> 13) & 0x00040004u));
-    const float z = (float)((zr[r] >> (4 * (g & 1))) & 0xFu);
+                               ((wv[r][2] >> 13) & 0x00040004u) | bias) - zb1;
     const float sc = (float)as_f16x2(sr[r]).x;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       a1[m] = dot2_acc(p15, xword(m, 15), a1[m]);
-      float t = fmaf(a64[m], 0.015625f, fmaf(a8[m], 0.125f, a1[m]));  // 2^-24 * sum x q
-      t = fmaf(-z, xs[m], t);                                          // 2^-24 * sum x (q - z)
+      const float t = fmaf(a64[m], 0.015625f, fmaf(a8[m], 0.125f, a1[m]));  // sum x (q - z)
       acc[r][m] = live ? sc * t : 0.0f;
     }
   }
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(1024) void gemv3_kernel(const f16* __restrict__ x, 
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         const float v = wave_sum_to_lane63(acc[r][m]);
-        if (lane == 63 && row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)(v * 0x1p24f);
+        if (lane == 63 && row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)v;
       }
     return;
   }
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(1024) void gemv3_kernel(const f16* __restrict__ x, 
     const int r = threadIdx.x / MB, m = threadIdx.x % MB;
     float v = 0.0f;
     for (int w = 0; w < nwaves; ++w) v += red[w][threadIdx.x];
-    if (row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)(v * 0x1p24f);
+    if (row0 + r < N) y[(int64_t)m * N + row0 + r] = (f16)v;
   }
 }
 
@@ -415,10 +417,11 @@ hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scale
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv_dot2_scaled(const void* x, const float* inv_s, const void* packed, const void* scales,
+hipError_t launch_gemv_dot2_scaled(const void* x, const float* s, const float* inv_s, const void* packed,
+                                   const void* scales,
                                    const void* zeros, void* y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  if (M == 1) return gemv_rows_launch<1, true>(x, packed, scales, zeros, y, N, K, st, inv_s);
-  if (M == 2) return gemv_rows_launch<2, true>(x, packed, scales, zeros, y, N, K, st, inv_s);
+  if (M == 1) return gemv_rows_launch<1, true>(x, packed, scales, zeros, y, N, K, st, s, inv_s);
+  if (M == 2) return gemv_rows_launch<2, true>(x, packed, scales, zeros, y, N, K, st, s, inv_s);
   return hipErrorInvalidValue;
 }
 
@@ -433,23 +436,27 @@ hipError_t launch_inverse_scale(const float* s, int64_t K, float* inv_s, hipStre
   return hipGetLastError();
 }
 
-// xs[m][k] = fp16(fp32(x[m][k]) * inv_s[k]); 8 channels per thread (K % 8 == 0).
-__global__ void scale_input_kernel(const f16* __restrict__ x, const float* __restrict__ inv_s, int64_t M, int64_t K,
+// xs[m][k] = fp16(fp32(x[m][k]) / s[k]): one IEEE fp32 division (correctly
+// rounded), then rounded once more to fp16; 8 channels per thread (K % 8 == 0).
+__global__ void scale_input_kernel(const f16* __restrict__ x, const float* __restrict__ s, int64_t M, int64_t K,
                                    f16* __restrict__ xs) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // chunk of 8 channels
   if (i >= M * (K / 8)) return;
   const int64_t k0 = (i % (K / 8)) * 8;
   const uint4 v = reinterpret_cast<const uint4*>(x)[i];
-  const float4 a = *reinterpret_cast<const float4*>(inv_s + k0), b = *reinterpret_cast<const float4*>(inv_s + k0 + 4);
-  const uint4 r{scale_pair(v.x, a.x, a.y), scale_pair(v.y, a.z, a.w), scale_pair(v.z, b.x, b.y),
-                scale_pair(v.w, b.z, b.w)};
+  const float4 a = *reinterpret_cast<const float4*>(s + k0), b = *reinterpret_cast<const float4*>(s + k0 + 4);
+  auto div_pair = [](uint32_t xw, float sa, float sb) {
+    const f16x2 h = as_f16x2(xw);
+    return as_u32(f16x2{(f16)((float)h.x / sa), (f16)((float)h.y / sb)});
+  };
+  const uint4 r{div_pair(v.x, a.x, a.y), div_pair(v.y, a.z, a.w), div_pair(v.z, b.x, b.y), div_pair(v.w, b.z, b.w)};
   reinterpret_cast<uint4*>(xs)[i] = r;
 }
 
-hipError_t launch_scale_input(const void* x, const float* inv_s, int64_t M, int64_t K, void* xs, hipStream_t st) {
+hipError_t launch_scale_input(const void* x, const float* s, int64_t M, int64_t K, void* xs, hipStream_t st) {
   const int64_t chunks = M * (K / 8);
   scale_input_kernel<<<dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st>>>(
-      reinterpret_cast<const f16*>(x), inv_s, M, K, reinterpret_cast<f16*>(xs));
+      reinterpret_cast<const f16*>(x), s, M, K, reinterpret_cast<f16*>(xs));
   return hipGetLastError();
 }
 
