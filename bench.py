@@ -235,32 +235,29 @@ def run_decode_3bit(args, torch, awq, dev):
 
 def run_decode_scaled(args, torch, awq, dev):
     """The decode step of run_decode with x not yet divided by s: awq_gemm_scaled divides it
-    (exactly, from s and inv_s = 1/s of awq_inverse_scale) inside the GEMV's x load on the
-    4096 x 4096 layers and with a separate scaling launch on the larger ones.  Bytes per
-    step add s and inv_s (8 K per layer).  s is a^0.5 of a lognormal channel profile."""
+    exactly (one scaling launch into a workspace, then the product) on every layer.  Bytes per
+    step add s (4 K per layer).  s is a^0.5 of a lognormal channel profile."""
     from gen import activations_fp16
-    step_bytes = sum(gemv_bytes(1, K, N) + 8 * K for _, K, N in LAYERS_7B)
+    step_bytes = sum(gemv_bytes(1, K, N) + 4 * K for _, K, N in LAYERS_7B)
     copies = max(2, int(np.ceil((1 << 30) / step_bytes)) + 1)
     layers = [Layer(n, K, N, torch, awq, copies, dev) for n, K, N in LAYERS_7B]
     for L in layers:
         g = np.random.default_rng(2200 + L.K)
         sv = np.sqrt(np.exp(g.normal(0.0, 0.8, L.K))).astype(np.float32)
         L.s = torch.from_numpy(sv).to(dev)
-        L.inv = awq.awq_inverse_scale(L.s)
-        L.ws = torch.empty(max(awq.awq_gemm_scaled_workspace_bytes(1, L.N, L.K), 16), dtype=torch.uint8, device=dev)
+        L.ws = torch.empty(awq.awq_gemm_scaled_workspace_bytes(1, L.N, L.K), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(c):
         for L in layers:
             p, s, z = L.copies[c]
-            awq.awq_gemm_scaled(L.x, L.s, p, s, z, out=L.y, workspace=L.ws, inv_s=L.inv)
+            awq.awq_gemm_scaled(L.x, L.s, p, s, z, out=L.y, workspace=L.ws)
 
     ms = time_steps(torch, step, copies, args.steps, args.warmup)
     del layers
-    fused = [n for n, K, N in LAYERS_7B if awq.awq_gemm_scaled_workspace_bytes(1, N, K) == 0]
     return dict(us_per_step=round(ms * 1e3, 3), GBs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
                 hbm_frac=round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), bytes_per_step=step_bytes,
-                launches=len(LAYERS_7B) + len(LAYERS_7B) - len(fused), fused_layers=fused)
+                launches=2 * len(LAYERS_7B))
 
 
 def run_sweep(args, torch, awq, dev):
@@ -613,7 +610,7 @@ def main():
         log("decode, q/k/v and gate/up fused by concatenated rows (4 launches)")
         legs["decode_fused_qkv_gateup"] = run_decode_fused(args, torch, awq, dev)
         torch.cuda.empty_cache()
-        log("decode, x divided by s on the device (fused into the GEMV on 4096 x 4096 layers)")
+        log("decode, x divided by s on the device (a scaling launch before each product)")
         legs["decode_llama2_7b_scaled_input"] = run_decode_scaled(args, torch, awq, dev)
         torch.cuda.empty_cache()
         log("decode, 3-bit weights (7 launches)")

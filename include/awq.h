@@ -257,21 +257,11 @@ int awq_gemm_bits(const void* x, const void* packed, const void* scales, const v
  * The input side of the per-channel scaling ([summary] paragraph 3: a weight
  * channel scaled up by s has its input divided by s, so the product keeps its
  * value).  awq_gemm takes x already divided; these calls do the division on
- * the device, fused into the decode GEMV where that kernel serves M.  The
- * scaled input is fp16(x / s): one IEEE fp32 division of fp32(x) by s
- * (correctly rounded), rounded once more to fp16 (round to nearest even).
+ * the device.  The scaled input is fp16(x / s): one IEEE fp32 division of
+ * fp32(x) by s (correctly rounded), rounded once more to fp16 (round to
+ * nearest even).
  *
- * awq_inverse_scale -- inv_s[k] = 1 / s[k], IEEE fp32 division (correctly
- * rounded), once per layer; awq_gemm_scaled's fused path needs it.
- *   s      device fp32 [K]   the s written by awq_quantize
- *   inv_s  device fp32 [K]   out
- * Requires 1 <= K <= 2^20.
- */
-int awq_inverse_scale(const float* s, int64_t K, float* inv_s, void* stream);
-
-/*
- * awq_scale_input -- xs[m][k] = fp16(fp32(x[m][k]) / s[k]), the division
- * correctly rounded in fp32, then rounded to fp16.
+ * awq_scale_input -- xs[m][k] = fp16(fp32(x[m][k]) / s[k]).
  *   x      device fp16 [M][K]
  *   s      device fp32 [K]   per-channel scale (awq_quantize's s)
  *   xs     device fp16 [M][K]   out (may not overlap x)
@@ -280,30 +270,22 @@ int awq_inverse_scale(const float* s, int64_t K, float* inv_s, void* stream);
 int awq_scale_input(const void* x, const float* s, int64_t M, int64_t K, void* xs, void* stream);
 
 /*
- * awq_gemm_scaled -- y = awq_scale_input(x, s) times w_hat^T: the product
- * of awq_gemm_bits on the scaled input, bit for bit.  At 4 bits with M = 1, and
- * M = 2 with K < 16384 (the vector-ALU GEMV), on layers with N * K <= 2^24, the
- * division happens in the GEMV's own x load: one launch, no intermediate, and
- * awq_gemm_scaled_workspace_bytes is 0 (workspace may be NULL).  There the
- * quotient comes from inv_s and one exact residual step (q0 = x inv_s,
- * r = x - s q0 in one fma, q = q0 + r inv_s in one fma), which equals the
- * correctly rounded x / s when inv_s is the correctly rounded 1/s and the
- * quotient is a normal fp32 number: s must be awq_inverse_scale's input and
- * inv_s its output, and every s must lie in [2^-64, 2^64] (awq_quantize's s
- * always does).  Otherwise the scaled input goes through `workspace` (device,
- * M * K * 2 bytes rounded up to 256) and awq_gemm_bits runs on it: on larger
- * layers the fused form's per-block re-read of s and inv_s costs more than the
- * second launch.
+ * awq_gemm_scaled -- y = awq_scale_input(x, s) times w_hat^T: the scaled input
+ * is written to `workspace` (device, awq_gemm_scaled_workspace_bytes =
+ * M * K * 2 bytes rounded up to 256), then the product of awq_gemm_bits runs
+ * on it, so y equals awq_gemm_bits on awq_scale_input's output bit for bit.
+ * (Dividing inside the decode GEMV's own x load instead repeats the division
+ * in every block, since each block spans all of K; done exactly that measured
+ * slower than the separate launch on every decode layer shape.)
  *   x      device fp16 [M][K]   activations, not divided by s
  *   s      device fp32 [K]      per-channel scale
- *   inv_s  device fp32 [K]      awq_inverse_scale(s)
  *   other arguments as awq_gemm_bits
  * Requires what awq_gemm_bits requires.
  */
 size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits);
-int awq_gemm_scaled(const void* x, const float* s, const float* inv_s, const void* packed, const void* scales,
-                    const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits,
-                    void* workspace, size_t workspace_bytes, void* stream);
+int awq_gemm_scaled(const void* x, const float* s, const void* packed, const void* scales, const void* zeros,
+                    void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /*
  * awq_unpack -- logical view of the packed format, for checking it.

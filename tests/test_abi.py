@@ -112,24 +112,21 @@ def test_gemm_argument_errors_before_launch():
 def test_input_scaling_queries_and_errors_before_launch():
     lib = _lib_()
     ws = lib.awq_gemm_scaled_workspace_bytes
-    assert ws(1, 4096, 4096, 4) == 0 and ws(2, 4096, 4096, 4) == 0  # fused into the GEMV's x load
-    assert ws(1, 11008, 4096, 4) == 4096 * 2                           # larger layer: scale, then GEMV
-    assert ws(2, 300, 16384, 4) == 2 * 16384 * 2                        # M = 2 on long rows: another kernel
+    assert ws(1, 4096, 4096, 4) == 4096 * 2 and ws(2, 300, 16384, 4) == 2 * 16384 * 2
     assert ws(3, 64, 4096, 4) == 3 * 4096 * 2 and ws(1, 64, 4096, 3) == 4096 * 2
     assert ws(5, 64, 136, 4) == (5 * 136 * 2 + 255) // 256 * 256
     assert ws(0, 64, 4096, 4) == 0 and ws(1, 64, 4096, 5) == 0
-    assert lib.awq_inverse_scale(None, 128, FAKE, None) == INVALID
-    assert lib.awq_inverse_scale(FAKE, 0, FAKE, None) == INVALID
     assert lib.awq_scale_input(FAKE, FAKE, 1, 12, FAKE, None) == INVALID       # K % 8
     assert lib.awq_scale_input(FAKE, FAKE, 0, 128, FAKE, None) == INVALID
+    assert lib.awq_scale_input(FAKE, None, 1, 128, FAKE, None) == INVALID
     f = lib.awq_gemm_scaled
-    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 4, None, 0, None) == INVALID
-    assert f(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 4, None, 0, None) == INVALID
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 128, 4, None, 0, None) == INVALID   # K % group
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 5, None, 0, None) == INVALID   # bits
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, None, 0, None) == WS_SMALL
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE, 767, None) == WS_SMALL
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE_MISALIGNED, 768, None) == MISALIGNED
+    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 4, FAKE, 256, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 4, None, 256, None) == INVALID   # workspace
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 128, 4, FAKE, 256, None) == INVALID   # K % group
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 5, FAKE, 256, None) == INVALID   # bits
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE, 767, None) == WS_SMALL
+    assert "workspace" in awq.awq_last_error()
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 128, 4, FAKE_MISALIGNED, 768, None) == MISALIGNED
     assert "workspace" in awq.awq_last_error()
 
 
@@ -151,11 +148,9 @@ MISALIGNED_CASES = {
                                 12: "workspace"}),
     "awq_gemm_bits": ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 256, 128, 4, None),
                       {0: "x", 1: "packed", 2: "scales", 3: "zeros", 4: "y"}),
-    "awq_inverse_scale": ((FAKE, 256, FAKE, None), {0: "s", 2: "inv_s"}),
     "awq_scale_input": ((FAKE, FAKE, 1, 256, FAKE, None), {0: "x", 1: "s", 4: "xs"}),
-    "awq_gemm_scaled": ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 256, 128, 4, FAKE, 1 << 20, None),
-                        {0: "x", 1: "s", 2: "inv_s", 3: "packed", 4: "scales", 5: "zeros", 6: "y",
-                         12: "workspace"}),
+    "awq_gemm_scaled": ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 256, 128, 4, FAKE, 1 << 20, None),
+                        {0: "x", 1: "s", 2: "packed", 3: "scales", 4: "zeros", 5: "y", 11: "workspace"}),
     "awq_unpack_bits": ((FAKE, FAKE, 64, 256, 128, 4, FAKE, FAKE, None),
                         {0: "packed", 1: "zeros", 6: "codes", 7: "zeros_u8"}),
 }

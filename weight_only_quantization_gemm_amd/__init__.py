@@ -13,7 +13,6 @@ from .api import (  # noqa: F401
     awq_gemm,
     awq_gemm_scaled,
     awq_gemm_scaled_workspace_bytes,
-    awq_inverse_scale,
     awq_keep_fp16_ablation,
     awq_last_error,
     awq_pack,

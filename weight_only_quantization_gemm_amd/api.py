@@ -201,15 +201,6 @@ def awq_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros:
     return out
 
 
-def awq_inverse_scale(s: torch.Tensor) -> torch.Tensor:
-    """inv_s = 1 / s (fp32 [K], IEEE division on the device), once per layer."""
-    _need(s, "s", torch.float32, 1)
-    inv = torch.empty_like(s)
-    with torch.cuda.device(s.device):
-        check(load().awq_inverse_scale(s.data_ptr(), s.shape[0], inv.data_ptr(), _stream(s.device)))
-    return inv
-
-
 def awq_scale_input(x: torch.Tensor, s: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """xs = fp16(fp32(x) / s) per input channel (IEEE fp32 division, then fp16); x fp16 [M][K]."""
     _need(x, "x", torch.float16, 2)
@@ -234,12 +225,9 @@ def awq_gemm_scaled_workspace_bytes(M: int, N: int, K: int, bits: int = 4) -> in
 
 def awq_gemm_scaled(x: torch.Tensor, s: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
                     zeros: torch.Tensor, out: Optional[torch.Tensor] = None, group: int = GROUP,
-                    bits: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-                    inv_s: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y = awq_scale_input(x, s) @ w_hat^T; x fp16 [M][K] not divided by s.  inv_s is
-    awq_inverse_scale(s) (computed here when not given; a layer computes it once).  At 4 bits,
-    M <= 2 and N * K <= 2^24 the division happens inside the GEMV's x load (no workspace);
-    otherwise a workspace of awq_gemm_scaled_workspace_bytes bytes is taken from `workspace`
+                    bits: Optional[int] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = awq_scale_input(x, s) @ w_hat^T; x fp16 [M][K] not divided by s.  The scaled input
+    goes through a workspace of awq_gemm_scaled_workspace_bytes bytes, taken from `workspace`
     or allocated."""
     _need(x, "x", torch.float16, 2)
     _need(s, "s", torch.float32, 1)
@@ -254,12 +242,6 @@ def awq_gemm_scaled(x: torch.Tensor, s: torch.Tensor, packed: torch.Tensor, scal
     if s.shape[0] != K or packed.shape[1] != packed_words(K, bits) or tuple(scales.shape) != (N, G) or \
             tuple(zeros.shape) != (N, (G + 1) // 2):
         raise ValueError("s/packed/scales/zeros do not match x's K")
-    if inv_s is None:
-        inv_s = awq_inverse_scale(s)
-    else:
-        _need(inv_s, "inv_s", torch.float32, 1)
-        if inv_s.shape[0] != K:
-            raise ValueError("inv_s must have K entries")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
     else:
@@ -267,12 +249,12 @@ def awq_gemm_scaled(x: torch.Tensor, s: torch.Tensor, packed: torch.Tensor, scal
         if tuple(out.shape) != (M, N):
             raise ValueError("out must be fp16 [M][N]")
     need = awq_gemm_scaled_workspace_bytes(M, N, K, bits)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     with torch.cuda.device(x.device):
-        check(load().awq_gemm_scaled(x.data_ptr(), s.data_ptr(), inv_s.data_ptr(), packed.data_ptr(),
-                                     scales.data_ptr(), zeros.data_ptr(), out.data_ptr(), M, N, K, group, bits,
-                                     _ptr(workspace), need if need else 0, _stream(x.device)))
+        check(load().awq_gemm_scaled(x.data_ptr(), s.data_ptr(), packed.data_ptr(), scales.data_ptr(),
+                                     zeros.data_ptr(), out.data_ptr(), M, N, K, group, bits, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream(x.device)))
     return out
 
 

@@ -377,15 +377,6 @@ int awq_gemm_bits(const void* x, const void* packed, const void* scales, const v
   AWQ_GUARD_END
 }
 
-int awq_inverse_scale(const float* s, int64_t K, float* inv_s, void* stream) {
-  AWQ_GUARD_BEGIN
-  AWQ_REQUIRE(s && inv_s, AWQ_ERROR_INVALID_VALUE, "s and inv_s must not be NULL");
-  AWQ_REQUIRE(K >= 1 && K <= (int64_t(1) << 20), AWQ_ERROR_INVALID_VALUE, "K=%lld outside [1, 2^20]", (long long)K);
-  if (int st = check_aligned({{s, "s"}, {inv_s, "inv_s"}})) return st;
-  return device_status(awq::launch_inverse_scale(s, K, inv_s, as_stream(stream)), "awq_inverse_scale");
-  AWQ_GUARD_END
-}
-
 int awq_scale_input(const void* x, const float* s, int64_t M, int64_t K, void* xs, void* stream) {
   AWQ_GUARD_BEGIN
   AWQ_REQUIRE(x && s && xs, AWQ_ERROR_INVALID_VALUE, "x, s and xs must not be NULL");
@@ -395,16 +386,6 @@ int awq_scale_input(const void* x, const float* s, int64_t M, int64_t K, void* x
   if (int st = check_aligned({{x, "x"}, {s, "s"}, {xs, "xs"}})) return st;
   return device_status(awq::launch_scale_input(x, s, M, K, xs, as_stream(stream)), "awq_scale_input");
   AWQ_GUARD_END
-}
-
-// The division fused into the M <= 2 GEMV's x load costs every block another read
-// of inv_s (4 bytes per channel, twice what x takes): on layers up to 4096 x 4096
-// that is cheaper than a second launch (measured on 4096 x 4096: 5.1 us fused,
-// 5.6 us as scale-then-GEMV, 3.8 us unscaled); on larger ones the extra L2 traffic
-// costs more than the launch (4096 x 11008: 10.1 against 7.9 us; 8192 x 28672:
-// 31.2 against 23.2 us), so those take the two-launch path.
-static bool scaled_fused(int64_t M, int64_t N, int64_t K, int32_t bits) {
-  return bits == 4 && awq::gemv_dot2_supported(M, K) && N * K <= (int64_t(1) << 24);
 }
 
 // The scaled input through a buffer of M * K halfs: awq_scale_input, then the
@@ -421,32 +402,26 @@ static hipError_t gemm_scaled_via(const void* x, const float* s, const void* pac
 
 size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits) {
   if (M < 1 || N < 1 || K < 1 || (bits != 4 && bits != 3)) return 0;
-  if (scaled_fused(M, N, K, bits)) return 0;  // no intermediate
   return (size_t)((M * K * 2 + 255) / 256 * 256);
 }
 
-int awq_gemm_scaled(const void* x, const float* s, const float* inv_s, const void* packed, const void* scales,
-                    const void* zeros, void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+int awq_gemm_scaled(const void* x, const float* s, const void* packed, const void* scales, const void* zeros,
+                    void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   AWQ_GUARD_BEGIN
-  AWQ_REQUIRE(x && s && inv_s && packed && scales && zeros && y, AWQ_ERROR_INVALID_VALUE,
-              "x, s, inv_s, packed, scales, zeros and y must not be NULL");
+  AWQ_REQUIRE(x && s && packed && scales && zeros && y && workspace, AWQ_ERROR_INVALID_VALUE,
+              "x, s, packed, scales, zeros, y and workspace must not be NULL");
   int st = check_layer(N, K, group);
   if (st == AWQ_OK) st = check_bits(bits);
   if (st != AWQ_OK) return st;
   AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
-  if (int st2 = check_aligned({{x, "x"}, {s, "s"}, {inv_s, "inv_s"}, {packed, "packed"}, {scales, "scales"},
-                                {zeros, "zeros"}, {y, "y"}}))
+  if (int st2 = check_aligned({{x, "x"}, {s, "s"}, {packed, "packed"}, {scales, "scales"}, {zeros, "zeros"},
+                                {y, "y"}, {workspace, "workspace"}}))
     return st2;
   const size_t need = awq_gemm_scaled_workspace_bytes(M, N, K, bits);
-  const hipStream_t hs = as_stream(stream);
-  if (need == 0)
-    return device_status(awq::launch_gemv_dot2_scaled(x, s, inv_s, packed, scales, zeros, y, M, N, K, hs),
-                         "awq_gemm_scaled");
-  AWQ_REQUIRE(workspace && workspace_bytes >= need, AWQ_ERROR_WORKSPACE_TOO_SMALL,
+  AWQ_REQUIRE(workspace_bytes >= need, AWQ_ERROR_WORKSPACE_TOO_SMALL,
               "workspace_bytes=%zu below awq_gemm_scaled_workspace_bytes=%zu", workspace_bytes, need);
-  if (int st2 = check_aligned({{workspace, "workspace"}})) return st2;
-  return device_status(gemm_scaled_via(x, s, packed, scales, zeros, y, M, N, K, bits, workspace, hs),
+  return device_status(gemm_scaled_via(x, s, packed, scales, zeros, y, M, N, K, bits, workspace, as_stream(stream)),
                        "awq_gemm_scaled");
   AWQ_GUARD_END
 }

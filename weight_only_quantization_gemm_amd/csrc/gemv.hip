@@ -44,28 +44,6 @@ __device__ inline float dot2_acc(f16x2 a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, a), __builtin_bit_cast(h16x2, b), c, false);
 }
 
-// The correctly rounded quotient x / s in fp32 from inv = RN(1/s), with no
-// division instruction.  q0 = RN(x inv) can be off by a little more than one
-// ulp, so one residual step q1 = RN(q0 + RN(x - s q0) inv) first makes it
-// faithful (within one ulp); then the residual r = x - s q1 is exact in one
-// fma, and RN(q1 + r inv) is the correctly rounded quotient (Markstein's
-// theorem on division with a correctly rounded reciprocal; it holds while
-// x / s is a normal fp32 number).  q0 is kept when it is 0, so a zero x keeps
-// its sign.
-__device__ inline float div_by_scale(float x, float s, float inv) {
-  const float q0 = x * inv;
-  const float q1 = fmaf(fmaf(-q0, s, x), inv, q0);
-  const float q2 = fmaf(fmaf(-q1, s, x), inv, q1);
-  return q0 == 0.0f ? q0 : q2;
-}
-
-// The fp16 pair xw divided channel-wise by (sa, sb): fp16(RN32(x / s)) per
-// value, the fp32 quotient rounded once more to fp16.
-__device__ inline uint32_t scale_pair(uint32_t xw, float sa, float sb, float ia, float ib) {
-  const f16x2 v = as_f16x2(xw);
-  return as_u32(f16x2{(f16)div_by_scale((float)v.x, sa, ia), (f16)div_by_scale((float)v.y, sb, ib)});
-}
-
 // DPP add: v + v[permuted lane]; lanes whose source row is masked off add 0.
 template <int CTRL, int ROW_MASK>
 __device__ inline float dpp_add(float v) {
@@ -94,18 +72,10 @@ __host__ __device__ inline int gemv_waves(int64_t K) {
 }
 
 // K <= 32768 (at most 1024 chunks) keeps a block within 16 waves.
-//
-// With SC, x is first divided by the per-channel scale s of the method
-// ([summary] paragraph 3: a channel whose weights were scaled up by s has its
-// input divided by s): each lane also loads s and inv_s = RN(1/s) (fp32, 256 B
-// for its 32 channels) with its other loads, and every x value becomes
-// fp16(RN32(x / s)) (div_by_scale) before the products -- the values
-// awq_scale_input writes, so the result equals this kernel on those values.
-template <int MB, int R, bool SC = false>
+template <int MB, int R>
 __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                     const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                                                    f16* __restrict__ y, int N, int K, const float* __restrict__ s_in,
-                                                    const float* __restrict__ inv_s) {
+                                                    f16* __restrict__ y, int N, int K) {
   __shared__ float red[kMaxWaves][R * MB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = gemv_waves(K);  // == blockDim.x / 64, from the arguments (all preloaded)
@@ -137,7 +107,6 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
   uint32_t sr[R], zr[R];
   uint4 xv[MB][4];
   u32x4 wv[R];
-  float4 sv[SC ? 8 : 1], iv[SC ? 8 : 1];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     sr[r] = srow[r][g];
@@ -147,29 +116,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int u = 0; u < 4; ++u) xv[m][u] = reinterpret_cast<const uint4*>(x + (int64_t)m * K)[c * 4 + u];
-  if constexpr (SC) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      sv[u] = reinterpret_cast<const float4*>(s_in)[c * 8 + u];
-      iv[u] = reinterpret_cast<const float4*>(inv_s)[c * 8 + u];
-    }
-  }
 #pragma unroll
   for (int r = 0; r < R; ++r) wv[r] = __builtin_nontemporal_load(wrow[r] + c);
   __builtin_amdgcn_sched_barrier(0);
-
-  if constexpr (SC) {  // x word u.{x,y,z,w} holds channels 8u + {0,1}, {2,3}, {4,5}, {6,7} of the chunk
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4 sa = sv[2 * u], sb = sv[2 * u + 1], ia = iv[2 * u], ib = iv[2 * u + 1];
-        xv[m][u].x = scale_pair(xv[m][u].x, sa.x, sa.y, ia.x, ia.y);
-        xv[m][u].y = scale_pair(xv[m][u].y, sa.z, sa.w, ia.z, ia.w);
-        xv[m][u].z = scale_pair(xv[m][u].z, sb.x, sb.y, ib.x, ib.y);
-        xv[m][u].w = scale_pair(xv[m][u].w, sb.z, sb.w, ib.z, ib.w);
-      }
-  }
 
   const uint32_t bias = bias_in_vgpr();
   float acc[R][MB];
@@ -228,15 +177,15 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const f16* __restrict__ x, c
   }
 }
 
-template <int MB, int R, bool SC>
+template <int MB, int R>
 static hipError_t gemv_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                              int64_t N, int64_t K, const float* s, const float* inv_s, hipStream_t st) {
+                              int64_t N, int64_t K, hipStream_t st) {
   const int waves = gemv_waves(K);
   if (waves > kMaxWaves) return hipErrorInvalidValue;
   dim3 grid((unsigned)((N + R - 1) / R));
-  gemv_kernel<MB, R, SC><<<grid, dim3(waves * kWave), 0, st>>>(
+  gemv_kernel<MB, R><<<grid, dim3(waves * kWave), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
-      reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)N, (int)K, s, inv_s);
+      reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -257,13 +206,12 @@ bool gemv_dot2_supported(int64_t M, int64_t K) {
 // layer; 4 elsewhere, which keeps more blocks in flight (4096 x 11008 at
 // 6.1 us and 11008 x 4096 at 6.8 us, against 6.8 and 7.2 us with 8).  More
 // chunks per lane (fewer waves) measured slower on every shape.
-template <int MB, bool SC = false>
+template <int MB>
 static hipError_t gemv_rows_launch(const void* x, const void* packed, const void* scales, const void* zeros,
-                                   void* y, int64_t N, int64_t K, hipStream_t st, const float* s = nullptr,
-                                   const float* inv_s = nullptr) {
+                                   void* y, int64_t N, int64_t K, hipStream_t st) {
   if ((K >= 8192 && N >= 8192) || (MB == 2 && N >= 16384))
-    return gemv_launch<MB, 8, SC>(x, packed, scales, zeros, y, N, K, s, inv_s, st);
-  return gemv_launch<MB, 4, SC>(x, packed, scales, zeros, y, N, K, s, inv_s, st);
+    return gemv_launch<MB, 8>(x, packed, scales, zeros, y, N, K, st);
+  return gemv_launch<MB, 4>(x, packed, scales, zeros, y, N, K, st);
 }
 
 // 3-bit format (three words per 32 channels of a row; see the packer).  The
@@ -415,25 +363,6 @@ hipError_t launch_gemv_dot2(const void* x, const void* packed, const void* scale
   if (M == 1) return gemv_rows_launch<1>(x, packed, scales, zeros, y, N, K, st);
   if (M == 2) return gemv_rows_launch<2>(x, packed, scales, zeros, y, N, K, st);
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_gemv_dot2_scaled(const void* x, const float* s, const float* inv_s, const void* packed,
-                                   const void* scales,
-                                   const void* zeros, void* y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  if (M == 1) return gemv_rows_launch<1, true>(x, packed, scales, zeros, y, N, K, st, s, inv_s);
-  if (M == 2) return gemv_rows_launch<2, true>(x, packed, scales, zeros, y, N, K, st, s, inv_s);
-  return hipErrorInvalidValue;
-}
-
-// inv_s[k] = 1 / s[k], IEEE fp32 division (correctly rounded).
-__global__ void inverse_scale_kernel(const float* __restrict__ s, int64_t K, float* __restrict__ inv_s) {
-  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k < K) inv_s[k] = 1.0f / s[k];
-}
-
-hipError_t launch_inverse_scale(const float* s, int64_t K, float* inv_s, hipStream_t st) {
-  inverse_scale_kernel<<<dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st>>>(s, K, inv_s);
-  return hipGetLastError();
 }
 
 // xs[m][k] = fp16(fp32(x[m][k]) / s[k]): one IEEE fp32 division (correctly
