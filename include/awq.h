@@ -288,6 +288,27 @@ int awq_gemm_scaled(const void* x, const float* s, const void* packed, const voi
                     size_t workspace_bytes, void* stream);
 
 /*
+ * awq_gemm_scaled_static -- awq_gemm_scaled with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The call allocates
+ * nothing: the scaled input goes to a static device array of
+ * AWQ_STATIC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call made with that device current).  y equals awq_gemm_scaled's
+ * bit for bit.  Every call on one device shares that device's array, which
+ * keeps the last call's contents (each call writes the part it then reads, so
+ * nothing needs clearing): calls that overlap on one device -- on different
+ * streams, or from threads with no ordering between them -- race and give
+ * unspecified results; calls ordered on one stream do not.
+ * Requires awq_gemm_scaled_workspace_bytes(M, N, K, bits) <=
+ * AWQ_STATIC_SCRATCH_BYTES (M * K <= 2^23 halfs; otherwise
+ * AWQ_ERROR_INVALID_VALUE) and what awq_gemm_scaled requires.
+ */
+#define AWQ_STATIC_SCRATCH_BYTES (16u << 20)
+int awq_gemm_scaled_static(const void* x, const float* s, const void* packed, const void* scales, const void* zeros,
+                           void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* stream);
+
+/*
  * awq_unpack -- logical view of the packed format, for checking it.
  *   codes     device uint8 [N][K]     out: code of every weight
  *   zeros_u8  device uint8 [N][K/g]   out: zero point of every group

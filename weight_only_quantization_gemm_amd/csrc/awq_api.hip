@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "awq.h"
@@ -127,6 +128,36 @@ QuantizeWorkspace quantize_workspace(int64_t N, int64_t K, int64_t M, int32_t n_
   }
   w.total = off;
   return w;
+}
+
+// The device array behind awq_gemm_scaled_static: the scaled input of calls
+// made by callers that cannot allocate.  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol, never a device address: the address is looked up
+// per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[AWQ_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call made
+// with that device current.
+int device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(AWQ_ERROR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(AWQ_ERROR_DEVICE, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(AWQ_ERROR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return AWQ_OK;
 }
 
 }  // namespace
@@ -423,6 +454,29 @@ int awq_gemm_scaled(const void* x, const float* s, const void* packed, const voi
               "workspace_bytes=%zu below awq_gemm_scaled_workspace_bytes=%zu", workspace_bytes, need);
   return device_status(gemm_scaled_via(x, s, packed, scales, zeros, y, M, N, K, bits, workspace, as_stream(stream)),
                        "awq_gemm_scaled");
+  AWQ_GUARD_END
+}
+
+int awq_gemm_scaled_static(const void* x, const float* s, const void* packed, const void* scales, const void* zeros,
+                           void* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(x && s && packed && scales && zeros && y, AWQ_ERROR_INVALID_VALUE,
+              "x, s, packed, scales, zeros and y must not be NULL");
+  int st = check_layer(N, K, group);
+  if (st == AWQ_OK) st = check_bits(bits);
+  if (st != AWQ_OK) return st;
+  AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
+  const size_t need = awq_gemm_scaled_workspace_bytes(M, N, K, bits);
+  AWQ_REQUIRE(need <= AWQ_STATIC_SCRATCH_BYTES, AWQ_ERROR_INVALID_VALUE,
+              "M * K * 2 = %zu bytes exceeds the static scratch of %u bytes", (size_t)(M * K * 2),
+              (unsigned)AWQ_STATIC_SCRATCH_BYTES);
+  if (int st2 = check_aligned({{x, "x"}, {s, "s"}, {packed, "packed"}, {scales, "scales"}, {zeros, "zeros"},
+                                {y, "y"}}))
+    return st2;
+  void* xs = nullptr;
+  if (int st2 = device_scratch(&xs)) return st2;
+  return device_status(gemm_scaled_via(x, s, packed, scales, zeros, y, M, N, K, bits, xs, as_stream(stream)),
+                       "awq_gemm_scaled_static");
   AWQ_GUARD_END
 }
 
