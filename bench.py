@@ -152,7 +152,7 @@ def time_steps(torch, step, copies, steps, warmup):
     return ev0.elapsed_time(ev1) / steps
 
 
-def run_decode(args, torch, awq, dev):
+def run_decode(args, torch, awq, dev, per_layer=True):
     step_bytes = sum(gemv_bytes(1, K, N) for _, K, N in LAYERS_7B)
     copies = max(2, int(np.ceil((1 << 30) / step_bytes)) + 1)
     layers = [Layer(n, K, N, torch, awq, copies, dev) for n, K, N in LAYERS_7B]
@@ -171,18 +171,23 @@ def run_decode(args, torch, awq, dev):
     bytes_per_launch = step_bytes / launches
     achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
 
-    # per layer: a graph of `copies` launches of that layer alone (each weight copy once)
+    # per layer: a graph of that layer alone over its own rotating copies, more than 1 GiB of
+    # that layer's bytes (so the 256 MB Infinity Cache cannot serve them)
     detail = {}
-    for L in layers:
-        def one(L=L):
-            for c in range(copies):
-                p, s, z = L.copies[c]
+    for L in (layers if per_layer else []):
+        own = max(3, -(-(1 << 30) // L.bytes) + 1)
+        extra = [tuple(t.clone() for t in L.copies[0]) for _ in range(max(0, own - copies))]
+        pool = (L.copies + extra)[:own]
+
+        def one(L=L, pool=pool):
+            for p, s, z in pool:
                 awq.awq_gemm(L.x, p, s, z, out=L.y)
         g = graph_of(torch, one)
-        ms = time_replays(torch, [g], max(5, args.steps // copies), 2) / copies
-        detail[L.name] = dict(K=L.K, N=L.N, bytes=L.bytes, us=round(ms * 1e3, 3),
+        ms = time_replays(torch, [g], max(5, args.steps // len(pool)), 2) / len(pool)
+        detail[L.name] = dict(K=L.K, N=L.N, bytes=L.bytes, us=round(ms * 1e3, 3), copies=len(pool),
                               GBs=round(L.bytes / (ms * 1e-3) / 1e9, 1))
-        del g
+        del g, pool, extra
+        torch.cuda.empty_cache()
     return dict(step_bytes=step_bytes, copies=copies, ms_per_step=ms_per_step, wall_s=wall,
                 kern_ms=kern_ms, achieved=achieved, bytes_per_launch=bytes_per_launch, per_layer=detail,
                 layers=layers)
@@ -386,19 +391,27 @@ def run_ablation(torch, awq, dev, W, X, search_loss):
                 awq_search_ratio_vs_rtn=float(search_loss.min() / search_loss[0]))
 
 
-def search_roofline_ms(M, K, N, n_alpha=20, statistics=True):
-    """Composite roofline of one awq_quantize call, sum over its phases of
-    max(bytes / 8 TB/s, flops / 2.5 PFLOP/s), algorithmic amounts: statistics read X
-    once (2 M K bytes); the Gram is a symmetric product (M K (K + 1) flops); each alpha
-    reads W and writes its error as an fp16 hi/lo pair (6 N K bytes) and forms the
-    quadratic form as the three-term fp16 split (3 x 2 N K^2 flops); the pack reads W
-    and writes the packed layer."""
-    bw, pk = HBM_PEAK_GBS * 1e9, 2.5e15
+def search_roofline_ms(M, K, N, n_alpha=20, statistics=True, accounting="method"):
+    """Composite roofline of one awq_quantize call: the sum over its phases of
+    max(bytes / 8 TB/s, flops / 2.5 PFLOP/s), in milliseconds.
+
+    accounting="method" counts what the method needs: the statistics read X once
+    (2 M K bytes) and, where the Gram form applies (M >= K), form G as a symmetric product
+    (M K (K + 1) flops); each alpha reads W once (2 N K bytes) and evaluates the output MSE
+    as a quadratic form (2 N K min(M, K) flops); the pack reads W and writes the packed
+    layer.  accounting="split" counts the work of this implementation's loss instead: per
+    alpha the error written and read back as an fp16 hi/lo pair (6 N K bytes) and the
+    quadratic form as the three-term split (3 x 2 N K^2 flops)."""
+    bw, pk = HBM_PEAK_GBS * 1e9, FP16_PEAK_TFLOPS * 1e12
     t = 0.0
     if statistics:  # without: taken from an earlier call on the same input
         t += 2.0 * M * K / bw
-        t += M * K * (K + 1) / pk
-    t += n_alpha * max(6.0 * N * K / bw, 6.0 * N * K * K / pk)
+        if M >= K:
+            t += M * K * (K + 1) / pk
+    if accounting == "method":
+        t += n_alpha * max(2.0 * N * K / bw, 2.0 * N * K * min(M, K) / pk)
+    else:
+        t += n_alpha * max(6.0 * N * K / bw, 6.0 * N * K * K / pk)
     t += (2.0 * N * K + gemv_bytes(1, K, N)) / bw
     return t * 1e3
 
@@ -463,13 +476,19 @@ def run_search(args, torch, awq, dev):
         del ws, Ws
         torch.cuda.empty_cache()
     roof = sum(search_roofline_ms(M, K, N) for _, K, N in LAYERS_7B)
+    roof_split = sum(search_roofline_ms(M, K, N, accounting="split") for _, K, N in LAYERS_7B)
     roof_shared = sum(search_roofline_ms(M, Ks[l][0], Ks[l][1], statistics=j == 0)
                       for group in by_src.values() for j, (_, l) in enumerate(group))
     for lname, r_ in res.items():
         r_["roofline_ms"] = round(search_roofline_ms(M, r_["K"], r_["N"]), 3)
+        r_["roofline_ms_split_accounting"] = round(search_roofline_ms(M, r_["K"], r_["N"], accounting="split"), 3)
     return dict(layers=res, s_per_layer=round(total_ms / 7 / 1e3, 4), total_s=round(total_ms / 1e3, 3),
                 calib_rows=M, n_alpha=20, composite_roofline_s=round(roof / 1e3, 4),
                 composite_roofline_frac=round(roof / total_ms, 4),
+                composite_roofline_accounting="method: X read once, symmetric Gram, per alpha W read once "
+                                              "and 2 N K min(M, K) loss flops at the fp16 peak, pack",
+                composite_roofline_s_split_accounting=round(roof_split / 1e3, 4),
+                composite_roofline_frac_split_accounting=round(roof_split / total_ms, 4),
                 total_s_shared_statistics=round(shared_ms / 1e3, 3),
                 s_per_layer_shared_statistics=round(shared_ms / 7 / 1e3, 4),
                 composite_roofline_s_shared_statistics=round(roof_shared / 1e3, 4),
@@ -538,8 +557,110 @@ def run_cpu_baseline(layers_spec, budget_s: float):
                        f"(fp64 dequantize + matmul), {dt:.1f} s")
 
 
+def load_ceilings():
+    """ctypes view of libawq_ceilings.so (include/awq_ceilings.h)."""
+    import ctypes
+    path = os.path.join(ROOT, "weight_only_quantization_gemm_amd", "libawq_ceilings.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    lib.awq_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_void_p]
+    lib.awq_ceiling_mfma_f16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p]
+    return lib
+
+
+CEILING_READ_SIZES = [("7B 4096x4096 layer", 8732672), ("7B 4096x11008 layer", 23455232),
+                      ("70B 8192x10240 layer", 43618304), ("70B 8192x28672 layer", 122101760), ("1 GiB", 1 << 30)]
+
+
+def run_ceilings(args, torch, dev):
+    """What one device reaches with nothing but the product kernels' own access pattern:
+    a streaming read of each decode layer's size with 16-byte non-temporal loads (rotating
+    copies over more than 1 GiB, graph-timed), and dense fp16 matrix-core throughput
+    (v_mfma_f32_32x32x16_f16, 8 independent chains per wave, one or two waves per SIMD)."""
+    lib = load_ceilings()
+    out = {"stream_read": {}, "mfma_f16_32x32x16": {}}
+    for label, nbytes in CEILING_READ_SIZES:
+        nb = nbytes // 16 * 16
+        copies = max(2, -(-int(1.1 * (1 << 30)) // nb) + 1)
+        bufs = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        blocks = int(min(max(1, nb // 16 // 1024), 8192))
+        sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+
+        def run(bufs=bufs, blocks=blocks, sink=sink, nb=nb):
+            st = torch.cuda.current_stream().cuda_stream
+            for b in bufs:
+                assert lib.awq_ceiling_stream_read(b.data_ptr(), nb, sink.data_ptr(), blocks, st) == 0
+        g = graph_of(torch, run)
+        ms = time_replays(torch, [g], max(3, 40 // copies), 1) / copies
+        out["stream_read"][label] = dict(bytes=nb, us=round(ms * 1e3, 3), GBs=round(nb / (ms * 1e-3) / 1e9, 1),
+                                         hbm_frac=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), copies=copies)
+        del g, bufs, sink
+        torch.cuda.empty_cache()
+    for wps in (1, 2):
+        blocks, iters = 256, 8192
+        sink = torch.empty(blocks * 4 * wps, dtype=torch.float32, device=dev)
+        st = torch.cuda.current_stream().cuda_stream
+        assert lib.awq_ceiling_mfma_f16(sink.data_ptr(), blocks, 16, wps, st) == 0  # warm-up
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        assert lib.awq_ceiling_mfma_f16(sink.data_ptr(), blocks, iters, wps, st) == 0
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        flops = blocks * 4 * wps * iters * 8 * 32768.0
+        out["mfma_f16_32x32x16"][f"{wps}_wave_per_simd"] = dict(
+            us=round(ms * 1e3, 1), TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1),
+            frac=round(flops / (ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4))
+    return out
+
+
+TRACE_FILE = os.path.join(ROOT, "profiles", "gemv_llama2_7b_decode_m1_trace.md")
+
+
+def trace_summary_for_roofline():
+    """The headline kernel's figures from the committed rocprofv3 trace summary of the decode
+    profile mode (the same step graphs as the timed region), when it was taken on the current
+    GEMV source; else None."""
+    if not os.path.exists(TRACE_FILE):
+        return None
+    text = open(TRACE_FILE).read()
+    fields = dict(re.findall(r"^(source_hash|mean_launch_us|span_per_launch_us|dispatches):\s*(\S+)", text, re.M))
+    if fields.get("source_hash") != source_hash(GEMV_SOURCES):
+        return None
+    return dict(file=os.path.relpath(TRACE_FILE, ROOT), mean_launch_us=float(fields["mean_launch_us"]),
+                span_per_launch_us=float(fields["span_per_launch_us"]), dispatches=int(fields["dispatches"]))
+
+
+def summarize_trace(csv_path, pattern, out_lines):
+    """Per-kernel dispatch statistics from a rocprofv3 kernel_trace.csv: count and mean /
+    median duration of the kernels whose name contains `pattern`, and the span from the first
+    such dispatch's start to the last one's end divided by their count (the trace's analogue
+    of a timed region divided by its launches)."""
+    import csv
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if pattern in r.get("Kernel_Name", ""):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    if not rows:
+        raise SystemExit(f"no dispatch of a kernel matching {pattern!r} in {csv_path}")
+    rows.sort()
+    d = np.array([e - b for b, e in rows], dtype=np.float64) / 1e3
+    span = (max(e for _, e in rows) - rows[0][0]) / 1e3
+    out_lines += [f"dispatches: {len(rows)}", f"mean_launch_us: {d.mean():.3f}",
+                  f"median_launch_us: {np.median(d):.3f}", f"min_launch_us: {d.min():.3f}",
+                  f"max_launch_us: {d.max():.3f}", f"span_per_launch_us: {span / len(rows):.3f}",
+                  f"source_hash: {source_hash(GEMV_SOURCES)}"]
+    return out_lines
+
+
 def profile_mode(args, torch, awq, dev):
-    """Short runs for rocprofv3 counter passes: the decode GEMVs, a plain copy, or one GEMM / decode layer."""
+    """Short runs for rocprofv3: the headline decode step graphs alone, a plain copy (counter
+    scale), one GEMM or decode-ring layer, or the ceiling kernels."""
     if args.profile_mode == "copy":
         n = 256 << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -548,6 +669,9 @@ def profile_mode(args, torch, awq, dev):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps(dict(profile_mode="copy", bytes_per_copy=n, launches=5)))
+        return
+    if args.profile_mode == "ceilings":
+        print(json.dumps(dict(profile_mode="ceilings", **run_ceilings(args, torch, dev))))
         return
     if args.profile_mode in ("gemm", "ring"):
         # one layer, 20 launches: the M = 256 GEMM on (4096, 11008), or the M = 16 decode
@@ -564,9 +688,11 @@ def profile_mode(args, torch, awq, dev):
         torch.cuda.synchronize()
         print(json.dumps(dict(profile_mode=args.profile_mode, K=K, N=N, M=M, launches=20)))
         return
-    r = run_decode(args, torch, awq, dev)
-    print(json.dumps(dict(profile_mode="gemv", alg_bytes_per_launch=r["bytes_per_launch"], kern_ms=r["kern_ms"],
-                          per_layer=r["per_layer"])))
+    # decode: the headline's step graphs only (warm-up and timed replays, as in the default run)
+    r = run_decode(args, torch, awq, dev, per_layer=False)
+    print(json.dumps(dict(profile_mode="decode", alg_bytes_per_launch=r["bytes_per_launch"],
+                          ms_per_step=r["ms_per_step"], avg_launch_us=round(r["kern_ms"] * 1e3, 3),
+                          steps=args.steps, warmup=args.warmup, launches_per_step=len(LAYERS_7B))))
 
 
 def main():
@@ -580,8 +706,15 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-decode-legs", action="store_true",
                     help="skip the fused, scaled-input and 3-bit decode legs (the headline step only)")
-    ap.add_argument("--profile-mode", choices=["gemv", "copy", "gemm", "ring"], default=None)
+    ap.add_argument("--profile-mode", choices=["decode", "copy", "gemm", "ring", "ceilings"], default=None)
+    ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV", default=None,
+                    help="print the dispatch statistics of a rocprofv3 kernel_trace.csv (no GPU) and exit")
+    ap.add_argument("--kernel", default="gemv_kernel", help="kernel-name substring for --summarize-trace")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print("\n".join(summarize_trace(args.summarize_trace, args.kernel, [])))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the W4A16 kernels are measured on one MI355X; "
               f"--gpus {args.gpus} is not supported: column-parallel layers would shard N and row-parallel ones K, "
@@ -616,6 +749,10 @@ def main():
         log("decode, 3-bit weights (7 launches)")
         legs["decode_llama2_7b_3bit"] = run_decode_3bit(args, torch, awq, dev)
         torch.cuda.empty_cache()
+    if not args.no_ceilings:
+        log("ceilings: streaming read and fp16 matrix-core loop")
+        legs["ceilings"] = run_ceilings(args, torch, dev)
+        torch.cuda.empty_cache()
     if not args.no_sweep:
         log("sweep: (4096, 11008) at M = 1..1024")
         legs["batch_sweep_4096x11008"] = run_sweep(args, torch, awq, dev)
@@ -642,6 +779,7 @@ def main():
         cpu = run_cpu_baseline(LAYERS_7B, args.cpu_budget)
 
     traffic = measured_traffic(dec["bytes_per_launch"])
+    trace = trace_summary_for_roofline()
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -663,7 +801,9 @@ def main():
                      "traffic": None if traffic is None else round(traffic, 0),
                      "kernel": "awq::gemv_kernel (M=1)", "avg_launch_us": round(dec["kern_ms"] * 1e3, 3),
                      "alg_bytes_per_launch": round(dec["bytes_per_launch"], 1),
-                     "timing": "HIP events around the timed graph replays / launches in the region"},
+                     "timing": "HIP events on the replay stream around the timed graph replays, divided by the "
+                               "launches in the region (7 per step, back to back)",
+                     "trace": trace},
         "cpu_baseline": cpu,
         "per_layer": dec["per_layer"],
         "legs": legs,

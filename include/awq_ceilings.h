@@ -1,0 +1,50 @@
+/*
+ * libawq_ceilings -- two measurement kernels for gfx950 that bound what the
+ * libawq kernels can reach on one device: a streaming read (the HBM ceiling
+ * the decode GEMV is measured against) and a dense fp16 matrix-core loop (the
+ * MFMA ceiling of the GEMM and the search contractions).  They compute nothing
+ * of the method; only bench.py's ceiling leg calls them.
+ *
+ * Memory and streams follow libawq (include/awq.h): device pointers of the
+ * current device, 16-byte aligned, owned by the caller; work enqueued on
+ * `stream` (a hipStream_t as void*), no host synchronisation.  Each call
+ * returns 0 on success, 1 for invalid arguments (nothing launched), 4 when the
+ * launch fails.
+ */
+#ifndef AWQ_CEILINGS_H_
+#define AWQ_CEILINGS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * awq_ceiling_stream_read -- reads `bytes` bytes of `src` once with 16-byte
+ * non-temporal loads (the decode GEMV's weight loads), `blocks` blocks of 256
+ * threads in a grid-stride order over 16-byte pieces; each block folds what it
+ * read into one word and stores it to sink[block] (so no load is dead code).
+ *   src    device, bytes % 16 == 0, bytes >= 16
+ *   sink   device uint32 [blocks]
+ * Requires 1 <= blocks <= 65536.
+ */
+int awq_ceiling_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
+
+/*
+ * awq_ceiling_mfma_f16 -- each of `blocks` blocks of 4 * waves_per_simd waves
+ * (256 or 512 threads: one or two waves per SIMD when one block runs per
+ * compute unit) runs `iters` rounds of 8 independent v_mfma_f32_32x32x16_f16
+ * on register operands and stores one float per wave to sink.
+ * Work: blocks * 4 * waves_per_simd * iters * 8 * 32768 flops.
+ *   sink   device fp32 [blocks * 4 * waves_per_simd]
+ * Requires 1 <= blocks <= 65536, 1 <= iters <= 2^20, waves_per_simd 1 or 2.
+ */
+int awq_ceiling_mfma_f16(float* sink, int32_t blocks, int32_t iters, int32_t waves_per_simd, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_CEILINGS_H_ */

@@ -88,9 +88,9 @@ def test_workspace_query():
     # Gram form (M >= K): X^T fp16, G fp32 + fp16 hi/lo, E' fp16 hi/lo
     big = awq.awq_quantize_workspace_bytes(4096, 11008, 65536, 128, 20)
     assert big >= 2 * 11008 * 65536 + 8 * 11008 * 11008 + 4 * 4096 * 11008
-    # direct form (M < K): E in fp32, no Gram buffers
+    # direct form (M < K): E in fp32, no Gram buffers; s (fp32) and 1/s (fp64) per alpha
     small = awq.awq_quantize_workspace_bytes(4096, 11008, 64, 128, 20)
-    assert 4 * 4096 * 11008 <= small < 4 * 4096 * 11008 + (1 << 20)
+    assert 4 * 4096 * 11008 + 12 * 20 * 11008 <= small < 4 * 4096 * 11008 + 12 * 20 * 11008 + (1 << 20)
 
 
 def _lib_():

@@ -1,4 +1,5 @@
-"""Builds libawq.so (all HIP sources, gfx950 only) next to this file."""
+"""Builds libawq.so (the library's HIP sources, gfx950 only) and libawq_ceilings.so (the
+measurement kernels bench.py compares against) next to this file."""
 from __future__ import annotations
 
 import concurrent.futures as cf
@@ -12,8 +13,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq.so")
+CEILINGS_LIB = os.path.join(PKG, "libawq_ceilings.so")
 
 SOURCES = ["awq_api.hip", "stats.hip", "gram.hip", "quant.hip", "loss.hip", "gemv.hip", "skinny.hip", "gemm.hip", "gemm_pipe.hip"]
+CEILINGS_SOURCES = ["ceilings.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -38,7 +41,7 @@ FILE_FLAGS = {"gemm_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 
 
 def flags_for(src: str) -> list:
-    return FLAGS + FILE_FLAGS.get(os.path.basename(src).replace("_probe", ""), [])
+    return FLAGS + FILE_FLAGS.get(os.path.basename(src), [])
 
 
 def _compile(src: str) -> str:
@@ -53,18 +56,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    """Compiles every source and links libawq.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), 8)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(jobs: int | None = None) -> str:
+    """Compiles every source, links libawq.so and libawq_ceilings.so; returns libawq.so's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    sources = SOURCES + CEILINGS_SOURCES
+    jobs = jobs or min(len(sources), 8)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = dict(zip(sources, ex.map(_compile, sources)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CEILINGS_SOURCES], CEILINGS_LIB)
     return LIB
 
 

@@ -88,7 +88,7 @@ int check_layer(int64_t N, int64_t K, int32_t group) {
 // The statistics of X come first, at offsets that depend on K and M only.
 struct QuantizeWorkspace {
   bool direct;
-  size_t a, s_all, xt, g, gh, gl, ex, eh, el, e32, partial, loss, b, mask, total;
+  size_t a, s_all, inv_all, xt, g, gh, gl, ex, eh, el, e32, partial, loss, b, mask, total;
   int64_t mp, partials;
 };
 
@@ -114,6 +114,7 @@ QuantizeWorkspace quantize_workspace(int64_t N, int64_t K, int64_t M, int32_t n_
     w.g = take(sizeof(float) * (size_t)K * (size_t)K);
   }
   w.s_all = take(sizeof(float) * (size_t)n_alpha * (size_t)K);
+  w.inv_all = take(sizeof(double) * (size_t)n_alpha * (size_t)K);
   if (w.direct) {
     w.e32 = take(sizeof(float) * (size_t)N * (size_t)K);
   } else {
@@ -279,6 +280,7 @@ int awq_quantize_shared(const void* W, const void* X, int64_t N, int64_t K, int6
   char* base = static_cast<char*>(workspace);
   double* a = reinterpret_cast<double*>(base + w.a);
   float* s_all = reinterpret_cast<float*>(base + w.s_all);
+  double* inv_all = reinterpret_cast<double*>(base + w.inv_all);
   double* partial = reinterpret_cast<double*>(base + w.partial);
   double* L = loss ? loss : reinterpret_cast<double*>(base + w.loss);
   hipStream_t hs = as_stream(stream);
@@ -288,11 +290,12 @@ int awq_quantize_shared(const void* W, const void* X, int64_t N, int64_t K, int6
   // hi/lo split of G) sit in the workspace ahead of everything that depends on N,
   // so a call with the same X, M and K may take them from the previous call.
   hipError_t e = reuse_statistics ? hipSuccess : awq::launch_channel_mean_abs(X, M, K, a, hs);
-  if (e == hipSuccess) e = awq::launch_scales(a, grid, n_alpha, K, s_all, hs);
+  if (e == hipSuccess) e = awq::launch_scales(a, grid, n_alpha, K, s_all, inv_all, hs);
   if (w.direct) {
     float* E = reinterpret_cast<float*>(base + w.e32);
     for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
-      e = awq::launch_quant_error32(W, s_all + (size_t)i * (size_t)K, nullptr, N, K, bits, E, hs);
+      e = awq::launch_quant_error32(W, s_all + (size_t)i * (size_t)K, inv_all + (size_t)i * (size_t)K, nullptr, N, K,
+                                    bits, E, hs);
       if (e == hipSuccess) e = awq::launch_loss_direct(X, E, M, N, K, partial, hs);
       if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, L + i, hs);
     }
@@ -310,7 +313,8 @@ int awq_quantize_shared(const void* W, const void* X, int64_t N, int64_t K, int6
       if (e == hipSuccess) e = awq::launch_gram_split(G, K, ex, Ghi, Glo, hs);
     }
     for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
-      e = awq::launch_quant_error(W, s_all + (size_t)i * (size_t)K, ex, nullptr, N, K, bits, Ehi, Elo, hs);
+      e = awq::launch_quant_error(W, s_all + (size_t)i * (size_t)K, inv_all + (size_t)i * (size_t)K, ex, nullptr, N,
+                                  K, bits, Ehi, Elo, hs);
       if (e == hipSuccess) e = awq::launch_loss_partials(Ehi, Elo, Ghi, Glo, N, K, partial, hs);
       if (e == hipSuccess) e = awq::launch_loss_reduce(partial, w.partials, mn, L + i, hs);
     }
@@ -371,10 +375,11 @@ int awq_keep_fp16_ablation(const void* W, const void* X, int64_t N, int64_t K, i
     e = awq::launch_keep_mask(sets[i], i == 0 ? 0 : n_keep, K, mask, hs);
     if (w.direct) {
       float* E = reinterpret_cast<float*>(base + w.e32);
-      if (e == hipSuccess) e = awq::launch_quant_error32(W, nullptr, mask, N, K, bits, E, hs);
+      if (e == hipSuccess) e = awq::launch_quant_error32(W, nullptr, nullptr, mask, N, K, bits, E, hs);
       if (e == hipSuccess) e = awq::launch_loss_direct(X, E, M, N, K, partial, hs);
     } else {
-      if (e == hipSuccess) e = awq::launch_quant_error(W, nullptr, ex, mask, N, K, bits, base + w.eh, base + w.el, hs);
+      if (e == hipSuccess)
+        e = awq::launch_quant_error(W, nullptr, nullptr, ex, mask, N, K, bits, base + w.eh, base + w.el, hs);
       if (e == hipSuccess) e = awq::launch_loss_partials(base + w.eh, base + w.el, base + w.gh, base + w.gl, N, K,
                                                          partial, hs);
     }

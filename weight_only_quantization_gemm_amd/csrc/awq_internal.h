@@ -22,14 +22,16 @@ hipError_t launch_transpose(const void* X, int64_t M, int64_t K, int64_t Mp, voi
 hipError_t launch_gram(const void* Xt, int64_t Mp, int64_t K, float* G, hipStream_t st);
 
 // quant.hip
+// s_all fp32 [n_alpha][K] and inv_all = 1 / s_all in fp64
 hipError_t launch_scales(const double* a, const AlphaGrid& al, int n_alpha, int64_t K, float* s_all,
-                         hipStream_t st);
-// bits: 4 (16 levels) or 3 (8 levels)
+                         double* inv_all, hipStream_t st);
+// bits: 4 (16 levels) or 3 (8 levels); s and inv (its fp64 reciprocal) both NULL or both given
 // keep: NULL, or uint8 [K] marking channels whose error is 0 (kept exact)
-hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, const uint8_t* keep, int64_t N,
-                              int64_t K, int bits, void* Ehi, void* Elo, hipStream_t st);
-hipError_t launch_quant_error32(const void* W, const float* s, const uint8_t* keep, int64_t N, int64_t K, int bits,
-                                float* E, hipStream_t st);
+hipError_t launch_quant_error(const void* W, const float* s, const double* inv, const int32_t* ex,
+                              const uint8_t* keep, int64_t N, int64_t K, int bits, void* Ehi, void* Elo,
+                              hipStream_t st);
+hipError_t launch_quant_error32(const void* W, const float* s, const double* inv, const uint8_t* keep, int64_t N,
+                                int64_t K, int bits, float* E, hipStream_t st);
 hipError_t launch_top_channels(const double* v, int64_t K, int n_keep, int32_t* out, hipStream_t st);
 hipError_t launch_keep_mask(const int32_t* keep, int n_keep, int64_t K, uint8_t* mask, hipStream_t st);
 hipError_t launch_pack(const void* W, const float* s, int64_t N, int64_t K, int bits, void* packed, void* scales,

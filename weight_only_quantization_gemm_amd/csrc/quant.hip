@@ -21,20 +21,24 @@
 
 namespace awq {
 
+// s_all[i][k] = fp32(a_k ^ alpha_i) (1 where a_k = 0), and inv_all[i][k] =
+// 1 / s in fp64 for the error kernels (one division per channel and alpha
+// here instead of one per weight there).
 __global__ void scales_kernel(const double* __restrict__ a, AlphaGrid al, int n_alpha, int64_t K,
-                              float* __restrict__ s_all) {
+                              float* __restrict__ s_all, double* __restrict__ inv_all) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int i = blockIdx.y;
   if (k >= K || i >= n_alpha) return;
   double ak = a[k];
   float s = (ak == 0.0) ? 1.0f : (float)pow(ak, (double)al.v[i]);
   s_all[(int64_t)i * K + k] = s;
+  inv_all[(int64_t)i * K + k] = 1.0 / (double)s;
 }
 
 hipError_t launch_scales(const double* a, const AlphaGrid& al, int n_alpha, int64_t K, float* s_all,
-                         hipStream_t st) {
+                         double* inv_all, hipStream_t st) {
   dim3 grid((unsigned)((K + 255) / 256), (unsigned)n_alpha);
-  scales_kernel<<<grid, dim3(256), 0, st>>>(a, al, n_alpha, K, s_all);
+  scales_kernel<<<grid, dim3(256), 0, st>>>(a, al, n_alpha, K, s_all, inv_all);
   return hipGetLastError();
 }
 
@@ -95,13 +99,37 @@ __device__ inline void quantize8(const float w[8], const float s[8], Quant8& r) 
   for (int i = 0; i < 8; ++i) r.q[i] = fminf(fmaxf(rintf(r.v[i] / r.sc) + r.z, 0.0f), qmax);
 }
 
+// The fp64 factors 1/s of 8 channels (1 where s is NULL).
+__device__ inline void load_inv8(const double* inv, int64_t k0, double out[8]) {
+  if (inv == nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = 1.0;
+    return;
+  }
+  const double2* p = reinterpret_cast<const double2*>(inv + k0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double2 v = p[i];
+    out[2 * i] = v.x;
+    out[2 * i + 1] = v.y;
+  }
+}
+
+// E = w_hat / s - w in fp64 as one fma of the exact w_hat = (q - z) * sc (an
+// integer times an fp16 value, exact in fp32) with the fp64 1/s: within one
+// fp64 rounding of the quotient form, far below the fp32 E is kept in.
+__device__ inline double weight_error(float q, float z, float sc, double inv, float w) {
+  return fma((double)((q - z) * sc), inv, -(double)w);
+}
+
 // Weight error of the search, pre-scaled for the loss contraction:
-// E'[n][k] = ((q - z) * sc / s - w) * 2^e_k, evaluated in fp64, rounded to
-// fp32 and stored as an fp16 pair hi = fp16(E'), lo = fp16(E' - hi).  One
-// thread per 8 channels.  Channels with keep[k] != 0 (keep may be NULL) stay
-// exact: their error is 0.
+// E'[n][k] = (w_hat / s - w) * 2^e_k, evaluated in fp64, rounded to fp32 and
+// stored as an fp16 pair hi = fp16(E'), lo = fp16(E' - hi).  One thread per 8
+// channels.  Channels with keep[k] != 0 (keep may be NULL) stay exact: their
+// error is 0.
 template <int QMAX>
 __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
+                                                          const double* __restrict__ inv,
                                                           const int32_t* __restrict__ ex,
                                                           const uint8_t* __restrict__ keep, int64_t N, int64_t K,
                                                           f16* __restrict__ Ehi, f16* __restrict__ Elo) {
@@ -112,18 +140,19 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restric
   if (idx >= N * K8) return;
   const int64_t n = idx / K8, w = idx - n * K8;
   float wf[8], sf[8];
+  double iv[8];
   load_w8(W, idx, wf);
   load_s8(s, w * 8, sf);
+  load_inv8(inv, w * 8, iv);
   Quant8 r;
   quantize8<QMAX>(wf, sf, r);
-  const double scd = (double)r.sc;
   uint32_t hw[4], lw[4];
 #pragma unroll
   for (int i = 0; i < 8; i += 2) {
     f16x2 h, l;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      double e = ((double)(r.q[i + u] - r.z) * scd) / (double)sf[i + u] - (double)wf[i + u];
+      double e = weight_error(r.q[i + u], r.z, r.sc, iv[i + u], wf[i + u]);
       if (keep != nullptr && keep[w * 8 + i + u]) e = 0.0;
       const float v = (float)ldexp(e, ex[w * 8 + i + u]);
       const f16 hi = (f16)v;
@@ -140,6 +169,7 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restric
 // Unscaled weight error in fp32 for the direct form of the loss.
 template <int QMAX>
 __global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
+                                                            const double* __restrict__ inv,
                                                             const uint8_t* __restrict__ keep, int64_t N, int64_t K,
                                                             float* __restrict__ E) {
   const int64_t K8 = K / 8;
@@ -147,15 +177,16 @@ __global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restr
   if (idx >= N * K8) return;  // whole 16-lane segments, as above
   const int64_t n = idx / K8, w = idx - n * K8;
   float wf[8], sf[8];
+  double iv[8];
   load_w8(W, idx, wf);
   load_s8(s, w * 8, sf);
+  load_inv8(inv, w * 8, iv);
   Quant8 r;
   quantize8<QMAX>(wf, sf, r);
-  const double scd = (double)r.sc;
   float e[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    e[i] = (float)(((double)(r.q[i] - r.z) * scd) / (double)sf[i] - (double)wf[i]);
+    e[i] = (float)weight_error(r.q[i], r.z, r.sc, iv[i], wf[i]);
     if (keep != nullptr && keep[w * 8 + i]) e[i] = 0.0f;
   }
   float4* out = reinterpret_cast<float4*>(E + n * K + w * 8);
@@ -163,23 +194,24 @@ __global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restr
   out[1] = make_float4(e[4], e[5], e[6], e[7]);
 }
 
-hipError_t launch_quant_error32(const void* W, const float* s, const uint8_t* keep, int64_t N, int64_t K, int bits,
-                                float* E, hipStream_t st) {
+hipError_t launch_quant_error32(const void* W, const float* s, const double* inv, const uint8_t* keep, int64_t N,
+                                int64_t K, int bits, float* E, hipStream_t st) {
   const dim3 grid((unsigned)((N * (K / 8) + 255) / 256)), block(256);
   auto Wp = reinterpret_cast<const uint4*>(W);
-  if (bits == 3) quant_error32_kernel<7><<<grid, block, 0, st>>>(Wp, s, keep, N, K, E);
-  else quant_error32_kernel<15><<<grid, block, 0, st>>>(Wp, s, keep, N, K, E);
+  if (bits == 3) quant_error32_kernel<7><<<grid, block, 0, st>>>(Wp, s, inv, keep, N, K, E);
+  else quant_error32_kernel<15><<<grid, block, 0, st>>>(Wp, s, inv, keep, N, K, E);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_error(const void* W, const float* s, const int32_t* ex, const uint8_t* keep, int64_t N,
-                              int64_t K, int bits, void* Ehi, void* Elo, hipStream_t st) {
+hipError_t launch_quant_error(const void* W, const float* s, const double* inv, const int32_t* ex,
+                              const uint8_t* keep, int64_t N, int64_t K, int bits, void* Ehi, void* Elo,
+                              hipStream_t st) {
   const dim3 grid((unsigned)((N * (K / 8) + 255) / 256)), block(256);
   auto Wp = reinterpret_cast<const uint4*>(W);
   auto hi = reinterpret_cast<f16*>(Ehi);
   auto lo = reinterpret_cast<f16*>(Elo);
-  if (bits == 3) quant_error_kernel<7><<<grid, block, 0, st>>>(Wp, s, ex, keep, N, K, hi, lo);
-  else quant_error_kernel<15><<<grid, block, 0, st>>>(Wp, s, ex, keep, N, K, hi, lo);
+  if (bits == 3) quant_error_kernel<7><<<grid, block, 0, st>>>(Wp, s, inv, ex, keep, N, K, hi, lo);
+  else quant_error_kernel<15><<<grid, block, 0, st>>>(Wp, s, inv, ex, keep, N, K, hi, lo);
   return hipGetLastError();
 }
 
