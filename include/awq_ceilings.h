@@ -23,14 +23,16 @@ extern "C" {
 
 /*
  * awq_ceiling_stream_read -- reads `bytes` bytes of `src` once with 16-byte
- * non-temporal loads (the decode GEMV's weight loads), `blocks` blocks of 256
- * threads in a grid-stride order over 16-byte pieces; each block folds what it
- * read into one word and stores it to sink[block] (so no load is dead code).
+ * non-temporal loads (the decode GEMV's weight loads).  Each thread issues its
+ * `loads_per_thread` loads (1, 2 or 4; the 256 threads of a block cover
+ * consecutive pieces) before using any, and the grid spans the whole range: one
+ * round trip per thread, as the decode GEMV makes.  What a thread read is
+ * folded into one word, stored to sink[block % 1024] only when it equals a
+ * fixed pattern (practically never), so no load is dead code.
  *   src    device, bytes % 16 == 0, bytes >= 16
- *   sink   device uint32 [blocks]
- * Requires 1 <= blocks <= 65536.
+ *   sink   device uint32 [1024]
  */
-int awq_ceiling_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
+int awq_ceiling_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t loads_per_thread, void* stream);
 
 /*
  * awq_ceiling_mfma_f16 -- each of `blocks` blocks of 4 * waves_per_simd waves

@@ -13,30 +13,27 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Four 16-byte pieces per lane per round (all issued before any is used), the
-// lanes of the grid covering consecutive pieces.
+// One round trip per thread: each lane issues its L 16-byte pieces (the
+// lanes of a block covering 256 L consecutive pieces) before using any, and
+// the grid covers the whole range, so every load of the kernel is in flight
+// at once up to what the device holds.  The folded value is stored only when
+// it equals a fixed pattern (practically never): the kernel costs its loads
+// alone, and they stay live.
+template <int L>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                           uint32_t* __restrict__ sink) {
-  __shared__ uint32_t red[4];
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * 256 * L + threadIdx.x;
+  u32x4 v[L];
+#pragma unroll
+  for (int u = 0; u < L; ++u) {
+    int64_t i = base + (int64_t)u * 256;
+    i = i < n16 ? i : n16 - 1;
+    v[u] = __builtin_nontemporal_load(src + i);
+  }
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    u32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 v = __builtin_nontemporal_load(src + i);
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+  for (int u = 0; u < L; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  if (acc == 0x9E3779B9u) sink[blockIdx.x & 1023u] = acc;
 }
 
 // Eight independent accumulation chains per wave keep the matrix core's
@@ -71,11 +68,19 @@ __global__ __launch_bounds__(64 * WAVES) void mfma_f16_kernel(float* __restrict_
 
 extern "C" {
 
-int awq_ceiling_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream) {
-  if (!src || !sink || bytes < 16 || bytes % 16 || blocks < 1 || blocks > 65536) return 1;
+int awq_ceiling_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t loads_per_thread,
+                            void* stream) {
+  if (!src || !sink || bytes < 16 || bytes % 16) return 1;
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(sink)) & 15u) return 1;
-  stream_read_kernel<<<dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(
-      reinterpret_cast<const u32x4*>(src), (int64_t)(bytes / 16), sink);
+  const int L = loads_per_thread;
+  const int64_t n16 = (int64_t)(bytes / 16), blocks = (n16 + 256 * L - 1) / (256 * (int64_t)L);
+  if (blocks >= ((int64_t)1 << 31)) return 1;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const auto p = reinterpret_cast<const u32x4*>(src);
+  if (L == 1) stream_read_kernel<1><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(p, n16, sink);
+  else if (L == 2) stream_read_kernel<2><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(p, n16, sink);
+  else if (L == 4) stream_read_kernel<4><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(p, n16, sink);
+  else return 1;
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
