@@ -679,6 +679,28 @@ def profile_mode(args, torch, awq, dev):
     if args.profile_mode == "ceilings":
         print(json.dumps(dict(profile_mode="ceilings", **run_ceilings(args, torch, dev))))
         return
+    if args.profile_mode == "search":
+        # one awq_quantize per layer shape class of the 7B block (65,536 calibration rows,
+        # 20 alphas), each after a warm-up call on the same workspace
+        from gen import activations_fp16, normal_fp16, seed_for
+        M, out = 65536, {}
+        for li, (name, K, N) in enumerate([("q_proj", 4096, 4096), ("gate_proj", 4096, 11008),
+                                           ("down_proj", 11008, 4096)]):
+            X = torch.from_numpy(activations_fp16(M, K, seed=seed_for(5, 10 + li), lognormal=True)).to(dev)
+            W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=seed_for(5, 100 + li))).to(dev)
+            ws = torch.empty((awq.awq_quantize_workspace_bytes(N, K, M, 128, 20),), dtype=torch.uint8, device=dev)
+            awq.awq_quantize(W, X, None, workspace=ws)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            r = awq.awq_quantize(W, X, None, workspace=ws)
+            b.record()
+            torch.cuda.synchronize()
+            out[name] = dict(K=K, N=N, ms=round(a.elapsed_time(b), 2), alpha_index=int(r["best_alpha"].item()))
+            del X, W, ws, r
+            torch.cuda.empty_cache()
+        print(json.dumps(dict(profile_mode="search", calib_rows=M, layers=out)))
+        return
     if args.profile_mode in ("gemm", "ring"):
         # one layer, 20 launches: the M = 256 GEMM on (4096, 11008), or the M = 16 decode
         # ring kernel on (8192, 28672)
@@ -712,7 +734,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-decode-legs", action="store_true",
                     help="skip the fused, scaled-input and 3-bit decode legs (the headline step only)")
-    ap.add_argument("--profile-mode", choices=["decode", "copy", "gemm", "ring", "ceilings"], default=None)
+    ap.add_argument("--profile-mode", choices=["decode", "copy", "gemm", "ring", "ceilings", "search"], default=None)
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV", default=None,
                     help="print the dispatch statistics of a rocprofv3 kernel_trace.csv (no GPU) and exit")

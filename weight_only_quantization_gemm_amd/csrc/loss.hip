@@ -10,22 +10,31 @@
 //   G'_kj = G_kj 2^(-e_k - e_j),  E'_nk = E_nk 2^(e_k),  sum_n E'_n G' E'_n^T = sum_n E_n G E_n^T
 // exactly, and |G'| <= ~2 (Cauchy-Schwarz) while E' stays well inside fp16
 // range.  Each of E', G' is stored as an fp16 pair hi + lo (hi = fp16(v),
-// lo = fp16(v - hi)), and T = E' G' is formed on v_mfma_f32_32x32x16_f16 as
+// lo = fp16(v - hi)), and products are formed on v_mfma_f32_32x32x16_f16 as
 // hi.hi + hi.lo + lo.hi with fp32 accumulation (the dropped lo.lo term is
 // ~2^-22 relative).  Block partial sums go to fp64 and are reduced in a fixed
 // order, so the result is deterministic; it agrees with an fp64 evaluation to
 // about 1e-7 relative.
 //
+// Symmetry.  With the channels cut into 256-wide blocks I, J, and G symmetric,
+//   sum_n E_n G E_n^T = sum_n sum_{I <= J} E_{n,I} G''_{I,J} E_{n,J}^T
+// where G'' = 2 G' on the blocks off the diagonal and G' on it (the doubling is
+// exact): only the block-upper triangle is contracted, about half of the full
+// product's work.  The split kernel stores G'' directly.
+//
 // This Gram form is used when M >= K; for M < K see the direct form below.
 //
-// Blocking: 256 x 256 tiles of T = E' G' (rows n, columns j) over all K
-// channels.  Every tile has the same work, so the blocks of a launch run
-// side by side and stay in step, and the tiles are ordered so that the 32
-// blocks an XCD runs at once cover 4 E' panels x 8 G' panels: each operand
-// chunk is then fetched into that XCD's L2 once and read by 8 (or 4) blocks.
-// (Contracting only the channel blocks I <= J of the symmetric G' halves the
-// flops but gives blocks of unequal length, which drift apart and lose that
-// reuse; measured slower.)
+// Work split: for an n-tile (256 rows of E') and a channel block J, the segment
+// T = E' G''[., J] contracts channels 0 .. 256 (J + 1) - 1 in stages of 32.  All
+// segments, n-tile by n-tile and within one the longest J first, form one line
+// of stages, and each of kLossBlocks persistent blocks (one per compute unit)
+// takes an equal run of it; a run that crosses segment boundaries contracts
+// each piece into a 256 x 256 tile of T and adds sum E'[n][j] T[n][j] over the
+// tile to the block's partial.  The loss is linear in T, so the pieces of one
+// segment simply add: every compute unit does the same number of stages and
+// no fix-up pass is needed.  Block b's run index puts the runs of one XCD
+// (b % 8) side by side (mostly whole n-tiles, which then share E' through that
+// XCD's L2).
 #include "awq_common.h"
 #include "awq_internal.h"
 #include "mfma_pipe.h"
@@ -35,17 +44,33 @@ namespace awq {
 constexpr int kFT = 256;     // tile of T: 256 rows n x 256 columns j
 // Stage width, measured on the 7B shapes: two 32-channel stages beat four
 // 16-channel stages by 5-9 % (half the barriers).
-#ifndef AWQ_LOSS_KS
-#define AWQ_LOSS_KS 32
-#endif
-constexpr int kFKS = AWQ_LOSS_KS;            // channels per pipeline stage
-constexpr int kFStages = 64 / kFKS;          // 4 x 16 or 2 x 32 channels: 128 KB of LDS
+constexpr int kFKS = 32;                     // channels per pipeline stage
+constexpr int kFStages = 2;                  // two stages of 32 channels: 128 KB of LDS
 constexpr int kFLoads = 4 * (kFT / (512 / kFKS) / 8);  // direct loads per wave per stage
+
+constexpr int kLossBlocks = 256;  // persistent blocks: one per compute unit (128 KB of LDS each)
 
 static int64_t full_tiles_n(int64_t N) { return (N + kFT - 1) / kFT; }
 static int64_t full_tiles_j(int64_t K) { return (K + kFT - 1) / kFT; }
 
-int64_t loss_partial_count(int64_t N, int64_t K) { return full_tiles_n(N) * full_tiles_j(K); }
+// Stages of channel block J's segment: channels 0 .. min(256 (J + 1), K) - 1.
+__host__ __device__ inline int seg_stages(int J, int64_t K) {
+  const int64_t c = (int64_t)(J + 1) * kFT < K ? (int64_t)(J + 1) * kFT : K;
+  return (int)(c / kFKS);
+}
+
+// Stages of one n-tile's segments.
+__host__ __device__ inline int64_t stages_per_ntile(int64_t K) {
+  int64_t u = 0;
+  for (int J = 0; J < (int)full_tiles_j(K); ++J) u += seg_stages(J, K);
+  return u;
+}
+
+int64_t loss_partial_count(int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return kLossBlocks;
+}
 
 // e_k = floor(log2(G_kk) / 2), 0 where G_kk is 0 (a channel that is zero in every row).
 __global__ void channel_exponent_kernel(const float* __restrict__ G, int64_t K, int32_t* __restrict__ e) {
@@ -55,13 +80,16 @@ __global__ void channel_exponent_kernel(const float* __restrict__ G, int64_t K, 
   e[k] = (d > 0.0f) ? (ilogbf(d) >> 1) : 0;
 }
 
-// Ghi/Glo = split of G'_kj = G_kj 2^(-e_k - e_j); the scaling is exact in fp32.
+// Ghi/Glo = split of G''_kj = G_kj 2^(-e_k - e_j), doubled when k and j lie in
+// different 256-channel blocks (see the symmetry note above); the scaling is
+// exact in fp32.
 __global__ void gram_split_kernel(const float* __restrict__ G, const int32_t* __restrict__ e, int64_t K,
                                   f16* __restrict__ Ghi, f16* __restrict__ Glo) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= K * K) return;
   const int64_t k = i / K, j = i - k * K;
-  const float v = ldexpf(G[i], -(e[k] + e[j]));
+  const int off_diag = (k / kFT) != (j / kFT) ? 1 : 0;
+  const float v = ldexpf(G[i], off_diag - (e[k] + e[j]));
   const f16 hi = (f16)v;
   Ghi[i] = hi;
   Glo[i] = (f16)(v - (float)hi);
@@ -75,21 +103,6 @@ hipError_t launch_gram_split(const float* G, int64_t K, int32_t* e, void* Ghi, v
   return hipGetLastError();
 }
 
-// Tile of block b: XCD x = b % 8 takes the contiguous range of tile indices
-// [x * per, (x + 1) * per), and tile indices walk 4 n-tiles before advancing j.
-struct FullTile {
-  int t, jb, nb;
-};
-__device__ inline FullTile full_tile(int b, int nt, int jt) {
-  const int T = nt * jt, per = (T + 7) / 8;
-  const int t = (b & 7) * per + (b >> 3);
-  if (t >= T) return FullTile{-1, 0, 0};
-  const int g = t / (4 * jt);  // group of (up to) 4 n-tiles
-  const int gn = (nt - 4 * g) < 4 ? (nt - 4 * g) : 4;
-  const int w = t - g * 4 * jt;
-  return FullTile{t, w / gn, 4 * g + w % gn};
-}
-
 // Block: 512 threads = 8 waves (two per SIMD) in 2 (j) x 4 (n), wave tile
 // 128 j x 64 n.  The matrix cores form D[j][n] = sum_k G'[j][k] E'[n][k] =
 // T[n][j] (G' is symmetric): A operand = rows j of G', B operand = rows n of
@@ -99,115 +112,138 @@ __device__ inline FullTile full_tile(int b, int nt, int jt) {
 // 8-byte load per fp16 half.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void loss_full_kernel(const f16* __restrict__ Ehi, const f16* __restrict__ Elo, const f16* __restrict__ Ghi,
-                      const f16* __restrict__ Glo, int64_t N, int64_t K, int nt, int jt, double* __restrict__ partial) {
+                      const f16* __restrict__ Glo, int64_t N, int64_t K, int nt, int jt, int64_t per_n,
+                      double* __restrict__ partial) {
   constexpr int D = kFStages - 1;  // stages in flight ahead of the one computed
   // The only LDS variable of the kernel: with a second one the compiler tags every LDS
   // access with alias scopes, and then waits for all outstanding direct loads before
   // each fragment read (it cannot tell the stage being filled from the one being read),
   // which would serialize the pipeline.  The final reduction reuses the stage buffers.
   __shared__ __attribute__((aligned(16))) f16 lds[kFStages][4][kFT * kFKS];  // 131,072 B
-  const FullTile ft = full_tile((int)blockIdx.x, nt, jt);
-  if (ft.t < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wj = wave >> 2, wn = wave & 3, l32 = lane & 31;
-  const int64_t j0 = (int64_t)ft.jb * kFT, n0 = (int64_t)ft.nb * kFT;
-  const int64_t S = K / kFKS;
 
-  TilePlan<kFT, 8, kFKS> pgh, pgl, peh, pel;
-  pgh.init(Ghi, K, j0, K, wave, lane);
-  pgl.init(Glo, K, j0, K, wave, lane);
-  peh.init(Ehi, K, n0, N, wave, lane);
-  pel.init(Elo, K, n0, N, wave, lane);
-  // past the last stage the tail re-reads stage S - 1 into the free slot
-  auto issue = [&](int64_t s) {
-    const int64_t k0 = (s < S ? s : S - 1) * kFKS;
-    const int slot = (int)(s % kFStages);
-    pgh.issue(lds[slot][0], k0);
-    pgl.issue(lds[slot][1], k0);
-    peh.issue(lds[slot][2], k0);
-    pel.issue(lds[slot][3], k0);
-  };
+  // this block's run [pos, end) of the line of stages (gridDim.x is a multiple of 8)
+  const int64_t total = (int64_t)nt * per_n;
+  const int64_t r = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  int64_t pos = total * r / gridDim.x;
+  const int64_t end = total * (r + 1) / gridDim.x;
+  // the segment holding pos: n-tile nb, channel block J (longest first), stage s0 in it
+  int nb = (int)(pos / per_n), J = jt - 1;
+  int64_t s0 = pos - (int64_t)nb * per_n;
+  while (s0 >= seg_stages(J, K)) s0 -= seg_stages(J--, K);
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  double sum = 0.0;  // this lane's share of the block's partial
+  while (pos < end) {
+    const int64_t seg = seg_stages(J, K);
+    const int64_t S0 = s0, S = (seg - s0) < (end - pos) ? seg : s0 + (end - pos);  // stages [S0, S) of segment
+    const int64_t j0 = (int64_t)J * kFT, n0 = (int64_t)nb * kFT;
 
-  for (int t = 0; t < D; ++t) issue(t);
-  for (int64_t s = 0; s < S; ++s) {
-    wait_vmcnt<(D - 1) * kFLoads>();  // stage s has landed; stages s+1 .. s+D-1 may be pending
-    lds_barrier();                     // ... for every wave; stage s - 1 is no longer read
-    issue(s + D);
-    const int slot = (int)(s % kFStages);
-    const f16* Gh = lds[slot][0];
-    const f16* Gl = lds[slot][1];
-    const f16* Eh = lds[slot][2];
-    const f16* El = lds[slot][3];
-    auto fr = [](const f16* tile, int r, int c) { return kFKS == 32 ? frag32(tile, r, c) : frag16(tile, r, c); };
+    TilePlan<kFT, 8, kFKS> pgh, pgl, peh, pel;
+    pgh.init(Ghi, K, j0, K, wave, lane);
+    pgl.init(Glo, K, j0, K, wave, lane);
+    peh.init(Ehi, K, n0, N, wave, lane);
+    pel.init(Elo, K, n0, N, wave, lane);
+    // past the last stage the tail re-reads stage S - 1 into the free slot; stage s
+    // goes to ring slot (s - S0) % kFStages
+    auto issue = [&](int64_t st) {
+      const int64_t k0 = (st < S ? st : S - 1) * kFKS;
+      const int slot = (int)((st - S0) % kFStages);
+      pgh.issue(lds[slot][0], k0);
+      pgl.issue(lds[slot][1], k0);
+      peh.issue(lds[slot][2], k0);
+      pel.issue(lds[slot][3], k0);
+    };
+
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int hk = 0; hk < kFKS / 16; ++hk) {
-      const int c = 2 * hk + (lane >> 5);
-      f16x8 eh[2], el[2];
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        eh[b] = fr(Eh, wn * 64 + b * 32 + l32, c);
-        el[b] = fr(El, wn * 64 + b * 32 + l32, c);
-      }
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f16x8 gh = fr(Gh, wj * 128 + a * 32 + l32, c);
-        const f16x8 gl = fr(Gl, wj * 128 + a * 32 + l32, c);
+        for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.f;
+
+    lds_barrier();  // every wave is done with the ring before it is refilled
+    for (int t = 0; t < D; ++t) issue(S0 + t);
+    for (int64_t st = S0; st < S; ++st) {
+      wait_vmcnt<(D - 1) * kFLoads>();  // stage st has landed; stages st+1 .. st+D-1 may be pending
+      lds_barrier();                     // ... for every wave; stage st - 1 is no longer read
+      issue(st + D);
+      const int slot = (int)((st - S0) % kFStages);
+      const f16* Gh = lds[slot][0];
+      const f16* Gl = lds[slot][1];
+      const f16* Eh = lds[slot][2];
+      const f16* El = lds[slot][3];
+#pragma unroll
+      for (int hk = 0; hk < kFKS / 16; ++hk) {
+        const int c = 2 * hk + (lane >> 5);
+        f16x8 eh[2], el[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gh, eh[b], acc[a][b], 0, 0, 0);
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gh, el[b], acc[a][b], 0, 0, 0);
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gl, eh[b], acc[a][b], 0, 0, 0);
+          eh[b] = frag32(Eh, wn * 64 + b * 32 + l32, c);
+          el[b] = frag32(El, wn * 64 + b * 32 + l32, c);
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f16x8 gh = frag32(Gh, wj * 128 + a * 32 + l32, c);
+          const f16x8 gl = frag32(Gl, wj * 128 + a * 32 + l32, c);
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gh, eh[b], acc[a][b], 0, 0, 0);
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gh, el[b], acc[a][b], 0, 0, 0);
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gl, eh[b], acc[a][b], 0, 0, 0);
+          }
         }
       }
     }
-  }
-  wait_vmcnt<0>();  // the tail's redundant loads land before the block can exit
+    wait_vmcnt<0>();  // the tail's redundant loads land before the ring is reused or the block exits
 
-  // partial = sum over the tile of E'[n][j] * T[n][j], E' = hi + lo in fp32.  The lane's
-  // 32 E' pairs are all loaded before any is used (one round trip to memory); rows past N
-  // and channels past K (all 4 of a quad or none, K % 128 == 0) read a valid element and
-  // are dropped from the sum.
-  u32x2 hv[2][4][4], lv[2][4][4];
+    // sum over the tile of E'[n][j] * T[n][j], E' = hi + lo in fp32.  The lane's 32 E'
+    // pairs are all loaded before any is used (one round trip to memory); rows past N and
+    // channels past K (all 4 of a quad or none, K % 128 == 0) read a valid element and are
+    // dropped from the sum.
+    u32x2 hv[2][4][4], lv[2][4][4];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    int64_t n = n0 + wn * 64 + b * 32 + l32;
-    n = n < N ? n : N - 1;
+    for (int b = 0; b < 2; ++b) {
+      int64_t n = n0 + wn * 64 + b * 32 + l32;
+      n = n < N ? n : N - 1;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int64_t j = j0 + wj * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
-        j = j < K ? j : K - 4;
-        hv[b][a][q] = *reinterpret_cast<const u32x2*>(Ehi + n * K + j);
-        lv[b][a][q] = *reinterpret_cast<const u32x2*>(Elo + n * K + j);
-      }
+        for (int q = 0; q < 4; ++q) {
+          int64_t j = j0 + wj * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
+          j = j < K ? j : K - 4;
+          hv[b][a][q] = *reinterpret_cast<const u32x2*>(Ehi + n * K + j);
+          lv[b][a][q] = *reinterpret_cast<const u32x2*>(Elo + n * K + j);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t n = n0 + wn * 64 + b * 32 + l32;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t j = j0 + wj * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
+          if (n >= N || j >= K) continue;
+          const f16x2 h01 = as_f16x2(hv[b][a][q].x), h23 = as_f16x2(hv[b][a][q].y);
+          const f16x2 l01 = as_f16x2(lv[b][a][q].x), l23 = as_f16x2(lv[b][a][q].y);
+          const float e[4] = {(float)h01.x + (float)l01.x, (float)h01.y + (float)l01.y,
+                              (float)h23.x + (float)l23.x, (float)h23.y + (float)l23.y};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) sum += (double)e[u] * (double)acc[a][b][4 * q + u];
+        }
+    }
+
+    // next segment: the next channel block of this n-tile, or the next n-tile
+    pos += S - S0;
+    s0 = 0;
+    if (--J < 0) {
+      J = jt - 1;
+      ++nb;
+    }
   }
-  double sum = 0.0;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int64_t n = n0 + wn * 64 + b * 32 + l32;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t j = j0 + wj * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
-        if (n >= N || j >= K) continue;
-        const f16x2 h01 = as_f16x2(hv[b][a][q].x), h23 = as_f16x2(hv[b][a][q].y);
-        const f16x2 l01 = as_f16x2(lv[b][a][q].x), l23 = as_f16x2(lv[b][a][q].y);
-        const float e[4] = {(float)h01.x + (float)l01.x, (float)h01.y + (float)l01.y, (float)h23.x + (float)l23.x,
-                            (float)h23.y + (float)l23.y};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) sum += (double)e[u] * (double)acc[a][b][4 * q + u];
-      }
-  }
+
   sum = wave_sum(sum);
   double* red = reinterpret_cast<double*>(&lds[0][0][0]);
   __syncthreads();  // every wave is past its last fragment read
@@ -216,18 +252,16 @@ void loss_full_kernel(const f16* __restrict__ Ehi, const f16* __restrict__ Elo, 
   if (tid == 0) {
     double v = 0.0;
     for (int w = 0; w < 8; ++w) v += red[w];
-    partial[ft.t] = v;
+    partial[blockIdx.x] = v;
   }
 }
 
 hipError_t launch_loss_partials(const void* Ehi, const void* Elo, const void* Ghi, const void* Glo, int64_t N,
                                 int64_t K, double* partial, hipStream_t st) {
   const int nt = (int)full_tiles_n(N), jt = (int)full_tiles_j(K);
-  const int64_t T = (int64_t)nt * jt;
-  const int64_t blocks = (T + 7) / 8 * 8;
-  loss_full_kernel<<<dim3((unsigned)blocks), dim3(512), 0, st>>>(
+  loss_full_kernel<<<dim3((unsigned)kLossBlocks), dim3(512), 0, st>>>(
       reinterpret_cast<const f16*>(Ehi), reinterpret_cast<const f16*>(Elo), reinterpret_cast<const f16*>(Ghi),
-      reinterpret_cast<const f16*>(Glo), N, K, nt, jt, partial);
+      reinterpret_cast<const f16*>(Glo), N, K, nt, jt, stages_per_ntile(K), partial);
   return hipGetLastError();
 }
 

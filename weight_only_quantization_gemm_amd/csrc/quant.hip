@@ -52,8 +52,7 @@ struct Quant8 {
   f16 sc16;
 };
 
-__device__ inline void load_w8(const uint4* W, int64_t idx, float w[8]) {
-  uint4 raw = W[idx];
+__device__ inline void unpack_w8(const uint4 raw, float w[8]) {
   const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -62,6 +61,8 @@ __device__ inline void load_w8(const uint4* W, int64_t idx, float w[8]) {
     w[2 * i + 1] = (float)h.y;
   }
 }
+
+__device__ inline void load_w8(const uint4* W, int64_t idx, float w[8]) { unpack_w8(W[idx], w); }
 
 __device__ inline void load_s8(const float* s, int64_t k0, float out[8]) {
   if (s == nullptr) {
@@ -122,11 +123,18 @@ __device__ inline double weight_error(float q, float z, float sc, double inv, fl
   return fma((double)((q - z) * sc), inv, -(double)w);
 }
 
+// Rows per thread of the error kernels: a thread keeps its 8 channels' s, 1/s
+// and exponents in registers for kErrRows rows of W, whose words it loads
+// together before quantizing them.
+constexpr int kErrRows = 8;
+
 // Weight error of the search, pre-scaled for the loss contraction:
 // E'[n][k] = (w_hat / s - w) * 2^e_k, evaluated in fp64, rounded to fp32 and
-// stored as an fp16 pair hi = fp16(E'), lo = fp16(E' - hi).  One thread per 8
-// channels.  Channels with keep[k] != 0 (keep may be NULL) stay exact: their
-// error is 0.
+// stored as an fp16 pair hi = fp16(E'), lo = fp16(E' - hi).  Thread (row block
+// rb, word w) takes channels 8w .. 8w + 7 of rows kErrRows rb .. + kErrRows - 1;
+// the 16 threads of an aligned segment hold one 128-channel group of the same
+// rows (K / 8 is a multiple of 16).  Channels with keep[k] != 0 (keep may be
+// NULL) stay exact: their error is 0.
 template <int QMAX>
 __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
                                                           const double* __restrict__ inv,
@@ -134,39 +142,57 @@ __global__ __launch_bounds__(256) void quant_error_kernel(const uint4* __restric
                                                           const uint8_t* __restrict__ keep, int64_t N, int64_t K,
                                                           f16* __restrict__ Ehi, f16* __restrict__ Elo) {
   const int64_t K8 = K / 8;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // word index over N*K/8
-  // K8 is a multiple of 16, so a 16-lane segment never straddles rows; the
-  // grid covers whole segments, so every lane of a live segment is live.
-  if (idx >= N * K8) return;
-  const int64_t n = idx / K8, w = idx - n * K8;
-  float wf[8], sf[8];
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rb = idx / K8, w = idx - rb * K8, n0 = rb * kErrRows;
+  // the grid covers whole 16-lane segments, and all lanes of a segment share rb
+  if (n0 >= N) return;
+  float sf[8];
   double iv[8];
-  load_w8(W, idx, wf);
+  int32_t e8[8];
+  bool kept[8];
   load_s8(s, w * 8, sf);
   load_inv8(inv, w * 8, iv);
-  Quant8 r;
-  quantize8<QMAX>(wf, sf, r);
-  uint32_t hw[4], lw[4];
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    f16x2 h, l;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      double e = weight_error(r.q[i + u], r.z, r.sc, iv[i + u], wf[i + u]);
-      if (keep != nullptr && keep[w * 8 + i + u]) e = 0.0;
-      const float v = (float)ldexp(e, ex[w * 8 + i + u]);
-      const f16 hi = (f16)v;
-      h[u] = hi;
-      l[u] = (f16)(v - (float)hi);
-    }
-    hw[i / 2] = as_u32(h);
-    lw[i / 2] = as_u32(l);
+  {
+    const int4 a = *reinterpret_cast<const int4*>(ex + w * 8), b = *reinterpret_cast<const int4*>(ex + w * 8 + 4);
+    e8[0] = a.x; e8[1] = a.y; e8[2] = a.z; e8[3] = a.w;
+    e8[4] = b.x; e8[5] = b.y; e8[6] = b.z; e8[7] = b.w;
   }
-  *reinterpret_cast<uint4*>(Ehi + n * K + w * 8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-  *reinterpret_cast<uint4*>(Elo + n * K + w * 8) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kept[i] = keep != nullptr && keep[w * 8 + i];
+  uint4 raw[kErrRows];
+#pragma unroll
+  for (int r = 0; r < kErrRows; ++r) raw[r] = W[(n0 + r < N ? n0 + r : N - 1) * K8 + w];
+#pragma unroll
+  for (int r = 0; r < kErrRows; ++r) {
+    const int64_t n = n0 + r;
+    if (n >= N) break;  // uniform over the segment
+    float wf[8];
+    unpack_w8(raw[r], wf);
+    Quant8 q;
+    quantize8<QMAX>(wf, sf, q);
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      f16x2 h, l;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        double e = weight_error(q.q[i + u], q.z, q.sc, iv[i + u], wf[i + u]);
+        if (kept[i + u]) e = 0.0;
+        const float v = (float)ldexp(e, e8[i + u]);
+        const f16 hi = (f16)v;
+        h[u] = hi;
+        l[u] = (f16)(v - (float)hi);
+      }
+      hw[i / 2] = as_u32(h);
+      lw[i / 2] = as_u32(l);
+    }
+    *reinterpret_cast<uint4*>(Ehi + n * K + w * 8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *reinterpret_cast<uint4*>(Elo + n * K + w * 8) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
 }
 
-// Unscaled weight error in fp32 for the direct form of the loss.
+// Unscaled weight error in fp32 for the direct form of the loss; the same
+// mapping as above.
 template <int QMAX>
 __global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restrict__ W, const float* __restrict__ s,
                                                             const double* __restrict__ inv,
@@ -174,29 +200,43 @@ __global__ __launch_bounds__(256) void quant_error32_kernel(const uint4* __restr
                                                             float* __restrict__ E) {
   const int64_t K8 = K / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= N * K8) return;  // whole 16-lane segments, as above
-  const int64_t n = idx / K8, w = idx - n * K8;
-  float wf[8], sf[8];
+  const int64_t rb = idx / K8, w = idx - rb * K8, n0 = rb * kErrRows;
+  if (n0 >= N) return;  // whole 16-lane segments, as above
+  float sf[8];
   double iv[8];
-  load_w8(W, idx, wf);
+  bool kept[8];
   load_s8(s, w * 8, sf);
   load_inv8(inv, w * 8, iv);
-  Quant8 r;
-  quantize8<QMAX>(wf, sf, r);
-  float e[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    e[i] = (float)weight_error(r.q[i], r.z, r.sc, iv[i], wf[i]);
-    if (keep != nullptr && keep[w * 8 + i]) e[i] = 0.0f;
+  for (int i = 0; i < 8; ++i) kept[i] = keep != nullptr && keep[w * 8 + i];
+  uint4 raw[kErrRows];
+#pragma unroll
+  for (int r = 0; r < kErrRows; ++r) raw[r] = W[(n0 + r < N ? n0 + r : N - 1) * K8 + w];
+#pragma unroll
+  for (int r = 0; r < kErrRows; ++r) {
+    const int64_t n = n0 + r;
+    if (n >= N) break;
+    float wf[8];
+    unpack_w8(raw[r], wf);
+    Quant8 q;
+    quantize8<QMAX>(wf, sf, q);
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = kept[i] ? 0.0f : (float)weight_error(q.q[i], q.z, q.sc, iv[i], wf[i]);
+    float4* out = reinterpret_cast<float4*>(E + n * K + w * 8);
+    out[0] = make_float4(e[0], e[1], e[2], e[3]);
+    out[1] = make_float4(e[4], e[5], e[6], e[7]);
   }
-  float4* out = reinterpret_cast<float4*>(E + n * K + w * 8);
-  out[0] = make_float4(e[0], e[1], e[2], e[3]);
-  out[1] = make_float4(e[4], e[5], e[6], e[7]);
+}
+
+static dim3 error_grid(int64_t N, int64_t K) {
+  const int64_t threads = (N + kErrRows - 1) / kErrRows * (K / 8);
+  return dim3((unsigned)((threads + 255) / 256));
 }
 
 hipError_t launch_quant_error32(const void* W, const float* s, const double* inv, const uint8_t* keep, int64_t N,
                                 int64_t K, int bits, float* E, hipStream_t st) {
-  const dim3 grid((unsigned)((N * (K / 8) + 255) / 256)), block(256);
+  const dim3 grid = error_grid(N, K), block(256);
   auto Wp = reinterpret_cast<const uint4*>(W);
   if (bits == 3) quant_error32_kernel<7><<<grid, block, 0, st>>>(Wp, s, inv, keep, N, K, E);
   else quant_error32_kernel<15><<<grid, block, 0, st>>>(Wp, s, inv, keep, N, K, E);
@@ -206,7 +246,7 @@ hipError_t launch_quant_error32(const void* W, const float* s, const double* inv
 hipError_t launch_quant_error(const void* W, const float* s, const double* inv, const int32_t* ex,
                               const uint8_t* keep, int64_t N, int64_t K, int bits, void* Ehi, void* Elo,
                               hipStream_t st) {
-  const dim3 grid((unsigned)((N * (K / 8) + 255) / 256)), block(256);
+  const dim3 grid = error_grid(N, K), block(256);
   auto Wp = reinterpret_cast<const uint4*>(W);
   auto hi = reinterpret_cast<f16*>(Ehi);
   auto lo = reinterpret_cast<f16*>(Elo);
