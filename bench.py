@@ -526,19 +526,29 @@ def run_search_joint(args, torch, awq, dev):
                 calib_rows=M, n_alpha=20)
 
 
+def host_cpu():
+    """The host's CPU model and the threads the oracle's OpenMP loops use."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0) or os.cpu_count() or 1)
+    return model, threads, os.cpu_count()
+
+
 def run_cpu_baseline(layers_spec, budget_s: float):
-    """The oracle's fp64 W4A16 product over the 7 decode layers, on the host cores."""
+    """The C++ oracle's fp64 W4A16 product over the 7 decode layers, on the host cores."""
     import oracle
     from gen import activations_fp16, normal_fp16
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    model, threads, ncpu = host_cpu()
     prepared = []
     for name, K, N in layers_spec:
         W = normal_fp16((N, K), 0.02, seed=2000 + K + N)
-        q, z, sc = oracle.quantize_groups(W.astype(np.float32))
+        q, z, sc = oracle.quantize_groups(oracle.scale_weights(W, np.ones(K, np.float32)))
         x = activations_fp16(1, K, seed=2100 + K)
         prepared.append((x, q, z, sc, gemv_bytes(1, K, N)))
     nbytes = 0
@@ -553,8 +563,47 @@ def run_cpu_baseline(layers_spec, budget_s: float):
             break
     dt = time.perf_counter() - t0
     return dict(value=round(nbytes / dt / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"{steps} full decode steps (7 layers of the 7B block, M=1) through oracle.gemm "
-                       f"(fp64 dequantize + matmul), {dt:.1f} s")
+                cpu_model=model, host_cpus=ncpu,
+                sample=f"{steps} full decode steps (7 layers of the 7B block, M=1) through the C++ oracle's gemm "
+                       f"(fp64 dequantize + product, OpenMP over output rows), {dt:.1f} s")
+
+
+def run_oracle_timings(args):
+    """The C++ oracle timed on the host cores for the other timed workloads: the M = 256
+    product on (4096, 11008), and per 7B-block search shape class the statistics, the Gram
+    matrix (65,536 rows) and one alpha (quantize, error, loss); a full search is the
+    statistics plus 20 alphas.  Seconds, with the thread count and CPU model."""
+    import oracle
+    from gen import activations_fp16, normal_fp16, seed_for
+    model, threads, ncpu = host_cpu()
+    out = dict(cpu_model=model, threads=threads, host_cpus=ncpu)
+    K, N, M = 4096, 11008, 256
+    W = normal_fp16((N, K), 0.02, seed=3001)
+    q, z, sc = oracle.quantize_groups(oracle.scale_weights(W, np.ones(K, np.float32)))
+    x = activations_fp16(M, K, seed=3100 + M)
+    t0 = time.perf_counter()
+    oracle.gemm(x, q, z, sc)
+    dt = time.perf_counter() - t0
+    out["gemm_m256_4096x11008"] = dict(s=round(dt, 3), GFLOPs=round(2.0 * M * N * K / dt / 1e9, 2))
+    Mc = 65536
+    for li, (name, K, N) in enumerate([("q_proj", 4096, 4096), ("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)]):
+        X = activations_fp16(Mc, K, seed=seed_for(5, 10 + li), lognormal=True)
+        W = normal_fp16((N, K), 0.02, seed=seed_for(5, 100 + li))
+        t0 = time.perf_counter()
+        a = oracle.channel_mean_abs(X)
+        t1 = time.perf_counter()
+        G = oracle.gram(X)
+        t2 = time.perf_counter()
+        qa, za, sca, s = oracle.quantize_at(W, a, 0.35)
+        E = oracle.weight_error(W, qa, za, sca, s)
+        oracle.output_mse_gram(G, E, Mc)
+        t3 = time.perf_counter()
+        out[f"search_{name}_{K}x{N}"] = dict(stats_s=round(t1 - t0, 2), gram_s=round(t2 - t1, 2),
+                                             one_alpha_s=round(t3 - t2, 2),
+                                             full_search_s=round((t2 - t0) + 20 * (t3 - t2), 1))
+        log(f"oracle {name}: {out[f'search_{name}_{K}x{N}']}")
+        del X, W, G, E
+    return out
 
 
 def load_ceilings():
@@ -736,6 +785,9 @@ def main():
                     help="skip the fused, scaled-input and 3-bit decode legs (the headline step only)")
     ap.add_argument("--profile-mode", choices=["decode", "copy", "gemm", "ring", "ceilings", "search"], default=None)
     ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--oracle-timings", action="store_true",
+                    help="also time the C++ oracle on the M = 256 product and one search layer per shape class "
+                         "(minutes of host CPU time)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV", default=None,
                     help="print the dispatch statistics of a rocprofv3 kernel_trace.csv (no GPU) and exit")
     ap.add_argument("--kernel", default="gemv_kernel", help="kernel-name substring for --summarize-trace")
@@ -805,6 +857,9 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on host cores")
         cpu = run_cpu_baseline(LAYERS_7B, args.cpu_budget)
+    if args.oracle_timings:
+        log("oracle timings: M = 256 product and one search layer per shape class on the host cores")
+        legs["oracle_cpu_timings"] = run_oracle_timings(args)
 
     traffic = measured_traffic(dec["bytes_per_launch"])
     trace = trace_summary_for_roofline()

@@ -1,5 +1,6 @@
-"""Writes search_llama2_7b_block.json: the oracle's scale search on the seven linears
-of a Llama-2-7B-shaped block with 65,536 seeded calibration rows per input.
+"""Writes search_llama2_7b_block.json: the oracle's scale search (the C++ oracle,
+oracle/awq_oracle.cpp) on the seven linears of a Llama-2-7B-shaped block with 65,536
+seeded calibration rows per input.
 
 Calls only the seeded generator (gen) and the oracle.  Run from the repository root:
     python tests/golden/make_search_llama2_7b_block.py
@@ -37,8 +38,9 @@ def layer_weight(li, K, N):
 
 def main():
     alphas = oracle.alpha_grid(20)
-    out = {"_about": "oracle.search on the 7B-block search workload (65,536 calibration rows, lognormal channel "
-                      "profile, 1% outliers x20, 20 alphas, group 128); written by make_search_llama2_7b_block.py",
+    out = {"_about": "oracle.search (C++ oracle) on the 7B-block search workload (65,536 calibration rows, "
+                      "lognormal channel profile, 1% outliers x20, 20 alphas, group 128); written by "
+                      "make_search_llama2_7b_block.py",
            "calib_rows": M, "alphas": [float(a) for a in alphas], "layers": {}}
     cache = {}
     for li, (lname, src) in enumerate(layer_inputs_7b_block()):
@@ -52,7 +54,8 @@ def main():
         r = oracle.search(W, X, alphas=alphas)
         dt = time.time() - t0
         out["layers"][lname] = {"K": K, "N": N, "alpha_index": int(r["alpha_index"]),
-                                "losses": [float(v) for v in r["losses"]], "oracle_seconds": round(dt, 1)}
+                                "losses": [float(v) for v in r["losses"]], "oracle_seconds": round(dt, 1),
+                                "oracle_threads": os.cpu_count()}
         print(f"{lname}: alpha*={alphas[r['alpha_index']]:.2f} L*/L0={r['losses'][r['alpha_index']] / r['losses'][0]:.4f} "
               f"({dt:.0f} s)", flush=True)
     path = os.path.join(ROOT, "tests", "golden", "search_llama2_7b_block.json")

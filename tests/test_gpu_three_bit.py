@@ -180,11 +180,14 @@ def test_gemm3_decode_ring_wide_sampled_rows(N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(300, 640, 40), (1000, 16640, 24), (4100, 4096, 64), (11008, 4096, 20),
-                                   (10240, 8192, 24), (10240, 8192, 48), (9000, 4224, 50), (16400, 8320, 24)])
+                                   (10240, 8192, 24), (10240, 8192, 48), (9000, 4224, 50), (16400, 8320, 24),
+                                   (16400, 6144, 24), (10240, 6144, 48)])
 def test_gemm3_ring_mid_m(N, K, M):
-    """17 <= M <= 64 at 3 bits on the ring kernel with two or four x tiles per stage (10240 x
-    8192 and 9000 x 4224 take its fallback layout, where the 4-bit product takes other kernels:
-    one weight tile per block at M <= 32, two above)."""
+    """17 <= M <= 64 at 3 bits on the ring kernel with two or four x tiles per stage.  Most of
+    these shapes have a ring layout of their own (the 4-bit rule); layers with none at 3 bits
+    take the fallback layout: (16400, 6144) at M = 24 (wider than 12288 rows with
+    4096 < K < 8192: one weight tile per block) and (10240, 6144) and (9000, 4224) above M = 32
+    (two weight tiles per block)."""
     note(f"gemm3 ring mid N={N} K={K} M={M}")
     q, z, sc, p, scd, zd = _random_packed3(N, K, seed=N + K + M)
     x = activations_fp16(M, K, seed=N + M)

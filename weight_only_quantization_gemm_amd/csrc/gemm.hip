@@ -145,14 +145,10 @@ hipError_t launch_gemm3(const void* x, const void* packed, const void* scales, c
                         int64_t N, int64_t K, hipStream_t st) {
   if (gemv3_supported(M, K)) return launch_gemv3(x, packed, scales, zeros, y, M, N, K, st);
   if (ring3_supported(M, N, K)) return launch_ring3(x, packed, scales, zeros, y, M, N, K, st);
-#ifndef AWQ_NO_PIPE3
   if (ring_mid_pipe_preferred(M, N, K) && gemm_pipe3_supported(M, N, K))
     return launch_gemm_pipe3(x, packed, scales, zeros, y, M, N, K, st);
-#endif
   if (ring_mid_supported(M, N, K, 3)) return launch_ring_mid(x, packed, scales, zeros, y, M, N, K, 3, st);
-#ifndef AWQ_NO_PIPE3
   if (gemm_pipe3_supported(M, N, K)) return launch_gemm_pipe3(x, packed, scales, zeros, y, M, N, K, st);
-#endif
   if ((M + kBM - 1) / kBM > 65535) return hipErrorInvalidValue;  // grid.y limit
   dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
   gemm_kernel<3><<<grid, dim3(256), 0, st>>>(reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),

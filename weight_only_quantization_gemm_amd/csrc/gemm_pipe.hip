@@ -334,12 +334,7 @@ static bool pipe_fits(int64_t G) {
 // the 1 x 4 wave layout (wave tile 128 x 32: each unpacked weight operand
 // feeds four MFMAs) beats 2 x 2 by 10-15 %; two wave sets per block add ~3 %
 // at K = 4096 and are neutral at K = 8192.
-#ifndef AWQ_PIPE_KS
-#define AWQ_PIPE_KS 2
-#endif
-#ifndef AWQ_PIPE_WN
-#define AWQ_PIPE_WN 4
-#endif
+constexpr int kPipeSets128 = 2, kPipeWN128 = 4;
 
 // Shapes.  64-row x tiles in two channel sets (8 waves) over four stages for
 // M <= 64, and for larger M when their rounds over the 256 compute units cost
@@ -374,9 +369,9 @@ hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scale
   const int64_t G = K / kGroup;
   if (!pipe_rows64(M, N, G)) {
     if (pipe_fits<128, 3, kLdsBytes>(G))
-      return pipe_launch<128, 3, kLdsBytes, AWQ_PIPE_KS, AWQ_PIPE_WN>(x, packed, scales, zeros, y, M, N, K, st);
+      return pipe_launch<128, 3, kLdsBytes, kPipeSets128, kPipeWN128>(x, packed, scales, zeros, y, M, N, K, st);
     if (pipe_fits<128, 2, kLdsBytes>(G))
-      return pipe_launch<128, 2, kLdsBytes, 1, AWQ_PIPE_WN>(x, packed, scales, zeros, y, M, N, K, st);
+      return pipe_launch<128, 2, kLdsBytes, 1, kPipeWN128>(x, packed, scales, zeros, y, M, N, K, st);
     return hipErrorInvalidValue;
   }
   if (pipe_fits<64, 4, kLdsBytes>(G)) return pipe_launch<64, 4, kLdsBytes, 2, 4>(x, packed, scales, zeros, y, M, N, K, st);
@@ -400,7 +395,7 @@ hipError_t launch_gemm_pipe3(const void* x, const void* packed, const void* scal
   if (M <= 16) return hipErrorInvalidValue;
   if (!pipe_rows64(M, N, G)) {
     if (!pipe_fits<128, 3, kLdsBytes>(G)) return hipErrorInvalidValue;
-    return pipe_launch<128, 3, kLdsBytes, AWQ_PIPE_KS, AWQ_PIPE_WN, 3>(x, packed, scales, zeros, y, M, N, K, st);
+    return pipe_launch<128, 3, kLdsBytes, kPipeSets128, kPipeWN128, 3>(x, packed, scales, zeros, y, M, N, K, st);
   }
   if (!pipe_fits<64, 4, kLdsBytes>(G)) return hipErrorInvalidValue;
   return pipe_launch<64, 4, kLdsBytes, 2, 4, 3>(x, packed, scales, zeros, y, M, N, K, st);
