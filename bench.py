@@ -690,26 +690,35 @@ def trace_summary_for_roofline():
                 span_per_launch_us=float(fields["span_per_launch_us"]), dispatches=int(fields["dispatches"]))
 
 
-def summarize_trace(csv_path, pattern, out_lines):
-    """Per-kernel dispatch statistics from a rocprofv3 kernel_trace.csv: count and mean /
-    median duration of the kernels whose name contains `pattern`, and the span from the first
-    such dispatch's start to the last one's end divided by their count (the trace's analogue
+def summarize_trace(csv_path, pattern, out_lines, last=0):
+    """Dispatch statistics from a rocprofv3 kernel_trace.csv of the kernels whose name contains
+    `pattern` (only the last `last` such dispatches when last > 0: the timed region of a
+    profile-mode run): count, mean / median duration, per grid size, and the span from the
+    first dispatch's start to the last one's end divided by their count (the trace's analogue
     of a timed region divided by its launches)."""
     import csv
     rows = []
     with open(csv_path) as f:
         for r in csv.DictReader(f):
             if pattern in r.get("Kernel_Name", ""):
-                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+                grid = r.get("Grid_Size_X", r.get("Grid_Size", "?"))
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), grid))
     if not rows:
         raise SystemExit(f"no dispatch of a kernel matching {pattern!r} in {csv_path}")
     rows.sort()
-    d = np.array([e - b for b, e in rows], dtype=np.float64) / 1e3
-    span = (max(e for _, e in rows) - rows[0][0]) / 1e3
+    if last > 0:
+        rows = rows[-last:]
+    d = np.array([e - b for b, e, _ in rows], dtype=np.float64) / 1e3
+    span = (max(e for _, e, _ in rows) - rows[0][0]) / 1e3
     out_lines += [f"dispatches: {len(rows)}", f"mean_launch_us: {d.mean():.3f}",
                   f"median_launch_us: {np.median(d):.3f}", f"min_launch_us: {d.min():.3f}",
                   f"max_launch_us: {d.max():.3f}", f"span_per_launch_us: {span / len(rows):.3f}",
                   f"source_hash: {source_hash(GEMV_SOURCES)}"]
+    grids = {}
+    for (b, e, g) in rows:
+        grids.setdefault(g, []).append((e - b) / 1e3)
+    for g, v in sorted(grids.items(), key=lambda kv: int(kv[0]) if kv[0].isdigit() else 0):
+        out_lines.append(f"grid {g}: dispatches {len(v)}, mean_us {np.mean(v):.3f}, median_us {np.median(v):.3f}")
     return out_lines
 
 
@@ -791,9 +800,10 @@ def main():
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV", default=None,
                     help="print the dispatch statistics of a rocprofv3 kernel_trace.csv (no GPU) and exit")
     ap.add_argument("--kernel", default="gemv_kernel", help="kernel-name substring for --summarize-trace")
+    ap.add_argument("--last", type=int, default=0, help="--summarize-trace: only the last N matching dispatches")
     args = ap.parse_args()
     if args.summarize_trace:
-        print("\n".join(summarize_trace(args.summarize_trace, args.kernel, [])))
+        print("\n".join(summarize_trace(args.summarize_trace, args.kernel, [], args.last)))
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the W4A16 kernels are measured on one MI355X; "
@@ -863,6 +873,13 @@ def main():
 
     traffic = measured_traffic(dec["bytes_per_launch"])
     trace = trace_summary_for_roofline()
+    # The roofline's launch duration is the committed trace's per-dispatch mean over the same
+    # step graphs when it was taken on the current GEMV source (each launch timed alone by the
+    # profiler); the timed region divided by its launches, where back-to-back launches overlap
+    # one kernel's drain with the next one's start, is reported beside it.
+    live_us = dec["kern_ms"] * 1e3
+    launch_us = trace["mean_launch_us"] if trace else live_us
+    achieved = dec["bytes_per_launch"] / (launch_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -879,13 +896,15 @@ def main():
         "config": {"workload": "llama2_7b_decode_m1", "M": 1, "weights": "int4 g128 (fp16 scales, 4-bit zeros)",
                    "layers_KN": [[K, N] for _, K, N in LAYERS_7B], "bytes_per_step": dec["step_bytes"],
                    "rotating_weight_copies": dec["copies"], "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic, 0),
-                     "kernel": "awq::gemv_kernel (M=1)", "avg_launch_us": round(dec["kern_ms"] * 1e3, 3),
+                     "kernel": "awq::gemv_kernel (M=1)", "avg_launch_us": round(launch_us, 3),
                      "alg_bytes_per_launch": round(dec["bytes_per_launch"], 1),
-                     "timing": "HIP events on the replay stream around the timed graph replays, divided by the "
-                               "launches in the region (7 per step, back to back)",
+                     "timing": ("rocprofv3 per-dispatch mean over the timed step graphs (" + trace["file"] + ")")
+                     if trace else "HIP events on the replay stream around the timed graph replays / launches",
+                     "region_us_per_launch": round(live_us, 3),
+                     "region_frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
                      "trace": trace},
         "cpu_baseline": cpu,
         "per_layer": dec["per_layer"],
