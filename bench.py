@@ -722,6 +722,114 @@ def summarize_trace(csv_path, pattern, out_lines, last=0):
     return out_lines
 
 
+SEARCH_SOURCES = [f"weight_only_quantization_gemm_amd/csrc/{f}" for f in ("quant.hip", "loss.hip", "gram.hip", "stats.hip")]
+SEARCH_PROFILE_LAYERS = [("q_proj", 4096, 4096), ("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)]
+
+
+def summarize_search_trace(csv_path, calib_rows=65536, n_alpha=20):
+    """Markdown tables from the rocprofv3 kernel_trace.csv of `--profile-mode search` (each
+    layer searched twice on one workspace, in SEARCH_PROFILE_LAYERS order): the top kernels,
+    the loss per alpha of each layer's timed call, the HBM-bound phases against their
+    algorithmic bytes, and the Gram per K."""
+    import csv
+    from collections import defaultdict
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"],
+                         int(r.get("Grid_Size_X", r.get("Grid_Size", "0")))))
+    rows.sort()
+    us = lambda r: (r[1] - r[0]) / 1e3
+    out = []
+    tot = defaultdict(float)
+    cnt = defaultdict(int)
+    for r in rows:
+        tot[r[2]] += us(r)
+        cnt[r[2]] += 1
+    allt = sum(tot.values())
+    out += ["## top kernels", "", "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
+    for k in sorted(tot, key=lambda k: -tot[k])[:10]:
+        out.append(f"| `{k[:90]}` | {cnt[k]} | {tot[k]:.1f} | {tot[k] / cnt[k]:.1f} | {100 * tot[k] / allt:.1f} |")
+    # loss: 2 calls x n_alpha dispatches per layer, in layer order; the second call is the timed one
+    loss = [r for r in rows if "loss_full" in r[2]]
+    out += ["", "## loss per alpha (median over each layer's timed call)", "",
+            "Rates by the flops the kernel performs (three terms over the block-upper triangle of 256-blocks)",
+            "and by the method's own count (2 N K^2 per alpha: one full quadratic form).", "",
+            "| layer (K, N) | us per alpha | TFLOP/s done (of 2.5 PF) | TFLOP/s by the method's count |",
+            "|---|---|---|---|"]
+    for li, (name, K, N) in enumerate(SEARCH_PROFILE_LAYERS):
+        sel = loss[li * 2 * n_alpha + n_alpha:(li + 1) * 2 * n_alpha]
+        if not sel:
+            continue
+        t = float(np.median([us(r) for r in sel]))
+        jt = K // 256
+        tri = sum(min(256 * (J + 1), K) for J in range(jt)) * 256  # channels x columns contracted per n row
+        done = 3 * 2 * N * tri
+        meth = 2 * N * K * K
+        out.append(f"| {name} ({K}, {N}) | {t:.1f} | {done / t * 1e-6:.0f} ({done / t * 1e-6 / 25:.1f} %) | "
+                   f"{meth / t * 1e-6:.0f} ({meth / t * 1e-6 / 25:.1f} %) |")
+    # every awq_quantize call starts with its statistics pass: call c is layer c // 2
+    starts = [i for i, r in enumerate(rows) if "stats_accumulate" in r[2]]
+    layer_of = [None] * len(rows)
+    for c, i0 in enumerate(starts):
+        i1 = starts[c + 1] if c + 1 < len(starts) else len(rows)
+        for i in range(i0, i1):
+            layer_of[i] = SEARCH_PROFILE_LAYERS[min(c // 2, len(SEARCH_PROFILE_LAYERS) - 1)]
+    out += ["", "## HBM-bound phases", "",
+            "| kernel | layer (K, N) | dispatches | mean us | algorithmic bytes | GB/s (of 8 TB/s) |",
+            "|---|---|---|---|---|---|"]
+    groups = defaultdict(list)
+    for i, r in enumerate(rows):
+        for key in ("stats_accumulate", "transpose_kernel", "quant_error_kernel", "pack_kernel"):
+            if key in r[2] and layer_of[i] is not None:
+                groups[(key, layer_of[i])].append(us(r))
+    what = {"stats_accumulate": "X read", "transpose_kernel": "X read, X^T written",
+            "quant_error_kernel": "W read, E hi/lo written (per alpha)", "pack_kernel": "W read; codes, scales, zeros written"}
+    for key in ("stats_accumulate", "transpose_kernel", "quant_error_kernel", "pack_kernel"):
+        for lay in SEARCH_PROFILE_LAYERS:
+            v = groups.get((key, lay))
+            if not v:
+                continue
+            name, K, N = lay
+            alg = {"stats_accumulate": 2 * calib_rows * K, "transpose_kernel": 4 * calib_rows * K,
+                   "quant_error_kernel": 6 * N * K,
+                   "pack_kernel": 2 * N * K + N * K // 2 + N * K // 64 + N * ((K // 128 + 1) // 2)}[key]
+            m = float(np.mean(v))
+            out.append(f"| {key} ({what[key]}) | {name} ({K}, {N}) | {len(v)} | {m:.1f} | {alg} | "
+                       f"{alg / m * 1e-3:.0f} ({alg / m * 1e-3 / 80:.1f} %) |")
+    gram = [r for r in rows if "gram_kernel" in r[2]]
+    out += ["", "## Gram (X^T X over the calibration rows, symmetric half of 2 M K^2 flops)", "",
+            "| K | dispatches | mean us | TFLOP/s (of 2.5 PF) |", "|---|---|---|---|"]
+    seen = []
+    for name, K, N in SEARCH_PROFILE_LAYERS:
+        if K in seen:
+            continue
+        seen.append(K)
+    for i, K in enumerate(seen):
+        v = [us(r) for r in gram if r[3] == gram_grid_threads(K)]
+        if v:
+            m = float(np.mean(v))
+            fl = calib_rows * K * K
+            out.append(f"| {K} | {len(v)} | {m:.0f} | {fl / m * 1e-6:.0f} ({fl / m * 1e-6 / 25:.1f} %) |")
+    out += ["", f"kernel sources (sha256[:16] of {' + '.join(SEARCH_SOURCES)}): {source_hash(SEARCH_SOURCES)}"]
+    return out
+
+
+def gram_grid_threads(K):
+    """Threads in gram_kernel's grid for K channels (the launch's tile count per XCD, times 8 x 256)."""
+    nb, gs = K // 128, 4
+    ns = (nb + gs - 1) // gs
+    per = [0] * 8
+    s = 0
+    for si in range(ns):
+        for sj in range(si, ns):
+            ni = min(nb - gs * si, gs)
+            nj = min(nb - gs * sj, gs)
+            per[s % 8] += ni * (ni + 1) // 2 if si == sj else ni * nj
+            s += 1
+    return 8 * max(per) * 256
+
+
 def profile_mode(args, torch, awq, dev):
     """Short runs for rocprofv3: the headline decode step graphs alone, a plain copy (counter
     scale), one GEMM or decode-ring layer, or the ceiling kernels."""
@@ -742,8 +850,7 @@ def profile_mode(args, torch, awq, dev):
         # 20 alphas), each after a warm-up call on the same workspace
         from gen import activations_fp16, normal_fp16, seed_for
         M, out = 65536, {}
-        for li, (name, K, N) in enumerate([("q_proj", 4096, 4096), ("gate_proj", 4096, 11008),
-                                           ("down_proj", 11008, 4096)]):
+        for li, (name, K, N) in enumerate(SEARCH_PROFILE_LAYERS):
             X = torch.from_numpy(activations_fp16(M, K, seed=seed_for(5, 10 + li), lognormal=True)).to(dev)
             W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=seed_for(5, 100 + li))).to(dev)
             ws = torch.empty((awq.awq_quantize_workspace_bytes(N, K, M, 128, 20),), dtype=torch.uint8, device=dev)
@@ -799,11 +906,17 @@ def main():
                          "(minutes of host CPU time)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV", default=None,
                     help="print the dispatch statistics of a rocprofv3 kernel_trace.csv (no GPU) and exit")
+    ap.add_argument("--summarize-search-trace", metavar="KERNEL_TRACE_CSV", default=None,
+                    help="print the markdown tables of profiles/search_llama2_7b_block_trace.md from the kernel "
+                         "trace of --profile-mode search, and exit")
     ap.add_argument("--kernel", default="gemv_kernel", help="kernel-name substring for --summarize-trace")
     ap.add_argument("--last", type=int, default=0, help="--summarize-trace: only the last N matching dispatches")
     args = ap.parse_args()
     if args.summarize_trace:
         print("\n".join(summarize_trace(args.summarize_trace, args.kernel, [], args.last)))
+        return
+    if args.summarize_search_trace:
+        print("\n".join(summarize_search_trace(args.summarize_search_trace)))
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the W4A16 kernels are measured on one MI355X; "
