@@ -174,60 +174,66 @@ void loss_full_kernel(const f16* __restrict__ Ehi, const f16* __restrict__ Elo, 
       const f16* Gl = lds[slot][1];
       const f16* Eh = lds[slot][2];
       const f16* El = lds[slot][3];
+      // The stage's E' fragments are read up front; the G'' fragments of step i + 1
+      // (channel half hk, 32-row block a) are read while the matrix cores run step i.
+      constexpr int HK = kFKS / 16, STEPS = HK * 4;
+      f16x8 eh[HK][2], el[HK][2], gh[2], gl[2];
 #pragma unroll
-      for (int hk = 0; hk < kFKS / 16; ++hk) {
-        const int c = 2 * hk + (lane >> 5);
-        f16x8 eh[2], el[2];
+      for (int hk = 0; hk < HK; ++hk)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          eh[b] = frag32(Eh, wn * 64 + b * 32 + l32, c);
-          el[b] = frag32(El, wn * 64 + b * 32 + l32, c);
+          eh[hk][b] = frag32(Eh, wn * 64 + b * 32 + l32, 2 * hk + (lane >> 5));
+          el[hk][b] = frag32(El, wn * 64 + b * 32 + l32, 2 * hk + (lane >> 5));
         }
+      auto load_g = [&](int i, int buf) {
+        const int c = 2 * (i >> 2) + (lane >> 5), row = wj * 128 + (i & 3) * 32 + l32;
+        gh[buf] = frag32(Gh, row, c);
+        gl[buf] = frag32(Gl, row, c);
+      };
+      load_g(0, 0);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const f16x8 gh = frag32(Gh, wj * 128 + a * 32 + l32, c);
-          const f16x8 gl = frag32(Gl, wj * 128 + a * 32 + l32, c);
+      for (int i = 0; i < STEPS; ++i) {
+        if (i + 1 < STEPS) load_g(i + 1, (i + 1) & 1);
+        const int hk = i >> 2, a = i & 3, cb = i & 1;
 #pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gh, eh[b], acc[a][b], 0, 0, 0);
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gh, el[b], acc[a][b], 0, 0, 0);
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gl, eh[b], acc[a][b], 0, 0, 0);
-          }
+        for (int b = 0; b < 2; ++b) {
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gh[cb], eh[hk][b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gh[cb], el[hk][b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gl[cb], eh[hk][b], acc[a][b], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep each step's reads and MFMAs within the step
       }
     }
     wait_vmcnt<0>();  // the tail's redundant loads land before the ring is reused or the block exits
 
-    // sum over the tile of E'[n][j] * T[n][j], E' = hi + lo in fp32.  The lane's 32 E'
-    // pairs are all loaded before any is used (one round trip to memory); rows past N and
-    // channels past K (all 4 of a quad or none, K % 128 == 0) read a valid element and are
-    // dropped from the sum.
-    u32x2 hv[2][4][4], lv[2][4][4];
+    // sum over the tile of E'[n][j] * T[n][j], E' = hi + lo in fp32.  For each of its two
+    // rows n the lane loads its 16 E' pairs before using any (two round trips to memory;
+    // all 32 at once would not fit beside the accumulators, and the compiler then waited
+    // for the loads one by one); rows past N and channels past K (all 4 of a quad or none,
+    // K % 128 == 0) read a valid element and are dropped from the sum.
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      int64_t n = n0 + wn * 64 + b * 32 + l32;
-      n = n < N ? n : N - 1;
+      int64_t nl = n0 + wn * 64 + b * 32 + l32;
+      const bool nlive = nl < N;
+      nl = nlive ? nl : N - 1;
+      u32x2 hv[4][4], lv[4][4];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           int64_t j = j0 + wj * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
           j = j < K ? j : K - 4;
-          hv[b][a][q] = *reinterpret_cast<const u32x2*>(Ehi + n * K + j);
-          lv[b][a][q] = *reinterpret_cast<const u32x2*>(Elo + n * K + j);
+          hv[a][q] = *reinterpret_cast<const u32x2*>(Ehi + nl * K + j);
+          lv[a][q] = *reinterpret_cast<const u32x2*>(Elo + nl * K + j);
         }
-    }
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t n = n0 + wn * 64 + b * 32 + l32;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t j = j0 + wj * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
-          if (n >= N || j >= K) continue;
-          const f16x2 h01 = as_f16x2(hv[b][a][q].x), h23 = as_f16x2(hv[b][a][q].y);
-          const f16x2 l01 = as_f16x2(lv[b][a][q].x), l23 = as_f16x2(lv[b][a][q].y);
+          if (!nlive || j >= K) continue;
+          const f16x2 h01 = as_f16x2(hv[a][q].x), h23 = as_f16x2(hv[a][q].y);
+          const f16x2 l01 = as_f16x2(lv[a][q].x), l23 = as_f16x2(lv[a][q].y);
           const float e[4] = {(float)h01.x + (float)l01.x, (float)h01.y + (float)l01.y,
                               (float)h23.x + (float)l23.x, (float)h23.y + (float)l23.y};
 #pragma unroll
