@@ -87,21 +87,42 @@ hipError_t launch_channel_mean_abs(const void* X, int64_t M, int64_t K, double* 
 }
 
 // Xt[k][t] = X[t][k] for t < M, 0 for M <= t < Mp (Mp a multiple of 64).
-// 64x64 tiles through LDS; one extra column of padding avoids bank conflicts.
+// 64 x 64 tiles through LDS, 16 bytes per global access: a thread reads 8
+// channels of one row t (eight threads cover a row's 128 bytes) and writes 8
+// rows t of one channel k.  The LDS row pitch of 66 halfs puts the eight rows a
+// write gathers from (t = 8c .. 8c + 7 for the eight c of a wave) on distinct
+// banks; the row is stored as four 4-byte words (its 132-byte pitch is not
+// 16-byte aligned).  A row chunk past K (K % 8 == 0) or past M reads zeros.
+constexpr int kTP = 66;  // LDS pitch of the transpose tile, in halfs
+
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                         int64_t Mp, uint16_t* __restrict__ Xt) {
-  __shared__ uint16_t tile[64][65];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kTP];
   const int64_t t0 = (int64_t)blockIdx.x * 64;
   const int64_t k0 = (int64_t)blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
-  for (int r = ty; r < 64; r += 4) {
-    int64_t t = t0 + r, k = k0 + tx;
-    tile[r][tx] = (t < M && k < K) ? X[t * K + k] : (uint16_t)0;
+  const int c = threadIdx.x & 7, r = threadIdx.x >> 3;  // 8 chunks x 32 rows
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rr = r + 32 * h;
+    const int64_t t = t0 + rr, k = k0 + 8 * c;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (t < M && k < K) v = *reinterpret_cast<const uint4*>(X + t * K + k);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile + rr * kTP + 8 * c);
+    dst[0] = v.x;
+    dst[1] = v.y;
+    dst[2] = v.z;
+    dst[3] = v.w;
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) {
-    int64_t k = k0 + r, t = t0 + tx;
-    if (k < K && t < Mp) Xt[k * Mp + t] = tile[tx][r];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kk = r + 32 * h;  // channel within the tile; this thread writes rows 8c .. 8c + 7
+    const int64_t k = k0 + kk;
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[u] = (uint32_t)tile[(8 * c + 2 * u) * kTP + kk] | ((uint32_t)tile[(8 * c + 2 * u + 1) * kTP + kk] << 16);
+    if (k < K) *reinterpret_cast<uint4*>(Xt + k * Mp + t0 + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
