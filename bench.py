@@ -815,6 +815,65 @@ def summarize_search_trace(csv_path, calib_rows=65536, n_alpha=20):
     return out
 
 
+def summarize_search_counters(dirs, n_alpha=20):
+    """Markdown table of rocprofv3 --pmc passes over `--profile-mode search` restricted to the
+    loss and Gram kernels: per layer (loss, the timed call's dispatches) and per K (Gram), the
+    median of each counter over the dispatches, and ratios derived from them."""
+    import csv
+    import glob
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))  # (kernel, label) -> counter -> values
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            disp = defaultdict(dict)
+            names = {}
+            for r in csv.DictReader(open(f)):
+                did = int(r["Dispatch_Id"])
+                disp[did][r["Counter_Name"]] = float(r["Counter_Value"])
+                disp[did]["duration_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                names[did] = (r["Kernel_Name"], int(r.get("Grid_Size", "0")))
+            loss_ids = sorted(i for i in disp if "loss_full" in names[i][0])
+            for j, did in enumerate(loss_ids):
+                li, call = divmod(j, 2 * n_alpha)
+                if call >= n_alpha and li < len(SEARCH_PROFILE_LAYERS):  # the timed call
+                    name, K, N = SEARCH_PROFILE_LAYERS[li]
+                    for c, v in disp[did].items():
+                        vals[("loss_full_kernel", f"{name} ({K}, {N})")][c].append(v)
+            for did in disp:
+                if "gram_kernel" in names[did][0]:
+                    K = next((K for _, K, _ in SEARCH_PROFILE_LAYERS if gram_grid_threads(K) == names[did][1]), None)
+                    for c, v in disp[did].items():
+                        vals[("gram_kernel", f"K = {K}")][c].append(v)
+    keys = sorted(vals, key=lambda k: (k[0], k[1]))
+    counters = sorted({c for k in keys for c in vals[k]})
+    med = {k: {c: float(np.median(vals[k][c])) for c in vals[k]} for k in keys}
+    out = ["| counter | " + " | ".join(f"{k[0]} {k[1]}" for k in keys) + " |",
+           "|---|" + "---|" * len(keys)]
+    for c in counters:
+        out.append(f"| {c} | " + " | ".join(f"{med[k][c]:.4g}" if c in med[k] else "-" for k in keys) + " |")
+    derived = [
+        ("vector instructions per MFMA", lambda m: m["SQ_INSTS_VALU"] / m["SQ_INSTS_MFMA"]),
+        ("LDS instructions per MFMA", lambda m: m["SQ_INSTS_LDS"] / m["SQ_INSTS_MFMA"]),
+        ("MFMA-busy cycles / (1024 SIMDs x duration at 2.4 GHz)",
+         lambda m: m["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * m["duration_us"] * 2400)),
+        ("waiting / wave cycles (SQ_WAIT_ANY / SQ_WAVE_CYCLES)", lambda m: m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"]),
+        ("L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))", lambda m: m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"])),
+        ("fabric reads per dispatch, MB (FETCH_SIZE KiB x 1024 x 2: copy-calibrated factor 0.5)",
+         lambda m: m["FETCH_SIZE"] * 1024 * 2 / 1e6),
+        ("LDS bank-conflict cycles / LDS-active cycles", lambda m: m["SQ_LDS_BANK_CONFLICT"] / m["SQ_LDS_IDX_ACTIVE"]),
+    ]
+    out += ["", "| derived | " + " | ".join(f"{k[0]} {k[1]}" for k in keys) + " |", "|---|" + "---|" * len(keys)]
+    for label, fn in derived:
+        cells = []
+        for k in keys:
+            try:
+                cells.append(f"{fn(med[k]):.3g}")
+            except (KeyError, ZeroDivisionError):
+                cells.append("-")
+        out.append(f"| {label} | " + " | ".join(cells) + " |")
+    return out
+
+
 def gram_grid_threads(K):
     """Threads in gram_kernel's grid for K channels (the launch's tile count per XCD, times 8 x 256)."""
     nb, gs = K // 128, 4
@@ -909,6 +968,9 @@ def main():
     ap.add_argument("--summarize-search-trace", metavar="KERNEL_TRACE_CSV", default=None,
                     help="print the markdown tables of profiles/search_llama2_7b_block_trace.md from the kernel "
                          "trace of --profile-mode search, and exit")
+    ap.add_argument("--summarize-search-counters", metavar="PMC_DIR", nargs="+", default=None,
+                    help="print the counter tables of profiles/search_loss_gram_sq_counters.md from rocprofv3 --pmc "
+                         "output directories of --profile-mode search, and exit")
     ap.add_argument("--kernel", default="gemv_kernel", help="kernel-name substring for --summarize-trace")
     ap.add_argument("--last", type=int, default=0, help="--summarize-trace: only the last N matching dispatches")
     args = ap.parse_args()
@@ -917,6 +979,9 @@ def main():
         return
     if args.summarize_search_trace:
         print("\n".join(summarize_search_trace(args.summarize_search_trace)))
+        return
+    if args.summarize_search_counters:
+        print("\n".join(summarize_search_counters(args.summarize_search_counters)))
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the W4A16 kernels are measured on one MI355X; "
