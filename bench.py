@@ -291,14 +291,13 @@ def run_sweep(args, torch, awq, dev):
         out[str(M)] = dict(us=round(us, 3), GBs=round(nbytes / us / 1e3, 1),
                            hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                            TFLOPs=round(flops / us / 1e6, 2), mfma_frac=round(flops / us / 1e6 / FP16_PEAK_TFLOPS, 4),
-                           kernel="gemv_dot2" if M <= 2 else ("ring_mfma" if M <= 16 else "mfma_gemm"))
+                           kernel=awq.awq_gemm_kernel(M, N, K))
     return out
 
 
 def run_sweep3(args, torch, awq, dev):
-    """The same (K=4096, N=11008) layer with 3-bit codes at M = 1..1024 (decode batch sizes, and
-    M = 64 on the matrix-core ring kernel with four x tiles per stage) and prefill sizes 256 and 1024
-    on the pipelined matrix-core GEMM."""
+    """The same (K=4096, N=11008) layer with 3-bit codes at M = 1..1024 (`kernel` names what the
+    library's dispatch launched)."""
     from gen import activations_fp16, normal_fp16
     K, N = 4096, 11008
     W = torch.from_numpy(normal_fp16((N, K), 0.02, seed=3001)).to(dev)
@@ -321,7 +320,7 @@ def run_sweep3(args, torch, awq, dev):
         out[str(M)] = dict(us=round(us, 3), GBs=round(nbytes / us / 1e3, 1),
                            hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                            TFLOPs=round(2.0 * M * N * K / us / 1e6, 2),
-                           kernel="gemv3_dot2" if M <= 2 else "ring_mfma" if M <= 64 else "gemm_pipe_mfma")
+                           kernel=awq.awq_gemm_kernel(M, N, K, bits=3))
     del packs
     return out
 
@@ -360,12 +359,11 @@ def run_70b(args, torch, awq, dev):
             del g
             nbytes = gemv_bytes(M, K, N)
             per[name] = dict(K=K, N=N, us=round(us, 3), GBs=round(nbytes / us / 1e3, 1),
-                             hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4))
+                             hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), kernel=awq.awq_gemm_kernel(M, N, K))
             step_us += us
             step_bytes += nbytes
         out[str(M)] = dict(step_us=round(step_us, 3), GBs=round(step_bytes / step_us / 1e3, 1),
-                           hbm_frac=round(step_bytes / step_us / 1e3 / HBM_PEAK_GBS, 4),
-                           kernel="gemv_dot2" if M <= 2 else "ring_mfma", layers=per)
+                           hbm_frac=round(step_bytes / step_us / 1e3 / HBM_PEAK_GBS, 4), layers=per)
     del packs
     return out
 

@@ -252,6 +252,17 @@ int awq_gemm(const void* x, const void* packed, const void* scales, const void* 
  * M <= 65535 * 64 at 3 bits. */
 int awq_gemm_bits(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                   int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* stream);
+/* awq_gemm_kernel -- the kernel awq_gemm_bits launches for an M x K input and
+ * N x K weights at `bits`: a dry run of the same dispatch that launches
+ * nothing and touches no device (host-only; it works without a GPU).  Writes
+ * the kernel's name with its template arguments, block and grid, for example
+ * "ring_kernel<4,1,1,2,32> block=256 grid=257", NUL-terminated and truncated
+ * to `out_bytes` (160 bytes always suffice), to `out` (host).  For tests that
+ * must reach every branch of the dispatch, and for diagnostics.  Returns
+ * AWQ_OK, or AWQ_ERROR_INVALID_VALUE for sizes awq_gemm_bits refuses (then
+ * `out` holds the empty string) or a NULL `out`.
+ */
+int awq_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, char* out, size_t out_bytes);
 
 /*
  * The input side of the per-channel scaling ([summary] paragraph 3: a weight

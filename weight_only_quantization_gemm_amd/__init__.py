@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     awq_ablation_workspace_bytes,
     awq_channel_mean_abs,
     awq_gemm,
+    awq_gemm_kernel,
     awq_gemm_scaled,
     awq_gemm_scaled_workspace_bytes,
     awq_keep_fp16_ablation,

@@ -6,6 +6,7 @@ All arithmetic happens in the library's HIP kernels.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional, Sequence
 
 import numpy as np
@@ -199,6 +200,15 @@ def awq_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros:
         check(load().awq_gemm_bits(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
                                    out.data_ptr(), M, N, K, group, bits, _stream(x.device)))
     return out
+
+
+def awq_gemm_kernel(M: int, N: int, K: int, bits: int = 4, group: int = GROUP) -> str:
+    """The kernel awq_gemm launches for an M x K input and N x K weights (a host-only dry run of
+    its dispatch: the kernel's template arguments, block and grid)."""
+    _check_bits(bits)
+    buf = ctypes.create_string_buffer(160)
+    check(load().awq_gemm_kernel(int(M), int(N), int(K), int(group), int(bits), buf, len(buf)))
+    return buf.value.decode()
 
 
 def awq_scale_input(x: torch.Tensor, s: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

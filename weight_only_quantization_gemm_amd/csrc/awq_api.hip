@@ -12,6 +12,23 @@
 #include "awq.h"
 #include "awq_internal.h"
 
+namespace awq {
+namespace {
+thread_local KernelPlan* g_plan = nullptr;
+}  // namespace
+
+KernelPlan* active_plan() { return g_plan; }
+void install_plan(KernelPlan* p) { g_plan = p; }
+
+hipError_t plan_record(KernelPlan* p, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(p->text, sizeof(p->text), fmt, ap);
+  va_end(ap);
+  return hipSuccess;
+}
+}  // namespace awq
+
 namespace {
 
 thread_local std::string g_last_error = "no error";
@@ -389,6 +406,15 @@ int awq_keep_fp16_ablation(const void* W, const void* X, int64_t N, int64_t K, i
   AWQ_GUARD_END
 }
 
+// The product's dispatch on the code width and M (each launcher picks its own
+// kernel and layout; see the launchers for the measured rules).
+static hipError_t launch_product(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                                 int64_t M, int64_t N, int64_t K, int32_t bits, hipStream_t hs) {
+  if (bits == 3) return awq::launch_gemm3(x, packed, scales, zeros, y, M, N, K, hs);
+  if (M <= 16) return awq::launch_gemv(x, packed, scales, zeros, y, M, N, K, hs);
+  return awq::launch_gemm(x, packed, scales, zeros, y, M, N, K, hs);
+}
+
 int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M, int64_t N,
              int64_t K, int32_t group, void* stream) {
   return awq_gemm_bits(x, packed, scales, zeros, y, M, N, K, group, 4, stream);
@@ -405,11 +431,32 @@ int awq_gemm_bits(const void* x, const void* packed, const void* scales, const v
   AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
   if (int st2 = check_aligned({{x, "x"}, {packed, "packed"}, {scales, "scales"}, {zeros, "zeros"}, {y, "y"}}))
     return st2;
-  hipError_t e;
-  if (bits == 3) e = awq::launch_gemm3(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
-  else if (M <= 16) e = awq::launch_gemv(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
-  else e = awq::launch_gemm(x, packed, scales, zeros, y, M, N, K, as_stream(stream));
-  return device_status(e, "awq_gemm");
+  return device_status(launch_product(x, packed, scales, zeros, y, M, N, K, bits, as_stream(stream)), "awq_gemm");
+  AWQ_GUARD_END
+}
+
+int awq_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, char* out, size_t out_bytes) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(out && out_bytes > 0, AWQ_ERROR_INVALID_VALUE, "out must not be NULL and out_bytes must be positive");
+  out[0] = 0;
+  int st = check_layer(N, K, group);
+  if (st == AWQ_OK) st = check_bits(bits);
+  if (st != AWQ_OK) return st;
+  AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
+  struct Installed {  // the plan stays installed only for this call, also if something throws
+    awq::KernelPlan plan;
+    Installed() {
+      plan.text[0] = 0;
+      awq::install_plan(&plan);
+    }
+    ~Installed() { awq::install_plan(nullptr); }
+  } dry;
+  // a dry run computes the launch only: no pointer is dereferenced, nothing is enqueued
+  const hipError_t e = launch_product(nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, bits, nullptr);
+  AWQ_REQUIRE(e == hipSuccess && dry.plan.text[0] != 0, AWQ_ERROR_INVALID_VALUE,
+              "no kernel launches for M=%lld N=%lld K=%lld bits=%d", (long long)M, (long long)N, (long long)K, bits);
+  snprintf(out, out_bytes, "%s", dry.plan.text);
+  return AWQ_OK;
   AWQ_GUARD_END
 }
 
@@ -431,9 +478,7 @@ static hipError_t gemm_scaled_via(const void* x, const float* s, const void* pac
                                   void* xs, hipStream_t hs) {
   hipError_t e = awq::launch_scale_input(x, s, M, K, xs, hs);
   if (e != hipSuccess) return e;
-  if (bits == 3) return awq::launch_gemm3(xs, packed, scales, zeros, y, M, N, K, hs);
-  if (M <= 16) return awq::launch_gemv(xs, packed, scales, zeros, y, M, N, K, hs);
-  return awq::launch_gemm(xs, packed, scales, zeros, y, M, N, K, hs);
+  return launch_product(xs, packed, scales, zeros, y, M, N, K, bits, hs);
 }
 
 size_t awq_gemm_scaled_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits) {

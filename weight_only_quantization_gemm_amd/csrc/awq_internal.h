@@ -87,4 +87,15 @@ hipError_t launch_gemv3(const void* x, const void* packed, const void* scales, c
 hipError_t launch_gemm3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                         int64_t M, int64_t N, int64_t K, hipStream_t st);
 
+// Dry runs of the product dispatch.  While a KernelPlan is installed on the
+// calling thread, each product launcher writes the kernel it would launch (its
+// template arguments, block and grid) into it and returns hipSuccess without
+// launching anything; the dispatch above it is the ordinary one.
+struct KernelPlan {
+  char text[160];
+};
+KernelPlan* active_plan();  // the calling thread's installed plan, or null
+void install_plan(KernelPlan* p);
+hipError_t plan_record(KernelPlan* p, const char* fmt, ...);
+
 }  // namespace awq

@@ -135,6 +135,7 @@ hipError_t launch_gemm(const void* x, const void* packed, const void* scales, co
   if (gemm_pipe_supported(M, N, K)) return launch_gemm_pipe(x, packed, scales, zeros, y, M, N, K, st);
   if ((M + kBM - 1) / kBM > 65535) return hipErrorInvalidValue;  // grid.y limit
   dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
+  if (KernelPlan* p = active_plan()) return plan_record(p, "gemm_kernel<4> block=256 grid=%ux%u", grid.x, grid.y);
   gemm_kernel<4><<<grid, dim3(256), 0, st>>>(reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),
                                              reinterpret_cast<const f16*>(scales),
                                              reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), M, N, K);
@@ -151,6 +152,7 @@ hipError_t launch_gemm3(const void* x, const void* packed, const void* scales, c
   if (gemm_pipe3_supported(M, N, K)) return launch_gemm_pipe3(x, packed, scales, zeros, y, M, N, K, st);
   if ((M + kBM - 1) / kBM > 65535) return hipErrorInvalidValue;  // grid.y limit
   dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
+  if (KernelPlan* p = active_plan()) return plan_record(p, "gemm_kernel<3> block=256 grid=%ux%u", grid.x, grid.y);
   gemm_kernel<3><<<grid, dim3(256), 0, st>>>(reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),
                                              reinterpret_cast<const f16*>(scales),
                                              reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), M, N, K);

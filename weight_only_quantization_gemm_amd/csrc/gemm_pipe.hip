@@ -318,6 +318,9 @@ static hipError_t pipe_launch(const void* x, const void* packed, const void* sca
                               int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int mt = (int)((M + BM - 1) / BM), nt = (int)((N + kPBN - 1) / kPBN);
   const int64_t blocks = (int64_t)((nt + kXcds - 1) / kXcds) * kXcds * mt;
+  if (KernelPlan* p = active_plan())
+    return plan_record(p, "gemm_pipe_kernel<%d,%d,%d,%d,%d,%d> block=%d grid=%lld", BM, STAGES, LDS_BYTES, KS, WN, BITS,
+                       256 * KS, (long long)blocks);
   gemm_pipe_kernel<BM, STAGES, LDS_BYTES, KS, WN, BITS><<<dim3((unsigned)blocks), dim3(256 * KS), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed),
       reinterpret_cast<const f16*>(scales), reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), M, N,

@@ -183,6 +183,8 @@ static hipError_t gemv_launch(const void* x, const void* packed, const void* sca
   const int waves = gemv_waves(K);
   if (waves > kMaxWaves) return hipErrorInvalidValue;
   dim3 grid((unsigned)((N + R - 1) / R));
+  if (KernelPlan* p = active_plan())
+    return plan_record(p, "gemv_kernel<%d,%d> block=%d grid=%u", MB, R, waves * kWave, grid.x);
   gemv_kernel<MB, R><<<grid, dim3(waves * kWave), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
       reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)N, (int)K);
@@ -335,6 +337,8 @@ static hipError_t gemv3_launch(const void* x, const void* packed, const void* sc
                                int64_t N, int64_t K, hipStream_t st) {
   const int waves = gemv_waves(K);
   if (waves > kMaxWaves) return hipErrorInvalidValue;
+  if (KernelPlan* p = active_plan())
+    return plan_record(p, "gemv3_kernel<%d,%d> block=%d grid=%u", MB, R, waves * kWave, (unsigned)((N + R - 1) / R));
   gemv3_kernel<MB, R><<<dim3((unsigned)((N + R - 1) / R)), dim3(waves * kWave), 0, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
       reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)N, (int)K);

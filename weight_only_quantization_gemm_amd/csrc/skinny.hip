@@ -26,10 +26,11 @@
 // The register-staged kernel (skinny_kernel): wave w takes groups w, w+W, ....
 // For one group a wave loads 16 B per lane: lane l reads the (l/16)-th 16-byte
 // quarter of the group's 64 B in row l%16, so one load instruction fetches 16
-// rows x 64 B.  All loads of a batch of P groups (and, without LDS staging,
-// their x fragments) are issued before any is used.  x is staged once per
-// block in LDS when it fits, before the first weight load.  It serves
-// 17 <= M <= 64, and 2 <= M <= 16 where the ring kernel's LDS does not fit.
+// rows x 64 B.  All loads of a batch of P groups (and their x fragments, when
+// they fit in registers) are issued before any is used.  It serves the shapes
+// the ring kernel declines because the block's scales and zeros leave its
+// rings no LDS (K beyond ~130,000 at 17 <= M <= 64, ~260,000 at M <= 16), and
+// M = 1 beyond the GEMV's K = 32768.
 //
 // The ring kernel (ring_kernel, 3 <= M <= 16, and M = 2 on rows of 16384
 // channels or more) moves weights and x fragments
@@ -40,7 +41,6 @@
 namespace awq {
 
 constexpr int kSkinnyMaxWaves = 8;
-constexpr size_t kSkinnyLdsBudget = 64 * 1024;
 
 // Waves per block: about P groups per wave, at most kSkinnyMaxWaves.  It is a
 // function of K alone, so the kernel derives it from its arguments (which the
@@ -51,10 +51,10 @@ __host__ __device__ inline int skinny_waves(int64_t K) {
   return w < 1 ? 1 : (w > kSkinnyMaxWaves ? kSkinnyMaxWaves : (int)w);
 }
 
-template <int RW, int P, int MT, bool XLDS>
+template <int RW, int P, int MT>
 __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ packed,
                                                      const f16* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                                                     f16* __restrict__ y, int M, int N32, int K32, int red_offset) {
+                                                     f16* __restrict__ y, int M, int N32, int K32) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int64_t N = N32, K = K32;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -80,18 +80,9 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // x goes into LDS before any weight load is issued: vector-memory loads
-  // complete in order, so waiting for the copy must not include them.
-  f16* xs = reinterpret_cast<f16*>(smem);
-  if (XLDS) {
-    const int64_t n16 = (int64_t)M * K / 8;
-    for (int64_t i = threadIdx.x; i < n16; i += W * kWave)
-      reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
-    __syncthreads();
-  }
-  // Without LDS staging the batch's x fragments are loaded together with its
-  // weights, before the first wait, when they fit in registers; otherwise per group.
-  constexpr bool XPRE = !XLDS && P * MT <= 4;
+  // The batch's x fragments are loaded together with its weights, before the
+  // first wait, when they fit in registers; otherwise per group.
+  constexpr bool XPRE = P * MT <= 4;
   const uint32_t bias = bias_in_vgpr();
 
   for (int64_t gb = wave; gb < G; gb += (int64_t)W * P) {
@@ -132,7 +123,6 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           if constexpr (XPRE) a[mt][s] = ap[p][mt][s];
-          else if constexpr (XLDS) a[mt][s] = *reinterpret_cast<const f16x8*>(xs + xrow[mt] * K + k0 + 8 * s);
           else a[mt][s] = *reinterpret_cast<const f16x8*>(x + xrow[mt] * K + k0 + 8 * s);
         }
 #pragma unroll
@@ -160,7 +150,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
   }
 
   // sum the waves' tiles: lane holds y[m = 16*mt + 4*kq + r][n0 + 16t + nl]
-  float* red = reinterpret_cast<float*>(smem + red_offset);
+  float* red = reinterpret_cast<float*>(smem);
   if (MT == 1) {  // one slot per wave, then a fixed-order sum per output
 #pragma unroll
     for (int t = 0; t < RW; ++t)
@@ -206,21 +196,16 @@ template <int RW, int P, int MT = 1>
 static hipError_t skinny_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                                 int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int W = skinny_waves<P>(K);
-  const size_t red_bytes = (size_t)(MT == 1 ? W : 1) * RW * 16 * MT * 16 * sizeof(float);
-  const size_t xbytes = (size_t)M * (size_t)K * 2;
-  const bool xlds = xbytes + red_bytes <= kSkinnyLdsBudget;
-  const size_t red_offset = xlds ? xbytes : 0;
-  const size_t lds = red_offset + red_bytes;
+  const size_t lds = (size_t)(MT == 1 ? W : 1) * RW * 16 * MT * 16 * sizeof(float);  // the waves' partial tiles
   dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW))), block((unsigned)(W * kWave));
   auto xp = reinterpret_cast<const f16*>(x);
   auto pp = reinterpret_cast<const uint32_t*>(packed);
   auto sp = reinterpret_cast<const f16*>(scales);
   auto zp = reinterpret_cast<const uint8_t*>(zeros);
   auto yp = reinterpret_cast<f16*>(y);
-  if (xlds)
-    skinny_kernel<RW, P, MT, true><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, (int)N, (int)K, (int)red_offset);
-  else
-    skinny_kernel<RW, P, MT, false><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, (int)N, (int)K, (int)red_offset);
+  if (KernelPlan* p = active_plan())
+    return plan_record(p, "skinny_kernel<%d,%d,%d> block=%u grid=%u", RW, P, MT, block.x, grid.x);
+  skinny_kernel<RW, P, MT><<<grid, block, lds, st>>>(xp, pp, sp, zp, yp, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -506,6 +491,8 @@ static hipError_t ring_launch(const void* x, const void* packed, const void* sca
   const size_t lds = ring_lds_bytes<BITS, RW, P, S, MX>(W, K);
   if (lds > kLdsBytes) return hipErrorInvalidValue;
   dim3 grid((unsigned)((N + 16 * RW - 1) / (16 * RW))), block((unsigned)(W * kWave));
+  if (KernelPlan* p = active_plan())
+    return plan_record(p, "ring_kernel<%d,%d,%d,%d,%d> block=%u grid=%u", BITS, RW, P, S, MX, block.x, grid.x);
   ring_kernel<BITS, RW, P, S, MX><<<grid, block, lds, st>>>(
       reinterpret_cast<const f16*>(x), reinterpret_cast<const uint32_t*>(packed), reinterpret_cast<const f16*>(scales),
       reinterpret_cast<const uint8_t*>(zeros), reinterpret_cast<f16*>(y), (int)M, (int)N, (int)K, W);
@@ -666,42 +653,32 @@ hipError_t launch_ring3(const void* x, const void* packed, const void* scales, c
   return ring_run<3>(x, packed, scales, zeros, y, M, N, K, r, mx, st);
 }
 
-// 17 <= M <= 64: the register-staged kernel with M in up to four 16-row
-// m-tiles; each unpacked weight operand feeds one MFMA per m-tile.  Measured
-// against the pipelined GEMM (M = 24, 32, 48, 64 on the 7B/70B shapes) it wins
-// on layers up to 8192 wide (4096 x 4096 at 14-25 us against 24 us, 8192 x
-// 8192 at 27-46 us against 53 us, 28672 x 8192 at 81-139 us against 239 us)
-// and, with four tiles per wave in batches of two groups, on wider K = 4096
-// layers up to M = 32 (4096 x 11008 at 22-24 us against 25 us; at M = 48 the
-// GEMM takes 25.5 us against 29) and on layers up to 12288 wide to M = 32
-// (8192 x 10240 at M = 24: 43 us against 54); elsewhere the GEMM is faster
-// (8192 x 28672 at M = 24: 84 us against 67).
+// 17 <= M <= 64 where the ring declines: the register-staged kernel with M in
+// up to four 16-row m-tiles (each unpacked weight operand feeds one MFMA per
+// m-tile) on layers up to 8192 rows whose K leaves the ring no LDS beside the
+// block's scales and zeros (K beyond ~130,000); every other such layer goes to
+// the pipelined GEMM (or, past its LDS too, the general-shape kernel).
+// Measured against the pipelined GEMM at M = 24..64 on layers up to 8192 rows,
+// before the ring took them: 4096 x 4096 at 14-25 us against 24 us, 8192 x 8192
+// at 27-46 us against 53 us, 28672 x 8192 at 81-139 us against 239 us.
 bool gemv_wide_preferred(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16 || M > 64) return false;
-  return N <= 8192 || (M <= 32 && (K <= 4096 || N <= 12288));
-}
-
-template <int RW, int P>
-static hipError_t wide_launch(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                              int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  if (M <= 32) return skinny_launch<RW, P, 2>(x, packed, scales, zeros, y, M, N, K, st);
-  if (M <= 48) return skinny_launch<RW, P, 3>(x, packed, scales, zeros, y, M, N, K, st);
-  return skinny_launch<RW, P, 4>(x, packed, scales, zeros, y, M, N, K, st);
+  (void)K;
+  return M > 16 && M <= 64 && N <= 8192;
 }
 
 hipError_t launch_gemv_wide(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t st) {
   if (M <= 16 || M > 64) return hipErrorInvalidValue;
-  if (N <= 8192) return wide_launch<2, 1>(x, packed, scales, zeros, y, M, N, K, st);
-  return wide_launch<4, 2>(x, packed, scales, zeros, y, M, N, K, st);
+  if (M <= 32) return skinny_launch<2, 1, 2>(x, packed, scales, zeros, y, M, N, K, st);
+  if (M <= 48) return skinny_launch<2, 1, 3>(x, packed, scales, zeros, y, M, N, K, st);
+  return skinny_launch<2, 1, 4>(x, packed, scales, zeros, y, M, N, K, st);
 }
 
-// M <= 16 beyond the GEMV's range runs on the ring kernel.  The register-staged kernel above
-// serves the layers whose scales and zeros do not fit in LDS beside the rings
-// (K beyond about 260000), with its tile shape measured on the same layers:
-// one 16-row tile per wave by default; four tiles per wave in batches of two
-// groups on wide layers (N >= 16384, or N >= 8192 with K = 4096 and M > 8);
-// two tiles per wave on long K (>= 16384) and for M > 8 on 8192-wide layers.
+// M <= 16 beyond the GEMV's range runs on the ring kernel.  Where the ring
+// declines (2 <= M <= 16 with K at least 16384 whose block scales and zeros
+// leave the rings no LDS, and M = 1 beyond the GEMV's K = 32768) the
+// register-staged kernel runs with two 16-row weight tiles per wave in batches
+// of four groups (measured best on long K among its layouts).
 hipError_t launch_gemv(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
                        int64_t N, int64_t K, hipStream_t st) {
   if (M < 1 || M > 16) return hipErrorInvalidValue;
@@ -709,10 +686,7 @@ hipError_t launch_gemv(const void* x, const void* packed, const void* scales, co
   const RingShape r = ring_shape(M, N, K);
   int mx;
   if (ring_select<4>(M, K, r, &mx)) return ring_run<4>(x, packed, scales, zeros, y, M, N, K, r, mx, st);
-  if (K >= 16384) return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
-  if (N >= 16384 || (M > 8 && N >= 8192 && K <= 4096)) return skinny_launch<4, 2>(x, packed, scales, zeros, y, M, N, K, st);
-  if (M > 8 && N >= 8192) return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
-  return skinny_launch<1, 4>(x, packed, scales, zeros, y, M, N, K, st);
+  return skinny_launch<2, 4>(x, packed, scales, zeros, y, M, N, K, st);
 }
 
 }  // namespace awq
