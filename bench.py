@@ -724,6 +724,73 @@ SEARCH_SOURCES = [f"weight_only_quantization_gemm_amd/csrc/{f}" for f in ("quant
 SEARCH_PROFILE_LAYERS = [("q_proj", 4096, 4096), ("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)]
 
 
+def summarize_decode_counters(dec_fetch, dec_write, copy_fetch, copy_write, steps=40):
+    """The body of profiles/gemv_llama2_7b_decode_m1_counters.txt from four rocprofv3 --pmc
+    output directories: FETCH_SIZE and WRITE_SIZE over `--profile-mode decode` and over
+    `--profile-mode copy` (a 256 MiB device copy, which calibrates each counter)."""
+    import csv
+    import glob
+
+    def rows(d):
+        out = []
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r.get("Grid_Size", "0")),
+                            float(r["Counter_Value"])))
+        return sorted(out)
+
+    def calib(d, copied_kib):
+        v = [c for _, name, _, c in rows(d) if "copyBuffer" in name or "copy" in name.lower()]
+        return float(np.median(v)) / copied_kib, float(np.median(v))
+
+    copied = (256 << 20) / 1024
+    f_fac, f_raw = calib(copy_fetch, copied)
+    w_fac, w_raw = calib(copy_write, copied)
+    per_shape = {}
+    for d, key in ((dec_fetch, "f"), (dec_write, "w")):
+        g = [x for x in rows(d) if "gemv_kernel" in x[1]][-7 * steps:]
+        for _, _, grid, c in g:
+            per_shape.setdefault(grid, {"f": [], "w": []})[key].append(c)
+    # grid threads = (N / 4) blocks of 4 rows x one wave per 2048 channels x 64 lanes
+    shapes = {(N // 4) * (-(-K // 2048)) * 64: (K, N) for _, K, N in LAYERS_7B}
+    out = [f"source_hash: {source_hash(GEMV_SOURCES)}   (sha256[:16] of csrc/gemv.hip + csrc/awq_common.h when "
+           "the counters were taken)",
+           "Commands (one counter per pass; `cd /tmp && export TMPDIR=/tmp` first; `$REPO` is the repository root):",
+           f"  rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/pmc_decode_FETCH_SIZE -o pmc --output-format csv -- "
+           f"python $REPO/bench.py --profile-mode decode --steps {steps} --warmup 5",
+           f"  rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/pmc_decode_WRITE_SIZE -o pmc --output-format csv -- "
+           f"python $REPO/bench.py --profile-mode decode --steps {steps} --warmup 5",
+           "  (the same two with --profile-mode copy: a 256 MiB device-to-device copy, for calibration)",
+           "  python bench.py --summarize-decode-counters gpurun_out/pmc_decode_FETCH_SIZE "
+           "gpurun_out/pmc_decode_WRITE_SIZE gpurun_out/pmc_copy_FETCH_SIZE gpurun_out/pmc_copy_WRITE_SIZE",
+           "",
+           f"Calibration (256 MiB copy = {copied:.0f} KiB read and written): FETCH_SIZE reads {f_raw:.1f} KiB -> "
+           f"factor {f_fac:.5f}; WRITE_SIZE reads {w_raw:.1f} KiB -> factor {w_fac:.5f}.  HBM bytes = FETCH_SIZE / "
+           "fetch factor + WRITE_SIZE / write factor.",
+           f"Figures: medians over the {7 * steps} GEMV dispatches of the {steps} timed steps.",
+           "",
+           "| shape (K, N) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes | algorithmic bytes | ratio |",
+           "|---|---|---|---|---|---|---|"]
+    hbm_step, alg_step = 0.0, 0.0
+    for grid in sorted(per_shape):
+        K, N = shapes.get(grid, (None, None))
+        if K is None:
+            continue
+        fk = float(np.median(per_shape[grid]["f"]))
+        wk = float(np.median(per_shape[grid]["w"]))
+        hbm = fk * 1024 / f_fac + wk * 1024 / w_fac
+        alg = gemv_bytes(1, K, N)
+        n_in_step = sum(1 for _, k, nn in LAYERS_7B if (k, nn) == (K, N))
+        hbm_step += n_in_step * hbm
+        alg_step += n_in_step * alg
+        out.append(f"| ({K}, {N}) | {len(per_shape[grid]['f'])} | {fk:.1f} | {wk:.1f} | {hbm:.0f} | {alg} | "
+                   f"{hbm / alg:.4f} |")
+    n = len(LAYERS_7B)
+    out += ["", f"hbm_bytes_per_launch: {hbm_step / n:.1f}", f"alg_bytes_per_launch: {alg_step / n:.1f}",
+            f"ratio: {hbm_step / alg_step:.4f}   (step-weighted over the {n} launches of a decode step)"]
+    return out
+
+
 def summarize_search_trace(csv_path, calib_rows=65536, n_alpha=20):
     """Markdown tables from the rocprofv3 kernel_trace.csv of `--profile-mode search` (each
     layer searched twice on one workspace, in SEARCH_PROFILE_LAYERS order): the top kernels,
@@ -966,6 +1033,9 @@ def main():
     ap.add_argument("--summarize-search-trace", metavar="KERNEL_TRACE_CSV", default=None,
                     help="print the markdown tables of profiles/search_llama2_7b_block_trace.md from the kernel "
                          "trace of --profile-mode search, and exit")
+    ap.add_argument("--summarize-decode-counters", metavar="PMC_DIR", nargs=4, default=None,
+                    help="print profiles/gemv_llama2_7b_decode_m1_counters.txt's body from the FETCH_SIZE and "
+                         "WRITE_SIZE passes over --profile-mode decode and --profile-mode copy, and exit")
     ap.add_argument("--summarize-search-counters", metavar="PMC_DIR", nargs="+", default=None,
                     help="print the counter tables of profiles/search_loss_gram_sq_counters.md from rocprofv3 --pmc "
                          "output directories of --profile-mode search, and exit")
@@ -977,6 +1047,9 @@ def main():
         return
     if args.summarize_search_trace:
         print("\n".join(summarize_search_trace(args.summarize_search_trace)))
+        return
+    if args.summarize_decode_counters:
+        print("\n".join(summarize_decode_counters(*args.summarize_decode_counters)))
         return
     if args.summarize_search_counters:
         print("\n".join(summarize_search_counters(args.summarize_search_counters)))
