@@ -791,6 +791,24 @@ def summarize_decode_counters(dec_fetch, dec_write, copy_fetch, copy_write, step
     return out
 
 
+def search_call_layers(names):
+    """Layer (an entry of SEARCH_PROFILE_LAYERS) of each dispatch of `--profile-mode search`, from
+    the kernel names in dispatch order: every awq_quantize call starts with its statistics pass,
+    and call c searches layer c // 2."""
+    starts = [i for i, n in enumerate(names) if "stats_accumulate" in n]
+    layer_of = [None] * len(names)
+    for c, i0 in enumerate(starts):
+        i1 = starts[c + 1] if c + 1 < len(starts) else len(names)
+        for i in range(i0, i1):
+            layer_of[i] = SEARCH_PROFILE_LAYERS[min(c // 2, len(SEARCH_PROFILE_LAYERS) - 1)]
+    return layer_of
+
+
+def is_gram_kernel(name):
+    """The Gram's own dispatches: gram_kernel and, where tiles are split, gram_fixup_kernel."""
+    return "gram_kernel" in name or "gram_fixup_kernel" in name
+
+
 def summarize_search_trace(csv_path, calib_rows=65536, n_alpha=20):
     """Markdown tables from the rocprofv3 kernel_trace.csv of `--profile-mode search` (each
     layer searched twice on one workspace, in SEARCH_PROFILE_LAYERS order): the top kernels,
@@ -833,13 +851,7 @@ def summarize_search_trace(csv_path, calib_rows=65536, n_alpha=20):
         meth = 2 * N * K * K
         out.append(f"| {name} ({K}, {N}) | {t:.1f} | {done / t * 1e-6:.0f} ({done / t * 1e-6 / 25:.1f} %) | "
                    f"{meth / t * 1e-6:.0f} ({meth / t * 1e-6 / 25:.1f} %) |")
-    # every awq_quantize call starts with its statistics pass: call c is layer c // 2
-    starts = [i for i, r in enumerate(rows) if "stats_accumulate" in r[2]]
-    layer_of = [None] * len(rows)
-    for c, i0 in enumerate(starts):
-        i1 = starts[c + 1] if c + 1 < len(starts) else len(rows)
-        for i in range(i0, i1):
-            layer_of[i] = SEARCH_PROFILE_LAYERS[min(c // 2, len(SEARCH_PROFILE_LAYERS) - 1)]
+    layer_of = search_call_layers([r[2] for r in rows])
     out += ["", "## HBM-bound phases", "",
             "| kernel | layer (K, N) | dispatches | mean us | algorithmic bytes | GB/s (of 8 TB/s) |",
             "|---|---|---|---|---|---|"]
@@ -862,16 +874,17 @@ def summarize_search_trace(csv_path, calib_rows=65536, n_alpha=20):
             m = float(np.mean(v))
             out.append(f"| {key} ({what[key]}) | {name} ({K}, {N}) | {len(v)} | {m:.1f} | {alg} | "
                        f"{alg / m * 1e-3:.0f} ({alg / m * 1e-3 / 80:.1f} %) |")
-    gram = [r for r in rows if "gram_kernel" in r[2]]
+    # the Gram of each call: gram_kernel plus its fix-up pass, summed
+    gram_calls = defaultdict(float)
+    starts = [i for i, r in enumerate(rows) if "stats_accumulate" in r[2]]
+    for i, r in enumerate(rows):
+        if is_gram_kernel(r[2]) and layer_of[i] is not None:
+            gram_calls[(layer_of[i][1], max(c for c, i0 in enumerate(starts) if i0 <= i))] += us(r)
     out += ["", "## Gram (X^T X over the calibration rows, symmetric half of 2 M K^2 flops)", "",
-            "| K | dispatches | mean us | TFLOP/s (of 2.5 PF) |", "|---|---|---|---|"]
-    seen = []
-    for name, K, N in SEARCH_PROFILE_LAYERS:
-        if K in seen:
-            continue
-        seen.append(K)
-    for i, K in enumerate(seen):
-        v = [us(r) for r in gram if r[3] == gram_grid_threads(K)]
+            "Per awq_quantize call: gram_kernel, plus gram_fixup_kernel where the last round's tiles are split.", "",
+            "| K | calls | mean us | TFLOP/s (of 2.5 PF) |", "|---|---|---|---|"]
+    for K in sorted({K for _, K, _ in SEARCH_PROFILE_LAYERS}):
+        v = [t for (k, _), t in gram_calls.items() if k == K]
         if v:
             m = float(np.mean(v))
             fl = calib_rows * K * K
@@ -904,11 +917,12 @@ def summarize_search_counters(dirs, n_alpha=20):
                     name, K, N = SEARCH_PROFILE_LAYERS[li]
                     for c, v in disp[did].items():
                         vals[("loss_full_kernel", f"{name} ({K}, {N})")][c].append(v)
-            for did in disp:
-                if "gram_kernel" in names[did][0]:
-                    K = next((K for _, K, _ in SEARCH_PROFILE_LAYERS if gram_grid_threads(K) == names[did][1]), None)
+            order = sorted(disp)
+            layer_of = dict(zip(order, search_call_layers([names[i][0] for i in order])))
+            for did in order:
+                if "gram_kernel" in names[did][0] and layer_of[did] is not None:
                     for c, v in disp[did].items():
-                        vals[("gram_kernel", f"K = {K}")][c].append(v)
+                        vals[("gram_kernel", f"K = {layer_of[did][1]}")][c].append(v)
     keys = sorted(vals, key=lambda k: (k[0], k[1]))
     counters = sorted({c for k in keys for c in vals[k]})
     med = {k: {c: float(np.median(vals[k][c])) for c in vals[k]} for k in keys}
@@ -937,21 +951,6 @@ def summarize_search_counters(dirs, n_alpha=20):
                 cells.append("-")
         out.append(f"| {label} | " + " | ".join(cells) + " |")
     return out
-
-
-def gram_grid_threads(K):
-    """Threads in gram_kernel's grid for K channels (the launch's tile count per XCD, times 8 x 256)."""
-    nb, gs = K // 128, 4
-    ns = (nb + gs - 1) // gs
-    per = [0] * 8
-    s = 0
-    for si in range(ns):
-        for sj in range(si, ns):
-            ni = min(nb - gs * si, gs)
-            nj = min(nb - gs * sj, gs)
-            per[s % 8] += ni * (ni + 1) // 2 if si == sj else ni * nj
-            s += 1
-    return 8 * max(per) * 256
 
 
 def profile_mode(args, torch, awq, dev):

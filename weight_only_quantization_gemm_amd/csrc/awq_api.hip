@@ -101,11 +101,12 @@ int check_layer(int64_t N, int64_t K, int32_t group) {
 
 // Workspace of awq_quantize, carved in this order (each piece 256-byte aligned).
 // M < K uses the direct form of the loss (E in fp32); M >= K the Gram form
-// (channel exponents, G as scaled fp16 hi/lo, X^T and G in fp32, E' hi/lo).
+// (channel exponents, G as scaled fp16 hi/lo, X^T, G in fp32 and the fp64
+// partial tiles of its split tiles, E' hi/lo).
 // The statistics of X come first, at offsets that depend on K and M only.
 struct QuantizeWorkspace {
   bool direct;
-  size_t a, s_all, inv_all, xt, g, gh, gl, ex, eh, el, e32, partial, loss, b, mask, total;
+  size_t a, s_all, inv_all, xt, g, gp, gh, gl, ex, eh, el, e32, partial, loss, b, mask, total;
   int64_t mp, partials;
 };
 
@@ -129,6 +130,7 @@ QuantizeWorkspace quantize_workspace(int64_t N, int64_t K, int64_t M, int32_t n_
     w.gl = take(2 * (size_t)K * (size_t)K);
     w.xt = take(2 * (size_t)K * (size_t)w.mp);
     w.g = take(sizeof(float) * (size_t)K * (size_t)K);
+    w.gp = take(awq::gram_partial_bytes(K, w.mp));
   }
   w.s_all = take(sizeof(float) * (size_t)n_alpha * (size_t)K);
   w.inv_all = take(sizeof(double) * (size_t)n_alpha * (size_t)K);
@@ -326,7 +328,7 @@ int awq_quantize_shared(const void* W, const void* X, int64_t N, int64_t K, int6
     void* Elo = base + w.el;
     if (!reuse_statistics) {
       if (e == hipSuccess) e = awq::launch_transpose(X, M, K, w.mp, xt, hs);
-      if (e == hipSuccess) e = awq::launch_gram(xt, w.mp, K, G, hs);
+      if (e == hipSuccess) e = awq::launch_gram(xt, w.mp, K, G, reinterpret_cast<double*>(base + w.gp), hs);
       if (e == hipSuccess) e = awq::launch_gram_split(G, K, ex, Ghi, Glo, hs);
     }
     for (int i = 0; i < n_alpha && e == hipSuccess; ++i) {
@@ -383,7 +385,9 @@ int awq_keep_fp16_ablation(const void* W, const void* X, int64_t N, int64_t K, i
   int32_t* ex = reinterpret_cast<int32_t*>(base + w.ex);
   if (!w.direct) {
     if (e == hipSuccess) e = awq::launch_transpose(X, M, K, w.mp, base + w.xt, hs);
-    if (e == hipSuccess) e = awq::launch_gram(base + w.xt, w.mp, K, reinterpret_cast<float*>(base + w.g), hs);
+    if (e == hipSuccess)
+      e = awq::launch_gram(base + w.xt, w.mp, K, reinterpret_cast<float*>(base + w.g),
+                           reinterpret_cast<double*>(base + w.gp), hs);
     if (e == hipSuccess)
       e = awq::launch_gram_split(reinterpret_cast<float*>(base + w.g), K, ex, base + w.gh, base + w.gl, hs);
   }

@@ -19,7 +19,9 @@ hipError_t launch_channel_mean_abs(const void* X, int64_t M, int64_t K, double* 
 hipError_t launch_transpose(const void* X, int64_t M, int64_t K, int64_t Mp, void* Xt, hipStream_t st);
 
 // gram.hip: G = Xt Xt^T (fp32 [K][K], fp64 accumulation) from Xt fp16 [K][Mp], Mp % 64 == 0, K % 64 == 0.
-hipError_t launch_gram(const void* Xt, int64_t Mp, int64_t K, float* G, hipStream_t st);
+// partial: gram_partial_bytes(K, Mp) bytes of device scratch (may be null when that is 0)
+hipError_t launch_gram(const void* Xt, int64_t Mp, int64_t K, float* G, double* partial, hipStream_t st);
+size_t gram_partial_bytes(int64_t K, int64_t Mp);
 
 // quant.hip
 // s_all fp32 [n_alpha][K] and inv_all = 1 / s_all in fp64
