@@ -252,6 +252,40 @@ int awq_gemm(const void* x, const void* packed, const void* scales, const void* 
  * M <= 65535 * 64 at 3 bits. */
 int awq_gemm_bits(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                   int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* stream);
+/* awq_gemm_ws -- awq_gemm_bits with a workspace, in which the matrix-core GEMM
+ * can split its work evenly over the compute units instead of giving each block
+ * whole output tiles (stream-K: block v of P takes the v-th P-th of the
+ * (tile, 128-channel group) pairs; a tile whose groups are split between blocks
+ * is summed by the block that finishes it last, which adds the blocks' fp32
+ * partials in the order of their K ranges, so y is deterministic).  The split
+ * applies for M > 32 when whole tiles would leave at least half of the compute
+ * units idle in their last round and every unit gets at least 8 groups; the
+ * workspace size query says whether it does (0 bytes: it does not, and the call
+ * is awq_gemm_bits).  The split changes the scheduling, not the product: it is
+ * awq_gemm's ([summary] paragraph 9, the batched regime).
+ *   workspace        device, >= awq_gemm_workspace_bytes(M, N, K, bits) bytes
+ *                    (may be NULL when that is 0); it holds the blocks' partial
+ *                    tiles and, after them, tile counters that must be zero
+ *                    before the first call on a new workspace: clear it once
+ *                    after allocating it (every call leaves the counters zero,
+ *                    so the workspace then serves calls of any size)
+ *   other arguments  as awq_gemm_bits
+ * Calls that share a workspace must not overlap in time (one stream, or ordered
+ * by events).  Where the split applies, y agrees with awq_gemm_bits to fp32
+ * rounding (the sum over K is grouped differently), and a layer stored with
+ * others' rows concatenated (fused q/k/v) may differ from the separate layers in
+ * the last bit; elsewhere y is awq_gemm_bits's bit for bit.
+ * Errors: those of awq_gemm_bits; AWQ_ERROR_INVALID_VALUE for a NULL workspace
+ * that is needed, AWQ_ERROR_WORKSPACE_TOO_SMALL, AWQ_ERROR_MISALIGNED for a
+ * workspace not 16-byte aligned. */
+size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits);
+int awq_gemm_ws(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
+                int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, void* workspace,
+                size_t workspace_bytes, void* stream);
+/* awq_gemm_ws_kernel -- awq_gemm_kernel for awq_gemm_ws (given a large enough
+ * workspace); the text ends in " stream-K" where the split applies. */
+int awq_gemm_ws_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, char* out, size_t out_bytes);
+
 /* awq_gemm_kernel -- the kernel awq_gemm_bits launches for an M x K input and
  * N x K weights at `bits`: a dry run of the same dispatch that launches
  * nothing and touches no device (host-only; it works without a GPU).  Writes

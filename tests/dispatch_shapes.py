@@ -1,4 +1,4 @@
-"""One product shape per kernel the dispatch of awq_gemm / awq_gemm_bits can launch.
+"""One product shape per kernel the dispatch of awq_gemm_bits (and of awq_gemm_ws) can launch.
 
 Each entry is (kernel, (M, N, K, bits)): awq_gemm_kernel(M, N, K, bits) names that kernel
 (its template arguments; block and grid depend on the shape).  tests/test_dispatch.py checks
@@ -54,6 +54,17 @@ BRANCHES = [
     ("gemm_pipe_kernel<128,3,163840,2,4,3>", (65, 16400, 128, 3)),
     ("gemm_kernel<4>", (65, 64, 32896, 4)),
     ("gemm_kernel<3>", (1, 64, 32896, 3)),
+]
+
+# The same kernels where awq_gemm_ws (a workspace given) splits their work over the compute
+# units (stream-K): awq_gemm_ws_kernel names the kernel and ends in "stream-K".
+STREAMK_BRANCHES = [
+    ("gemm_pipe_kernel<64,4,163840,2,4,4>", (37, 2000, 16384, 4)),
+    ("gemm_pipe_kernel<64,3,163840,1,2,4>", (33, 4096, 28672, 4)),
+    ("gemm_pipe_kernel<128,2,163840,1,4,4>", (200, 1000, 32768, 4)),
+    ("gemm_pipe_kernel<128,3,163840,2,4,4>", (256, 16400, 1024, 4)),
+    ("gemm_pipe_kernel<64,4,163840,2,4,3>", (40, 4000, 16384, 3)),
+    ("gemm_pipe_kernel<128,3,163840,2,4,3>", (256, 16400, 1024, 3)),
 ]
 
 # Sizes whose products the coverage check enumerates (both code widths): every M class of the

@@ -219,6 +219,37 @@ def test_bits_argument_errors_before_launch():
     assert lib.awq_gemm_bits(FAKE_MISALIGNED, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, 3, None) == MISALIGNED
 
 
+def test_gemm_ws_argument_errors_before_launch():
+    """awq_gemm_ws: the workspace size query is 0 where the GEMM splits no work (and for bad
+    sizes), a needed workspace must be given, large enough and 16-byte aligned, and the other
+    arguments are checked as for awq_gemm_bits."""
+    lib = _lib_()
+    f = lib.awq_gemm_ws
+    M, N, K = 64, 8192, 8192  # split: 64 tiles of 64 groups over 256 compute units
+    nb = lib.awq_gemm_workspace_bytes(M, N, K, 4)
+    assert nb > 0 and nb % 256 == 0
+    assert lib.awq_gemm_workspace_bytes(M, N, K, 3) == nb
+    for bad in ((0, N, K, 4), (M, 0, K, 4), (M, N, 100, 4), (M, N, K, 2), (32, N, K, 4), (1, N, K, 4)):
+        assert lib.awq_gemm_workspace_bytes(*bad) == 0, bad
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, 128, 4, None, 0, None) == INVALID
+    assert "workspace" in awq.awq_last_error()
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, 128, 4, FAKE, nb - 256, None) == WS_SMALL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, 128, 4, FAKE_MISALIGNED, nb, None) == MISALIGNED
+    for pos in range(5):
+        args = [FAKE] * 5
+        args[pos] = FAKE_MISALIGNED
+        assert f(*args, M, N, K, 128, 4, FAKE, nb, None) == MISALIGNED, pos
+        args[pos] = None
+        assert f(*args, M, N, K, 128, 4, FAKE, nb, None) == INVALID, pos
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, 128, 5, FAKE, nb, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, M, N, 100, 128, 4, FAKE, nb, None) == INVALID
+    buf = ctypes.create_string_buffer(160)
+    assert lib.awq_gemm_ws_kernel(M, N, K, 128, 4, buf, 160) == OK
+    assert buf.value.decode().endswith("stream-K")
+    assert lib.awq_gemm_ws_kernel(16, N, K, 128, 4, buf, 160) == OK
+    assert not buf.value.decode().endswith("stream-K")
+
+
 def test_ablation_argument_errors_before_launch():
     lib = _lib_()
     f = lib.awq_keep_fp16_ablation

@@ -7,11 +7,12 @@ import itertools
 import pytest
 
 import weight_only_quantization_gemm_amd as awq
-from dispatch_shapes import BRANCHES, SEARCH_GRID
+from dispatch_shapes import BRANCHES, SEARCH_GRID, STREAMK_BRANCHES
 
 
 def _kernel(M, N, K, bits):
-    return awq.awq_gemm_kernel(M, N, K, bits=bits).split(" ")[0]
+    """The kernel awq_gemm_bits (no workspace: whole output tiles) launches."""
+    return awq.awq_gemm_kernel(M, N, K, bits=bits, workspace=False).split(" ")[0]
 
 
 def test_listed_shapes_select_their_kernel():
@@ -30,6 +31,30 @@ def test_dispatch_reaches_only_listed_kernels():
     assert not missing, f"kernels without a parity shape: {missing}"
     unreached = listed - set(reached)
     assert not unreached, f"listed kernels the grid no longer reaches: {unreached}"
+
+
+def test_streamk_reaches_only_listed_kernels():
+    """With a workspace the dispatch is the same except where the GEMM splits its work: those
+    kernels (texts ending in "stream-K") are the listed stream-K branches, and the workspace
+    size query is positive exactly there."""
+    listed = {n for n, _ in STREAMK_BRANCHES}
+    for name, (M, N, K, bits) in STREAMK_BRANCHES:
+        text = awq.awq_gemm_kernel(M, N, K, bits=bits, workspace=True)
+        assert text.split(" ")[0] == name and text.endswith("stream-K"), (name, text)
+    reached = {}
+    for bits in (4, 3):
+        for M, N, K in itertools.product(SEARCH_GRID["M"], SEARCH_GRID["N"], SEARCH_GRID["K"]):
+            text = awq.awq_gemm_kernel(M, N, K, bits=bits, workspace=True)
+            split = text.endswith("stream-K")
+            assert split == (awq.awq_gemm_workspace_bytes(M, N, K, bits) > 0), (M, N, K, bits, text)
+            if split:
+                reached.setdefault(text.split(" ")[0], (M, N, K, bits))
+                assert M > 32
+            else:
+                assert text == awq.awq_gemm_kernel(M, N, K, bits=bits, workspace=False)
+    missing = {k: v for k, v in reached.items() if k not in listed}
+    assert not missing, f"stream-K kernels without a parity shape: {missing}"
+    assert listed == set(reached)
 
 
 def test_dispatch_by_m_class():

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import weight_only_quantization_gemm_amd as awq
-from dispatch_shapes import BRANCHES
+from dispatch_shapes import BRANCHES, STREAMK_BRANCHES
 from gen import activations_fp16
 from layout import assert_y_close
 from test_gpu_parity import _random_packed, dev, host, note
@@ -19,11 +19,23 @@ pytestmark = pytest.mark.gpu
 def test_each_dispatched_kernel(name, shape):
     M, N, K, bits = shape
     note(f"dispatch {name} M={M} N={N} K={K} bits={bits}")
-    assert awq.awq_gemm_kernel(M, N, K, bits=bits).split(" ")[0] == name
+    assert awq.awq_gemm_kernel(M, N, K, bits=bits, workspace=False).split(" ")[0] == name
+    _run(name, M, N, K, bits, workspace=None)
+
+
+@pytest.mark.parametrize("name,shape", STREAMK_BRANCHES, ids=[n + "-stream-K" for n, _ in STREAMK_BRANCHES])
+def test_each_streamk_kernel(name, shape):
+    M, N, K, bits = shape
+    note(f"dispatch stream-K {name} M={M} N={N} K={K} bits={bits}")
+    assert awq.awq_gemm_kernel(M, N, K, bits=bits).endswith("stream-K")
+    _run(name, M, N, K, bits, workspace="auto")
+
+
+def _run(name, M, N, K, bits, workspace):
     seed = M * 7 + N * 3 + K + bits
     q, z, sc, p, scd, zd = (_random_packed3 if bits == 3 else _random_packed)(N, K, seed=seed)
     x = activations_fp16(M, K, seed=seed + 1)
-    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    y = host(awq.awq_gemm(dev(x), p, scd, zd, workspace=workspace))
     if N <= 300:
         rows = np.arange(N)
     else:

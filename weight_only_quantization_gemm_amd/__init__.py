@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     awq_gemm_kernel,
     awq_gemm_scaled,
     awq_gemm_scaled_workspace_bytes,
+    awq_gemm_workspace_bytes,
     awq_keep_fp16_ablation,
     awq_last_error,
     awq_pack,

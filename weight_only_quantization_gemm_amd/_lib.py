@@ -33,6 +33,9 @@ SIGNATURES = {
                                            c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "awq_gemm_bits": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
     "awq_gemm_kernel": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_i32, ctypes.c_char_p, c_size]),
+    "awq_gemm_workspace_bytes": (c_size, [c_i64, c_i64, c_i64, c_i32]),
+    "awq_gemm_ws": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "awq_gemm_ws_kernel": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_i32, ctypes.c_char_p, c_size]),
     "awq_unpack_bits": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "awq_ablation_workspace_bytes": (c_size, [c_i64, c_i64, c_i64, c_i32]),
     "awq_keep_fp16_ablation": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp,

@@ -174,10 +174,29 @@ def awq_quantize(W: torch.Tensor, X: torch.Tensor, alphas: Optional[Sequence[flo
     return dict(packed=packed, scales=scales, zeros=zeros, s=s, best_alpha=best, loss=loss, alphas=al, bits=bits)
 
 
+# awq_gemm_ws workspaces cached per (device, stream): tile counters start at zero and every
+# call leaves them zero; calls on one stream are ordered, so they may share one.
+_GEMM_WS = {}
+
+
+def _gemm_workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream)
+    ws = _GEMM_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _GEMM_WS[key] = ws
+    return ws
+
+
 def awq_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
-             out: Optional[torch.Tensor] = None, group: int = GROUP, bits: Optional[int] = None) -> torch.Tensor:
+             out: Optional[torch.Tensor] = None, group: int = GROUP, bits: Optional[int] = None,
+             workspace="auto") -> torch.Tensor:
     """y = x @ w_hat^T with fp32 accumulation; x fp16 [M][K] (already divided by s).  bits
-    (4 or 3) defaults to the width the packed tensor's shape says it was written at."""
+    (4 or 3) defaults to the width the packed tensor's shape says it was written at.
+    workspace: "auto" (awq_gemm_ws with a workspace cached for the device and stream, so the
+    GEMM may split its work over the compute units), a zero-initialized uint8 device tensor
+    of at least awq_gemm_workspace_bytes(M, N, K, bits) bytes, or None (awq_gemm_bits: whole
+    output tiles per block)."""
     _need(x, "x", torch.float16, 2)
     _need(packed, "packed", torch.int32, 2)
     _need(scales, "scales", torch.float16, 2)
@@ -196,18 +215,40 @@ def awq_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros:
         _need(out, "out", torch.float16, 2)
         if tuple(out.shape) != (M, N):
             raise ValueError("out must be fp16 [M][N]")
+    lib = load()
+    need = lib.awq_gemm_workspace_bytes(M, N, K, bits) if workspace is not None else 0
     with torch.cuda.device(x.device):
-        check(load().awq_gemm_bits(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
-                                   out.data_ptr(), M, N, K, group, bits, _stream(x.device)))
+        stream = _stream(x.device)
+        if need == 0:
+            check(lib.awq_gemm_bits(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                    out.data_ptr(), M, N, K, group, bits, stream))
+            return out
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError('workspace must be "auto", None or a uint8 device tensor')
+            ws = _gemm_workspace(x.device, stream, need)
+        else:
+            _need(workspace, "workspace", torch.uint8, 1)
+            ws = workspace
+        check(lib.awq_gemm_ws(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                              out.data_ptr(), M, N, K, group, bits, ws.data_ptr(), ws.numel(), stream))
     return out
 
 
-def awq_gemm_kernel(M: int, N: int, K: int, bits: int = 4, group: int = GROUP) -> str:
+def awq_gemm_workspace_bytes(M: int, N: int, K: int, bits: int = 4) -> int:
+    """Workspace bytes awq_gemm_ws needs for this product (0: it splits no work)."""
+    _check_bits(bits)
+    return int(load().awq_gemm_workspace_bytes(int(M), int(N), int(K), int(bits)))
+
+
+def awq_gemm_kernel(M: int, N: int, K: int, bits: int = 4, group: int = GROUP, workspace: bool = True) -> str:
     """The kernel awq_gemm launches for an M x K input and N x K weights (a host-only dry run of
-    its dispatch: the kernel's template arguments, block and grid)."""
+    its dispatch: the kernel's template arguments, block and grid), with a workspace (as
+    awq_gemm's default does) or without."""
     _check_bits(bits)
     buf = ctypes.create_string_buffer(160)
-    check(load().awq_gemm_kernel(int(M), int(N), int(K), int(group), int(bits), buf, len(buf)))
+    fn = load().awq_gemm_ws_kernel if workspace else load().awq_gemm_kernel
+    check(fn(int(M), int(N), int(K), int(group), int(bits), buf, len(buf)))
     return buf.value.decode()
 
 

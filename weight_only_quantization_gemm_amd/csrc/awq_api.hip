@@ -413,10 +413,10 @@ int awq_keep_fp16_ablation(const void* W, const void* X, int64_t N, int64_t K, i
 // The product's dispatch on the code width and M (each launcher picks its own
 // kernel and layout; see the launchers for the measured rules).
 static hipError_t launch_product(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                                 int64_t M, int64_t N, int64_t K, int32_t bits, hipStream_t hs) {
-  if (bits == 3) return awq::launch_gemm3(x, packed, scales, zeros, y, M, N, K, hs);
+                                 int64_t M, int64_t N, int64_t K, int32_t bits, hipStream_t hs, void* ws = nullptr) {
+  if (bits == 3) return awq::launch_gemm3(x, packed, scales, zeros, y, M, N, K, ws, hs);
   if (M <= 16) return awq::launch_gemv(x, packed, scales, zeros, y, M, N, K, hs);
-  return awq::launch_gemm(x, packed, scales, zeros, y, M, N, K, hs);
+  return awq::launch_gemm(x, packed, scales, zeros, y, M, N, K, ws, hs);
 }
 
 int awq_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M, int64_t N,
@@ -439,7 +439,47 @@ int awq_gemm_bits(const void* x, const void* packed, const void* scales, const v
   AWQ_GUARD_END
 }
 
+size_t awq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits) {
+  if (M < 1 || N < 1 || K < 1 || K % AWQ_GROUP != 0 || (bits != 4 && bits != 3)) return 0;
+  return awq::gemm_pipe_streamk(M, N, K, bits) ? awq::gemm_pipe_workspace_bytes(M, N) : 0;
+}
+
+int awq_gemm_ws(const void* x, const void* packed, const void* scales, const void* zeros, void* y, int64_t M,
+                int64_t N, int64_t K, int32_t group, int32_t bits, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  AWQ_GUARD_BEGIN
+  AWQ_REQUIRE(x && packed && scales && zeros && y, AWQ_ERROR_INVALID_VALUE,
+              "x, packed, scales, zeros and y must not be NULL");
+  int st = check_layer(N, K, group);
+  if (st == AWQ_OK) st = check_bits(bits);
+  if (st != AWQ_OK) return st;
+  AWQ_REQUIRE(M >= 1 && M <= (int64_t(1) << 22), AWQ_ERROR_INVALID_VALUE, "M=%lld outside [1, 2^22]", (long long)M);
+  const size_t need = awq_gemm_workspace_bytes(M, N, K, bits);
+  AWQ_REQUIRE(workspace || need == 0, AWQ_ERROR_INVALID_VALUE, "workspace must not be NULL (%zu bytes needed)", need);
+  if (int st2 = check_aligned({{x, "x"}, {packed, "packed"}, {scales, "scales"}, {zeros, "zeros"}, {y, "y"},
+                                {workspace, "workspace"}}))
+    return st2;
+  AWQ_REQUIRE(workspace_bytes >= need, AWQ_ERROR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+              need);
+  return device_status(launch_product(x, packed, scales, zeros, y, M, N, K, bits, as_stream(stream),
+                                      need ? workspace : nullptr),
+                       "awq_gemm_ws");
+  AWQ_GUARD_END
+}
+
+static int gemm_kernel_query(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, bool with_ws, char* out,
+                             size_t out_bytes);
+
 int awq_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, char* out, size_t out_bytes) {
+  return gemm_kernel_query(M, N, K, group, bits, false, out, out_bytes);
+}
+
+int awq_gemm_ws_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, char* out, size_t out_bytes) {
+  return gemm_kernel_query(M, N, K, group, bits, true, out, out_bytes);
+}
+
+static int gemm_kernel_query(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, bool with_ws, char* out,
+                             size_t out_bytes) {
   AWQ_GUARD_BEGIN
   AWQ_REQUIRE(out && out_bytes > 0, AWQ_ERROR_INVALID_VALUE, "out must not be NULL and out_bytes must be positive");
   out[0] = 0;
@@ -456,7 +496,9 @@ int awq_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits
     ~Installed() { awq::install_plan(nullptr); }
   } dry;
   // a dry run computes the launch only: no pointer is dereferenced, nothing is enqueued
-  const hipError_t e = launch_product(nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, bits, nullptr);
+  // a dry run never dereferences the workspace: any non-null address stands for one
+  void* ws = with_ws && awq_gemm_workspace_bytes(M, N, K, bits) ? reinterpret_cast<void*>(uintptr_t(256)) : nullptr;
+  const hipError_t e = launch_product(nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, bits, nullptr, ws);
   AWQ_REQUIRE(e == hipSuccess && dry.plan.text[0] != 0, AWQ_ERROR_INVALID_VALUE,
               "no kernel launches for M=%lld N=%lld K=%lld bits=%d", (long long)M, (long long)N, (long long)K, bits);
   snprintf(out, out_bytes, "%s", dry.plan.text);

@@ -75,19 +75,24 @@ hipError_t launch_gemv(const void* x, const void* packed, const void* scales, co
 bool gemm_pipe_supported(int64_t M, int64_t N, int64_t K);
 bool gemm_pipe3_supported(int64_t M, int64_t N, int64_t K);  // 3-bit codes, M > 16
 bool ring_mid_pipe_preferred(int64_t M, int64_t N, int64_t K);
+// ws: null, or gemm_pipe_workspace_bytes(M, N) bytes whose counter part is zero (left zero): the
+// pipelined GEMM then splits its work evenly over the compute units (stream-K)
+size_t gemm_pipe_workspace_bytes(int64_t M, int64_t N);
+// whether the pipelined GEMM splits its work (stream-K) when it is given a workspace
+bool gemm_pipe_streamk(int64_t M, int64_t N, int64_t K, int bits);
 hipError_t launch_gemm_pipe3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                             int64_t M, int64_t N, int64_t K, hipStream_t st);
+                             int64_t M, int64_t N, int64_t K, void* ws, hipStream_t st);
 hipError_t launch_gemm_pipe(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                            int64_t M, int64_t N, int64_t K, hipStream_t st);
+                            int64_t M, int64_t N, int64_t K, void* ws, hipStream_t st);
 hipError_t launch_gemm(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                       int64_t M, int64_t N, int64_t K, hipStream_t st);
+                       int64_t M, int64_t N, int64_t K, void* ws, hipStream_t st);
 // 3-bit format: GEMV for M = 1 and short-row M = 2 (gemv.hip), the ring kernel up to M = 16 (skinny.hip),
 // the general-shape matrix-core kernel otherwise (gemm.hip)
 bool gemv3_supported(int64_t M, int64_t K);
 hipError_t launch_gemv3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
                         int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm3(const void* x, const void* packed, const void* scales, const void* zeros, void* y,
-                        int64_t M, int64_t N, int64_t K, hipStream_t st);
+                        int64_t M, int64_t N, int64_t K, void* ws, hipStream_t st);
 
 // Dry runs of the product dispatch.  While a KernelPlan is installed on the
 // calling thread, each product launcher writes the kernel it would launch (its
