@@ -567,10 +567,11 @@ def run_cpu_baseline(layers_spec, budget_s: float):
 
 
 def run_oracle_timings(args):
-    """The C++ oracle timed on the host cores for the other timed workloads: the M = 256
-    product on (4096, 11008), and per 7B-block search shape class the statistics, the Gram
-    matrix (65,536 rows) and one alpha (quantize, error, loss); a full search is the
-    statistics plus 20 alphas.  Seconds, with the thread count and CPU model."""
+    """The C++ oracle timed on the host cores for the other timed workloads: the (4096, 11008)
+    product at every M of the batch sweep, the Llama-2 70B linears at M = 1, 8, 16, and per
+    7B-block search shape class the statistics, the Gram matrix (65,536 rows) and one alpha
+    (quantize, error, loss); a full search is the statistics plus 20 alphas.  Seconds, with the
+    thread count and CPU model."""
     import oracle
     from gen import activations_fp16, normal_fp16, seed_for
     model, threads, ncpu = host_cpu()
@@ -583,6 +584,30 @@ def run_oracle_timings(args):
     oracle.gemm(x, q, z, sc)
     dt = time.perf_counter() - t0
     out["gemm_m256_4096x11008"] = dict(s=round(dt, 3), GFLOPs=round(2.0 * M * N * K / dt / 1e9, 2))
+    # the batch sweep on the same layer, and the Llama-2 70B linears at M = 1, 8, 16: one product each
+    sweep = {}
+    for Ms in (1, 2, 4, 8, 16, 64, 256, 1024):
+        xs = activations_fp16(Ms, K, seed=3100 + Ms)
+        t0 = time.perf_counter()
+        oracle.gemm(xs, q, z, sc)
+        dt = time.perf_counter() - t0
+        sweep[str(Ms)] = dict(s=round(dt, 4), GFLOPs=round(2.0 * Ms * N * K / dt / 1e9, 2))
+    out["sweep_4096x11008"] = sweep
+    l70 = {}
+    for name, K7, N7 in LAYERS_70B:
+        W7 = normal_fp16((N7, K7), 0.015, seed=7000 + K7 + N7)
+        q7, z7, sc7 = oracle.quantize_groups(oracle.scale_weights(W7, np.ones(K7, np.float32)))
+        del W7
+        for M7 in (1, 8, 16):
+            x7 = activations_fp16(M7, K7, seed=7100 + M7 + K7)
+            t0 = time.perf_counter()
+            oracle.gemm(x7, q7, z7, sc7)
+            dt = time.perf_counter() - t0
+            l70[f"{name}_m{M7}"] = dict(K=K7, N=N7, M=M7, s=round(dt, 4),
+                                         GBs=round(gemv_bytes(M7, K7, N7) / dt / 1e9, 3))
+        del q7, z7, sc7
+    out["llama2_70b_layers"] = l70
+    log(f"oracle sweep and 70B layers: {sweep['1024']['s']} s at M = 1024")
     Mc = 65536
     for li, (name, K, N) in enumerate([("q_proj", 4096, 4096), ("gate_proj", 4096, 11008), ("down_proj", 11008, 4096)]):
         X = activations_fp16(Mc, K, seed=seed_for(5, 10 + li), lognormal=True)
