@@ -53,6 +53,35 @@ __device__ inline f16x2 zero_biased(uint32_t zero) {
   return as_f16x2(0x64006400u | zero | (zero << 16));
 }
 
+// The zero point in the two forms word_minus_zero() subtracts: the fp16x2
+// pairs (1024 + zero) and -(64 + zero) (64 has spacing 1/16, so zero sits at
+// bit 4 of the mantissa; 0xD400 is -64).
+struct ZeroForms {
+  f16x2 zb1, nz64;
+};
+__device__ inline ZeroForms zero_forms(uint32_t zero) {
+  return {as_f16x2(0x64006400u | zero | (zero << 16)), as_f16x2(0xD400D400u | (zero << 4) | (zero << 20))};
+}
+
+// The eight (code - zero) values of packed word w in channel order, exact, as
+// a matrix-core operand.  With w8 = w >> 8, the four channel pairs are the
+// 0x000F000F and 0x00F000F0 fields of w and of w8.  An and-or with the bias
+// turns the low field into 1024 + code and the high field into 1024 + 16 code
+// (below 2048, where the fp16 spacing is 1).  One packed subtraction of
+// (1024 + zero) leaves code - zero for the low fields; one packed fma,
+// (1024 + 16 code) / 16 - (64 + zero), does so for the high ones (the exact
+// result is an integer of magnitude at most 15, so the single rounding is
+// exact).  One shift per word instead of three.
+__device__ inline f16x8 word_minus_zero(uint32_t w, uint32_t bias, ZeroForms z) {
+  const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+  const uint32_t w8 = w >> 8;
+  const f16x2 q0 = as_f16x2((w & 0x000F000Fu) | bias) - z.zb1;
+  const f16x2 q1 = __builtin_elementwise_fma(as_f16x2((w & 0x00F000F0u) | bias), sixteenth, z.nz64);
+  const f16x2 q2 = as_f16x2((w8 & 0x000F000Fu) | bias) - z.zb1;
+  const f16x2 q3 = __builtin_elementwise_fma(as_f16x2((w8 & 0x00F000F0u) | bias), sixteenth, z.nz64);
+  return f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+}
+
 __device__ inline uint32_t zero_of(const uint8_t* zeros_row, int g) {
   return (zeros_row[g >> 1] >> (4 * (g & 1))) & 0xFu;
 }

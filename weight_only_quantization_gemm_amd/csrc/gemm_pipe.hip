@@ -273,7 +273,8 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
       const f16* Ah = st + ahalf * S::A_HALF;
       const f16* Bt = st + 2 * S::A_HALF;
       u32x4 wv[S::JB][S::STEPS / 4];
-      f16x2 zb[S::JB], sc2[S::JB];
+      ZeroForms zf[S::JB];
+      f16x2 sc2[S::JB];
 #pragma unroll
       for (int j = 0; j < S::JB; ++j) {
         const int row = wn * S::TN + j * 32 + l32;
@@ -287,7 +288,7 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
             wv[j][q] = u32x4{wp[0], wp[1], wp[2], 0u};
           }
         }
-        zb[j] = zero_biased((mz[mrow[j] * P2 + (g >> 1)] >> (4 * (g & 1))) & 0xFu);
+        zf[j] = zero_forms((mz[mrow[j] * P2 + (g >> 1)] >> (4 * (g & 1))) & 0xFu);
         const uint32_t sbits = msc[mrow[j] * G + g];
         sc2[j] = as_f16x2(sbits | (sbits << 16));
       }
@@ -306,17 +307,14 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
               const uint32_t bits =
                   pp < 15 ? ((w[pp / 5] >> (3 * (pp % 5))) & 0x00070007u)
                           : (((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) | ((w[2] >> 13) & 0x00040004u));
-              q[uu] = (as_f16x2(bits | magic) - zb[j]) * sc2[j];
+              q[uu] = (as_f16x2(bits | magic) - zf[j].zb1) * sc2[j];
             }
             bq[j] = f16x8{q[0].x, q[0].y, q[1].x, q[1].y, q[2].x, q[2].y, q[3].x, q[3].y};
             continue;
           }
-          const uint32_t word = wv[j][st_ >> 2][st_ & 3];
-          const f16x2 q0 = (as_f16x2((word & 0x000F000Fu) | magic) - zb[j]) * sc2[j];
-          const f16x2 q1 = (as_f16x2(((word >> 4) & 0x000F000Fu) | magic) - zb[j]) * sc2[j];
-          const f16x2 q2 = (as_f16x2(((word >> 8) & 0x000F000Fu) | magic) - zb[j]) * sc2[j];
-          const f16x2 q3 = (as_f16x2(((word >> 12) & 0x000F000Fu) | magic) - zb[j]) * sc2[j];
-          bq[j] = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+          // exact code - zero, then one rounding by the scale: fp16 of s (q - z)
+          const f16x8 sc8 = f16x8{sc2[j].x, sc2[j].y, sc2[j].x, sc2[j].y, sc2[j].x, sc2[j].y, sc2[j].x, sc2[j].y};
+          bq[j] = word_minus_zero(wv[j][st_ >> 2][st_ & 3], magic, zf[j]) * sc8;
         }
       };
       f16x8 av[2][S::AB], bq[2][S::JB];

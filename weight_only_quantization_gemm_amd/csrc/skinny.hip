@@ -127,16 +127,13 @@ __global__ __launch_bounds__(512) void skinny_kernel(const f16* __restrict__ x, 
         }
 #pragma unroll
       for (int t = 0; t < RW; ++t) {
-        const f16x2 zb = zero_biased(zz[p][t]);
+        const ZeroForms zf = zero_forms(zz[p][t]);
         f32x4 d[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) d[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const uint32_t word = wv[p][t][s];
-          const f16x2 q0 = pair_biased(word, 0, bias) - zb, q1 = pair_biased(word, 1, bias) - zb;
-          const f16x2 q2 = pair_biased(word, 2, bias) - zb, q3 = pair_biased(word, 3, bias) - zb;
-          const f16x8 b = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+          const f16x8 b = word_minus_zero(wv[p][t][s], bias, zf);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][s], b, d[mt], 0, 0, 0);
         }
@@ -391,6 +388,10 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
       const int64_t g = c * P + i;
       const bool live = g < G;
       const int gc = (int)(live ? g : G - 1);
+      // Every LDS read of the chunk (x fragments, then each tile's codes, zero
+      // byte and scale) is issued before the first use: one LDS round trip per
+      // chunk rather than one per tile.  The scale is read unconditionally (gc is
+      // clamped) and zeroed by a select for chunks past G.
       f16x8 a[MT][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -398,35 +399,46 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
         for (int s = 0; s < 4; ++s)
           a[mt][s] = *reinterpret_cast<const f16x8*>(src + WBYTES + xr[mt] * XROWB +
                                                      ((i * 16 + kq * 4 + s) ^ (xr[mt] & 15)) * 16);
+      u32x4 wt[RW];
+      uint32_t zt[RW];
+      f16 st[RW];
 #pragma unroll
       for (int t = 0; t < RW; ++t) {
         const int r = 16 * t + nl;
-        const f16x2 zb = zero_biased((zl[r * P2 + (gc >> 1)] >> (4 * (gc & 1))) & 0xFu);
+        if constexpr (BITS == 4) {
+          wt[t] = *reinterpret_cast<const u32x4*>(src + t * TILE + nl * ROWB + ((i * 4 + kq) ^ ring_swizzle<P>(nl)) * 16);
+        } else {
+          // the three words of the lane's 32 channels (rows of 48 bytes: 16 rows on
+          // distinct banks)
+          const uint32_t* wp = reinterpret_cast<const uint32_t*>(src + r * 48 + kq * 12);
+          wt[t] = u32x4{wp[0], wp[1], wp[2], 0u};
+        }
+        zt[t] = zl[r * P2 + (gc >> 1)];
+        st[t] = sl[r * G + gc];
+      }
+#pragma unroll
+      for (int t = 0; t < RW; ++t) {
+        const ZeroForms zf = zero_forms((zt[t] >> (4 * (gc & 1))) & 0xFu);
         f32x4 d[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) d[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (BITS == 4) {
-          const u32x4 w =
-              *reinterpret_cast<const u32x4*>(src + t * TILE + nl * ROWB + ((i * 4 + kq) ^ ring_swizzle<P>(nl)) * 16);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const f16x2 q0 = pair_biased(w[s], 0, bias) - zb, q1 = pair_biased(w[s], 1, bias) - zb;
-            const f16x2 q2 = pair_biased(w[s], 2, bias) - zb, q3 = pair_biased(w[s], 3, bias) - zb;
-            const f16x8 b = f16x8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+            const f16x8 b = word_minus_zero(wt[t][s], bias, zf);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][s], b, d[mt], 0, 0, 0);
           }
         } else {
-          // the three words of the lane's 32 channels (rows of 48 bytes: 16 rows on
-          // distinct banks); channel pair p of the chunk, as fp16 (1024 + code) pairs
-          const uint32_t* wp = reinterpret_cast<const uint32_t*>(src + r * 48 + kq * 12);
-          const uint32_t w[3] = {wp[0], wp[1], wp[2]};
+          // channel pair p of the chunk, as fp16 (1024 + code) pairs less (1024 + zero)
+          const uint32_t w[3] = {wt[t][0], wt[t][1], wt[t][2]};
           f16x2 q[16];
 #pragma unroll
-          for (int pp = 0; pp < 15; ++pp) q[pp] = as_f16x2(((w[pp / 5] >> (3 * (pp % 5))) & 0x00070007u) | bias) - zb;
+          for (int pp = 0; pp < 15; ++pp)
+            q[pp] = as_f16x2(((w[pp / 5] >> (3 * (pp % 5))) & 0x00070007u) | bias) - zf.zb1;
           q[15] = as_f16x2(((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) | ((w[2] >> 13) & 0x00040004u) |
                            bias) -
-                  zb;
+                  zf.zb1;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const f16x8 b = f16x8{q[4 * s].x,     q[4 * s].y,     q[4 * s + 1].x, q[4 * s + 1].y,
@@ -435,7 +447,7 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
             for (int mt = 0; mt < MT; ++mt) d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][s], b, d[mt], 0, 0, 0);
           }
         }
-        const float scf = live ? (float)sl[r * G + gc] : 0.0f;
+        const float scf = live ? (float)st[t] : 0.0f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
