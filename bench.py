@@ -638,6 +638,8 @@ def load_ceilings():
     lib = ctypes.CDLL(path)
     lib.awq_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
                                             ctypes.c_void_p]
+    lib.awq_ceiling_stream_read_store.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                                  ctypes.c_int32, ctypes.c_void_p]
     lib.awq_ceiling_mfma_f16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_void_p]
     return lib
@@ -651,31 +653,38 @@ def run_ceilings(args, torch, dev):
     """What one device reaches with nothing but the product kernels' own access pattern:
     a streaming read of each decode layer's size with 16-byte non-temporal loads, one round
     trip per thread (rotating copies over more than 1 GiB, graph-timed; the faster of one and
-    two loads per thread), and dense fp16 matrix-core throughput (v_mfma_f32_32x32x16_f16, 8
+    two loads per thread), the same read with each block ending in one dependent store (as a
+    decode GEMV block ends with its y values), and dense fp16 matrix-core throughput (v_mfma_f32_32x32x16_f16, 8
     independent chains per wave, one or two waves per SIMD)."""
     lib = load_ceilings()
-    out = {"stream_read": {}, "mfma_f16_32x32x16": {}}
+    out = {"stream_read": {}, "stream_read_store": {}, "mfma_f16_32x32x16": {}}
     sink = torch.zeros(1024, dtype=torch.int32, device=dev)
     for label, nbytes in CEILING_READ_SIZES:
         nb = nbytes // 16 * 16
         copies = max(2, -(-int(1.1 * (1 << 30)) // nb) + 1)
         bufs = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(copies)]
-        best = None
-        for L in (1, 2):
-            def run(bufs=bufs, nb=nb, L=L):
-                st = torch.cuda.current_stream().cuda_stream
-                for b in bufs:
-                    assert lib.awq_ceiling_stream_read(b.data_ptr(), nb, sink.data_ptr(), L, st) == 0
-            g = graph_of(torch, run)
-            ms = time_replays(torch, [g], max(3, 40 // copies), 1) / copies
-            del g
-            if best is None or ms < best[0]:
-                best = (ms, L)
-        ms, L = best
-        out["stream_read"][label] = dict(bytes=nb, us=round(ms * 1e3, 3), GBs=round(nb / (ms * 1e-3) / 1e9, 1),
-                                         hbm_frac=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), copies=copies,
-                                         loads_per_thread=L)
-        del bufs
+        words = -(-nb // 4096)  # blocks at one load per thread
+        outs = torch.zeros(words, dtype=torch.int32, device=dev)
+        for kind in ("stream_read", "stream_read_store"):
+            best = None
+            for L in (1, 2):
+                def run(bufs=bufs, nb=nb, L=L, kind=kind):
+                    st = torch.cuda.current_stream().cuda_stream
+                    for b in bufs:
+                        if kind == "stream_read":
+                            assert lib.awq_ceiling_stream_read(b.data_ptr(), nb, sink.data_ptr(), L, st) == 0
+                        else:
+                            assert lib.awq_ceiling_stream_read_store(b.data_ptr(), nb, outs.data_ptr(), words, L, st) == 0
+                g = graph_of(torch, run)
+                ms = time_replays(torch, [g], max(3, 40 // copies), 1) / copies
+                del g
+                if best is None or ms < best[0]:
+                    best = (ms, L)
+            ms, L = best
+            out[kind][label] = dict(bytes=nb, us=round(ms * 1e3, 3), GBs=round(nb / (ms * 1e-3) / 1e9, 1),
+                                    hbm_frac=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), copies=copies,
+                                    loads_per_thread=L)
+        del bufs, outs
         torch.cuda.empty_cache()
     for wps in (1, 2):
         blocks, iters = 256, 8192

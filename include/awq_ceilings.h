@@ -1,9 +1,10 @@
 /*
- * libawq_ceilings -- two measurement kernels for gfx950 that bound what the
+ * libawq_ceilings -- measurement kernels for gfx950 that bound what the
  * libawq kernels can reach on one device: a streaming read (the HBM ceiling
- * the decode GEMV is measured against) and a dense fp16 matrix-core loop (the
- * MFMA ceiling of the GEMM and the search contractions).  They compute nothing
- * of the method; only bench.py's ceiling leg calls them.
+ * the decode GEMV is measured against), the same read ending each block with
+ * one dependent store (the decode GEMV's shape), and a dense fp16 matrix-core
+ * loop (the MFMA ceiling of the GEMM and the search contractions).  They
+ * compute nothing of the method; only bench.py's ceiling leg calls them.
  *
  * Memory and streams follow libawq (include/awq.h): device pointers of the
  * current device, 16-byte aligned, owned by the caller; work enqueued on
@@ -33,6 +34,19 @@ extern "C" {
  *   sink   device uint32 [1024]
  */
 int awq_ceiling_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t loads_per_thread, void* stream);
+
+/*
+ * awq_ceiling_stream_read_store -- the read of awq_ceiling_stream_read, with
+ * each 256-thread block finishing as a decode GEMV block does: its threads'
+ * folded words are combined across the block (shuffles, then LDS after a
+ * barrier) and one 4-byte store per block writes the result to out[block].
+ * The difference from awq_ceiling_stream_read is what a kernel that writes its
+ * outputs after all of its loads pays for that dependent store.
+ *   out        device uint32 [out_words], out_words >= the number of blocks,
+ *              ceil(bytes / (4096 loads_per_thread))
+ */
+int awq_ceiling_stream_read_store(const void* src, size_t bytes, uint32_t* out, size_t out_words,
+                                  int32_t loads_per_thread, void* stream);
 
 /*
  * awq_ceiling_mfma_f16 -- each of `blocks` blocks of 4 * waves_per_simd waves

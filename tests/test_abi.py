@@ -40,6 +40,26 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), f"{n} not exported"
 
 
+def test_ceilings_library_exports_and_refuses_bad_arguments():
+    """libawq_ceilings.so (the measurement kernels bench.py compares against) exports what
+    include/awq_ceilings.h declares and refuses bad arguments before launching."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "awq_ceilings.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(awq_ceiling_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["awq_ceiling_mfma_f16", "awq_ceiling_stream_read", "awq_ceiling_stream_read_store"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_quantization_gemm_amd", "libawq_ceilings.so"))
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    f = lib.awq_ceiling_stream_read_store
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
+    nb = 1 << 20  # 256 blocks at one load per thread, 128 at two
+    assert f(FAKE, nb, FAKE, 255, 1, None) == INVALID       # out holds fewer words than blocks
+    assert f(FAKE, nb, FAKE, 128, 3, None) == INVALID       # loads per thread not 1, 2 or 4
+    assert f(FAKE_MISALIGNED, nb, FAKE, 256, 1, None) == INVALID
+    assert f(FAKE, nb, FAKE_MISALIGNED, 256, 1, None) == INVALID
+    assert f(FAKE, nb + 8, FAKE, 257, 1, None) == INVALID  # bytes not a multiple of 16
+    assert f(None, nb, FAKE, 256, 1, None) == INVALID
+
+
 def test_version_and_status_strings():
     assert awq.awq_version() >= 10000
     assert awq.awq_status_string(0) == "AWQ_OK"
