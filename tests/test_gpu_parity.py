@@ -268,6 +268,33 @@ def test_gemm_one_hot_reproduces_dequantized_column(M):
         assert np.array_equal(y[m], col.astype(np.float16)), (m, k)
 
 
+@pytest.mark.parametrize("M,N", [(1, 80), (2, 80), (3, 80), (5, 80), (9, 80), (16, 80), (24, 80), (40, 80),
+                                 (64, 80), (100, 80), (256, 80), (512, 8192)])
+def test_gemm_one_hot_every_code_position_exact(M, N):
+    """Row m of x is the unit vector of channel 37 m mod K (37 is odd, so the channels cover all
+    eight nibble positions of a packed word, all four words of a 16-byte piece and all four
+    groups), with unit scales and every (code, zero) pair present: y[m][n] must equal
+    code - zero exactly, on whichever kernel the M class takes (GEMV, decode ring, matrix-core
+    ring and pipelined GEMM with 64- and 128-row tiles)."""
+    K = 512
+    kernel = awq.awq_gemm_kernel(M, N, K)
+    note(f"gemm one-hot every position M={M}: {kernel}")
+    n = np.arange(N)[:, None]
+    q = ((n + np.arange(K)[None, :] * 5) % 16).astype(np.uint8)        # every code on every row
+    z = ((n * 3 + np.arange(K // 128)[None, :] * 7) % 16).astype(np.uint8)  # every zero point
+    sc = np.ones((N, K // 128), np.float16)
+    p, zb = encode(q, z)
+    pd, scd, zbd = dev(p), dev(sc), dev(zb)
+    for shift in range(16 if M <= 2 else 1):  # one or two channels per launch: 16 launches
+        ks = [(37 * (m + M * shift)) % K for m in range(M)]
+        x = np.zeros((M, K), np.float16)
+        x[np.arange(M), ks] = 1.0
+        y = host(awq.awq_gemm(dev(x), pd, scd, zbd))
+        want = (q[:, ks].astype(np.int32) - z[:, np.array(ks) // 128].astype(np.int32)).T.astype(np.float16)
+        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), \
+            f"M={M} ({kernel}) shift {shift}: first mismatch at {np.argwhere(y != want)[:3].tolist()}"
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 64, 256), (2, 64, 256), (5, 64, 256), (8, 64, 256), (9, 64, 256),
                                    (64, 64, 256), (1, 4096, 4096), (2, 11008, 4096), (1, 4096, 11008),
                                    (1, 8192, 28672), (16, 300, 4096), (256, 300, 4096)])

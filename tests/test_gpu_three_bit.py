@@ -121,6 +121,30 @@ def test_gemm3_one_hot_reproduces_dequantized_column(M):
         assert np.array_equal(y[m], col.astype(np.float16)), (m, k)
 
 
+@pytest.mark.parametrize("M,N", [(1, 80), (2, 80), (5, 80), (16, 80), (24, 80), (64, 80), (256, 80), (512, 8192)])
+def test_gemm3_one_hot_every_code_position_exact(M, N):
+    """3-bit twin of the 4-bit exact one-hot test: row m of x is the unit vector of channel
+    37 m mod K (all 32 positions of a three-word chunk, the two spare-bit channels included),
+    unit scales, every (code, zero) pair present; y[m][n] = code - zero exactly."""
+    K = 512
+    kernel = awq.awq_gemm_kernel(M, N, K, bits=3)
+    note(f"gemm3 one-hot every position M={M}: {kernel}")
+    n = np.arange(N)[:, None]
+    q = ((n + np.arange(K)[None, :] * 3) % 8).astype(np.uint8)
+    z = ((n * 5 + np.arange(K // 128)[None, :] * 3) % 8).astype(np.uint8)
+    sc = np.ones((N, K // 128), np.float16)
+    p, zb = encode3(q, z)
+    pd, scd, zbd = dev(p), dev(sc), dev(zb)
+    for shift in range(16 if M <= 2 else 1):  # one or two channels per launch: 16 launches
+        ks = [(37 * (m + M * shift)) % K for m in range(M)]
+        x = np.zeros((M, K), np.float16)
+        x[np.arange(M), ks] = 1.0
+        y = host(awq.awq_gemm(dev(x), pd, scd, zbd, bits=3))
+        want = (q[:, ks].astype(np.int32) - z[:, np.array(ks) // 128].astype(np.int32)).T.astype(np.float16)
+        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), \
+            f"M={M} ({kernel}) shift {shift}: first mismatch at {np.argwhere(y != want)[:3].tolist()}"
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 64, 256), (2, 64, 256), (5, 64, 256), (64, 64, 256), (1, 4096, 4096),
                                    (2, 1000, 11008), (16, 300, 4096), (100, 300, 1024)])
 def test_gemm3_codes_equal_zeros_gives_zero(M, N, K):
