@@ -1162,6 +1162,17 @@ def main():
     live_us = dec["kern_ms"] * 1e3
     launch_us = trace["mean_launch_us"] if trace else live_us
     achieved = dec["bytes_per_launch"] / (launch_us * 1e-6) / 1e9
+    # The measured floor of a kernel that reads each layer's bytes and ends every block with a
+    # dependent store (the ceiling leg, same run), averaged over the step's launches.
+    floor = None
+    srs = legs.get("ceilings", {}).get("stream_read_store", {})
+    by_bytes = {v["bytes"]: v["us"] for v in srs.values()}
+    if all(gemv_bytes(1, K, N) in by_bytes for _, K, N in LAYERS_7B):
+        f_us = sum(by_bytes[gemv_bytes(1, K, N)] for _, K, N in LAYERS_7B) / len(LAYERS_7B)
+        floor = {"kind": "streaming read of each layer's bytes, every block ending in one dependent store "
+                         "(legs.ceilings.stream_read_store, this run)",
+                 "us_per_launch": round(f_us, 3), "frac_of_floor": round(f_us / launch_us, 4),
+                 "region_frac_of_floor": round(f_us / live_us, 4)}
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -1187,7 +1198,7 @@ def main():
                      if trace else "HIP events on the replay stream around the timed graph replays / launches",
                      "region_us_per_launch": round(live_us, 3),
                      "region_frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
-                     "trace": trace},
+                     "trace": trace, "floor": floor},
         "cpu_baseline": cpu,
         "per_layer": dec["per_layer"],
         "legs": legs,
