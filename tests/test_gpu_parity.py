@@ -376,6 +376,43 @@ def test_gemm_fused_rows_equal_separate_layers(M):
     assert np.array_equal(yf.view(np.uint16), np.concatenate(ys, axis=1).view(np.uint16))
 
 
+@pytest.mark.parametrize("M", [1 << 22, (1 << 22) - 3])
+def test_gemm_largest_m(M):
+    """The largest M the boundary accepts (2^22 rows) with K = 1024: x holds 2^32 elements, so
+    any 32-bit offset into x or y would wrap.  x is drawn on the device from a seeded generator
+    (8 GB); sampled rows, among them those on both sides of element 2^31 and the last ones
+    (the ragged last tile when M = 2^22 - 3), are checked against the oracle."""
+    N, K = 48, 1024
+    note(f"gemm largest M={M} N={N} K={K}: {awq.awq_gemm_kernel(M, N, K)}")
+    q, z, sc, p, scd, zd = _random_packed(N, K, seed=77)
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(78)
+    x = torch.randn((M, K), generator=gen, device="cuda:0", dtype=torch.float16)
+    y = awq.awq_gemm(x, p, scd, zd)
+    rng = np.random.default_rng(79)
+    edge = (1 << 31) // K  # first row whose elements lie at or past 2^31
+    rows = np.unique(np.concatenate([[0, 1, 2, edge - 2, edge - 1, edge, edge + 1, M - 3, M - 2, M - 1],
+                                     rng.integers(0, M, size=22)]))
+    idx = torch.from_numpy(rows).to("cuda:0")
+    xs = host(x.index_select(0, idx))
+    ys = host(y.index_select(0, idx))
+    del x, y
+    torch.cuda.empty_cache()
+    assert_y_close(ys, oracle.gemm(xs, q, z, sc), f"largest M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 16, 24, 100])
+def test_gemm_largest_k(M):
+    """The largest K the boundary accepts (2^20 channels, 8192 groups per row): the register-staged
+    and general-shape kernels that take layers whose scales and zeros leave the LDS rings no room."""
+    N, K = 40, 1 << 20
+    note(f"gemm largest K M={M} N={N} K={K}: {awq.awq_gemm_kernel(M, N, K)}")
+    q, z, sc, p, scd, zd = _random_packed(N, K, seed=80 + M)
+    x = activations_fp16(M, K, seed=81 + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    assert_y_close(y, oracle.gemm(x, q, z, sc), f"largest K M={M}")
+
+
 def test_gemm_determinism():
     note("gemm determinism")
     q, z, sc, p, scd, zd = _random_packed(1000, 2048, seed=8)

@@ -106,6 +106,17 @@ def test_gemm3_parity_shapes(N, K, M):
     assert_y_close(y, oracle.gemm(x, q, z, sc), f"N={N} K={K} M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 100])
+def test_gemm3_largest_k(M):
+    """3 bits at the largest K the boundary accepts (2^20 channels): the general-shape kernel."""
+    N, K = 40, 1 << 20
+    note(f"gemm3 largest K M={M} N={N} K={K}: {awq.awq_gemm_kernel(M, N, K, bits=3)}")
+    q, z, sc, p, scd, zd = _random_packed3(N, K, seed=90 + M)
+    x = activations_fp16(M, K, seed=91 + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd, bits=3))
+    assert_y_close(y, oracle.gemm(x, q, z, sc), f"3-bit largest K M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_gemm3_one_hot_reproduces_dequantized_column(M):
     note(f"gemm3 one-hot M={M}")
