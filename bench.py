@@ -987,6 +987,43 @@ def summarize_search_counters(dirs, n_alpha=20):
     return out
 
 
+def summarize_sq_counters(dirs, pattern, units_per_wave=0):
+    """Markdown table of rocprofv3 --pmc passes (one output directory each) over the dispatches
+    whose kernel name contains `pattern`: the median of each counter, then per-wave, per-unit
+    ratios when `units_per_wave` (the pipeline stages or groups a wave runs) is given."""
+    import csv
+    import glob
+    from collections import defaultdict
+    vals = defaultdict(list)
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                if pattern in r["Kernel_Name"]:
+                    vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    med = {c: float(np.median(v)) for c, v in vals.items()}
+    out = [f"dispatches per counter: {max((len(v) for v in vals.values()), default=0)}", "",
+           "| counter | value |", "|---|---|"]
+    out += [f"| {c} | {med[c]:.6g} |" for c in sorted(med)]
+    derived = [
+        ("LDS bank-conflict cycles / LDS-active cycles", lambda m: m["SQ_LDS_BANK_CONFLICT"] / m["SQ_LDS_IDX_ACTIVE"]),
+        ("MFMA-busy cycles / (4 x busy CU cycles)", lambda m: m["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * m["SQ_BUSY_CU_CYCLES"])),
+        ("MFMA co-executing with vector ALU / MFMA-busy cycles",
+         lambda m: m["SQ_VALU_MFMA_COEXEC_CYCLES"] / m["SQ_VALU_MFMA_BUSY_CYCLES"]),
+        ("waiting / wave cycles (SQ_WAIT_ANY / SQ_WAVE_CYCLES)", lambda m: m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"]),
+    ]
+    if units_per_wave:
+        per = lambda c: (lambda m: m[c] / (m["SQ_WAVES"] * units_per_wave))
+        derived += [(f"{c} per wave and unit", per(c))
+                    for c in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM")]
+    out += ["", "| derived | value |", "|---|---|"]
+    for label, fn in derived:
+        try:
+            out.append(f"| {label} | {fn(med):.4g} |")
+        except (KeyError, ZeroDivisionError):
+            out.append(f"| {label} | - |")
+    return out
+
+
 def profile_mode(args, torch, awq, dev):
     """Short runs for rocprofv3: the headline decode step graphs alone, a plain copy (counter
     scale), one GEMM or decode-ring layer, or the ceiling kernels."""
@@ -1072,7 +1109,13 @@ def main():
     ap.add_argument("--summarize-search-counters", metavar="PMC_DIR", nargs="+", default=None,
                     help="print the counter tables of profiles/search_loss_gram_sq_counters.md from rocprofv3 --pmc "
                          "output directories of --profile-mode search, and exit")
-    ap.add_argument("--kernel", default="gemv_kernel", help="kernel-name substring for --summarize-trace")
+    ap.add_argument("--summarize-sq-counters", metavar="PMC_DIR", nargs="+", default=None,
+                    help="print the median of each counter over the --kernel dispatches of rocprofv3 --pmc output "
+                         "directories (e.g. of --profile-mode ring or gemm), and exit")
+    ap.add_argument("--units-per-wave", type=int, default=0,
+                    help="--summarize-sq-counters: pipeline stages (or groups) each wave runs, for per-unit ratios")
+    ap.add_argument("--kernel", default="gemv_kernel",
+                    help="kernel-name substring for --summarize-trace and --summarize-sq-counters")
     ap.add_argument("--last", type=int, default=0, help="--summarize-trace: only the last N matching dispatches")
     args = ap.parse_args()
     if args.summarize_trace:
@@ -1086,6 +1129,9 @@ def main():
         return
     if args.summarize_search_counters:
         print("\n".join(summarize_search_counters(args.summarize_search_counters)))
+        return
+    if args.summarize_sq_counters:
+        print("\n".join(summarize_sq_counters(args.summarize_sq_counters, args.kernel, args.units_per_wave)))
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: the W4A16 kernels are measured on one MI355X; "

@@ -253,6 +253,23 @@ def test_gemm_parity_block_tails(N, K, M):
     assert_y_close(y, oracle.gemm(x, q, z, sc), f"N={N} K={K} M={M}")
 
 
+@pytest.mark.parametrize("K", [2048, 4096, 8192, 16384, 32768, 6144, 12288])
+@pytest.mark.parametrize("N", [512, 520])
+@pytest.mark.parametrize("M", [8, 100])
+def test_gemm_parity_scale_layouts(K, N, M):
+    """The matrix-core kernels stage a block's group scales in LDS with a row-dependent
+    permutation of 16-byte pieces where a row of scales is a power-of-two number of pieces
+    (G = K / 128 = 16 .. 256 here); G = 48 and 96 keep the plain layout.  M = 8 runs the decode
+    ring kernel, M = 100 the pipelined GEMM; N = 520 leaves a ragged last block, whose scales
+    are copied element by element into the same layout.  Every (row, group) scale is distinct,
+    so a misplaced one shows in y."""
+    note(f"gemm scale layout K={K} N={N} M={M}")
+    q, z, sc, p, scd, zd = _random_packed(N, K, seed=K + N + M)
+    x = activations_fp16(M, K, seed=77 + M)
+    y = host(awq.awq_gemm(dev(x), p, scd, zd))
+    assert_y_close(y, oracle.gemm(x, q, z, sc), f"K={K} N={N} M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 4, 8, 16])
 def test_gemm_one_hot_reproduces_dequantized_column(M):
     note(f"gemm one-hot M={M}")

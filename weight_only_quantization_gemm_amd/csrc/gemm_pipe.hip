@@ -88,6 +88,27 @@ __device__ __forceinline__ void dma_blob(unsigned char* dst, const unsigned char
   }
 }
 
+// The block's scales ([rows][G] fp16, rows x 2G bytes of the caller's array)
+// into LDS in the layout of ScaleSwizzle: with a swizzled layout every row is
+// whole 16-byte pieces, and the lane that fills LDS piece v fetches the
+// source piece that belongs there.  Otherwise as dma_blob.
+template <int NW>
+__device__ __forceinline__ void dma_scales(unsigned char* dst, const unsigned char* __restrict__ src, int64_t len,
+                                           const ScaleSwizzle& sw, int lg_ch, int wave, int lane, int tid) {
+  if (sw.mask == 0) {
+    dma_blob<NW>(dst, src, len, wave, lane, tid);
+    return;
+  }
+  const int64_t n16 = len / 16;  // a swizzled row is whole pieces
+  wave = __builtin_amdgcn_readfirstlane(wave);
+  for (int64_t base = (int64_t)wave * 64; base < n16; base += 64 * NW) {
+    const int64_t i = base + lane;
+    if (i < n16)
+      __builtin_amdgcn_global_load_lds((global_ptr_t)(src + 16 * sw.piece_src(i, lg_ch)), (lds_ptr_t)(dst + 16 * base),
+                                       16, 0, 0);
+  }
+}
+
 // KS = 1: one set of 4 waves; MFMA lanes of half h take channels 64h + 8s of
 // a group at step s = 0..7.  KS = 2 (two waves per SIMD): 8 waves; waves
 // 4i .. 4i + 3 form set i, which covers the whole output tile over channels
@@ -140,6 +161,8 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
   const int64_t G = K / kGroup, P2 = (G + 1) / 2;
   const int G32 = (int)G;
   const f16* packed_h = reinterpret_cast<const f16*>(packed);  // a row is K / 4 halfs
+  const ScaleSwizzle ssw(G);  // the staged scales' layout
+  const int lg_ch = __builtin_ctzll((unsigned long long)G) - 3;
 
   // This block's units.  Whole tiles: block id -> (m tile, n tile), ids b and
   // b + 8 land on one XCD and share n.  Stream-K: block b runs virtual block
@@ -238,7 +261,8 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     // would make the in-order vector-memory count unusable for the direct loads).
     unsigned char* meta = reinterpret_cast<unsigned char*>(lds) + S::PIPE_BYTES;
     const int64_t soff = (kPBN * G * 2 + 15) / 16 * 16;
-    dma_blob<S::NW>(meta, reinterpret_cast<const unsigned char*>(scales) + n0 * G * 2, rows * G * 2, wave, lane, tid);
+    dma_scales<S::NW>(meta, reinterpret_cast<const unsigned char*>(scales) + n0 * G * 2, rows * G * 2, ssw, lg_ch, wave,
+                      lane, tid);
     dma_blob<S::NW>(meta + soff, zeros + n0 * P2, rows * P2, wave, lane, tid);
     const uint16_t* msc = reinterpret_cast<const uint16_t*>(meta);
     const uint8_t* mz = meta + soff;
@@ -246,11 +270,12 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
 #pragma unroll
     for (int i = 0; i < D; ++i) issue(gl + i, i);
 
-    int mrow[S::JB];  // LDS meta row of the lane's weight rows (clamped to the tile's rows)
+    int mrow[S::JB], msx[S::JB];  // LDS meta row of the lane's weight rows (clamped to the tile's rows), scale xor
 #pragma unroll
     for (int j = 0; j < S::JB; ++j) {
       const int r = wn * S::TN + j * 32 + l32;
       mrow[j] = r < rows ? r : (int)rows - 1;
+      msx[j] = ssw.xor_of(mrow[j]);
     }
 
     f32x16 acc[S::AB][S::JB];
@@ -289,7 +314,7 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
           }
         }
         zf[j] = zero_forms((mz[mrow[j] * P2 + (g >> 1)] >> (4 * (g & 1))) & 0xFu);
-        const uint32_t sbits = msc[mrow[j] * G + g];
+        const uint32_t sbits = msc[mrow[j] * G + (g ^ msx[j])];
         sc2[j] = as_f16x2(sbits | (sbits << 16));
       }
       // Software-pipelined over the MFMA steps of the group: the A fragments

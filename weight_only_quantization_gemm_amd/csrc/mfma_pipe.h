@@ -140,4 +140,33 @@ __device__ __forceinline__ f16x8 frag16(const f16* lds_tile, int r, int c) {
   return *reinterpret_cast<const f16x8*>(lds_tile + r * 16 + ((c ^ ((r >> 3) & 1)) << 3));
 }
 
+// Layout of a block's group scales staged in LDS as [rows][G] fp16.  The
+// matrix-core kernels read one scale per row at a fixed group g, from 16 or
+// 32 consecutive rows at once; with rows of 2G bytes in a power-of-two
+// multiple of 16 bytes those reads pile onto a few of the 64 four-byte banks
+// (G = 64: every row starts on one of two banks).  Where a row is CH = G / 8
+// 16-byte pieces and CH is a power of two, piece c of row r is therefore
+// stored in slot c ^ ((r >> shift) & (CH - 1)), shift = log2 of the rows that
+// share one 256-byte bank line: 16 consecutive rows then cover 16 distinct
+// bank positions at every g.  Other G keep the plain layout (their row pitch
+// already spreads the rows, or a row is not a whole number of pieces).
+struct ScaleSwizzle {
+  int shift = 0, mask = 0;  // mask 0: plain layout
+  __device__ __forceinline__ ScaleSwizzle(int64_t G) {
+    const int64_t ch = G / 8;
+    if (G % 8 == 0 && ch > 1 && (ch & (ch - 1)) == 0) {
+      mask = (int)ch - 1;
+      const int lg = __builtin_ctzll((unsigned long long)G);  // G = 2^lg
+      shift = lg >= 7 ? 0 : 7 - lg;
+    }
+  }
+  // XOR that maps group g of row r to its staged element: r G + (g ^ xor_of(r))
+  __device__ __forceinline__ int xor_of(int r) const { return ((r >> shift) & mask) << 3; }
+  // Source 16-byte piece (counted from the blob's first row) of LDS piece v;
+  // lg_ch = log2(CH), needed only when mask != 0.
+  __device__ __forceinline__ int64_t piece_src(int64_t v, int lg_ch) const {
+    return mask == 0 ? v : (v ^ (((v >> lg_ch) >> shift) & mask));
+  }
+};
+
 }  // namespace awq

@@ -37,6 +37,7 @@
 // from memory straight into per-wave LDS rings; it is described with its code.
 #include "awq_common.h"
 #include "awq_internal.h"
+#include "mfma_pipe.h"
 
 namespace awq {
 
@@ -273,6 +274,8 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
   const int SCB = (int)(32 * RW * G), ZB = (int)(16 * RW * P2);
   f16* sl = reinterpret_cast<f16*>(smem + (size_t)W * S * STAGE);
   uint8_t* zl = reinterpret_cast<uint8_t*>(smem + (size_t)W * S * STAGE + ((SCB + 1023) & ~1023));
+  const ScaleSwizzle ssw(G);  // the staged scales' layout
+  const int lg_ch = __builtin_ctzll((unsigned long long)G) - 3;
 
   // Weight DMA source of this lane per instruction, less the group's offset (4-bit:
   // row start + quarter, and the piece's group within the chunk in dgi; 3-bit: row
@@ -337,8 +340,8 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
     const unsigned char* gz = zeros + n0 * P2;
     for (int b = wave * kWave; b < SCB / 16; b += W * kWave) {
       const int v = b + lane < SCB / 16 ? b + lane : SCB / 16 - 1;  // lanes past the end land in the padding
-      __builtin_amdgcn_global_load_lds((global_void*)(gs + v * 16), (lds_void*)(reinterpret_cast<unsigned char*>(sl) + b * 16),
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)(gs + ssw.piece_src(v, lg_ch) * 16),
+                                       (lds_void*)(reinterpret_cast<unsigned char*>(sl) + b * 16), 16, 0, 0);
     }
     for (int b = wave * kWave; b < ZB / 16; b += W * kWave) {
       const int v = b + lane < ZB / 16 ? b + lane : ZB / 16 - 1;
@@ -347,8 +350,8 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
   } else {
     for (int i = threadIdx.x; i < 16 * RW * G; i += W * kWave) {
       const int r = (int)(i / G);
-      const int64_t n = n0 + r;
-      sl[i] = scales[(n < N ? n : N - 1) * G + (i - (int64_t)r * G)];
+      const int64_t n = n0 + r, g = i - (int64_t)r * G;
+      sl[(int64_t)r * G + (g ^ ssw.xor_of(r))] = scales[(n < N ? n : N - 1) * G + g];
     }
     for (int i = threadIdx.x; i < ZB; i += W * kWave) {
       const int r = (int)(i / P2);
@@ -360,6 +363,9 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
   // the staged scales and zeros are read by every wave: all of this wave's loads land, then the barrier
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
+  int sxr[RW];  // scale xor of the lane's row in each weight tile
+#pragma unroll
+  for (int t = 0; t < RW; ++t) sxr[t] = ssw.xor_of(16 * t + nl);
   int xr[MT];  // LDS x row of the lane's A operand in x tile mt (rows past MX repeat the last)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) xr[mt] = 16 * mt + nl < MX ? 16 * mt + nl : MX - 1;
@@ -414,7 +420,7 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
           wt[t] = u32x4{wp[0], wp[1], wp[2], 0u};
         }
         zt[t] = zl[r * P2 + (gc >> 1)];
-        st[t] = sl[r * G + gc];
+        st[t] = sl[r * G + (gc ^ sxr[t])];
       }
 #pragma unroll
       for (int t = 0; t < RW; ++t) {
