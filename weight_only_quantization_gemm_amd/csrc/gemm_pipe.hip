@@ -94,7 +94,7 @@ __device__ __forceinline__ void dma_blob(unsigned char* dst, const unsigned char
 // source piece that belongs there.  Otherwise as dma_blob.
 template <int NW>
 __device__ __forceinline__ void dma_scales(unsigned char* dst, const unsigned char* __restrict__ src, int64_t len,
-                                           const ScaleSwizzle& sw, int lg_ch, int wave, int lane, int tid) {
+                                           const ScaleSwizzle& sw, int wave, int lane, int tid) {
   if (sw.mask == 0) {
     dma_blob<NW>(dst, src, len, wave, lane, tid);
     return;
@@ -104,7 +104,7 @@ __device__ __forceinline__ void dma_scales(unsigned char* dst, const unsigned ch
   for (int64_t base = (int64_t)wave * 64; base < n16; base += 64 * NW) {
     const int64_t i = base + lane;
     if (i < n16)
-      __builtin_amdgcn_global_load_lds((global_ptr_t)(src + 16 * sw.piece_src(i, lg_ch)), (lds_ptr_t)(dst + 16 * base),
+      __builtin_amdgcn_global_load_lds((global_ptr_t)(src + 16 * sw.piece_src(i)), (lds_ptr_t)(dst + 16 * base),
                                        16, 0, 0);
   }
 }
@@ -162,7 +162,6 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
   const int G32 = (int)G;
   const f16* packed_h = reinterpret_cast<const f16*>(packed);  // a row is K / 4 halfs
   const ScaleSwizzle ssw(G);  // the staged scales' layout
-  const int lg_ch = __builtin_ctzll((unsigned long long)G) - 3;
 
   // This block's units.  Whole tiles: block id -> (m tile, n tile), ids b and
   // b + 8 land on one XCD and share n.  Stream-K: block b runs virtual block
@@ -261,8 +260,8 @@ void gemm_pipe_kernel(const f16* __restrict__ x, const uint32_t* __restrict__ pa
     // would make the in-order vector-memory count unusable for the direct loads).
     unsigned char* meta = reinterpret_cast<unsigned char*>(lds) + S::PIPE_BYTES;
     const int64_t soff = (kPBN * G * 2 + 15) / 16 * 16;
-    dma_scales<S::NW>(meta, reinterpret_cast<const unsigned char*>(scales) + n0 * G * 2, rows * G * 2, ssw, lg_ch, wave,
-                      lane, tid);
+    dma_scales<S::NW>(meta, reinterpret_cast<const unsigned char*>(scales) + n0 * G * 2, rows * G * 2, ssw, wave, lane,
+                      tid);
     dma_blob<S::NW>(meta + soff, zeros + n0 * P2, rows * P2, wave, lane, tid);
     const uint16_t* msc = reinterpret_cast<const uint16_t*>(meta);
     const uint8_t* mz = meta + soff;

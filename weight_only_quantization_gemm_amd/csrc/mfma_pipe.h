@@ -151,20 +151,19 @@ __device__ __forceinline__ f16x8 frag16(const f16* lds_tile, int r, int c) {
 // bank positions at every g.  Other G keep the plain layout (their row pitch
 // already spreads the rows, or a row is not a whole number of pieces).
 struct ScaleSwizzle {
-  int shift = 0, mask = 0;  // mask 0: plain layout
-  __device__ __forceinline__ ScaleSwizzle(int64_t G) {
+  int shift = 0, mask = 0, lg_ch = 0;  // mask 0: plain layout; lg_ch = log2(CH)
+  __device__ __forceinline__ explicit ScaleSwizzle(int64_t G) {
     const int64_t ch = G / 8;
     if (G % 8 == 0 && ch > 1 && (ch & (ch - 1)) == 0) {
       mask = (int)ch - 1;
-      const int lg = __builtin_ctzll((unsigned long long)G);  // G = 2^lg
-      shift = lg >= 7 ? 0 : 7 - lg;
+      lg_ch = __builtin_ctzll((unsigned long long)ch);
+      shift = lg_ch >= 4 ? 0 : 4 - lg_ch;  // rows of 2G = 2^(lg_ch + 4) bytes, 2^shift of them per 256 bytes
     }
   }
   // XOR that maps group g of row r to its staged element: r G + (g ^ xor_of(r))
   __device__ __forceinline__ int xor_of(int r) const { return ((r >> shift) & mask) << 3; }
-  // Source 16-byte piece (counted from the blob's first row) of LDS piece v;
-  // lg_ch = log2(CH), needed only when mask != 0.
-  __device__ __forceinline__ int64_t piece_src(int64_t v, int lg_ch) const {
+  // Source 16-byte piece (counted from the blob's first row) of LDS piece v.
+  __device__ __forceinline__ int64_t piece_src(int64_t v) const {
     return mask == 0 ? v : (v ^ (((v >> lg_ch) >> shift) & mask));
   }
 };

@@ -275,7 +275,6 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
   f16* sl = reinterpret_cast<f16*>(smem + (size_t)W * S * STAGE);
   uint8_t* zl = reinterpret_cast<uint8_t*>(smem + (size_t)W * S * STAGE + ((SCB + 1023) & ~1023));
   const ScaleSwizzle ssw(G);  // the staged scales' layout
-  const int lg_ch = __builtin_ctzll((unsigned long long)G) - 3;
 
   // Weight DMA source of this lane per instruction, less the group's offset (4-bit:
   // row start + quarter, and the piece's group within the chunk in dgi; 3-bit: row
@@ -340,7 +339,7 @@ __global__ __launch_bounds__(512) void ring_kernel(const f16* __restrict__ x, co
     const unsigned char* gz = zeros + n0 * P2;
     for (int b = wave * kWave; b < SCB / 16; b += W * kWave) {
       const int v = b + lane < SCB / 16 ? b + lane : SCB / 16 - 1;  // lanes past the end land in the padding
-      __builtin_amdgcn_global_load_lds((global_void*)(gs + ssw.piece_src(v, lg_ch) * 16),
+      __builtin_amdgcn_global_load_lds((global_void*)(gs + ssw.piece_src(v) * 16),
                                        (lds_void*)(reinterpret_cast<unsigned char*>(sl) + b * 16), 16, 0, 0);
     }
     for (int b = wave * kWave; b < ZB / 16; b += W * kWave) {
